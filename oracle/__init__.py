@@ -1,0 +1,203 @@
+"""fp64 CPU oracle of the linear-attention segment transform (HYPIC).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+path (``hybrid_caching_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``pic_oracle.c`` (plain C, fp64, plain loops); this
+module only marshals numpy arrays into it.  What each call computes:
+
+* ``build``      -- per (segment, layer, head): lambda_C = sum ln(alpha),
+  That_C = prod (I - beta k k^T) (dense), plain T_C and S(C|0) from a zero
+  state.  [xix.ai HYPIC article (French), paragraph on linear layers: the
+  accumulated transition operator T_C and the zero-start final state S(C|0)]
+* ``recurrence`` -- the unsplit per-token recurrence from S_in.
+* ``compose``    -- S <- T_C S + S(C|0) along a chain of cached pairs.
+  [same paragraph: left-multiply by T_C, then add]
+* ``naive_add``  -- S_in + sum S(C|0), the ablation.  [same paragraph]
+
+Forms: 0 = scalar decay, 1 = diagonal gate, 2 = dense gated delta (GDN form).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+SCALAR, DIAG, DENSE = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pic_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libpic_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def compile_oracle(out_path: str = _LIB_PATH, src: str = _SRC, extra_flags=()) -> str:
+    """Compile the oracle's C source with gcc into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", *extra_flags, "-o", out_path, src,
+           "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def _bind(lib):
+    lib.oracle_build.restype = ctypes.c_int
+    lib.oracle_build.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, _dp,
+                                 _i64p, ctypes.c_int, _dp, _dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_recurrence.restype = ctypes.c_int
+    lib.oracle_recurrence.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, _dp, _dp, _dp,
+                                      ctypes.c_int]
+    lib.oracle_compose.restype = ctypes.c_int
+    lib.oracle_compose.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, ctypes.c_int,
+                                   _i64p, _i32p, _dp, _dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_naive_add.restype = ctypes.c_int
+    lib.oracle_naive_add.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int64, _dp, ctypes.c_int, _i64p, _i32p, _dp, _dp,
+                                     ctypes.c_int]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (compiling first if needed) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if (not os.path.exists(_LIB_PATH)
+                    or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+                compile_oracle()
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a, t=_dp):
+    if a is None:
+        return ctypes.cast(None, t)
+    return a.ctypes.data_as(t)
+
+
+def build(form, k, v, alpha, beta, offsets, *, literal=False, want_T=False, threads=None,
+          lib=None):
+    """Build the pair of every (segment, layer, head).
+
+    k: [B, N, H, dk]; v: [B, N, H, dv]; alpha: [B, N, H] (diag: [B, N, H, dk]);
+    beta: [B, N, H] or None (= 1; ignored for scalar/diag); offsets: n_seg+1 ints.
+    Returns dict with lam [n_seg, B, H(, dk)], That [n_seg, B, H, dk, dk] (dense),
+    T (plain T_C, if want_T or literal) and S [n_seg, B, H, dk, dv], all fp64.
+    """
+    lib = lib or load()
+    k, v, alpha = _f64(k), _f64(v), _f64(alpha)
+    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    B, N, H, dk = k.shape
+    dv = v.shape[3]
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n_seg = len(offs) - 1
+    lam = np.zeros((n_seg, B, H, dk) if form == DIAG else (n_seg, B, H))
+    That = np.zeros((n_seg, B, H, dk, dk)) if form == DENSE else None
+    T = np.zeros((n_seg, B, H, dk, dk)) if (want_T or literal) else None
+    S = np.zeros((n_seg, B, H, dk, dv))
+    rc = lib.oracle_build(form, int(bool(literal)), B, H, dk, dv, N, _ptr(k), _ptr(v),
+                          _ptr(alpha), _ptr(beta), _ptr(offs, _i64p), n_seg, _ptr(lam),
+                          _ptr(That), _ptr(T), _ptr(S), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_build rejected its arguments")
+    out = {"lam": lam, "S": S}
+    if That is not None:
+        out["That"] = That
+    if T is not None:
+        out["T"] = T
+    return out
+
+
+def recurrence(form, k, v, alpha, beta, S_in=None, *, threads=None, lib=None):
+    """Unsplit literal recurrence over all N tokens from S_in: returns [B, H, dk, dv]."""
+    lib = lib or load()
+    k, v, alpha = _f64(k), _f64(v), _f64(alpha)
+    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    B, N, H, dk = k.shape
+    dv = v.shape[3]
+    S_in = _f64(S_in)
+    out = np.zeros((B, H, dk, dv))
+    rc = lib.oracle_recurrence(form, B, H, dk, dv, N, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(S_in), _ptr(out), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_recurrence rejected its arguments")
+    return out
+
+
+def _chains(chain_offsets, chain_idx):
+    off = np.ascontiguousarray(np.asarray(chain_offsets, dtype=np.int64))
+    idx = np.ascontiguousarray(np.asarray(chain_idx, dtype=np.int32))
+    if idx.size == 0:
+        idx = np.zeros(1, dtype=np.int32)
+    return off, idx
+
+
+def compose(form, lam, That, S, chain_offsets, chain_idx, S_in=None, *, want_pair=False,
+            threads=None, lib=None):
+    """Compose chains of pool pairs onto S_in.
+
+    Pool: lam [P, B, H(, dk)], That [P, B, H, dk, dk] (dense; None otherwise),
+    S [P, B, H, dk, dv].  Request r applies pool entries
+    chain_idx[chain_offsets[r]:chain_offsets[r+1]] in order.  Returns S_out
+    [R, B, H, dk, dv] (and the chain's own (lam, That) if want_pair).
+    """
+    lib = lib or load()
+    lam, S = _f64(lam), _f64(S)
+    That = _f64(That) if form == DENSE else None
+    P, B, H, dk, dv = S.shape
+    off, idx = _chains(chain_offsets, chain_idx)
+    R = len(off) - 1
+    S_in = _f64(S_in)
+    S_out = np.zeros((R, B, H, dk, dv))
+    lam_out = np.zeros((R,) + lam.shape[1:]) if want_pair else None
+    That_out = np.zeros((R, B, H, dk, dk)) if (want_pair and form == DENSE) else None
+    rc = lib.oracle_compose(form, B, H, dk, dv, P, _ptr(lam), _ptr(That), _ptr(S), R,
+                            _ptr(off, _i64p), _ptr(idx, _i32p), _ptr(S_in), _ptr(S_out),
+                            _ptr(lam_out), _ptr(That_out), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_compose rejected its arguments")
+    if want_pair:
+        return S_out, lam_out, That_out
+    return S_out
+
+
+def naive_add(S, chain_offsets, chain_idx, S_in=None, *, threads=None, lib=None):
+    """S_in + sum of the chain's zero-start states: returns [R, B, H, dk, dv]."""
+    lib = lib or load()
+    S = _f64(S)
+    P, B, H, dk, dv = S.shape
+    off, idx = _chains(chain_offsets, chain_idx)
+    R = len(off) - 1
+    S_in = _f64(S_in)
+    S_out = np.zeros((R, B, H, dk, dv))
+    rc = lib.oracle_naive_add(B, H, dk, dv, P, _ptr(S), R, _ptr(off, _i64p), _ptr(idx, _i32p),
+                              _ptr(S_in), _ptr(S_out), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_naive_add rejected its arguments")
+    return S_out
