@@ -1,0 +1,218 @@
+"""ctypes binding of ``libpic.so`` (the C ABI declared in ``include/pic.h``).
+
+Argument marshalling only: every step of the segment transform runs in the
+HIP kernels of the library.  torch supplies device memory and the stream.
+There is no fallback: if the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpic.so")
+
+FORM_SCALAR, FORM_DIAG, FORM_DENSE = 0, 1, 2
+DT_F32, DT_BF16 = 0, 1
+
+STATUS = {0: "PIC_OK", -1: "PIC_ERR_NULL", -2: "PIC_ERR_DIMS", -3: "PIC_ERR_OFFSETS",
+          -4: "PIC_ERR_CHAIN", -5: "PIC_ERR_WORKSPACE", -6: "PIC_ERR_UNSUPPORTED",
+          -7: "PIC_ERR_HIP", -8: "PIC_ERR_ALIGN"}
+
+_i, _i32, _i64, _sz, _p = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/pic.h
+SIGNATURES = {
+    "pic_abi_version": (_i, []),
+    "pic_status_string": (ctypes.c_char_p, [_i]),
+    "pic_last_error": (ctypes.c_char_p, []),
+    "pic_segment_build_workspace": (_sz, [_i, _i, _i, _i, _i, _i64, _i32]),
+    "pic_validate_build": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
+                                _p, _p, _p, _sz]),
+    "pic_segment_build": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
+                               _p, _p, _p, _sz, _p]),
+    "pic_compose_workspace": (_sz, [_i32, _i64]),
+    "pic_validate_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
+                                  _sz]),
+    "pic_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _sz,
+                         _p]),
+    "pic_validate_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz]),
+    "pic_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "pic_materialize_T": (_i, [_i, _i64, _i, _p, _p, _p, _p]),
+}
+
+_LIB = None
+
+
+class PicError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)}: {detail}")
+        self.code = code
+
+
+def load(path: str = LIB_PATH):
+    """Load libpic.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m hybrid_caching_amd._build`"
+                          " (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise PicError(code, where, load().pic_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _host_i64(x):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_i32(x):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    if a.size == 0:
+        a = np.zeros(1, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _need(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _workspace(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=None):
+    """Cached pairs of every (segment, layer, head).
+
+    k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
+    [B, N, H] (diag: [B, N, H, dk]), beta: fp32 [B, N, H] or None (= 1; dense
+    only), seg_offsets: host ints [n_seg+1].  Returns dict(log_scale, T_hat
+    (dense only), S0) of fp32 device tensors laid out [n_seg, B, H, ...].
+    """
+    lib = load()
+    B, N, H, dk = k.shape
+    dv = v.shape[3]
+    if k.dtype != v.dtype or k.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k and v must both be bfloat16 or both float32")
+    dt = DT_BF16 if k.dtype == torch.bfloat16 else DT_F32
+    for t, n, d in ((k, "k", None), (v, "v", None), (alpha, "alpha", torch.float32),
+                    (beta, "beta", torch.float32), (q, "q", None)):
+        _need(t, n, d)
+    offs, offs_p = _host_i64(seg_offsets)
+    n_seg = len(offs) - 1
+    dev = k.device
+    if out is None:
+        lam_shape = (n_seg, B, H, dk) if form == FORM_DIAG else (n_seg, B, H)
+        out = {"log_scale": torch.empty(lam_shape, dtype=torch.float32, device=dev),
+               "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
+        if form == FORM_DENSE:
+            out["T_hat"] = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
+    ws_n = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
+    ws = _workspace(ws_n, dev)
+    rc = lib.pic_segment_build(form, dt, B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                               _ptr(beta), offs_p, n_seg, _ptr(out["log_scale"]),
+                               _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
+                               _stream(dev))
+    _check(rc, "pic_segment_build")
+    return out
+
+
+def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, chain_idx,
+                S_in=None, *, out=None):
+    """Fold chains of pool pairs into states: S <- e^lam That S + S0 per step.
+
+    pool_S0: [P, B, H, dk, dv]; pool_log_scale [P, B, H] (diag [P, B, H, dk]);
+    pool_T_hat [P, B, H, dk, dk] (dense; None otherwise).  Returns S_out
+    [R, B, H, dk, dv] (``out`` may be S_in for an in-place update)."""
+    lib = load()
+    P, B, H, dk, dv = pool_S0.shape
+    for t, n in ((pool_log_scale, "pool_log_scale"), (pool_T_hat, "pool_T_hat"),
+                 (pool_S0, "pool_S0"), (S_in, "S_in"), (out, "out")):
+        _need(t, n, torch.float32)
+    off, off_p = _host_i64(chain_offsets)
+    idx, idx_p = _host_i32(chain_idx)
+    R = len(off) - 1
+    dev = pool_S0.device
+    if out is None:
+        out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.pic_compose_workspace(R, int(off[-1])), dev)
+    rc = lib.pic_compose(form, B, H, dk, dv, P, _ptr(pool_log_scale), _ptr(pool_T_hat),
+                         _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in), _ptr(out), _ptr(ws),
+                         ws.numel(), _stream(dev))
+    _check(rc, "pic_compose")
+    return out
+
+
+def pic_naive_add(pool_S0, chain_offsets, chain_idx, S_in=None, *, out=None):
+    """The ablation: S_out = S_in + sum of the chain's S0 (no operator)."""
+    lib = load()
+    P, B, H, dk, dv = pool_S0.shape
+    for t, n in ((pool_S0, "pool_S0"), (S_in, "S_in"), (out, "out")):
+        _need(t, n, torch.float32)
+    off, off_p = _host_i64(chain_offsets)
+    idx, idx_p = _host_i32(chain_idx)
+    R = len(off) - 1
+    dev = pool_S0.device
+    if out is None:
+        out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.pic_compose_workspace(R, int(off[-1])), dev)
+    rc = lib.pic_naive_add(B, H, dk, dv, P, _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in),
+                           _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "pic_naive_add")
+    return out
+
+
+def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):
+    """Plain fp32 operators T_C = e^lam That for every unit of log_scale."""
+    lib = load()
+    if form == FORM_DIAG:
+        dk = log_scale.shape[-1]
+        lead = log_scale.shape[:-1]
+    elif form == FORM_DENSE:
+        dk = T_hat.shape[-1]
+        lead = log_scale.shape
+    else:
+        if dk is None:
+            raise ValueError("dk is required for the scalar form")
+        lead = log_scale.shape
+    _need(log_scale, "log_scale", torch.float32)
+    _need(T_hat, "T_hat", torch.float32)
+    n_units = 1
+    for s in lead:
+        n_units *= int(s)
+    out = torch.empty(tuple(lead) + (dk, dk), dtype=torch.float32, device=log_scale.device)
+    rc = lib.pic_materialize_T(form, n_units, dk, _ptr(log_scale), _ptr(T_hat), _ptr(out),
+                               _stream(log_scale.device))
+    _check(rc, "pic_materialize_T")
+    return out

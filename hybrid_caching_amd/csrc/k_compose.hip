@@ -1,0 +1,246 @@
+// k_compose.hip -- reuse-time kernels of the segment transform:
+//   * dense compose      S <- e^lambda_p * That_p * S + S0_p along a chain,
+//                        one 128x128x128 split-bf16 MFMA product per step;
+//   * elementwise compose (scalar / diagonal forms)  S <- e^lambda_p (.) S + S0_p;
+//   * naive add          S <- S + S0_p (the ablation);
+//   * materialize        plain fp32 T_C = e^lambda That.
+// [xix.ai HYPIC article (French), paragraph on linear layers: reuse of a cached
+//  segment left-multiplies the running state by T_C and adds S(C|0), in time
+//  independent of the segment's length; plain addition omits T.]
+#include <algorithm>
+#include "mfma_util.hpp"
+#include "pic_internal.hpp"
+
+namespace pic {
+namespace {
+
+// ---------------------------------------------------------------------------
+// elementwise compose / naive add
+// ---------------------------------------------------------------------------
+// One thread owns 4 consecutive state elements (a float4 inside one row) of
+// one chain unit (request, layer, head) and walks the chain; 256 threads per
+// block, blocks_per_unit blocks per unit.  All loads are 16-byte coalesced.
+constexpr int kElemThreads = 256;
+
+template <bool NAIVE, bool DIAG>
+__global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs a,
+                                                                    int blocks_per_unit) {
+  const int64_t BH = int64_t(a.batch) * a.heads;
+  const int nelem4 = a.dk * a.dv / 4;
+  const int64_t unit = blockIdx.x / blocks_per_unit;
+  const int e4 = (blockIdx.x % blocks_per_unit) * kElemThreads + threadIdx.x;
+  if (e4 >= nelem4) return;
+  const int64_t r = unit / BH, bh = unit % BH;
+  const int row = (e4 * 4) / a.dv;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.S_in) s = reinterpret_cast<const float4*>(a.S_in)[unit * nelem4 + e4];
+  const float4* S0 = reinterpret_cast<const float4*>(a.pool_S0);
+  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
+  int64_t c = c0;
+  // four steps at a time: issue the loads together, then fold in order
+  for (; c + 4 <= c1; c += 4) {
+    float4 x[4];
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t pu = int64_t(a.d_chain_idx[c + u]) * BH + bh;
+      x[u] = S0[pu * nelem4 + e4];
+      if (!NAIVE) sc[u] = DIAG ? a.pool_log_scale[pu * a.dk + row] : a.pool_log_scale[pu];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (NAIVE) {
+        s.x += x[u].x; s.y += x[u].y; s.z += x[u].z; s.w += x[u].w;
+      } else {
+        const float t = expf(sc[u]);
+        s.x = fmaf(t, s.x, x[u].x); s.y = fmaf(t, s.y, x[u].y);
+        s.z = fmaf(t, s.z, x[u].z); s.w = fmaf(t, s.w, x[u].w);
+      }
+    }
+  }
+  for (; c < c1; ++c) {
+    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+    const float4 x = S0[pu * nelem4 + e4];
+    if (NAIVE) {
+      s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+    } else {
+      const float t = expf(DIAG ? a.pool_log_scale[pu * a.dk + row] : a.pool_log_scale[pu]);
+      s.x = fmaf(t, s.x, x.x); s.y = fmaf(t, s.y, x.y);
+      s.z = fmaf(t, s.z, x.z); s.w = fmaf(t, s.w, x.w);
+    }
+  }
+  reinterpret_cast<float4*>(a.S_out)[unit * nelem4 + e4] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dense compose
+// ---------------------------------------------------------------------------
+// One workgroup per chain unit (request, layer, head).  Wave w owns columns
+// [32w, 32w+32) of the running state S (dk x dv) in MFMA accumulators, as
+// DKP/32 row tiles.  Each chain step stages That_p in LDS as hi/lo bf16 rows
+// (padded stride to spread LDS banks) and forms That_p * S with split-bf16
+// MFMAs (3 per 32x32x16 block), taking the B operand straight from the
+// accumulators of the old S (K order permuted to match, see mfma_util.hpp).
+// Then S <- e^lambda * (That S) + S0_p.  Sizes not a multiple of 32 are
+// zero-padded, which leaves the result unchanged.
+template <int DKP>
+__global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
+  constexpr int NT = DKP / 32;
+  constexpr int LDR = DKP + 4;  // row stride of the staged operator, in bf16
+  __shared__ __bf16 th_hi[DKP * LDR];
+  __shared__ __bf16 th_lo[DKP * LDR];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, cl = lane & 31;
+  const int dk = a.dk, dv = a.dv;
+  const int64_t BH = int64_t(a.batch) * a.heads;
+  const int64_t unit = blockIdx.x;
+  const int64_t r = unit / BH, bh = unit % BH;
+  const int n = wave * 32 + cl;  // state column of this lane
+  const bool ncol = n < dv;
+  const int64_t sdd = int64_t(dk) * dv;
+
+  f32x16 S[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = t * 32 + acc_row(q, g);
+      S[t][q] = (a.S_in && ncol && row < dk) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
+    }
+  }
+
+  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+    const float* Tp = a.pool_T_hat + pu * int64_t(dk) * dk;
+    __syncthreads();  // every wave is done reading the previous operator
+    for (int e = threadIdx.x; e < DKP * DKP / 4; e += blockDim.x) {
+      const int row = (e * 4) / DKP, col = (e * 4) % DKP;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < dk && col < dk) x = *reinterpret_cast<const float4*>(Tp + row * dk + col);
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 h = to_bf16(xs[j]);
+        th_hi[row * LDR + col + j] = h;
+        th_lo[row * LDR + col + j] = to_bf16(xs[j] - from_bf16(h));
+      }
+    }
+    __syncthreads();
+    const float scale = expf(a.pool_log_scale[pu]);
+
+    f32x16 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2 * NT; ++ks) {
+      const int t = ks >> 1, h = ks & 1;
+      bf16x8 bhi, blo;
+      split_acc_half(S[t], h, bhi, blo);
+      const int kc = 32 * t + 16 * h + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const int arow = mt * 32 + cl;
+        const bf16x8 ahi = lds_perm8(th_hi + arow * LDR, kc);
+        const bf16x8 alo = lds_perm8(th_lo + arow * LDR, kc);
+        acc[mt] = mfma32(alo, bhi, acc[mt]);
+        acc[mt] = mfma32(ahi, blo, acc[mt]);
+        acc[mt] = mfma32(ahi, bhi, acc[mt]);
+      }
+    }
+    const float* S0p = a.pool_S0 + pu * sdd;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = t * 32 + acc_row(q, g);
+        const float s0 = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+        S[t][q] = fmaf(scale, acc[t][q], s0);
+      }
+    }
+  }
+
+  if (ncol) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = t * 32 + acc_row(q, g);
+        if (row < dk) a.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// plain operator
+// ---------------------------------------------------------------------------
+__global__ void materialize_kernel(int form, int64_t n_units, int dk, const float* log_scale,
+                                   const float* T_hat, float* T_out) {
+  const int64_t total = n_units * dk * dk;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t u = e / (int64_t(dk) * dk);
+    const int i = int((e / dk) % dk), j = int(e % dk);
+    float v;
+    if (form == kDense) {
+      v = expf(log_scale[u]) * T_hat[e];
+    } else if (form == kScalar) {
+      v = (i == j) ? expf(log_scale[u]) : 0.f;
+    } else {
+      v = (i == j) ? expf(log_scale[u * dk + i]) : 0.f;
+    }
+    T_out[e] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s) {
+  const int nelem4 = a.dk * a.dv / 4;
+  const int bpu = (nelem4 + kElemThreads - 1) / kElemThreads;
+  const int64_t units = int64_t(a.n_req) * a.batch * a.heads;
+  const int64_t blocks = units * bpu;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (naive)
+    hipLaunchKernelGGL((compose_elem_kernel<true, false>), dim3(unsigned(blocks)),
+                       dim3(kElemThreads), 0, s, a, bpu);
+  else if (a.form == kDiag)
+    hipLaunchKernelGGL((compose_elem_kernel<false, true>), dim3(unsigned(blocks)),
+                       dim3(kElemThreads), 0, s, a, bpu);
+  else
+    hipLaunchKernelGGL((compose_elem_kernel<false, false>), dim3(unsigned(blocks)),
+                       dim3(kElemThreads), 0, s, a, bpu);
+  return hipGetLastError();
+}
+
+hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s) {
+  const int64_t units = int64_t(a.n_req) * a.batch * a.heads;
+  if (units <= 0) return hipSuccess;
+  if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int waves = (a.dv + 31) / 32;
+  const dim3 grid{unsigned(units), 1, 1};
+  const dim3 block{unsigned(64 * waves), 1, 1};
+  const int dkp = (a.dk + 31) / 32 * 32;
+  switch (dkp) {
+    case 32: hipLaunchKernelGGL(compose_dense_kernel<32>, grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL(compose_dense_kernel<64>, grid, block, 0, s, a); break;
+    case 96: hipLaunchKernelGGL(compose_dense_kernel<96>, grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(compose_dense_kernel<128>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
+                                const float* T_hat, float* T_out, hipStream_t s) {
+  const int64_t total = n_units * dk * dk;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(materialize_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, form, n_units,
+                     dk, log_scale, T_hat, T_out);
+  return hipGetLastError();
+}
+
+}  // namespace pic

@@ -1,0 +1,354 @@
+// pic_host.cpp -- the C ABI declared in include/pic.h: argument validation,
+// host-side planning (segment order, chain tables), workspace layout and
+// kernel launches.  Validation touches no HIP API, so it can be exercised on
+// a machine without a GPU.
+#include "pic.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <vector>
+
+#include "pic_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PIC_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+// product of non-negative sizes, or -1 on int64 overflow
+int64_t mul_sizes(std::initializer_list<int64_t> xs) {
+  int64_t p = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && p > std::numeric_limits<int64_t>::max() / x) return -1;
+    p *= x;
+  }
+  return p;
+}
+
+int check_common_dims(int batch, int heads, int dk, int dv) {
+  if (batch < 1 || heads < 1)
+    return fail(PIC_ERR_DIMS, "batch (%d) and heads (%d) must be >= 1", batch, heads);
+  if (!dim_ok(dk) || !dim_ok(dv))
+    return fail(PIC_ERR_DIMS, "dk (%d) and dv (%d) must be multiples of 16 in [16, 128]", dk,
+                dv);
+  return PIC_OK;
+}
+
+// Build workspace: offsets (n_seg+1 int64) then order (n_seg int32).
+size_t build_ws_bytes(int32_t n_seg) {
+  if (n_seg < 0) return 0;
+  return align_up(sizeof(int64_t) * (size_t(n_seg) + 1)) + align_up(sizeof(int32_t) * size_t(n_seg));
+}
+
+size_t compose_ws_bytes(int32_t n_req, int64_t total) {
+  if (n_req < 0 || total < 0) return 0;
+  return align_up(sizeof(int64_t) * (size_t(n_req) + 1)) +
+         align_up(sizeof(int32_t) * size_t(std::max<int64_t>(total, 1)));
+}
+
+int check_chains(int64_t pool_size, int32_t n_req, const int64_t* off, const int32_t* idx) {
+  if (n_req < 0) return fail(PIC_ERR_DIMS, "n_req (%d) must be >= 0", n_req);
+  if (pool_size < 0) return fail(PIC_ERR_DIMS, "pool_size must be >= 0");
+  if (!off) return fail(PIC_ERR_NULL, "chain_offsets is NULL");
+  if (off[0] != 0) return fail(PIC_ERR_CHAIN, "chain_offsets[0] = %lld, must be 0", (long long)off[0]);
+  for (int32_t r = 0; r < n_req; ++r)
+    if (off[r + 1] < off[r])
+      return fail(PIC_ERR_CHAIN, "chain_offsets decrease at request %d", r);
+  const int64_t total = off[n_req];
+  if (total > 0 && !idx) return fail(PIC_ERR_NULL, "chain_idx is NULL");
+  if (total > std::numeric_limits<int32_t>::max())
+    return fail(PIC_ERR_CHAIN, "chain too long");
+  for (int64_t s = 0; s < total; ++s)
+    if (idx[s] < 0 || int64_t(idx[s]) >= pool_size)
+      return fail(PIC_ERR_CHAIN, "chain_idx[%lld] = %d outside [0, %lld)", (long long)s, idx[s],
+                  (long long)pool_size);
+  return PIC_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// every non-null device pointer must be 16-byte aligned
+int check_align(std::initializer_list<const void*> ptrs) {
+  int i = 0;
+  for (const void* p : ptrs) {
+    if (p && misaligned(p)) return fail(PIC_ERR_ALIGN, "device pointer argument %d is not 16-byte aligned", i);
+    ++i;
+  }
+  return PIC_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PIC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pic_abi_version(void) { return PIC_ABI_VERSION; }
+
+const char* pic_status_string(int status) {
+  switch (status) {
+    case PIC_OK: return "ok";
+    case PIC_ERR_NULL: return "required pointer is NULL";
+    case PIC_ERR_DIMS: return "unsupported or inconsistent sizes";
+    case PIC_ERR_OFFSETS: return "bad segment offsets";
+    case PIC_ERR_CHAIN: return "bad chain offsets or pool index";
+    case PIC_ERR_WORKSPACE: return "workspace missing or too small";
+    case PIC_ERR_UNSUPPORTED: return "unsupported form, dtype or argument combination";
+    case PIC_ERR_HIP: return "HIP runtime error";
+    case PIC_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+const char* pic_last_error(void) { return g_last_error; }
+
+/* ------------------------------------------------------------------ build */
+
+size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int dv,
+                                   int64_t n_tokens, int32_t n_seg) {
+  (void)form; (void)batch; (void)heads; (void)dk; (void)dv; (void)n_tokens;
+  return build_ws_bytes(n_seg);
+}
+
+int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                       int64_t n_tokens, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const int64_t* seg_offsets,
+                       int32_t n_seg, const float* log_scale, const float* T_hat,
+                       const float* S0, const void* workspace, size_t workspace_bytes) {
+  (void)q;  // never read: the pair does not depend on queries
+  (void)beta;
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
+  if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
+  if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
+  const int64_t per_gate = (form == PIC_FORM_DIAG) ? dk : 1;
+  if (mul_sizes({batch, n_tokens, heads, std::max(dk, dv)}) < 0 ||
+      mul_sizes({n_seg, batch, heads, dk, std::max(dk, dv)}) < 0 ||
+      mul_sizes({batch, n_tokens, heads, per_gate}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (!seg_offsets) return fail(PIC_ERR_NULL, "seg_offsets is NULL");
+  if (n_tokens > 0 && (!k || !v || !alpha))
+    return fail(PIC_ERR_NULL, "k, v and alpha are required");
+  if (!log_scale || !S0) return fail(PIC_ERR_NULL, "log_scale and S0 outputs are required");
+  if (form == PIC_FORM_DENSE && !T_hat)
+    return fail(PIC_ERR_NULL, "T_hat output is required for the dense form");
+  if (form != PIC_FORM_DENSE && T_hat)
+    return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
+  if (seg_offsets[0] != 0)
+    return fail(PIC_ERR_OFFSETS, "seg_offsets[0] = %lld, must be 0", (long long)seg_offsets[0]);
+  for (int32_t s = 0; s < n_seg; ++s)
+    if (seg_offsets[s + 1] < seg_offsets[s])
+      return fail(PIC_ERR_OFFSETS, "seg_offsets decrease at segment %d", s);
+  if (seg_offsets[n_seg] != n_tokens)
+    return fail(PIC_ERR_OFFSETS, "seg_offsets[n_seg] = %lld, must equal n_tokens = %lld",
+                (long long)seg_offsets[n_seg], (long long)n_tokens);
+  if (int rc = check_align({k, v, alpha, beta, log_scale, T_hat, S0, workspace})) return rc;
+  const size_t need = build_ws_bytes(n_seg);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                      int64_t n_tokens, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const int64_t* seg_offsets,
+                      int32_t n_seg, float* log_scale, float* T_hat, float* S0,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_build(form, qkv_dtype, batch, heads, dk, dv, n_tokens, q, k, v,
+                                  alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0,
+                                  workspace, workspace_bytes))
+    return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Plan: visit segments longest first (ties by index), so that long units
+  // start early and short ones fill the tail of the launch.
+  std::vector<int32_t> order(n_seg);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return seg_offsets[a + 1] - seg_offsets[a] > seg_offsets[b + 1] - seg_offsets[b];
+  });
+  char* ws = static_cast<char*>(workspace);
+  int64_t* d_off = reinterpret_cast<int64_t*>(ws);
+  int32_t* d_order = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
+  hipError_t e = hipMemcpyAsync(d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copying segment offsets");
+  e = hipMemcpyAsync(d_order, order.data(), sizeof(int32_t) * size_t(n_seg),
+                     hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copying segment order");
+  pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
+                   k, v, alpha, beta, d_off, d_order, log_scale, T_hat, S0};
+  e = (form == PIC_FORM_DENSE) ? pic::launch_build_dense(a, s)
+                               : pic::launch_build_scalar_diag(a, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the build kernel");
+  return ok();
+}
+
+/* ---------------------------------------------------------------- compose */
+
+size_t pic_compose_workspace(int32_t n_req, int64_t chain_total) {
+  return compose_ws_bytes(n_req, chain_total);
+}
+
+int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                         const float* pool_log_scale, const float* pool_T_hat,
+                         const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                         const int32_t* chain_idx, const float* S_in, const float* S_out,
+                         const void* workspace, size_t workspace_bytes) {
+  (void)S_in;
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (mul_sizes({pool_size, batch, heads, dk, std::max(dk, dv)}) < 0 ||
+      mul_sizes({n_req, batch, heads, dk, dv}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (int rc = check_chains(pool_size, n_req, chain_offsets, chain_idx)) return rc;
+  const int64_t total = chain_offsets[n_req];
+  if (n_req > 0 && !S_out) return fail(PIC_ERR_NULL, "S_out is required");
+  if (total > 0 && (!pool_S0 || !pool_log_scale))
+    return fail(PIC_ERR_NULL, "pool_S0 and pool_log_scale are required");
+  if (total > 0 && form == PIC_FORM_DENSE && !pool_T_hat)
+    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense form");
+  if (form != PIC_FORM_DENSE && pool_T_hat)
+    return fail(PIC_ERR_UNSUPPORTED, "pool_T_hat must be NULL for scalar and diagonal forms");
+  if (int rc = check_align({pool_log_scale, pool_T_hat, pool_S0, S_in, S_out, workspace}))
+    return rc;
+  const size_t need = compose_ws_bytes(n_req, total);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_validate_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size,
+                           const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                           const int32_t* chain_idx, const float* S_in, const float* S_out,
+                           const void* workspace, size_t workspace_bytes) {
+  (void)S_in;
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (mul_sizes({pool_size, batch, heads, dk, dv}) < 0 ||
+      mul_sizes({n_req, batch, heads, dk, dv}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (int rc = check_chains(pool_size, n_req, chain_offsets, chain_idx)) return rc;
+  const int64_t total = chain_offsets[n_req];
+  if (n_req > 0 && !S_out) return fail(PIC_ERR_NULL, "S_out is required");
+  if (total > 0 && !pool_S0) return fail(PIC_ERR_NULL, "pool_S0 is required");
+  if (int rc = check_align({pool_S0, S_in, S_out, workspace})) return rc;
+  const size_t need = compose_ws_bytes(n_req, total);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+static int enqueue_chains(int32_t n_req, const int64_t* off, const int32_t* idx, void* workspace,
+                          hipStream_t s, const int64_t** d_off, const int32_t** d_idx) {
+  char* ws = static_cast<char*>(workspace);
+  int64_t* o = reinterpret_cast<int64_t*>(ws);
+  int32_t* i = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_req) + 1)));
+  hipError_t e = hipMemcpyAsync(o, off, sizeof(int64_t) * (size_t(n_req) + 1),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copying chain offsets");
+  const int64_t total = off[n_req];
+  if (total > 0) {
+    e = hipMemcpyAsync(i, idx, sizeof(int32_t) * size_t(total), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copying chain indices");
+  }
+  *d_off = o;
+  *d_idx = i;
+  return PIC_OK;
+}
+
+int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
+                int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
+                const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (int rc = pic_validate_compose(form, batch, heads, dk, dv, pool_size, pool_log_scale,
+                                    pool_T_hat, pool_S0, n_req, chain_offsets, chain_idx, S_in,
+                                    S_out, workspace, workspace_bytes))
+    return rc;
+  if (n_req == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t* d_off;
+  const int32_t* d_idx;
+  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
+    return rc;
+  pic::ComposeArgs a{form, batch, heads, dk, dv, pool_size, pool_log_scale, pool_T_hat,
+                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out};
+  hipError_t e = (form == PIC_FORM_DENSE) ? pic::launch_compose_dense(a, s)
+                                          : pic::launch_compose_elementwise(a, false, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
+  return ok();
+}
+
+int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const float* pool_S0,
+                  int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
+                  const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (int rc = pic_validate_naive_add(batch, heads, dk, dv, pool_size, pool_S0, n_req,
+                                      chain_offsets, chain_idx, S_in, S_out, workspace,
+                                      workspace_bytes))
+    return rc;
+  if (n_req == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t* d_off;
+  const int32_t* d_idx;
+  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
+    return rc;
+  pic::ComposeArgs a{PIC_FORM_SCALAR, batch, heads, dk, dv, pool_size, nullptr, nullptr,
+                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out};
+  hipError_t e = pic::launch_compose_elementwise(a, true, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the naive-add kernel");
+  return ok();
+}
+
+/* ------------------------------------------------------------ materialize */
+
+int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
+                      const float* T_hat, float* T_out, void* stream) {
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
+  if (!dim_ok(dk)) return fail(PIC_ERR_DIMS, "dk (%d) must be a multiple of 16 in [16, 128]", dk);
+  if (n_units < 0 || mul_sizes({n_units, dk, dk}) < 0)
+    return fail(PIC_ERR_DIMS, "bad n_units");
+  if (n_units == 0) return ok();
+  if (!log_scale || !T_out) return fail(PIC_ERR_NULL, "log_scale and T_out are required");
+  if (form == PIC_FORM_DENSE && !T_hat) return fail(PIC_ERR_NULL, "T_hat is required");
+  if (form != PIC_FORM_DENSE && T_hat)
+    return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
+  if (int rc = check_align({log_scale, T_hat, T_out})) return rc;
+  hipError_t e = pic::launch_materialize_T(form, n_units, dk, log_scale, T_hat, T_out,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the materialize kernel");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// pic_internal.hpp -- launcher interface between the C-ABI host layer and the
+// HIP kernels of the segment transform.  Internal: not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace pic {
+
+enum Form : int { kScalar = 0, kDiag = 1, kDense = 2 };
+
+// Sizes of one build call, after validation.
+struct BuildArgs {
+  int form;
+  bool qkv_bf16;
+  int batch, heads, dk, dv;
+  int64_t n_tokens;
+  int32_t n_seg;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;          // dense only, may be null (= 1)
+  const int64_t* d_offsets;   // device copy of the segment offsets [n_seg+1]
+  const int32_t* d_order;     // device: segment visiting order [n_seg]
+  float* log_scale;
+  float* T_hat;
+  float* S0;
+};
+
+// One compose / naive-add call, after validation.
+struct ComposeArgs {
+  int form;
+  int batch, heads, dk, dv;
+  int64_t pool_size;
+  const float* pool_log_scale;
+  const float* pool_T_hat;
+  const float* pool_S0;
+  int32_t n_req;
+  const int64_t* d_chain_off;  // device [n_req+1]
+  const int32_t* d_chain_idx;  // device [chain_total]
+  int64_t chain_total;
+  const float* S_in;           // may be null
+  float* S_out;
+};
+
+hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
+hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
+hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
+hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
+hipError_t launch_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
+                                const float* T_hat, float* T_out, hipStream_t s);
+
+}  // namespace pic

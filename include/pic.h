@@ -1,0 +1,206 @@
+/*
+ * pic.h -- C ABI of the linear-attention segment transform used by
+ * position-independent caching (PIC) for hybrid-attention LLMs (HYPIC),
+ * implemented for AMD MI355X (gfx950) with HIP.
+ *
+ * The method.  A linear-attention layer keeps, per head, a recurrent state
+ * S in R^{dk x dv}; every token applies a linear transition T_t to it and
+ * adds a write term:  S_t = T_t S_{t-1} + beta_t k_t v_t^T.  For a prompt
+ * segment C this library computes the cached pair
+ *     T_C    = T_L ... T_1            (product of the token transitions)
+ *     S(C|0) = final state of C started from S = 0,
+ * which depends on the segment's own tokens only, and on reuse composes
+ *     S(C1.C2) = T(C2) S(C1) + S(C2)
+ * (left-multiply the running state by T_C, then add S(C|0)), in time
+ * independent of the segment length.
+ *   [xix.ai HYPIC article (French), paragraph on linear layers: transition
+ *    operators, the composition identity, prefix independence, the failure
+ *    of plain addition under decay / gating / delta erasure.
+ *    remio.ai HYPIC article (Japanese), section on how HYPIC composes
+ *    linear-attention states: cache at first prefill, reuse by applying the
+ *    cached transition and adding the zero-start contribution; scalar,
+ *    diagonal and dense transition forms.]
+ *
+ * Transition families (the pages name RetNet/Mamba2, GLA and DeltaNet/GDN;
+ * the per-token formulas are the plainest reading of each family):
+ *     PIC_FORM_SCALAR  T_t = alpha_t I                     beta = 1
+ *     PIC_FORM_DIAG    T_t = Diag(alpha_t), alpha_t in (0,1]^dk, beta = 1
+ *     PIC_FORM_DENSE   T_t = alpha_t (I - beta_t k_t k_t^T)   (GDN form)
+ *
+ * Split operator.  At realistic gates T_C underflows fp32 within a few
+ * thousand tokens, so the operator is returned as
+ *     T_C = e^{lambda_C} * That_C,   lambda_C = sum_t ln(alpha_t)
+ * with lambda per head (scalar, dense) or per key channel (diagonal), and
+ * That_C = prod_t (I - beta_t k_t k_t^T) (dense only; I for the others).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major (last index fastest).  Device pointers
+ *     must be 16-byte aligned (PIC_ERR_ALIGN otherwise) and point to memory
+ *     of the current HIP device.  Host arrays (offsets, chains) are read during the call only.
+ *   - Layout of per-token inputs:  k, q [batch][n_tokens][heads][dk],
+ *     v [batch][n_tokens][heads][dv], alpha [batch][n_tokens][heads]
+ *     (diag: [batch][n_tokens][heads][dk]), beta [batch][n_tokens][heads].
+ *     "batch" indexes independent layers (or layer-sized groups); segments
+ *     are token ranges shared by all of them.
+ *   - Layout of pairs (a "pool" of cached segments, and the build output):
+ *     log_scale [P][batch][heads] (diag: [P][batch][heads][dk]),
+ *     T_hat [P][batch][heads][dk][dk] (dense), S0 [P][batch][heads][dk][dv].
+ *     The build writes segment s of the call at pool index s.
+ *   - States: S_in, S_out [n_req][batch][heads][dk][dv], fp32.
+ *   - Ownership: every buffer belongs to the caller.  The library keeps no
+ *     state between calls and allocates no device memory; scratch goes into
+ *     the caller's workspace (size from the *_workspace query).
+ *   - Asynchrony: a return of PIC_OK means the work is validated and
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream).  Results
+ *     are ready once the stream is synchronised.  Host arrays may be reused
+ *     as soon as the call returns.
+ *   - Errors: a negative PIC_ERR_* code.  Every argument check happens on
+ *     the host before any HIP call; on error nothing is enqueued and no
+ *     output is touched, except PIC_ERR_HIP (a launch or copy failed after
+ *     validation).  pic_last_error() gives a per-thread message.  No C++
+ *     exception crosses this interface.  Calls are thread-safe.
+ *   - Preconditions not checked on the device: 0 < alpha <= 1, finite
+ *     inputs.  Empty segments are allowed and give the identity pair
+ *     (lambda = 0, That = I, S0 = 0); an empty chain gives S_out = S_in.
+ *   - Supported sizes: dk, dv multiples of 16 in [16, 128]; heads, batch >= 1;
+ *     n_seg >= 1 (build).  Other sizes return PIC_ERR_DIMS.
+ */
+#ifndef PIC_H_
+#define PIC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PIC_ABI_VERSION 1
+
+enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2 };
+enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
+
+enum pic_status {
+  PIC_OK = 0,
+  PIC_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  PIC_ERR_DIMS = -2,        /* unsupported or inconsistent sizes                 */
+  PIC_ERR_OFFSETS = -3,     /* offsets[0] != 0, decreasing, or last != n_tokens  */
+  PIC_ERR_CHAIN = -4,       /* chain offsets bad or an index outside [0, pool)   */
+  PIC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the query result   */
+  PIC_ERR_UNSUPPORTED = -6, /* unknown form or dtype                             */
+  PIC_ERR_HIP = -7,         /* a HIP call failed after validation                */
+  PIC_ERR_ALIGN = -8        /* a device pointer is not 16-byte aligned           */
+};
+
+/* ABI version of the loaded library (PIC_ABI_VERSION at build time). */
+int pic_abi_version(void);
+
+/* Static text of a status code. */
+const char* pic_status_string(int status);
+
+/* Message of the calling thread's last failing call ("" if none). */
+const char* pic_last_error(void);
+
+/* ----------------------------------------------------------------------
+ * Segment build: the cached pair of every (segment, layer, head).
+ *   [xix.ai HYPIC article, paragraph on linear layers: at a segment's first
+ *    prefill, cache (T_C, S(C|0)); both depend only on the segment's tokens.]
+ *
+ * form        PIC_FORM_*
+ * qkv_dtype   storage type of q, k, v: PIC_DT_BF16 or PIC_DT_F32
+ * batch, heads, dk, dv, n_tokens   sizes (see layouts above)
+ * q           may be NULL; never read: the pair does not depend on queries
+ * k, v        device, qkv_dtype
+ * alpha       device fp32 gates in (0, 1]
+ * beta        device fp32 [batch][n_tokens][heads]; dense only (ignored for
+ *             scalar/diag); NULL means beta = 1
+ * seg_offsets HOST int64[n_seg+1]: segment s = tokens [off[s], off[s+1]);
+ *             off[0] = 0, non-decreasing, off[n_seg] = n_tokens
+ * log_scale   device fp32 out, lambda_C, [n_seg][batch][heads] (diag: [..][dk])
+ * T_hat       device fp32 out, That_C [n_seg][batch][heads][dk][dk]; required
+ *             for PIC_FORM_DENSE, must be NULL otherwise (That = I)
+ * S0          device fp32 out, S(C|0) [n_seg][batch][heads][dk][dv]
+ * workspace   device scratch of at least pic_segment_build_workspace() bytes
+ * stream      hipStream_t (NULL = null stream)
+ * -------------------------------------------------------------------- */
+size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int dv,
+                                   int64_t n_tokens, int32_t n_seg);
+
+int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                       int64_t n_tokens, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const int64_t* seg_offsets,
+                       int32_t n_seg, const float* log_scale, const float* T_hat,
+                       const float* S0, const void* workspace, size_t workspace_bytes);
+
+int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                      int64_t n_tokens, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const int64_t* seg_offsets,
+                      int32_t n_seg, float* log_scale, float* T_hat, float* S0,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Compose: fold chains of cached pairs into running states.
+ *   [xix.ai HYPIC article, paragraph on linear layers: on reuse,
+ *    S <- T_C S + S(C|0), i.e. S(C1.C2) = T(C2) S(C1) + S(C2), constant time
+ *    in the segment length.]
+ *
+ * For request r, chain entries chain_idx[chain_offsets[r] .. chain_offsets[r+1])
+ * are applied in order (first entry first):
+ *     S <- e^{log_scale_p} * That_p * S + S0_p
+ * per (layer, head), starting from S_in[r] (NULL = zero), result in S_out[r].
+ *
+ * pool_size      number of pool entries P
+ * pool_log_scale device fp32 [P][batch][heads] (diag: [P][batch][heads][dk])
+ * pool_T_hat     device fp32 [P][batch][heads][dk][dk]; dense only (else NULL)
+ * pool_S0        device fp32 [P][batch][heads][dk][dv]
+ * chain_offsets  HOST int64[n_req+1]: off[0] = 0, non-decreasing
+ * chain_idx      HOST int32[off[n_req]]: pool indices in [0, pool_size)
+ * S_in           device fp32 [n_req][batch][heads][dk][dv] or NULL (= 0)
+ * S_out          device fp32 out, same shape; may equal S_in (in place)
+ * -------------------------------------------------------------------- */
+size_t pic_compose_workspace(int32_t n_req, int64_t chain_total);
+
+int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                         const float* pool_log_scale, const float* pool_T_hat,
+                         const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                         const int32_t* chain_idx, const float* S_in, const float* S_out,
+                         const void* workspace, size_t workspace_bytes);
+
+int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
+                int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
+                const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* ----------------------------------------------------------------------
+ * Naive add (the ablation): S_out[r] = S_in[r] + sum over the chain of S0_p.
+ *   [xix.ai HYPIC article, paragraph on linear layers: adding zero-start
+ *    final states is exact only for plain linear attention; it leaves out
+ *    the T(C2) factor.]
+ * Arguments as for pic_compose (no operator needed).
+ * -------------------------------------------------------------------- */
+int pic_validate_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size,
+                           const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                           const int32_t* chain_idx, const float* S_in, const float* S_out,
+                           const void* workspace, size_t workspace_bytes);
+
+int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const float* pool_S0,
+                  int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
+                  const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* ----------------------------------------------------------------------
+ * Plain operator: T_out[u] = e^{log_scale[u]} * That[u] (dense), e^{lambda} I
+ * (scalar) or Diag(e^{lambda}) (diag), in fp32 (entries underflow to 0 as fp32
+ * must when lambda is very negative).  n_units pairs; layouts
+ * log_scale [n_units] (diag [n_units][dk]), T_hat [n_units][dk][dk] (dense,
+ * else NULL), T_out [n_units][dk][dk].
+ * -------------------------------------------------------------------- */
+int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
+                      const float* T_hat, float* T_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIC_H_ */

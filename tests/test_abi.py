@@ -1,0 +1,177 @@
+"""The C ABI on the host: the library loads, exports every function declared in
+include/pic.h, and its validation (which makes no HIP call) returns the
+documented status codes.  Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pic.h")
+
+OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+SCALAR, DIAG, DENSE = 0, 1, 2
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from hybrid_caching_amd import _build, _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        _build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pic_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("pic_segment_build", "pic_compose", "pic_naive_add", "pic_validate_build",
+              "pic_validate_compose", "pic_validate_naive_add", "pic_materialize_T",
+              "pic_last_error", "pic_status_string", "pic_abi_version",
+              "pic_segment_build_workspace", "pic_compose_workspace"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from hybrid_caching_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pic_abi_version() == 1
+    for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
+        s = lib.pic_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.pic_status_string(12345).decode() == "unknown status"
+
+
+# fake, aligned device addresses: validation never dereferences them
+A = 0x10000
+
+
+def P(i):
+    return ctypes.c_void_p(A * (i + 1))
+
+
+def offsets(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def vbuild(lib, form=DENSE, dt=BF16, B=1, H=2, dk=128, dv=128, N=100, offs=(0, 40, 100),
+           That=True, ws_bytes=None, k=None, alpha=None, S0=None, ws=None):
+    off, off_p = offsets(offs)
+    n_seg = len(off) - 1
+    need = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
+    return lib.pic_validate_build(form, dt, B, H, dk, dv, N, None, k or P(0), P(1),
+                                  alpha or P(2), P(3), off_p, n_seg, P(4),
+                                  P(5) if That else None, S0 or P(6), ws or P(7),
+                                  need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_build_accepts_good_arguments(lib):
+    assert vbuild(lib) == OK
+    assert vbuild(lib, form=SCALAR, That=False) == OK
+    assert vbuild(lib, form=DIAG, That=False, dt=F32, dk=16, dv=48) == OK
+    assert vbuild(lib, offs=(0, 0, 100, 100)) == OK  # empty segments are allowed
+    assert lib.pic_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"form": 7}, EUNSUP), ({"dt": 5}, EUNSUP),
+    ({"dk": 8}, EDIMS), ({"dv": 144}, EDIMS), ({"dk": 24}, EDIMS), ({"B": 0}, EDIMS),
+    ({"H": 0}, EDIMS),
+    ({"offs": (1, 40, 100)}, EOFF), ({"offs": (0, 50, 40, 100)}, EOFF),
+    ({"offs": (0, 40, 99)}, EOFF), ({"offs": (0, 40, 101)}, EOFF),
+    ({"That": False}, ENULL), ({"form": SCALAR, "That": True}, EUNSUP),
+    ({"ws_bytes": 8}, EWS),
+    ({"k": ctypes.c_void_p(A + 4)}, EALIGN), ({"S0": ctypes.c_void_p(A + 8)}, EALIGN),
+])
+def test_validate_build_rejects(lib, kw, code):
+    assert vbuild(lib, **kw) == code
+    assert lib.pic_last_error().decode() != ""
+
+
+def test_validate_build_null_pointers(lib):
+    off, off_p = offsets((0, 10))
+    ws = lib.pic_segment_build_workspace(DENSE, 1, 1, 16, 16, 10, 1)
+    args = [DENSE, BF16, 1, 1, 16, 16, 10, None, P(0), P(1), P(2), None, off_p, 1, P(4), P(5),
+            P(6), P(7), ws]
+    assert lib.pic_validate_build(*args) == OK
+    for i in (8, 9, 10, 12, 14, 15, 16, 17):  # k, v, alpha, offsets, lam, That, S0, workspace
+        bad = list(args)
+        bad[i] = None
+        rc = lib.pic_validate_build(*bad)
+        assert rc in (ENULL, EWS), (i, rc)
+
+
+def vcompose(lib, form=DENSE, B=1, H=2, dk=128, dv=128, pool=5, off=(0, 3, 3, 5),
+             idx=(4, 0, 1, 2, 3), That=True, ws_bytes=None, S_in=None):
+    o, o_p = offsets(off)
+    i = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    i_p = i.ctypes.data_as(ctypes.c_void_p) if i.size else None
+    R = len(o) - 1
+    need = lib.pic_compose_workspace(R, int(o[-1]))
+    return lib.pic_validate_compose(form, B, H, dk, dv, pool, P(0), P(1) if That else None,
+                                    P(2), R, o_p, i_p, S_in or P(3), P(4), P(5),
+                                    need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_compose(lib):
+    assert vcompose(lib) == OK
+    assert vcompose(lib, form=SCALAR, That=False) == OK
+    assert vcompose(lib, off=(0, 0), idx=()) == OK  # one empty chain
+    assert vcompose(lib, off=(0,), idx=()) == OK  # no requests
+    assert vcompose(lib, idx=(4, 0, 1, 2, 5)) == ECHAIN
+    assert vcompose(lib, idx=(4, 0, -1, 2, 3)) == ECHAIN
+    assert vcompose(lib, off=(1, 3, 3, 5)) == ECHAIN
+    assert vcompose(lib, off=(0, 3, 2, 5)) == ECHAIN
+    assert vcompose(lib, That=False) == ENULL
+    assert vcompose(lib, form=DIAG, That=True) == EUNSUP
+    assert vcompose(lib, ws_bytes=1) == EWS
+    assert vcompose(lib, dk=130) == EDIMS
+    assert vcompose(lib, S_in=ctypes.c_void_p(A + 2)) == EALIGN
+
+
+def test_validate_naive_add(lib):
+    o, o_p = offsets((0, 2))
+    i = np.array([1, 0], dtype=np.int32)
+    need = lib.pic_compose_workspace(1, 2)
+    args = [1, 2, 64, 64, 2, P(0), 1, o_p, i.ctypes.data_as(ctypes.c_void_p), None, P(1), P(2),
+            need]
+    assert lib.pic_validate_naive_add(*args) == OK
+    bad = list(args)
+    bad[4] = 1  # pool of one: index 1 out of range
+    assert lib.pic_validate_naive_add(*bad) == ECHAIN
+    bad = list(args)
+    bad[12] = 0
+    assert lib.pic_validate_naive_add(*bad) == EWS
+
+
+def test_workspace_queries_grow_with_the_plan(lib):
+    a = lib.pic_segment_build_workspace(DENSE, 1, 1, 128, 128, 100, 4)
+    b = lib.pic_segment_build_workspace(DENSE, 1, 1, 128, 128, 100, 4000)
+    assert 0 < a < b
+    assert 0 < lib.pic_compose_workspace(1, 4) < lib.pic_compose_workspace(64, 100000)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The HIP path and the oracle share no code and neither imports the other."""
+    pkg = os.path.join(ROOT, "hybrid_caching_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "pic_oracle" not in text, f
+    src = open(os.path.join(ROOT, "oracle", "pic_oracle.c"), encoding="utf-8").read()
+    assert "pic.h" not in src and "hybrid_caching_amd" not in src

@@ -1,0 +1,311 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI (via the
+ctypes binding), on seeded inputs: element by element at sizes the oracle
+finishes in seconds (several chunks, ragged tails, empty segments, every
+supported head size), bitwise on exact-arithmetic cases, and the error paths.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import DENSE, DIAG, SCALAR
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, assert_pair_close, build_both, lam_err,
+                               max_rel_units, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hybrid_caching_amd as pic
+    pic.load()  # fails loudly if the HIP library is missing
+
+
+def rand_case(form, B, H, dk, dv, offsets, seed, bf16=True, alpha=(0.9, 1.0), beta=(0.0, 1.0)):
+    """Seeded inputs with the configs' distributions (k rows L2-normalised for
+    the dense form, 1/sqrt(dk)-scaled otherwise), rounded to the storage type."""
+    rng = np.random.default_rng(seed)
+    N = int(offsets[-1])
+    k = rng.standard_normal((B, N, H, dk)).astype(np.float32)
+    if form == DENSE:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    else:
+        k *= np.float32(1 / np.sqrt(dk))
+    v = rng.standard_normal((B, N, H, dv)).astype(np.float32)
+    if form != DENSE:
+        v *= np.float32(1 / np.sqrt(dk))
+    if bf16:
+        k, v = synth.bf16_round(k), synth.bf16_round(v)
+    ashape = (B, N, H, dk) if form == DIAG else (B, N, H)
+    if form == DIAG:
+        a = (1 / (1 + np.exp(-rng.normal(3.0, 1.0, size=ashape)))).astype(np.float32)
+    else:
+        a = rng.uniform(*alpha, size=ashape).astype(np.float32)
+    b = rng.uniform(*beta, size=(B, N, H)).astype(np.float32) if form == DENSE else None
+    return k, v, a, b
+
+
+RAGGED = [0, 63, 127, 127, 300, 364]  # tails of 63 / 64 / 1 tokens, an empty segment
+
+
+# --------------------------------------------------------------------------
+# build
+# --------------------------------------------------------------------------
+
+def test_tiny_dense_fp32_config():
+    """1 layer, 2 heads, d = 16, 2 x 64 tokens, fp32: build, compose, naive add,
+    compared with the oracle and with the unsplit recurrence."""
+    w = synth.WORKLOADS["tiny_dense"]
+    x = synth.layer_inputs(w)
+    gpu, ref = build_both(DENSE, x["k"], x["v"], x["alpha"], x["beta"], x["offsets"], False)
+    assert_pair_close(gpu, ref, DENSE, TOL_F32)
+    import hybrid_caching_amd as pic
+    import torch
+    S_in = synth.random_state((1, 1, w.heads, w.dk, w.dv), seed=7)
+    for sin in (None, S_in):
+        out = pic.pic_compose(DENSE, to_dev(gpu["log_scale"]), to_dev(gpu["T_hat"]),
+                              to_dev(gpu["S0"]), [0, 2], [0, 1], to_dev(sin))
+        unsplit = oracle.recurrence(DENSE, x["k"], x["v"], x["alpha"], x["beta"],
+                                    None if sin is None else sin[0])
+        assert max_rel_units(out.cpu().numpy()[0], unsplit) <= TOL_F32
+        nv = pic.pic_naive_add(to_dev(gpu["S0"]), [0, 2], [0, 1], to_dev(sin))
+        ref_nv = oracle.naive_add(ref["S"], [0, 2], [0, 1], sin)
+        assert max_rel_units(nv.cpu().numpy(), ref_nv) <= TOL_F32
+    T = pic.pic_materialize_T(DENSE, to_dev(gpu["log_scale"]), to_dev(gpu["T_hat"]))
+    ref_T = oracle.build(DENSE, x["k"], x["v"], x["alpha"], x["beta"], x["offsets"],
+                         want_T=True)["T"]
+    torch.cuda.synchronize()
+    assert max_rel_units(T.cpu().numpy(), ref_T) <= TOL_F32
+
+
+@pytest.mark.parametrize("d", [16, 32, 48, 64, 96, 128])
+def test_dense_build_head_sizes(d):
+    k, v, a, b = rand_case(DENSE, 2, 3, d, d, RAGGED, seed=100 + d)
+    gpu, ref = build_both(DENSE, k, v, a, b, RAGGED, True)
+    assert_pair_close(gpu, ref, DENSE, TOL_BF16)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128), (32, 96)])
+def test_dense_build_unequal_dims(dk, dv):
+    k, v, a, b = rand_case(DENSE, 1, 2, dk, dv, [0, 100, 229], seed=dk + 7 * dv)
+    gpu, ref = build_both(DENSE, k, v, a, b, [0, 100, 229], True)
+    assert_pair_close(gpu, ref, DENSE, TOL_BF16)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_dense_build_fp32_inputs(d):
+    k, v, a, b = rand_case(DENSE, 1, 2, d, d, RAGGED, seed=300 + d, bf16=False)
+    gpu, ref = build_both(DENSE, k, v, a, b, RAGGED, False)
+    assert_pair_close(gpu, ref, DENSE, TOL_F32)
+
+
+def test_dense_build_beta_null_means_one():
+    k, v, a, _ = rand_case(DENSE, 1, 2, 64, 64, [0, 130], seed=5)
+    ones = np.ones(a.shape, dtype=np.float32)
+    gpu, ref = build_both(DENSE, k, v, a, None, [0, 130], True)
+    _, ref1 = build_both(DENSE, k, v, a, ones, [0, 130], True)
+    assert np.array_equal(ref["S"], ref1["S"])
+    assert_pair_close(gpu, ref1, DENSE, TOL_BF16)
+
+
+@pytest.mark.parametrize("form", [SCALAR, DIAG])
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_scalar_diag_build(form, d, bf16):
+    k, v, a, _ = rand_case(form, 2, 3, d, d, RAGGED, seed=400 + 10 * form + d, bf16=bf16)
+    gpu, ref = build_both(form, k, v, a, None, RAGGED, bf16)
+    assert_pair_close(gpu, ref, form, TOL_BF16 if bf16 else TOL_F32)
+
+
+def test_one_hot_dense_build_is_bitwise():
+    """k_t one-hot, beta = 1, alpha_t in {1, 1/2}, small integer v: every step of
+    the chunked algorithm is exact, so the pair must equal the closed form
+    S[j] = (prod of later gates) v_{t_j}, That = Diag(1[j unkeyed]) bit for bit."""
+    from tests.test_oracle_pins import one_hot_expected
+    dk = dv = 128
+    H = 2
+    cuts = [0, 63, 64 + 63, 64 + 63 + 500, 64 + 63 + 500 + 1024]
+    N = cuts[-1]
+    rng = np.random.default_rng(81)
+    j = rng.integers(0, dk, size=(N, H))
+    k = np.zeros((1, N, H, dk), dtype=np.float32)
+    k[0, np.arange(N)[:, None], np.arange(H)[None, :], j] = 1.0
+    v = rng.integers(-8, 8, size=(1, N, H, dv)).astype(np.float32)
+    alpha = np.where(rng.random((1, N, H)) < 1 / 32, 0.5, 1.0).astype(np.float32)
+    beta = np.ones((1, N, H), dtype=np.float32)
+    gpu, ref = build_both(DENSE, k, v, alpha, beta, cuts, True)
+    for s in range(len(cuts) - 1):
+        S, That, lam = one_hot_expected(k.astype(np.float64), v.astype(np.float64),
+                                        alpha.astype(np.float64), j, cuts[s], cuts[s + 1])
+        assert np.array_equal(gpu["S0"][s, 0], S.astype(np.float32)), f"segment {s}"
+        assert np.array_equal(gpu["T_hat"][s, 0], That.astype(np.float32)), f"segment {s}"
+        assert lam_err(gpu["log_scale"][s, 0], lam) <= 1e-6
+
+
+def test_query_is_not_read():
+    k, v, a, b = rand_case(DENSE, 1, 2, 64, 64, [0, 70], seed=9)
+    q1 = np.zeros_like(k)
+    q2 = np.random.default_rng(1).standard_normal(k.shape).astype(np.float32)
+    g1, _ = build_both(DENSE, k, v, a, b, [0, 70], True, q=q1)
+    g2, _ = build_both(DENSE, k, v, a, b, [0, 70], True, q=q2)
+    for key in g1:
+        assert np.array_equal(g1[key], g2[key])
+
+
+def test_build_is_deterministic():
+    import hybrid_caching_amd as pic
+    import torch
+    k, v, a, b = rand_case(DENSE, 2, 4, 128, 128, RAGGED, seed=11)
+    args = (DENSE, to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(a), to_dev(b),
+            RAGGED)
+    o1 = pic.pic_segment_build(*args)
+    o2 = pic.pic_segment_build(*args)
+    torch.cuda.synchronize()
+    for key in o1:
+        assert torch.equal(o1[key], o2[key])
+
+
+# --------------------------------------------------------------------------
+# compose / naive add
+# --------------------------------------------------------------------------
+
+def random_pool(form, P, B, H, dk, dv, seed, lam_range=(-2.0, 0.0)):
+    rng = np.random.default_rng(seed)
+    lam_shape = (P, B, H, dk) if form == DIAG else (P, B, H)
+    lam = rng.uniform(*lam_range, size=lam_shape).astype(np.float32)
+    That = None
+    if form == DENSE:
+        # products of a few reflector-like factors: norm <= 1, not symmetric
+        That = np.empty((P, B, H, dk, dk), dtype=np.float32)
+        for idx in np.ndindex(P, B, H):
+            M = np.eye(dk)
+            for _ in range(3):
+                x = rng.standard_normal(dk)
+                x /= np.linalg.norm(x)
+                M = (np.eye(dk) - rng.uniform(0, 1) * np.outer(x, x)) @ M
+            That[idx] = M
+    S = rng.standard_normal((P, B, H, dk, dv)).astype(np.float32)
+    return lam, That, S
+
+
+CHAINS = ([0, 5, 5, 12, 13], [3, 0, 7, 7, 1, 2, 3, 4, 5, 6, 8, 9, 0])
+
+
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("with_sin", [False, True])
+def test_compose_matches_oracle(form, d, with_sin):
+    import hybrid_caching_amd as pic
+    P, B, H = 10, 2, 3
+    lam, That, S = random_pool(form, P, B, H, d, d, seed=500 + d + form)
+    off, idx = CHAINS
+    R = len(off) - 1
+    S_in = synth.random_state((R, B, H, d, d), seed=3) if with_sin else None
+    out = pic.pic_compose(form, to_dev(lam), to_dev(That), to_dev(S), off, idx, to_dev(S_in))
+    ref = oracle.compose(form, lam, That, S, off, idx, S_in)
+    e = max_rel_units(out.cpu().numpy(), ref)
+    print(f"compose err {e:.3e}")
+    assert e <= TOL_F32
+    nv = pic.pic_naive_add(to_dev(S), off, idx, to_dev(S_in))
+    ref_nv = oracle.naive_add(S, off, idx, S_in)
+    assert max_rel_units(nv.cpu().numpy(), ref_nv) <= 1e-6
+
+
+def test_compose_in_place_and_empty_chains():
+    import hybrid_caching_amd as pic
+    import torch
+    lam, That, S = random_pool(DENSE, 4, 1, 2, 64, 64, seed=1)
+    off, idx = [0, 0, 2, 2], [1, 3]
+    S_in = synth.random_state((3, 1, 2, 64, 64), seed=4)
+    buf = to_dev(S_in)
+    pic.pic_compose(DENSE, to_dev(lam), to_dev(That), to_dev(S), off, idx, buf, out=buf)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    ref = oracle.compose(DENSE, lam, That, S, off, idx, S_in)
+    assert np.array_equal(got[0], S_in[0]) and np.array_equal(got[2], S_in[2])
+    assert max_rel_units(got, ref) <= TOL_F32
+
+
+def test_permutation_chain_compose_is_bitwise():
+    """That = permutation matrices, lambda = 0, small-integer states: every
+    product is exact, so the GPU must match the oracle bit for bit."""
+    import hybrid_caching_amd as pic
+    rng = np.random.default_rng(91)
+    P, B, H, d = 256, 2, 4, 128
+    That = np.zeros((P, B, H, d, d), dtype=np.float32)
+    for idx in np.ndindex(P, B, H):
+        That[idx][np.arange(d), rng.permutation(d)] = 1.0
+    lam = np.zeros((P, B, H), dtype=np.float32)
+    S = rng.integers(-4, 5, size=(P, B, H, d, d)).astype(np.float32)
+    R = 6
+    off = np.arange(R + 1) * 48
+    idx = rng.integers(0, P, size=off[-1]).astype(np.int32)
+    S_in = rng.integers(-4, 5, size=(R, B, H, d, d)).astype(np.float32)
+    out = pic.pic_compose(DENSE, to_dev(lam), to_dev(That), to_dev(S), off, idx, to_dev(S_in))
+    ref = oracle.compose(DENSE, lam, That, S, off, idx, S_in)
+    assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# split + compose equals the unsplit recurrence, with slow gates (T matters)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+def test_split_compose_equals_unsplit_slow_gates(form):
+    import hybrid_caching_amd as pic
+    import torch
+    B, H, d = 1, 4, 128
+    cuts = [0, 300, 301, 700, 1024]
+    k, v, a, b = rand_case(form, B, H, d, d, cuts, seed=700 + form, alpha=(0.999, 1.0),
+                           beta=(0.0, 0.05))
+    if form == DIAG:
+        a = np.clip(a ** 0.01, 0, 1).astype(np.float32)  # slow per-channel gates
+    dt = torch.bfloat16
+    pair = pic.pic_segment_build(form, to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(b), cuts)
+    n = len(cuts) - 1
+    out = pic.pic_compose(form, pair["log_scale"], pair.get("T_hat"), pair["S0"], [0, n],
+                          list(range(n)))
+    unsplit = oracle.recurrence(form, k, v, a, b)
+    got = out.cpu().numpy()[0]
+    # non-vacuity: the carried term is a sizeable part of the final state
+    ref_pair = oracle.build(form, k, v, a, b, cuts)
+    last = ref_pair["S"][-1]
+    carried = (unsplit - last).reshape(H, -1)
+    rho = float(np.min(np.linalg.norm(carried, axis=1)
+                       / np.linalg.norm(unsplit.reshape(H, -1), axis=1)))
+    assert rho >= 0.1, rho
+    e = max_rel_units(got, unsplit)
+    print(f"split/compose vs unsplit err {e:.3e}, rho {rho:.2f}")
+    assert e <= TOL_BF16
+    naive = pic.pic_naive_add(pair["S0"], [0, n], list(range(n))).cpu().numpy()[0]
+    assert max_rel_units(naive, unsplit) > 10 * e  # the ablation is visibly wrong
+
+
+# --------------------------------------------------------------------------
+# errors: nothing is enqueued, outputs untouched
+# --------------------------------------------------------------------------
+
+def test_errors_leave_outputs_untouched():
+    import hybrid_caching_amd as pic
+    import torch
+    k, v, a, b = rand_case(DENSE, 1, 2, 64, 64, [0, 100], seed=2)
+    out = {"log_scale": torch.full((1, 1, 2), float("nan"), device="cuda:0"),
+           "S0": torch.full((1, 1, 2, 64, 64), float("nan"), device="cuda:0"),
+           "T_hat": torch.full((1, 1, 2, 64, 64), float("nan"), device="cuda:0")}
+    dt = torch.bfloat16
+    with pytest.raises(pic.PicError) as ei:
+        pic.pic_segment_build(DENSE, to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(b),
+                              [0, 101], out=out)
+    assert ei.value.code == -3
+    torch.cuda.synchronize()
+    for t in out.values():
+        assert torch.isnan(t).all()
+    S_out = torch.full((1, 1, 2, 64, 64), float("nan"), device="cuda:0")
+    with pytest.raises(pic.PicError) as ei:
+        pic.pic_compose(DENSE, out["log_scale"], out["T_hat"], out["S0"], [0, 1], [1], out=S_out)
+    assert ei.value.code == -4
+    torch.cuda.synchronize()
+    assert torch.isnan(S_out).all()
