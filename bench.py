@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of the segment transform on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  plan + build the cached pair of every (segment, layer, head)  [dense GDN form]
+  + compose the segments in prompt order into one running state per layer
+  + the naive-add ablation over the same chain.
+Default workload: a Qwen3.5-35B-A3B-like linear-attention stack -- 30 linear
+layers x 32 heads, d_k = d_v = 128, fp32 state (2 MiB per layer), bf16 k/v
+with L2-normalised keys, beta ~ U(0,1), alpha ~ U(0.9,1) -- and a 128K-token
+prompt made of 32 segments of 4096 tokens, all built in one call.
+
+Prints one JSON line.  ``value`` is prompt tokens per second of the whole
+step (inputs resident in HBM before timing starts).  Per-kernel durations are
+measured with HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "segment build tokens/s + state composes/s (dense delta, H=32, d=128); % roofline"
+CHUNK = 64
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def dense_build_flops_per_token_head(d: int, c: int = CHUNK) -> float:
+    """Algorithmic flops of the chunked dense build per token and head:
+    the chunk's UT work 6*c*d (K K^T, U = A K, W = A V, each 2*c*d per token)
+    plus the chain update 8*d^2 (U That, K^T N, U S, K^T M, each 2*d^2 per
+    token)."""
+    return 6.0 * c * d + 8.0 * d * d
+
+
+def build_bytes(n_tok, layers, heads, dk, dv, n_seg, qkv_bytes=2):
+    """Algorithmic bytes of one build: k and v once, alpha and beta once, the
+    pairs out (That, S0, lambda)."""
+    inp = n_tok * layers * heads * ((dk + dv) * qkv_bytes + 8)
+    out = n_seg * layers * heads * (dk * dk + dk * dv + 1) * 4
+    return inp + out
+
+
+def compose_bytes(steps, layers, heads, dk, dv, n_req=1):
+    """One compose: That_p and S0_p read per step, the state read and written once."""
+    return steps * layers * heads * (dk * dk + dk * dv + 1) * 4 + 2 * n_req * layers * heads * dk * dv * 4
+
+
+def naive_bytes(steps, layers, heads, dk, dv, n_req=1):
+    return steps * layers * heads * dk * dv * 4 + n_req * layers * heads * dk * dv * 4
+
+
+def cpu_baseline(w, seconds: float, threads: int):
+    """The fp64 oracle (specialised path) on a bounded sample of the same
+    workload: whole (layer, head, segment) units of 4096 tokens, drawn with the
+    same distributions, as many as fit the time budget.  Returns prompt
+    tokens/s extrapolated to all layers and heads."""
+    import oracle
+    import synth
+    lib = oracle.load()
+    L = w.seg_lens[0]
+    # one (layer, segment) block: all heads; keep `threads` heads of it
+    units_done = 0
+    t0 = time.perf_counter()
+    rounds = 0
+    while True:
+        x = synth.segment_inputs(w, layer=rounds % w.layers, seg_id=rounds % w.n_seg, L=L)
+        h = min(threads, w.heads)
+        k = x["k"][None, :, :h]
+        v = x["v"][None, :, :h]
+        a = x["alpha"][None, :, :h]
+        b = x["beta"][None, :, :h]
+        oracle.build(w.form, k, v, a, b, [0, L], threads=threads, lib=lib)
+        units_done += h
+        rounds += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    token_units_per_s = units_done * L / dt          # token x (layer, head) per second
+    tokens_per_s = token_units_per_s / (w.layers * w.heads)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{units_done} (layer, head, segment) units of {L} tokens on the fp64 "
+                       f"oracle's specialised path in {dt:.1f} s; prompt tokens/s extrapolated "
+                       f"to {w.layers} layers x {w.heads} heads (build only)")}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="dense_30L_32x4096")
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = synth.scaled(w, layers=args.layers, name=w.name)
+    if w.form != synth.DENSE:
+        print("bench.py: the headline workload is the dense form", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pic.load()
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    offsets = w.offsets()
+
+    # ---- inputs resident in HBM
+    qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    k = torch.empty((B, N, H, dk), dtype=qdt, device=dev)
+    v = torch.empty((B, N, H, dv), dtype=qdt, device=dev)
+    alpha = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    for layer in range(B):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        k[layer].copy_(x["k"])
+        v[layer].copy_(x["v"])
+        alpha[layer].copy_(x["alpha"])
+        beta[layer].copy_(x["beta"])
+        del x
+    pairs = {"log_scale": torch.empty((n_seg, B, H), dtype=torch.float32, device=dev),
+             "T_hat": torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev),
+             "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
+    S_out = torch.empty((1, B, H, dk, dv), dtype=torch.float32, device=dev)
+    S_naive = torch.empty_like(S_out)
+    chain_off, chain_idx = [0, n_seg], list(range(n_seg))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record=None):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs)
+        e1.record(stream)
+        pic.pic_compose(w.form, pairs["log_scale"], pairs["T_hat"], pairs["S0"], chain_off,
+                        chain_idx, None, out=S_out)
+        e2.record(stream)
+        pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
+        e3.record(stream)
+        if record is not None:
+            record.append((e0, e1, e2, e3))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_build = np.mean([a.elapsed_time(b) for a, b, _, _ in recs]) / 1e3
+    t_comp = np.mean([b.elapsed_time(c) for _, b, c, _ in recs]) / 1e3
+    t_naive = np.mean([c.elapsed_time(d) for _, _, c, d in recs]) / 1e3
+    t_step_ev = np.mean([a.elapsed_time(d) for a, _, _, d in recs]) / 1e3
+    t_step = wall / args.steps
+
+    flops = dense_build_flops_per_token_head(dk) * N * B * H
+    achieved_tf = flops / t_build / 1e12
+    composes = n_seg * B  # pairs applied to a running state, per layer (all heads)
+    cb = compose_bytes(n_seg, B, H, dk, dv)
+    nb = naive_bytes(n_seg, B, H, dk, dv)
+    out = {
+        "metric": METRIC,
+        "value": N / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state, bf16 k/v, split-bf16 MFMA",
+        "data": "synthetic",
+        "config": {"workload": w.name, "form": "dense_gdn", "layers": B, "heads": H, "dk": dk,
+                   "dv": dv, "segments": n_seg, "segment_tokens": int(w.seg_lens[0]),
+                   "prompt_tokens": N, "chunk": CHUNK},
+        "build_tokens_per_s": N / t_build,
+        "composes_per_s": composes / t_comp,
+        "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3,
+               "step_events": t_step_ev * 1e3},
+        "roofline": {"kernel": "build_dense_kernel", "bound": "mfma", "achieved": achieved_tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tf / PEAK_BF16_TFLOPS, "traffic": None},
+        "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
+                             "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS},
+        "roofline_naive_add": {"bound": "hbm", "achieved": nb / t_naive / 1e9,
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
+        "build_hbm_gbs": build_bytes(N, B, H, dk, dv, n_seg) / t_build / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,5 +1,7 @@
 """Shared helpers of the GPU parity tests: move seeded inputs to the device,
 run the oracle on the same values, compare."""
+import os
+
 import numpy as np
 
 import oracle
@@ -67,15 +69,26 @@ def build_both(form, k, v, alpha, beta, offsets, bf16, q=None):
     return gpu, ref
 
 
+def report(line: str):
+    """Print a measured error and, if PIC_PARITY_LOG names a file, append it there."""
+    print(line)
+    path = os.environ.get("PIC_PARITY_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a", encoding="utf-8") as f:
+            f.write(f"{test}: {line}\n")
+
+
 def assert_pair_close(gpu, ref, form, tol):
     e_s = max_rel_units(gpu["S0"], ref["S"])
     e_l = lam_err(gpu["log_scale"], ref["lam"])
     msg = f"S0 err {e_s:.3e}, lambda err {e_l:.3e}"
+    e_t = 0.0
     if form == oracle.DENSE:
         e_t = max_rel_units(gpu["T_hat"], ref["That"])
         msg += f", That err {e_t:.3e}"
-        assert e_t <= tol, msg
-    print(msg)
+    report(msg)
+    assert e_t <= tol, msg
     assert e_s <= tol, msg
     assert e_l <= 1e-4, msg
     return msg

@@ -1,0 +1,180 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times (one build call for all segments, layers and heads; one compose call
+per chain batch).
+
+* scalar decay, 32 heads x d=128, 8 x 2048 tokens: every unit against the oracle;
+* diagonal gates, 32 heads x d=128, 16 x 4096 tokens: every unit;
+* dense GDN, 30 layers x 32 heads x d=128, 32 x 4096 tokens (128K prompt):
+  sampled units (the oracle rebuilds them one by one from the same inputs)
+  and sampled composed chains;
+* the slow-gate variants, where the carried term T(C2) S(C1) is a sizeable
+  part of the state, so composition really exercises T.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import (TOL_BF16, assert_pair_close, lam_err, max_rel_units, report,
+                               to_dev)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hybrid_caching_amd as pic
+    pic.load()
+
+
+def rho_of(composed_ref, last_S):
+    """min over units of ||carried|| / ||state|| with carried = state - S(C_last|0)."""
+    a = np.asarray(composed_ref, np.float64).reshape(-1, composed_ref.shape[-2] * composed_ref.shape[-1])
+    b = np.asarray(last_S, np.float64).reshape(a.shape)
+    return float(np.min(np.linalg.norm(a - b, axis=1) / np.linalg.norm(a, axis=1)))
+
+
+@pytest.mark.parametrize("name", ["scalar_8x2048", "scalar_8x2048_slow", "diag_16x4096",
+                                  "diag_16x4096_slow"])
+def test_scalar_diag_full_workload(name):
+    import hybrid_caching_amd as pic
+    import torch
+    w = synth.WORKLOADS[name]
+    x = synth.layer_inputs(w)
+    dt = torch.bfloat16
+    pair = pic.pic_segment_build(w.form, to_dev(x["k"], dt), to_dev(x["v"], dt),
+                                 to_dev(x["alpha"]), None, x["offsets"])
+    n = w.n_seg
+    comp = pic.pic_compose(w.form, pair["log_scale"], None, pair["S0"], [0, n], list(range(n)))
+    naive = pic.pic_naive_add(pair["S0"], [0, n], list(range(n)))
+    torch.cuda.synchronize()
+    gpu = {key: val.cpu().numpy() for key, val in pair.items()}
+    ref = oracle.build(w.form, x["k"], x["v"], x["alpha"], None, x["offsets"])
+    assert_pair_close(gpu, ref, w.form, TOL_BF16)
+    ref_c = oracle.compose(w.form, ref["lam"], None, ref["S"], [0, n], list(range(n)))
+    e = max_rel_units(comp.cpu().numpy(), ref_c)
+    rho = rho_of(ref_c[0], ref["S"][-1])
+    report(f"{name}: compose err {e:.3e}, rho {rho:.3f}")
+    assert e <= TOL_BF16
+    if name.endswith("_slow"):
+        assert rho >= 0.1
+    ref_n = oracle.naive_add(ref["S"], [0, n], list(range(n)))
+    assert max_rel_units(naive.cpu().numpy(), ref_n) <= TOL_BF16
+
+
+def _dense_full(name, layers, samples, chains):
+    """Build the dense stack on the GPU from device-drawn inputs, then check
+    sampled (layer, head, segment) units and sampled composed (layer, head)
+    chains against the oracle run on the same input values."""
+    import hybrid_caching_amd as pic
+    import torch
+    w = synth.WORKLOADS[name]
+    if layers is not None:
+        w = synth.scaled(w, layers=layers, name=w.name)
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    dev = torch.device("cuda:0")
+    k = torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=dev)
+    alpha = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    for layer in range(B):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        k[layer].copy_(x["k"])
+        v[layer].copy_(x["v"])
+        alpha[layer].copy_(x["alpha"])
+        beta[layer].copy_(x["beta"])
+    offsets = w.offsets()
+    pair = pic.pic_segment_build(w.form, k, v, alpha, beta, offsets)
+    comp = pic.pic_compose(w.form, pair["log_scale"], pair["T_hat"], pair["S0"], [0, n_seg],
+                           list(range(n_seg)))
+    naive = pic.pic_naive_add(pair["S0"], [0, n_seg], list(range(n_seg)))
+    torch.cuda.synchronize()
+
+    def unit_inputs(layer, head, s0, s1):
+        sl = slice(int(offsets[s0]), int(offsets[s1]))
+        f = lambda t: t[layer, sl, head].float().cpu().numpy()[None, :, None]
+        return f(k), f(v), f(alpha), f(beta)
+
+    rng = np.random.default_rng(2024)
+    for (layer, head, seg) in samples(rng, B, H, n_seg):
+        kk, vv, aa, bb = unit_inputs(layer, head, seg, seg + 1)
+        L = kk.shape[1]
+        ref = oracle.build(w.form, kk, vv, aa, bb, [0, L])
+        gpu = {"S0": pair["S0"][seg, layer, head].cpu().numpy()[None, None, None],
+               "T_hat": pair["T_hat"][seg, layer, head].cpu().numpy()[None, None, None],
+               "log_scale": pair["log_scale"][seg, layer, head].cpu().numpy()[None, None, None]}
+        report(f"{name} unit (layer {layer}, head {head}, seg {seg}):")
+        assert_pair_close(gpu, ref, w.form, TOL_BF16)
+    for (layer, head) in chains(rng, B, H):
+        kk, vv, aa, bb = unit_inputs(layer, head, 0, n_seg)
+        offs = offsets
+        ref = oracle.build(w.form, kk, vv, aa, bb, offs)
+        ref_c = oracle.compose(w.form, ref["lam"], ref["That"], ref["S"], [0, n_seg],
+                               list(range(n_seg)))
+        got = comp[0, layer, head].cpu().numpy()
+        e = max_rel_units(got, ref_c[0, 0, 0])
+        rho = rho_of(ref_c[0], ref["S"][-1])
+        en = max_rel_units(naive[0, layer, head].cpu().numpy(),
+                           oracle.naive_add(ref["S"], [0, n_seg], list(range(n_seg)))[0, 0, 0])
+        report(f"{name} chain (layer {layer}, head {head}): compose err {e:.3e}, rho {rho:.3f}, "
+               f"naive-add err {en:.3e}")
+        assert e <= TOL_BF16 and en <= TOL_BF16
+        if name.endswith("_slow"):
+            assert rho >= 0.1
+    return pair
+
+
+def test_dense_full_workload_sampled():
+    def samples(rng, B, H, n_seg):
+        fixed = [(0, 0, 0), (B - 1, H - 1, n_seg - 1), (B // 2, 7, n_seg // 2)]
+        extra = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_seg)))
+                 for _ in range(3)]
+        return fixed + extra
+
+    def chains(rng, B, H):
+        return [(B - 1, 3)]
+
+    _dense_full("dense_30L_32x4096", None, samples, chains)
+
+
+def test_dense_slow_gates_full_length_sampled():
+    """Slow gates at the full 32 x 4096 prompt (2 layers): composition of 32
+    built segments must match the oracle with a sizeable carried term."""
+    def samples(rng, B, H, n_seg):
+        return [(1, 5, 3)]
+
+    def chains(rng, B, H):
+        return [(0, 0)]
+
+    _dense_full("dense_30L_32x4096_slow", 2, samples, chains)
+
+
+def test_all_segments_empty():
+    """n_tokens = 0 with empty segments: identity pairs, zero states."""
+    import hybrid_caching_amd as pic
+    import torch
+    dev = torch.device("cuda:0")
+    k = torch.zeros((2, 0, 3, 64), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros((2, 0, 3, 64), dtype=torch.bfloat16, device=dev)
+    a = torch.zeros((2, 0, 3), dtype=torch.float32, device=dev)
+    pair = pic.pic_segment_build(2, k, v, a, None, [0, 0, 0])
+    torch.cuda.synchronize()
+    assert torch.all(pair["S0"] == 0) and torch.all(pair["log_scale"] == 0)
+    eye = torch.eye(64, device=dev).expand_as(pair["T_hat"])
+    assert torch.equal(pair["T_hat"], eye)
+
+
+def test_many_short_segments():
+    """Hundreds of segments of 1..200 tokens (ragged, every chunk tail)."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 200, size=300)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    w = synth.scaled(synth.WORKLOADS["dense_30L_32x4096"], layers=1, heads=2,
+                     seg_lens=tuple(int(x) for x in lens), name="dense_many_short")
+    x = synth.layer_inputs(w)
+    from tests.gpu_helpers import build_both
+    gpu, ref = build_both(w.form, x["k"], x["v"], x["alpha"], x["beta"], offs, True)
+    assert_pair_close(gpu, ref, w.form, TOL_BF16)
