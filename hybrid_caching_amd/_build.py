@@ -17,7 +17,8 @@ OBJ_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpic.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_scalar_diag.hip"]
+SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_pipe.hip",
+           "k_build_scalar_diag.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",

@@ -415,13 +415,8 @@ hipError_t launch_dense_t(const BuildArgs& a, hipStream_t s) {
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s) {
   const int d = a.dk > a.dv ? a.dk : a.dv;
   const int dp = d <= 32 ? 32 : (d <= 64 ? 64 : 128);
-  if (a.qkv_bf16) {
-    switch (dp) {
-      case 32: return launch_dense_t<32, true>(a, s);
-      case 64: return launch_dense_t<64, true>(a, s);
-      default: return launch_dense_t<128, true>(a, s);
-    }
-  }
+  // bf16 inputs take the software-pipelined kernel (k_build_dense_pipe.hip)
+  if (a.qkv_bf16) return launch_build_dense_pipe(a, s);
   switch (dp) {
     case 32: return launch_dense_t<32, false>(a, s);
     case 64: return launch_dense_t<64, false>(a, s);

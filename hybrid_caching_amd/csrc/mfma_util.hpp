@@ -102,6 +102,38 @@ __device__ __forceinline__ bf16x8 lds_perm8(const __bf16* row, int c0) {
   return r;
 }
 
+// v from another lane by a DPP pattern; lanes without a source (or in rows
+// outside ROW_MASK) get 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum of s over aligned groups of N lanes (N = 1, 2, 4 or 8), every lane of
+// the group receiving the sum; lane exchanges on DPP (no LDS round trip).
+template <int N>
+__device__ __forceinline__ float group_sum(float s) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+  if (N >= 2) s += dpp_f<0xB1>(s);   // partner lane ^ 1: quad_perm(1, 0, 3, 2)
+  if (N >= 4) s += dpp_f<0x4E>(s);   // partner lane ^ 2: quad_perm(2, 3, 0, 1)
+  if (N >= 8) s += dpp_f<0x141>(s);  // lane 7 - i of each half-row: the other quad
+  return s;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes, then row broadcasts of lanes 15
+// and 31 into the later rows.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x += dpp_f<0x111>(x);         // row_shr:1
+  x += dpp_f<0x112>(x);         // row_shr:2
+  x += dpp_f<0x114>(x);         // row_shr:4
+  x += dpp_f<0x118>(x);         // row_shr:8
+  x += dpp_f<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x += dpp_f<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // 8 consecutive bf16 (16 bytes) from LDS
 __device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);

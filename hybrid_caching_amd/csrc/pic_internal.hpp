@@ -46,6 +46,7 @@ struct ComposeArgs {
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
+hipError_t launch_build_dense_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
 hipError_t launch_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
