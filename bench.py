@@ -202,7 +202,7 @@ def main(argv=None):
         "composes_per_s": composes / t_comp,
         "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3,
                "step_events": t_step_ev * 1e3},
-        "roofline": {"kernel": "build_dense_kernel", "bound": "mfma", "achieved": achieved_tf,
+        "roofline": {"kernel": "build_dense_pipe_kernel", "bound": "mfma", "achieved": achieved_tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tf / PEAK_BF16_TFLOPS, "traffic": None},
         "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
