@@ -10,7 +10,7 @@
 // hold 32-column strips of S, waves [DP/32, 2*DP/32) strips of That, in MFMA
 // accumulators for the whole segment.  Per chunk of 64 tokens:
 //   1  stage K (row-major and transposed) and V^T into LDS from registers,
-//      gates (log2-prefix scan, one wave); prefetch the next chunk
+//      gates (DPP prefix scan of log2 alpha, one wave); prefetch the next chunk
 //   2  L = diag(beta) strictly-lower(K K^T)              (MFMA, exact in bf16)
 //   3  X = (I + L)^{-1}, 16x16 diagonal blocks: lanes share a column and
 //      combine partial sums with DPP lane exchanges
@@ -22,6 +22,12 @@
 //   7  M += U (sigma X) with sigma = -gamma (S) or -1 (That); S *= gamma;
 //      X += K^T M                                          (split-bf16 MFMA)
 // so that S <- gamma S + K^T (W - gamma U S) and That <- That - K^T (U That).
+//
+// Software pipeline.  Steps 1-6 of a chunk do not depend on the running
+// pair, so step 7 of chunk ci-1 is cut into four slices that run in the
+// phases of steps 1-4 of chunk ci (K^T is double-buffered by chunk parity);
+// the matrix-core work of one chunk fills the latency of the next one's
+// preparation.  The last chunk's step 7 runs after the loop.
 #include "mfma_util.hpp"
 #include "pic_internal.hpp"
 
@@ -46,14 +52,14 @@ struct PipeLds {
   static constexpr int R_USED = YM + 512 * 4;
   static constexpr int A_BYTES = C * A_LD * 2;  // one split part
   static constexpr int R_BYTES = (R_USED > 4 * A_BYTES) ? R_USED : 4 * A_BYTES;
-  static constexpr int KT = R_BYTES;
-  static constexpr int VT = KT + DP * KT_LD * 2;
+  static constexpr int KT = R_BYTES;                  // K^T, two buffers (chunk parity)
+  static constexpr int VT = KT + 2 * DP * KT_LD * 2;
   static constexpr int UH = VT + DP * KT_LD * 2;
   static constexpr int UL = UH + C * U_LD * 2;
   static constexpr int XM = UL + C * U_LD * 2;
   static constexpr int GB = XM + C * X_LD * 4;
   static constexpr int GR = GB + C * 4;
-  static constexpr int GG = GR + C * 4;
+  static constexpr int GG = GR + C * 4;  // gamma per chunk parity
   static constexpr int TOTAL = GG + 16;
   static_assert(KT % 16 == 0 && VT % 16 == 0 && UH % 16 == 0 && XM % 16 == 0, "alignment");
   static_assert(A_BYTES % 16 == 0 && LM % 16 == 0, "alignment");
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
   static_assert((C / 2) * (DP / 8) == NTH, "one staging item per thread");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   __bf16* Kr = reinterpret_cast<__bf16*>(smem + L::KR);
-  __bf16* Kt = reinterpret_cast<__bf16*>(smem + L::KT);
+  __bf16* Kt0 = reinterpret_cast<__bf16*>(smem + L::KT);
   __bf16* Vt = reinterpret_cast<__bf16*>(smem + L::VT);
   __bf16* Uh = reinterpret_cast<__bf16*>(smem + L::UH);
   __bf16* Ul = reinterpret_cast<__bf16*>(smem + L::UL);
@@ -167,16 +173,65 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
     return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
   };
 
-  f32x16 P[2];  // M of the chunk (seeded with W or 0)
+  f32x16 P[2];  // M of the chunk in flight (seeded with W or 0)
+
+  // step 7 slices for chunk pc (its U in LDS, its K^T in buffer pc & 1)
+  auto chain_um = [&](int mt, int pc) {  // P[mt] += U_mt (sigma X)
+    const int lane = opaque(threadIdx.x) & 63, g = lane >> 5, cl = lane & 31;
+    const float sigma = s_wave ? -gg[pc & 1] : -1.f;
+#pragma unroll
+    for (int ks = 0; ks < 2 * NT; ++ks) {
+      const int t = ks >> 1, hh = ks & 1;
+      float xv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = sigma * X[t][8 * hh + j];
+      bf16x8 bhi, blo;
+      split8(xv, bhi, blo);
+      const int kc = 32 * t + 16 * hh + 4 * g;
+      const bf16x8 ah = lds_perm8(Uh + (mt * 32 + cl) * ULD, kc);
+      const bf16x8 al = lds_perm8(Ul + (mt * 32 + cl) * ULD, kc);
+      P[mt] = mfma32(al, bhi, P[mt]);
+      P[mt] = mfma32(ah, blo, P[mt]);
+      P[mt] = mfma32(ah, bhi, P[mt]);
+    }
+  };
+  auto chain_ktm = [&](int mt, int pc) {  // X += K^T M_mt  (S first scaled by gamma)
+    const int lane = opaque(threadIdx.x) & 63, g = lane >> 5, cl = lane & 31;
+    const __bf16* Ktp = Kt0 + (pc & 1) * (DP * KT);
+    if (mt == 0 && s_wave) {
+      const float gam = gg[pc & 1];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) X[t] *= gam;
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 bhi, blo;
+      split_acc_half(P[mt], hh, bhi, blo);
+      const int kc = 32 * mt + 16 * hh + 4 * g;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 kh = lds_perm8(Ktp + (t * 32 + cl) * KT, kc);
+        X[t] = mfma32(kh, blo, X[t]);
+        X[t] = mfma32(kh, bhi, X[t]);
+      }
+    }
+  };
+
   if (n_chunks > 0) prefetch(0);
 #pragma unroll 1
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int tid = opaque(threadIdx.x), lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, cl = lane & 31;
     const int strip = wave % NT;
+    const bool chain = ci > 0;  // step 7 of chunk ci-1 rides along
+    __bf16* Kt = Kt0 + (ci & 1) * (DP * KT);
 
     // ---------------- 1: stage chunk ci, gates; prefetch chunk ci+1
     __syncthreads();  // the previous chunk is done with every LDS buffer
+    // The S wave and the That wave sharing a SIMD take their phase work in
+    // opposite orders (matrix slice first / preparation first), so that one's
+    // MFMAs overlap the other's VALU and LDS work.
+    if (chain && s_wave) chain_um(0, ci - 1);
     {
       const int t0 = 2 * (lane & 31), i0 = 8 * (2 * wave + (lane >> 5));
       const int64_t c0 = t_begin + int64_t(ci) * C;
@@ -199,14 +254,16 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
       gb[lane] = lane < len ? pb : 0.f;
       gr[lane] = exp2f(bend - x);
-      if (lane == 0) gg[0] = exp2f(bend);
+      if (lane == 0) gg[ci & 1] = exp2f(bend);
       lam += bend;
     }
     if (ci + 1 < n_chunks) prefetch(ci + 1);
+    if (chain && !s_wave) chain_um(0, ci - 1);
 
-    // ---------------- 2: L = diag(beta) strictly-lower(K K^T)
+    // ---------------- 2: L = diag(beta) strictly-lower(K K^T)  (That waves)
     __syncthreads();
-    for (int tile = wave; tile < 3; tile += NW) {
+    if (chain && s_wave) chain_um(1, ci - 1);
+    for (int tile = (wave + NT) % NW; tile < 3; tile += NW) {
       const int mt = (tile == 0) ? 0 : 1, nt = (tile == 2) ? 1 : 0;
       f32x16 acc = zero16();
 #pragma unroll
@@ -219,12 +276,15 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int r = mt * 32 + acc_row(q, g), c = nt * 32 + cl;
-        Lm[r * XL + c] = (c < r) ? gb[r] * acc[q] : 0.f;
+        const float bv = gb[r];
+        Lm[r * XL + c] = (c < r) ? bv * acc[q] : 0.f;
       }
     }
+    if (chain && !s_wave) chain_um(1, ci - 1);
 
     // ---------------- 3: 16x16 diagonal blocks of X by substitution
     __syncthreads();
+    if (chain && s_wave) chain_ktm(0, ci - 1);
     {
       const int col = tid / TPC, p = tid % TPC;
       const int o = 16 * (col >> 4), cc = col & 15;
@@ -249,9 +309,11 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
 #pragma unroll
       for (int j = 0; j < JPT; ++j) Xm[(o + p + TPC * j) * XL + o + cc] = xo[j];
     }
+    if (chain && !s_wave) chain_ktm(0, ci - 1);
 
     // ---------------- 4: 16x16 merges (Y = L X, then X = -X Y)
     __syncthreads();
+    if (chain && s_wave) chain_ktm(1, ci - 1);
     for (int e = tid; e < 512; e += NTH) {
       const int inst = e >> 8, r = (e >> 4) & 15, c = e & 15;
       const int orow = inst ? 48 : 16, ocol = inst ? 32 : 0;
@@ -261,6 +323,7 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
         s = fmaf(Lm[(orow + r) * XL + ocol + q], Xm[(ocol + q) * XL + ocol + c], s);
       Ym[e] = s;
     }
+    if (chain && !s_wave) chain_ktm(1, ci - 1);
     __syncthreads();
     for (int e = tid; e < 512; e += NTH) {
       const int inst = e >> 8, r = (e >> 4) & 15, c = e & 15;
@@ -368,45 +431,15 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
       P[mt] = acc;
     }
 
-    // ---------------- 7: chain update of this wave's strip
-    __syncthreads();  // U complete
-    const float gam = gg[0];
-    const float sigma = s_wave ? -gam : -1.f;
-#pragma unroll
-    for (int ks = 0; ks < 2 * NT; ++ks) {
-      const int t = ks >> 1, hh = ks & 1;
-      float xv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] = sigma * X[t][8 * hh + j];
-      bf16x8 bhi, blo;
-      split8(xv, bhi, blo);
-      const int kc = 32 * t + 16 * hh + 4 * g;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ah = lds_perm8(Uh + (mt * 32 + cl) * ULD, kc);
-        const bf16x8 al = lds_perm8(Ul + (mt * 32 + cl) * ULD, kc);
-        P[mt] = mfma32(al, bhi, P[mt]);
-        P[mt] = mfma32(ah, blo, P[mt]);
-        P[mt] = mfma32(ah, bhi, P[mt]);
-      }
-    }
-    if (s_wave) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) X[t] *= gam;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, hh = ks & 1;
-      bf16x8 bhi, blo;
-      split_acc_half(P[mt], hh, bhi, blo);
-      const int kc = 32 * mt + 16 * hh + 4 * g;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 kh = lds_perm8(Kt + (t * 32 + cl) * KT, kc);
-        X[t] = mfma32(kh, blo, X[t]);
-        X[t] = mfma32(kh, bhi, X[t]);
-      }
-    }
+  }
+
+  // ---------------- step 7 of the last chunk
+  if (n_chunks > 0) {
+    __syncthreads();  // U and K^T of the last chunk complete
+    chain_um(0, n_chunks - 1);
+    chain_um(1, n_chunks - 1);
+    chain_ktm(0, n_chunks - 1);
+    chain_ktm(1, n_chunks - 1);
   }
 
   // ---------------- write the pair
