@@ -176,23 +176,26 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
   f32x16 P[2];  // M of the chunk in flight (seeded with W or 0)
 
   // step 7 slices for chunk pc (its U in LDS, its K^T in buffer pc & 1)
-  auto chain_um = [&](int mt, int pc) {  // P[mt] += U_mt (sigma X)
+  auto chain_um = [&](int half, int pc) {  // P += U (sigma X) over K rows of one half
     const int lane = opaque(threadIdx.x) & 63, g = lane >> 5, cl = lane & 31;
     const float sigma = s_wave ? -gg[pc & 1] : -1.f;
 #pragma unroll
-    for (int ks = 0; ks < 2 * NT; ++ks) {
-      const int t = ks >> 1, hh = ks & 1;
+    for (int kk = 0; kk < NT; ++kk) {
+      const int ks = half * NT + kk, t = ks >> 1, hh = ks & 1;
       float xv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) xv[j] = sigma * X[t][8 * hh + j];
       bf16x8 bhi, blo;
       split8(xv, bhi, blo);
       const int kc = 32 * t + 16 * hh + 4 * g;
-      const bf16x8 ah = lds_perm8(Uh + (mt * 32 + cl) * ULD, kc);
-      const bf16x8 al = lds_perm8(Ul + (mt * 32 + cl) * ULD, kc);
-      P[mt] = mfma32(al, bhi, P[mt]);
-      P[mt] = mfma32(ah, blo, P[mt]);
-      P[mt] = mfma32(ah, bhi, P[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 ah = lds_perm8(Uh + (mt * 32 + cl) * ULD, kc);
+        const bf16x8 al = lds_perm8(Ul + (mt * 32 + cl) * ULD, kc);
+        P[mt] = mfma32(al, bhi, P[mt]);
+        P[mt] = mfma32(ah, blo, P[mt]);
+        P[mt] = mfma32(ah, bhi, P[mt]);
+      }
     }
   };
   auto chain_ktm = [&](int mt, int pc) {  // X += K^T M_mt  (S first scaled by gamma)

@@ -61,14 +61,26 @@ __device__ __forceinline__ int kperm(int h, int g, int j) {
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 __device__ __forceinline__ float from_bf16(__bf16 x) { return static_cast<float>(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// split a pair: hi = bf16(x) (round to nearest even, one packed convert),
+// unpacked back to fp32 by shift / mask, lo = bf16(x - hi) (x - hi exact)
+__device__ __forceinline__ void split2(float x0, float x1, unsigned& hp, unsigned& lp) {
+  const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+  hp = __builtin_bit_cast(unsigned, h);
+  const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xffff0000u);
+  lp = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2));
+}
+
 // split 8 fp32 values into hi/lo bf16 parts
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  unsigned h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    __bf16 h = to_bf16(x[j]);
-    hi[j] = h;
-    lo[j] = to_bf16(x[j] - from_bf16(h));
-  }
+  for (int j = 0; j < 4; ++j) split2(x[2 * j], x[2 * j + 1], h[j], l[j]);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
 }
 
 // B operand (hi/lo) from accumulator registers 8h .. 8h+7 of a tile
