@@ -93,6 +93,90 @@ def cpu_baseline(w, seconds: float, threads: int):
                        f"to {w.layers} layers x {w.heads} heads (build only)")}
 
 
+def bench_scalar_diag(w, args):
+    """Scalar-decay or diagonal-gate workload: build every pair, compose the
+    segments in order, naive add; one JSON line with HBM rooflines."""
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pic.load()
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    offsets = w.offsets()
+    qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    ashape = (B, N, H, dk) if w.form == synth.DIAG else (B, N, H)
+    k = torch.empty((B, N, H, dk), dtype=qdt, device=dev)
+    v = torch.empty((B, N, H, dv), dtype=qdt, device=dev)
+    alpha = torch.empty(ashape, dtype=torch.float32, device=dev)
+    for layer in range(B):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        k[layer].copy_(x["k"])
+        v[layer].copy_(x["v"])
+        alpha[layer].copy_(x["alpha"])
+    lam_shape = (n_seg, B, H, dk) if w.form == synth.DIAG else (n_seg, B, H)
+    pairs = {"log_scale": torch.empty(lam_shape, dtype=torch.float32, device=dev),
+             "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
+    S_out = torch.empty((1, B, H, dk, dv), dtype=torch.float32, device=dev)
+    S_naive = torch.empty_like(S_out)
+    chain_off, chain_idx = [0, n_seg], list(range(n_seg))
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rec=None):
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        pic.pic_segment_build(w.form, k, v, alpha, None, offsets, out=pairs)
+        e[1].record(stream)
+        pic.pic_compose(w.form, pairs["log_scale"], None, pairs["S0"], chain_off, chain_idx,
+                        None, out=S_out)
+        e[2].record(stream)
+        pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
+        e[3].record(stream)
+        if rec is not None:
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = [np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]) for i in range(3)]
+    gate_bytes = 4 * (dk if w.form == synth.DIAG else 1)
+    lam_out = 4 * (dk if w.form == synth.DIAG else 1)
+    qb = 2 if w.qkv_bf16 else 4
+    bb = N * B * H * ((dk + dv) * qb + gate_bytes) + n_seg * B * H * (dk * dv * 4 + lam_out)
+    cb = n_seg * B * H * (dk * dv * 4 + lam_out) + B * H * dk * dv * 4
+    nb = n_seg * B * H * dk * dv * 4 + B * H * dk * dv * 4
+    flops = 2.0 * N * B * H * dk * dv
+    gbs = lambda nbytes, t: nbytes / (t / 1e3) / 1e9
+    out = {"metric": f"{synth.FORM_NAMES[w.form]} segment build tokens/s; % HBM roofline",
+           "value": N / (ms[0] / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, bf16 k/v",
+           "data": "synthetic",
+           "config": {"workload": w.name, "form": synth.FORM_NAMES[w.form], "layers": B,
+                      "heads": H, "dk": dk, "dv": dv, "segments": n_seg,
+                      "segment_tokens": int(w.seg_lens[0]), "prompt_tokens": N},
+           "ms": {"build": ms[0], "compose": ms[1], "naive_add": ms[2]},
+           "roofline": {"kernel": "build_sd_kernel", "bound": "hbm",
+                        "achieved": gbs(bb, ms[0]), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs(bb, ms[0]) / PEAK_HBM_GBS, "traffic": None,
+                        "tflops": flops / (ms[0] / 1e3) / 1e12},
+           "roofline_compose": {"bound": "hbm", "achieved": gbs(cb, ms[1]),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": gbs(cb, ms[1]) / PEAK_HBM_GBS},
+           "roofline_naive_add": {"bound": "hbm", "achieved": gbs(nb, ms[2]),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs(nb, ms[2]) / PEAK_HBM_GBS}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,8 +201,7 @@ def main(argv=None):
     if args.layers:
         w = synth.scaled(w, layers=args.layers, name=w.name)
     if w.form != synth.DENSE:
-        print("bench.py: the headline workload is the dense form", file=sys.stderr)
-        return 2
+        return bench_scalar_diag(w, args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()

@@ -65,13 +65,12 @@ struct PipeLds {
   static_assert(A_BYTES % 16 == 0 && LM % 16 == 0, "alignment");
 };
 
-__device__ __forceinline__ void st_pair2(__bf16* p, unsigned short a, unsigned short b) {
-  *reinterpret_cast<unsigned*>(p) = unsigned(a) | (unsigned(b) << 16);
-}
-
-__device__ __forceinline__ unsigned short half_of(const uint4& w, int j) {
-  const unsigned x = (j < 2) ? w.x : (j < 4) ? w.y : (j < 6) ? w.z : w.w;
-  return (j & 1) ? (unsigned short)(x >> 16) : (unsigned short)(x & 0xffffu);
+// (element j of token a, element j of token b) as one packed pair: one
+// byte permute of the 32-bit words holding them
+__device__ __forceinline__ unsigned pair_of(const uint4& a, const uint4& b, int j) {
+  const unsigned wa = (j < 2) ? a.x : (j < 4) ? a.y : (j < 6) ? a.z : a.w;
+  const unsigned wb = (j < 2) ? b.x : (j < 4) ? b.y : (j < 6) ? b.z : b.w;
+  return __builtin_amdgcn_perm(wb, wa, (j & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // a copy of v the compiler cannot see through: keeps per-lane address
@@ -245,8 +244,8 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
       *reinterpret_cast<uint4*>(Kr + (t0 + 1) * KR + i0) = k1;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        st_pair2(Kt + (i0 + j) * KT + t0, half_of(k0, j), half_of(k1, j));
-        st_pair2(Vt + (i0 + j) * KT + t0, half_of(v0, j), half_of(v1, j));
+        *reinterpret_cast<unsigned*>(Kt + (i0 + j) * KT + t0) = pair_of(k0, k1, j);
+        *reinterpret_cast<unsigned*>(Vt + (i0 + j) * KT + t0) = pair_of(v0, v1, j);
       }
     }
     if (wave == 0) {
@@ -291,21 +290,21 @@ __global__ __launch_bounds__(4 * DP) void build_dense_pipe_kernel(BuildArgs a) {
     {
       const int col = tid / TPC, p = tid % TPC;
       const int o = 16 * (col >> 4), cc = col & 15;
-      float xo[JPT], lv[16][JPT];
+      float xo[JPT], lv[16][JPT];  // L entries this lane needs, zero above the diagonal
 #pragma unroll
       for (int r = 1; r < 16; ++r)
 #pragma unroll
-        for (int j = 0; j < JPT; ++j) lv[r][j] = Lm[(o + r) * XL + o + p + TPC * j];
+        for (int j = 0; j < JPT; ++j) {
+          const float v = Lm[(o + r) * XL + o + p + TPC * j];
+          lv[r][j] = (p + TPC * j < r) ? v : 0.f;
+        }
 #pragma unroll
       for (int j = 0; j < JPT; ++j) xo[j] = (p + TPC * j == cc) ? 1.f : 0.f;
 #pragma unroll
       for (int r = 1; r < 16; ++r) {
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < JPT; ++j) {
-          const int m = p + TPC * j;
-          s = (m < r) ? fmaf(lv[r][j], xo[j], s) : s;
-        }
+        for (int j = 0; j < JPT; ++j) s = fmaf(lv[r][j], xo[j], s);
         s = group_sum<TPC>(s);
         if (r > cc && p == (r % TPC)) xo[r / TPC] = -s;
       }

@@ -81,17 +81,21 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // (padded stride to spread LDS banks) and forms That_p * S with split-bf16
 // MFMAs (3 per 32x32x16 block), taking the B operand straight from the
 // accumulators of the old S (K order permuted to match, see mfma_util.hpp).
-// Then S <- e^lambda * (That S) + S0_p.  Sizes not a multiple of 32 are
-// zero-padded, which leaves the result unchanged.
+// Then S <- e^lambda * (That S) + S0_p.  The next step's operator is loaded
+// into registers while the current step's MFMAs run, and S0_p is loaded
+// before them.  Sizes not a multiple of 32 are zero-padded, which leaves the
+// result unchanged.
 template <int DKP>
 __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   constexpr int NT = DKP / 32;
-  constexpr int LDR = DKP + 4;  // row stride of the staged operator, in bf16
-  __shared__ __bf16 th_hi[DKP * LDR];
-  __shared__ __bf16 th_lo[DKP * LDR];
+  constexpr int LDR = DKP + 4;        // row stride of the staged operator, in bf16
+  constexpr int F4 = DKP * DKP / 4;   // float4 items of one operator
+  __shared__ __attribute__((aligned(16))) __bf16 th_hi[DKP * LDR];
+  __shared__ __attribute__((aligned(16))) __bf16 th_lo[DKP * LDR];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, cl = lane & 31;
+  const int nthr = blockDim.x;
   const int dk = a.dk, dv = a.dv;
   const int64_t BH = int64_t(a.batch) * a.heads;
   const int64_t unit = blockIdx.x;
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   const int n = wave * 32 + cl;  // state column of this lane
   const bool ncol = n < dv;
   const int64_t sdd = int64_t(dk) * dv;
+  const int per_thr = (F4 + nthr - 1) / nthr;  // <= 16 (DKP = 128, 256 threads)
 
   f32x16 S[NT];
 #pragma unroll
@@ -110,25 +115,51 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
     }
   }
 
-  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
-  for (int64_t c = c0; c < c1; ++c) {
-    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+  // operator of one chain step, as this thread's float4 items (zero padded)
+  float4 pre[16];
+  auto load_op = [&](int64_t pu) {
     const float* Tp = a.pool_T_hat + pu * int64_t(dk) * dk;
-    __syncthreads();  // every wave is done reading the previous operator
-    for (int e = threadIdx.x; e < DKP * DKP / 4; e += blockDim.x) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int e = threadIdx.x + it * nthr;
       const int row = (e * 4) / DKP, col = (e * 4) % DKP;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row < dk && col < dk) x = *reinterpret_cast<const float4*>(Tp + row * dk + col);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
+      if (it < per_thr && e < F4 && row < dk && col < dk)
+        x = *reinterpret_cast<const float4*>(Tp + row * dk + col);
+      pre[it] = x;
+    }
+  };
+
+  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
+  if (c0 < c1) load_op(int64_t(a.d_chain_idx[c0]) * BH + bh);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+    __syncthreads();  // every wave is done reading the previous operator
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 h = to_bf16(xs[j]);
-        th_hi[row * LDR + col + j] = h;
-        th_lo[row * LDR + col + j] = to_bf16(xs[j] - from_bf16(h));
+    for (int it = 0; it < 16; ++it) {
+      const int e = threadIdx.x + it * nthr;
+      if (it < per_thr && e < F4) {
+        const int row = (e * 4) / DKP, col = (e * 4) % DKP;
+        unsigned h0, l0, h1, l1;
+        split2(pre[it].x, pre[it].y, h0, l0);
+        split2(pre[it].z, pre[it].w, h1, l1);
+        *reinterpret_cast<uint2*>(th_hi + row * LDR + col) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(th_lo + row * LDR + col) = make_uint2(l0, l1);
       }
     }
-    __syncthreads();
+    if (c + 1 < c1) load_op(int64_t(a.d_chain_idx[c + 1]) * BH + bh);
+    // this step's S0 strip, loaded ahead of the products
+    const float* S0p = a.pool_S0 + pu * sdd;
+    f32x16 s0[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = t * 32 + acc_row(q, g);
+        s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+      }
     const float scale = expf(a.pool_log_scale[pu]);
+    __syncthreads();
 
     f32x16 acc[NT];
 #pragma unroll
@@ -149,16 +180,10 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
         acc[mt] = mfma32(ahi, bhi, acc[mt]);
       }
     }
-    const float* S0p = a.pool_S0 + pu * sdd;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = t * 32 + acc_row(q, g);
-        const float s0 = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
-        S[t][q] = fmaf(scale, acc[t][q], s0);
-      }
-    }
+      for (int q = 0; q < 16; ++q) S[t][q] = fmaf(scale, acc[t][q], s0[t][q]);
   }
 
   if (ncol) {
