@@ -237,7 +237,8 @@ hipError_t launch_sd_dp(const BuildArgs& a, hipStream_t s) {
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s) {
   const bool diag = a.form == kDiag;
-  if (a.qkv_bf16) return diag ? launch_sd_dp<true, true>(a, s) : launch_sd_dp<true, false>(a, s);
+  // bf16 inputs take the streaming kernel (k_build_sd_pipe.hip)
+  if (a.qkv_bf16) return launch_build_sd_pipe(a, s);
   return diag ? launch_sd_dp<false, true>(a, s) : launch_sd_dp<false, false>(a, s);
 }
 

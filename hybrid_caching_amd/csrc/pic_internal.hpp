@@ -45,6 +45,7 @@ struct ComposeArgs {
 };
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
+hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
