@@ -17,8 +17,10 @@ measured with HIP events recorded on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +34,55 @@ METRIC = "segment build tokens/s + state composes/s (dense delta, H=32, d=128); 
 CHUNK = 64
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "hybrid_caching_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# the source files each timed kernel is compiled from
+KERNEL_SOURCES = {
+    "build_dense_pipe_kernel": ["k_build_dense_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_sd_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the sources a kernel is built from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload`, read from the committed
+    hardware-counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a plain copy of known size).  None when there is no such
+    summary or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.hbm_counters.md")
+    try:
+        with open(path) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if fields.get("sources_sha256") != source_digest(kernel):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev, nbytes: int) -> None:
+    """One plain device copy of `nbytes` (reads nbytes, writes nbytes): the
+    reference dispatch against which the byte counters are scaled."""
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def dense_build_flops_per_token_head(d: int, c: int = CHUNK) -> float:
@@ -120,6 +171,9 @@ def bench_scalar_diag(w, args):
     S_out = torch.empty((1, B, H, dk, dv), dtype=torch.float32, device=dev)
     S_naive = torch.empty_like(S_out)
     chain_off, chain_idx = [0, n_seg], list(range(n_seg))
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration)
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -163,9 +217,11 @@ def bench_scalar_diag(w, args):
                       "heads": H, "dk": dk, "dv": dv, "segments": n_seg,
                       "segment_tokens": int(w.seg_lens[0]), "prompt_tokens": N},
            "ms": {"build": ms[0], "compose": ms[1], "naive_add": ms[2]},
-           "roofline": {"kernel": "build_sd_kernel", "bound": "hbm",
+           "roofline": {"kernel": "build_sd_pipe_kernel", "bound": "hbm",
                         "achieved": gbs(bb, ms[0]), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": gbs(bb, ms[0]) / PEAK_HBM_GBS, "traffic": None,
+                        "frac": gbs(bb, ms[0]) / PEAK_HBM_GBS,
+                        "traffic": measured_traffic("build_sd_pipe_kernel", w.name),
+                        "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
                         "tflops": flops / (ms[0] / 1e3) / 1e12},
            "roofline_compose": {"bound": "hbm", "achieved": gbs(cb, ms[1]),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -186,7 +242,16 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one plain device copy of BYTES (read BYTES, write BYTES) before "
+                         "timing, as a reference for hardware byte counters")
+    ap.add_argument("--source-digest", action="store_true",
+                    help="print the source digest of each timed kernel and exit")
     args = ap.parse_args(argv)
+    if args.source_digest:
+        for kname in KERNEL_SOURCES:
+            print(kname, source_digest(kname))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -228,6 +293,8 @@ def main(argv=None):
     S_naive = torch.empty_like(S_out)
     chain_off, chain_idx = [0, n_seg], list(range(n_seg))
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration)
 
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -287,10 +354,15 @@ def main(argv=None):
                "step_events": t_step_ev * 1e3},
         "roofline": {"kernel": "build_dense_pipe_kernel", "bound": "mfma", "achieved": achieved_tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tf / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved_tf / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("build_dense_pipe_kernel", w.name),
+                     "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes": build_bytes(N, B, H, dk, dv, n_seg)},
         "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
                              "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS},
+                             "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS,
+                             "traffic": measured_traffic("compose_dense_kernel", w.name),
+                             "algorithmic_bytes": cb},
         "roofline_naive_add": {"bound": "hbm", "achieved": nb / t_naive / 1e9,
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
