@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,13 +36,17 @@ SIGNATURES = {
                                _p, _p, _p, _sz, _p]),
     "pic_compose_workspace": (_sz, [_i32, _i64]),
     "pic_validate_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
-                                  _sz]),
-    "pic_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _sz,
-                         _p]),
+                                  _p, _p, _sz]),
+    "pic_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p,
+                         _sz, _p]),
     "pic_validate_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz]),
     "pic_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "pic_materialize_T": (_i, [_i, _i64, _i, _p, _p, _p, _p]),
+    "pic_plan_dump": (_i, [_i, _i32, _p, _p, _i64, _p, _i64]),
 }
+
+PLAN_BUILD, PLAN_COMPOSE = 0, 1
+PLAN_BUILD_COLS, PLAN_COMPOSE_COLS = 5, 3
 
 _LIB = None
 
@@ -149,12 +154,14 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
 
 
 def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, chain_idx,
-                S_in=None, *, out=None):
+                S_in=None, *, out=None, want_pair: bool = False):
     """Fold chains of pool pairs into states: S <- e^lam That S + S0 per step.
 
     pool_S0: [P, B, H, dk, dv]; pool_log_scale [P, B, H] (diag [P, B, H, dk]);
     pool_T_hat [P, B, H, dk, dk] (dense; None otherwise).  Returns S_out
-    [R, B, H, dk, dv] (``out`` may be S_in for an in-place update)."""
+    [R, B, H, dk, dv] (``out`` may be S_in for an in-place update).  With
+    ``want_pair`` returns (S_out, log_scale_out, T_hat_out): the chain's own
+    operator, sum of log scales and (dense) That_pn ... That_p1, else None."""
     lib = load()
     P, B, H, dk, dv = pool_S0.shape
     for t, n in ((pool_log_scale, "pool_log_scale"), (pool_T_hat, "pool_T_hat"),
@@ -166,11 +173,19 @@ def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, c
     dev = pool_S0.device
     if out is None:
         out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    lam_out = T_out = None
+    if want_pair:
+        lam_out = torch.empty((R,) + tuple(pool_log_scale.shape[1:]), dtype=torch.float32,
+                              device=dev)
+        if form == FORM_DENSE:
+            T_out = torch.empty((R, B, H, dk, dk), dtype=torch.float32, device=dev)
     ws = _workspace(lib.pic_compose_workspace(R, int(off[-1])), dev)
     rc = lib.pic_compose(form, B, H, dk, dv, P, _ptr(pool_log_scale), _ptr(pool_T_hat),
-                         _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in), _ptr(out), _ptr(ws),
-                         ws.numel(), _stream(dev))
+                         _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in), _ptr(out), _ptr(lam_out),
+                         _ptr(T_out), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "pic_compose")
+    if want_pair:
+        return out, lam_out, T_out
     return out
 
 
@@ -216,3 +231,24 @@ def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):
                                _stream(log_scale.device))
     _check(rc, "pic_materialize_T")
     return out
+
+
+def pic_plan_dump(kind: int, offsets, chain_idx=None, limit: int = 0):
+    """Host bookkeeping of a build (kind PLAN_BUILD: rows {segment, start,
+    length, n_chunks, tail} in visiting order; limit = n_tokens) or of a
+    compose (PLAN_COMPOSE: rows {request, step, pool index}; limit =
+    pool_size).  Pure host code; returns an int64 numpy array."""
+    lib = load()
+    off, off_p = _host_i64(offsets)
+    n = len(off) - 1
+    if kind == PLAN_BUILD:
+        rows, cols = n, PLAN_BUILD_COLS
+        idx_p = None
+    else:
+        rows, cols = int(off[-1]), PLAN_COMPOSE_COLS
+        _, idx_p = _host_i32(chain_idx)
+    table = np.zeros((max(rows, 1), cols), dtype=np.int64)
+    rc = lib.pic_plan_dump(kind, n, off_p, idx_p, int(limit),
+                           table.ctypes.data_as(ctypes.c_void_p), rows)
+    _check(rc, "pic_plan_dump")
+    return table[:rows]

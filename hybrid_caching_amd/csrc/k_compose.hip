@@ -85,7 +85,10 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // into registers while the current step's MFMAs run, and S0_p is loaded
 // before them.  Sizes not a multiple of 32 are zero-padded, which leaves the
 // result unchanged.
-template <int DKP>
+// PROD = true forms the chain's operator instead: the "state" is dk x dk,
+// starts at I, and each step is X <- That_p X (no scale, no additive term);
+// the launcher passes dv = dk and S_out = the That output.
+template <int DKP, bool PROD>
 __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   constexpr int NT = DKP / 32;
   constexpr int LDR = DKP + 4;        // row stride of the staged operator, in bf16
@@ -111,7 +114,10 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = t * 32 + acc_row(q, g);
-      S[t][q] = (a.S_in && ncol && row < dk) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
+      if (PROD)
+        S[t][q] = (row == n && row < dk) ? 1.f : 0.f;
+      else
+        S[t][q] = (a.S_in && ncol && row < dk) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
     }
   }
 
@@ -149,16 +155,19 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
     }
     if (c + 1 < c1) load_op(int64_t(a.d_chain_idx[c + 1]) * BH + bh);
     // this step's S0 strip, loaded ahead of the products
-    const float* S0p = a.pool_S0 + pu * sdd;
     f32x16 s0[NT];
+    float scale = 1.f;
+    if (!PROD) {
+      const float* S0p = a.pool_S0 + pu * sdd;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = t * 32 + acc_row(q, g);
-        s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
-      }
-    const float scale = expf(a.pool_log_scale[pu]);
+        for (int q = 0; q < 16; ++q) {
+          const int row = t * 32 + acc_row(q, g);
+          s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+        }
+      scale = expf(a.pool_log_scale[pu]);
+    }
     __syncthreads();
 
     f32x16 acc[NT];
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) S[t][q] = fmaf(scale, acc[t][q], s0[t][q]);
+      for (int q = 0; q < 16; ++q) S[t][q] = PROD ? acc[t][q] : fmaf(scale, acc[t][q], s0[t][q]);
   }
 
   if (ncol) {
@@ -196,6 +205,23 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// chain pair: log scale of the chain = sum of the entries' log scales
+// ---------------------------------------------------------------------------
+// One thread per (request, layer, head[, key channel]); consecutive threads
+// read consecutive entries of each pool row.
+__global__ void chain_log_scale_kernel(ComposeArgs a, int per) {
+  const int64_t BH = int64_t(a.batch) * a.heads;
+  const int64_t total = int64_t(a.n_req) * BH * per;
+  const int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+  if (e >= total) return;
+  const int64_t r = e / (BH * per), rest = e % (BH * per);
+  float acc = 0.f;
+  for (int64_t c = a.d_chain_off[r]; c < a.d_chain_off[r + 1]; ++c)
+    acc += a.pool_log_scale[int64_t(a.d_chain_idx[c]) * BH * per + rest];
+  a.log_scale_out[e] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -241,7 +267,8 @@ hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s) {
+template <bool PROD>
+hipError_t launch_dense_chain(const ComposeArgs& a, hipStream_t s) {
   const int64_t units = int64_t(a.n_req) * a.batch * a.heads;
   if (units <= 0) return hipSuccess;
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -250,12 +277,35 @@ hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s) {
   const dim3 block{unsigned(64 * waves), 1, 1};
   const int dkp = (a.dk + 31) / 32 * 32;
   switch (dkp) {
-    case 32: hipLaunchKernelGGL(compose_dense_kernel<32>, grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL(compose_dense_kernel<64>, grid, block, 0, s, a); break;
-    case 96: hipLaunchKernelGGL(compose_dense_kernel<96>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(compose_dense_kernel<128>, grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((compose_dense_kernel<32, PROD>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((compose_dense_kernel<64, PROD>), grid, block, 0, s, a); break;
+    case 96: hipLaunchKernelGGL((compose_dense_kernel<96, PROD>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((compose_dense_kernel<128, PROD>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s) {
+  return launch_dense_chain<false>(a, s);
+}
+
+hipError_t launch_chain_T_hat(const ComposeArgs& a, hipStream_t s) {
+  ComposeArgs t = a;
+  t.dv = a.dk;
+  t.S_in = nullptr;
+  t.pool_S0 = nullptr;
+  t.S_out = a.T_hat_out;
+  return launch_dense_chain<true>(t, s);
+}
+
+hipError_t launch_chain_log_scale(const ComposeArgs& a, hipStream_t s) {
+  const int per = (a.form == kDiag) ? a.dk : 1;
+  const int64_t total = int64_t(a.n_req) * a.batch * a.heads * per;
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(chain_log_scale_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, a, per);
   return hipGetLastError();
 }
 

@@ -103,6 +103,30 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(PIC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Visiting order of a build: longest segment first, ties by index, so that
+// long units start early and short ones fill the tail of the launch.
+std::vector<int32_t> build_order(const int64_t* off, int32_t n_seg) {
+  std::vector<int32_t> order(n_seg);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return off[a + 1] - off[a] > off[b + 1] - off[b];
+  });
+  return order;
+}
+
+int check_seg_offsets(const int64_t* seg_offsets, int32_t n_seg, int64_t n_tokens) {
+  if (!seg_offsets) return fail(PIC_ERR_NULL, "seg_offsets is NULL");
+  if (seg_offsets[0] != 0)
+    return fail(PIC_ERR_OFFSETS, "seg_offsets[0] = %lld, must be 0", (long long)seg_offsets[0]);
+  for (int32_t s = 0; s < n_seg; ++s)
+    if (seg_offsets[s + 1] < seg_offsets[s])
+      return fail(PIC_ERR_OFFSETS, "seg_offsets decrease at segment %d", s);
+  if (seg_offsets[n_seg] != n_tokens)
+    return fail(PIC_ERR_OFFSETS, "seg_offsets[n_seg] = %lld, must equal n_tokens = %lld",
+                (long long)seg_offsets[n_seg], (long long)n_tokens);
+  return PIC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,14 +185,7 @@ int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, in
     return fail(PIC_ERR_NULL, "T_hat output is required for the dense form");
   if (form != PIC_FORM_DENSE && T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
-  if (seg_offsets[0] != 0)
-    return fail(PIC_ERR_OFFSETS, "seg_offsets[0] = %lld, must be 0", (long long)seg_offsets[0]);
-  for (int32_t s = 0; s < n_seg; ++s)
-    if (seg_offsets[s + 1] < seg_offsets[s])
-      return fail(PIC_ERR_OFFSETS, "seg_offsets decrease at segment %d", s);
-  if (seg_offsets[n_seg] != n_tokens)
-    return fail(PIC_ERR_OFFSETS, "seg_offsets[n_seg] = %lld, must equal n_tokens = %lld",
-                (long long)seg_offsets[n_seg], (long long)n_tokens);
+  if (int rc = check_seg_offsets(seg_offsets, n_seg, n_tokens)) return rc;
   if (int rc = check_align({k, v, alpha, beta, log_scale, T_hat, S0, workspace})) return rc;
   const size_t need = build_ws_bytes(n_seg);
   if (!workspace || workspace_bytes < need)
@@ -187,13 +204,7 @@ int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int
                                   workspace, workspace_bytes))
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Plan: visit segments longest first (ties by index), so that long units
-  // start early and short ones fill the tail of the launch.
-  std::vector<int32_t> order(n_seg);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return seg_offsets[a + 1] - seg_offsets[a] > seg_offsets[b + 1] - seg_offsets[b];
-  });
+  const std::vector<int32_t> order = build_order(seg_offsets, n_seg);
   char* ws = static_cast<char*>(workspace);
   int64_t* d_off = reinterpret_cast<int64_t*>(ws);
   int32_t* d_order = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
@@ -221,6 +232,7 @@ int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t
                          const float* pool_log_scale, const float* pool_T_hat,
                          const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
                          const int32_t* chain_idx, const float* S_in, const float* S_out,
+                         const float* log_scale_out, const float* T_hat_out,
                          const void* workspace, size_t workspace_bytes) {
   (void)S_in;
   if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
@@ -238,7 +250,14 @@ int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t
     return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense form");
   if (form != PIC_FORM_DENSE && pool_T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "pool_T_hat must be NULL for scalar and diagonal forms");
-  if (int rc = check_align({pool_log_scale, pool_T_hat, pool_S0, S_in, S_out, workspace}))
+  if (form != PIC_FORM_DENSE && T_hat_out)
+    return fail(PIC_ERR_UNSUPPORTED, "T_hat_out must be NULL for scalar and diagonal forms");
+  if (form == PIC_FORM_DENSE && (!log_scale_out) != (!T_hat_out))
+    return fail(PIC_ERR_NULL, "the chain pair needs both log_scale_out and T_hat_out");
+  if (mul_sizes({n_req, batch, heads, dk, dk}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (int rc = check_align({pool_log_scale, pool_T_hat, pool_S0, S_in, S_out, log_scale_out,
+                            T_hat_out, workspace}))
     return rc;
   const size_t need = compose_ws_bytes(n_req, total);
   if (!workspace || workspace_bytes < need)
@@ -289,11 +308,11 @@ static int enqueue_chains(int32_t n_req, const int64_t* off, const int32_t* idx,
 int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
                 const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
                 int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
-                const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                const float* S_in, float* S_out, float* log_scale_out, float* T_hat_out,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = pic_validate_compose(form, batch, heads, dk, dv, pool_size, pool_log_scale,
                                     pool_T_hat, pool_S0, n_req, chain_offsets, chain_idx, S_in,
-                                    S_out, workspace, workspace_bytes))
+                                    S_out, log_scale_out, T_hat_out, workspace, workspace_bytes))
     return rc;
   if (n_req == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -301,11 +320,20 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
   const int32_t* d_idx;
   if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
     return rc;
-  pic::ComposeArgs a{form, batch, heads, dk, dv, pool_size, pool_log_scale, pool_T_hat,
-                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out};
+  pic::ComposeArgs a{form,   batch, heads, dk, dv, pool_size, pool_log_scale, pool_T_hat,
+                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out,
+                     log_scale_out, T_hat_out};
   hipError_t e = (form == PIC_FORM_DENSE) ? pic::launch_compose_dense(a, s)
                                           : pic::launch_compose_elementwise(a, false, s);
   if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
+  if (log_scale_out) {
+    e = pic::launch_chain_log_scale(a, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the chain log-scale kernel");
+  }
+  if (T_hat_out) {
+    e = pic::launch_chain_T_hat(a, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the chain operator kernel");
+  }
   return ok();
 }
 
@@ -324,7 +352,8 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
   if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
     return rc;
   pic::ComposeArgs a{PIC_FORM_SCALAR, batch, heads, dk, dv, pool_size, nullptr, nullptr,
-                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out};
+                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out,
+                     nullptr, nullptr};
   hipError_t e = pic::launch_compose_elementwise(a, true, s);
   if (e != hipSuccess) return hip_fail(e, "launching the naive-add kernel");
   return ok();
@@ -349,6 +378,52 @@ int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching the materialize kernel");
   return ok();
+}
+
+/* -------------------------------------------------------------- plan dump */
+
+int pic_plan_dump(int kind, int32_t n, const int64_t* offsets, const int32_t* chain_idx,
+                  int64_t limit, int64_t* table, int64_t table_rows) {
+  if (!table && table_rows > 0) return fail(PIC_ERR_NULL, "table is NULL");
+  if (kind == PIC_PLAN_BUILD) {
+    if (n < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n);
+    if (limit < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
+    if (chain_idx) return fail(PIC_ERR_UNSUPPORTED, "chain_idx must be NULL for a build plan");
+    if (int rc = check_seg_offsets(offsets, n, limit)) return rc;
+    if (table_rows < n)
+      return fail(PIC_ERR_WORKSPACE, "table of %d rows needed, %lld given", n,
+                  (long long)table_rows);
+    if (!table) return fail(PIC_ERR_NULL, "table is NULL");
+    const std::vector<int32_t> order = build_order(offsets, n);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t seg = order[i];
+      const int64_t len = offsets[seg + 1] - offsets[seg];
+      const int64_t nch = (len + PIC_CHUNK - 1) / PIC_CHUNK;
+      int64_t* row = table + int64_t(i) * PIC_PLAN_BUILD_COLS;
+      row[0] = seg;
+      row[1] = offsets[seg];
+      row[2] = len;
+      row[3] = nch;
+      row[4] = nch ? len - (nch - 1) * PIC_CHUNK : 0;
+    }
+    return ok();
+  }
+  if (kind == PIC_PLAN_COMPOSE) {
+    if (int rc = check_chains(limit, n, offsets, chain_idx)) return rc;
+    const int64_t total = offsets[n];
+    if (table_rows < total)
+      return fail(PIC_ERR_WORKSPACE, "table of %lld rows needed, %lld given", (long long)total,
+                  (long long)table_rows);
+    for (int32_t r = 0; r < n; ++r)
+      for (int64_t c = offsets[r]; c < offsets[r + 1]; ++c) {
+        int64_t* row = table + c * PIC_PLAN_COMPOSE_COLS;
+        row[0] = r;
+        row[1] = c - offsets[r];
+        row[2] = chain_idx[c];
+      }
+    return ok();
+  }
+  return fail(PIC_ERR_UNSUPPORTED, "unknown plan kind %d", kind);
 }
 
 }  // extern "C"

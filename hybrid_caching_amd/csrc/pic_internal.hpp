@@ -42,6 +42,8 @@ struct ComposeArgs {
   int64_t chain_total;
   const float* S_in;           // may be null
   float* S_out;
+  float* log_scale_out;        // chain pair: sum of log scales, may be null
+  float* T_hat_out;            // chain pair: product of That (dense), may be null
 };
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
@@ -50,6 +52,9 @@ hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
+// chain pair: log_scale_out (all forms) and That_out = That_pn ... That_p1 (dense)
+hipError_t launch_chain_log_scale(const ComposeArgs& a, hipStream_t s);
+hipError_t launch_chain_T_hat(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
                                 const float* T_hat, float* T_out, hipStream_t s);
 

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 1
+#define PIC_ABI_VERSION 2
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -149,6 +149,16 @@ int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int
  *     S <- e^{log_scale_p} * That_p * S + S0_p
  * per (layer, head), starting from S_in[r] (NULL = zero), result in S_out[r].
  *
+ * The chain's own pair (optional).  Composition is associative, so a chain
+ * p_1..p_n is itself a cached pair: T_chain = T_pn ... T_p1 and
+ * S(chain|0) = the result from a zero start.  With log_scale_out and (dense)
+ * T_hat_out given, the call also writes
+ *     log_scale_out[r] = sum over the chain of log_scale_p
+ *     T_hat_out[r]     = That_pn ... That_p1          (dense)
+ * (an empty chain gives 0 and I); S(chain|0) is S_out with S_in = NULL.
+ *   [xix.ai HYPIC article, paragraph on linear layers: the composition
+ *    identity S(C1.C2) = T(C2) S(C1) + S(C2) with T(C1.C2) = T(C2) T(C1).]
+ *
  * pool_size      number of pool entries P
  * pool_log_scale device fp32 [P][batch][heads] (diag: [P][batch][heads][dk])
  * pool_T_hat     device fp32 [P][batch][heads][dk][dk]; dense only (else NULL)
@@ -157,6 +167,12 @@ int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int
  * chain_idx      HOST int32[off[n_req]]: pool indices in [0, pool_size)
  * S_in           device fp32 [n_req][batch][heads][dk][dv] or NULL (= 0)
  * S_out          device fp32 out, same shape; may equal S_in (in place)
+ * log_scale_out  device fp32 out [n_req][batch][heads] (diag: [..][dk]), or
+ *                NULL (chain pair not wanted)
+ * T_hat_out      device fp32 out [n_req][batch][heads][dk][dk]: dense only,
+ *                given together with log_scale_out (PIC_ERR_NULL if only one
+ *                of the two is given); NULL for scalar / diagonal forms.
+ *                Neither output may overlap the pool.
  * -------------------------------------------------------------------- */
 size_t pic_compose_workspace(int32_t n_req, int64_t chain_total);
 
@@ -164,13 +180,14 @@ int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t
                          const float* pool_log_scale, const float* pool_T_hat,
                          const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
                          const int32_t* chain_idx, const float* S_in, const float* S_out,
+                         const float* log_scale_out, const float* T_hat_out,
                          const void* workspace, size_t workspace_bytes);
 
 int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
                 const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
                 int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
-                const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
-                void* stream);
+                const float* S_in, float* S_out, float* log_scale_out, float* T_hat_out,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Naive add (the ablation): S_out[r] = S_in[r] + sum over the chain of S0_p.
@@ -198,6 +215,36 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
  * -------------------------------------------------------------------- */
 int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
                       const float* T_hat, float* T_out, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Plan dump: the host-side bookkeeping a build or compose call would use,
+ * written to a host table so it can be checked exactly.  Pure host code: no
+ * HIP call, no device pointer.
+ *   [xix.ai HYPIC article, paragraph on linear layers: one cached pair per
+ *    segment, found by segment boundaries; the serving layer recognises the
+ *    boundaries and looks the pairs up.]
+ *
+ * kind = PIC_PLAN_BUILD: n = n_seg >= 1, offsets = seg_offsets (n+1 entries,
+ *   checked as in pic_validate_build against limit = n_tokens), chain_idx
+ *   must be NULL.  Writes n rows of PIC_PLAN_BUILD_COLS int64 each, in the
+ *   order the segments are visited (longest first, ties by index):
+ *     {segment, start, length, n_chunks, tail}
+ *   with n_chunks = ceil(length / PIC_CHUNK) and tail = the number of tokens
+ *   in the last chunk (0 for an empty segment).
+ * kind = PIC_PLAN_COMPOSE: n = n_req >= 0, offsets = chain_offsets (n+1),
+ *   chain_idx as in pic_compose, limit = pool_size.  Writes chain_total rows
+ *   of PIC_PLAN_COMPOSE_COLS int64 each, in application order:
+ *     {request, step within the chain, pool index}
+ * table_rows is the capacity of `table` in rows (PIC_ERR_WORKSPACE if too
+ * small).  Errors as for the matching validate call.
+ * -------------------------------------------------------------------- */
+enum pic_plan_kind { PIC_PLAN_BUILD = 0, PIC_PLAN_COMPOSE = 1 };
+#define PIC_PLAN_BUILD_COLS 5
+#define PIC_PLAN_COMPOSE_COLS 3
+#define PIC_CHUNK 64
+
+int pic_plan_dump(int kind, int32_t n, const int64_t* offsets, const int32_t* chain_idx,
+                  int64_t limit, int64_t* table, int64_t table_rows);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,9 @@ module only marshals numpy arrays into it.  What each call computes:
 * ``compose``    -- S <- T_C S + S(C|0) along a chain of cached pairs.
   [same paragraph: left-multiply by T_C, then add]
 * ``naive_add``  -- S_in + sum S(C|0), the ablation.  [same paragraph]
+* ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
+  its definition: segments as token ranges cut into 64-token chunks, visited
+  longest first; chains applied entry by entry.
 
 Forms: 0 = scalar decay, 1 = diagonal gate, 2 = dense gated delta (GDN form).
 """
@@ -201,3 +204,33 @@ def naive_add(S, chain_offsets, chain_idx, S_in=None, *, threads=None, lib=None)
     if rc != 0:
         raise ValueError("oracle_naive_add rejected its arguments")
     return S_out
+
+
+CHUNK = 64
+
+
+def plan_build(seg_offsets):
+    """One row per segment, in visiting order (longest first, ties by lower
+    index): (segment, start, length, n_chunks, tail), where n_chunks =
+    ceil(length / 64) and tail = tokens in the last chunk (0 if empty).
+    [segments are token ranges cut at their boundaries; xix.ai HYPIC article,
+    paragraph on linear layers]"""
+    off = [int(x) for x in seg_offsets]
+    n = len(off) - 1
+    lengths = [off[s + 1] - off[s] for s in range(n)]
+    order = sorted(range(n), key=lambda s: (-lengths[s], s))
+    rows = []
+    for s in order:
+        length = lengths[s]
+        n_chunks = (length + CHUNK - 1) // CHUNK
+        tail = length - CHUNK * (n_chunks - 1) if n_chunks else 0
+        rows.append((s, off[s], length, n_chunks, tail))
+    return np.array(rows, dtype=np.int64).reshape(n, 5)
+
+
+def plan_compose(chain_offsets, chain_idx):
+    """One row per chain entry, in application order: (request, step, pool index)."""
+    off = [int(x) for x in chain_offsets]
+    idx = [int(x) for x in chain_idx]
+    rows = [(r, c - off[r], idx[c]) for r in range(len(off) - 1) for c in range(off[r], off[r + 1])]
+    return np.array(rows, dtype=np.int64).reshape(len(rows), 3)

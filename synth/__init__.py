@@ -116,6 +116,47 @@ WORKLOADS["dense_30L_32x4096_slow"] = replace(WORKLOADS["dense_30L_32x4096"],
                                               beta=("uniform", 0.0, 0.02))
 
 
+def reuse_pool_lengths(seed: int = 105, pool_size: int = 256, lo: int = 512,
+                       hi: int = 8192) -> tuple:
+    """Token counts of the cached pool of the reuse workload, ~ U{lo..hi}."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7777]))
+    return tuple(int(x) for x in rng.integers(lo, hi + 1, size=pool_size))
+
+
+# composition-heavy reuse: a pool of 256 cached dense segments (lengths
+# U{512..8192}) for 30 layers x 32 heads x d=128; 64 requests, each composing
+# 48 distinct pool segments (Zipf s = 1.1) and 8 fresh 2048-token segments
+# in a shuffled order.  seg_lens are the pool's; the fresh segments are
+# drawn by ``reuse_fresh_workload``.
+REUSE = {"pool_size": 256, "n_req": 64, "pool_per_req": 48, "fresh_per_req": 8,
+         "fresh_len": 2048, "zipf_s": 1.1}
+WORKLOADS["reuse_256x30"] = Workload("reuse_256x30", DENSE, 30, 32, 128, 128,
+                                     reuse_pool_lengths(), 105, True, "l2", 1.0,
+                                     ("uniform", 0.9, 1.0), ("uniform", 0.0, 1.0),
+                                     extra=dict(REUSE))
+
+
+WORKLOADS["reuse_256x30_slow"] = replace(WORKLOADS["reuse_256x30"], name="reuse_256x30_slow",
+                                         alpha=("uniform", 0.9995, 1.0),
+                                         beta=("uniform", 0.0, 0.02))
+
+
+def reuse_fresh_workload(w: Workload) -> Workload:
+    """The fresh segments of a reuse workload (n_req x fresh_per_req of
+    fresh_len tokens), same distributions, its own seed stream."""
+    e = w.extra
+    return replace(w, name=w.name + "_fresh", seed=w.seed + 50,
+                   seg_lens=(e["fresh_len"],) * (e["n_req"] * e["fresh_per_req"]))
+
+
+def reuse_chains(w: Workload):
+    """Chains of the reuse workload: pool ids 0..pool_size-1, fresh ids
+    pool_size + fresh_per_req * r + j.  Returns (offsets, idx)."""
+    e = w.extra
+    return zipf_chains(e["pool_size"], e["n_req"], e["pool_per_req"], e["zipf_s"], w.seed,
+                       fresh_per_req=e["fresh_per_req"], fresh_base=e["pool_size"])
+
+
 def scaled(w: Workload, *, layers=None, heads=None, seg_lens=None, dk=None, dv=None,
            name=None) -> Workload:
     """A smaller copy of a workload with the same distributions."""

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ("pic_segment_build", "pic_compose", "pic_naive_add", "pic_validate_build",
               "pic_validate_compose", "pic_validate_naive_add", "pic_materialize_T",
               "pic_last_error", "pic_status_string", "pic_abi_version",
-              "pic_segment_build_workspace", "pic_compose_workspace"):
+              "pic_segment_build_workspace", "pic_compose_workspace", "pic_plan_dump"):
         assert n in names
 
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 1
+    assert lib.pic_abi_version() == 2
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -115,15 +115,16 @@ def test_validate_build_null_pointers(lib):
 
 
 def vcompose(lib, form=DENSE, B=1, H=2, dk=128, dv=128, pool=5, off=(0, 3, 3, 5),
-             idx=(4, 0, 1, 2, 3), That=True, ws_bytes=None, S_in=None):
+             idx=(4, 0, 1, 2, 3), That=True, ws_bytes=None, S_in=None, lam_out=None,
+             T_out=None):
     o, o_p = offsets(off)
     i = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
     i_p = i.ctypes.data_as(ctypes.c_void_p) if i.size else None
     R = len(o) - 1
     need = lib.pic_compose_workspace(R, int(o[-1]))
     return lib.pic_validate_compose(form, B, H, dk, dv, pool, P(0), P(1) if That else None,
-                                    P(2), R, o_p, i_p, S_in or P(3), P(4), P(5),
-                                    need if ws_bytes is None else ws_bytes)
+                                    P(2), R, o_p, i_p, S_in or P(3), P(4), lam_out, T_out,
+                                    P(5), need if ws_bytes is None else ws_bytes)
 
 
 def test_validate_compose(lib):
@@ -140,6 +141,71 @@ def test_validate_compose(lib):
     assert vcompose(lib, ws_bytes=1) == EWS
     assert vcompose(lib, dk=130) == EDIMS
     assert vcompose(lib, S_in=ctypes.c_void_p(A + 2)) == EALIGN
+
+
+def test_validate_compose_chain_pair(lib):
+    """The chain's own pair: dense needs log_scale_out and T_hat_out together;
+    the other forms take log_scale_out only."""
+    assert vcompose(lib, lam_out=P(6), T_out=P(7)) == OK
+    assert vcompose(lib, lam_out=P(6)) == ENULL
+    assert vcompose(lib, T_out=P(7)) == ENULL
+    assert vcompose(lib, form=SCALAR, That=False, lam_out=P(6)) == OK
+    assert vcompose(lib, form=DIAG, That=False, lam_out=P(6)) == OK
+    assert vcompose(lib, form=SCALAR, That=False, lam_out=P(6), T_out=P(7)) == EUNSUP
+    assert vcompose(lib, lam_out=P(6), T_out=ctypes.c_void_p(A + 6 * 4096 + 4)) == EALIGN
+
+
+# --------------------------------------------------------------------------
+# plan dump: exact bookkeeping against the oracle's definition of the plan
+# --------------------------------------------------------------------------
+
+def _plan_cases():
+    rng = np.random.default_rng(5)
+    cases = [[0, 64], [0, 0], [0, 63, 127, 127, 300, 364], [0, 1, 2, 3], [0, 4096] * 1]
+    for _ in range(20):
+        n = int(rng.integers(1, 40))
+        lens = rng.choice([0, 1, 63, 64, 65, 128, 200, 4096], size=n)
+        cases.append([0] + list(np.cumsum(lens)))
+    return cases
+
+
+def test_build_plan_matches_oracle_plan():
+    import oracle
+    from hybrid_caching_amd import _lib
+    for off in _plan_cases():
+        got = _lib.pic_plan_dump(_lib.PLAN_BUILD, off, limit=off[-1])
+        ref = oracle.plan_build(off)
+        assert got.dtype == np.int64 and np.array_equal(got, ref), off
+
+
+def test_compose_plan_matches_oracle_plan():
+    import oracle
+    from hybrid_caching_amd import _lib
+    rng = np.random.default_rng(6)
+    for R in (0, 1, 5, 64):
+        lens = rng.integers(0, 60, size=R)
+        off = [0] + list(np.cumsum(lens))
+        idx = rng.integers(0, 256, size=int(off[-1]))
+        got = _lib.pic_plan_dump(_lib.PLAN_COMPOSE, off, idx, limit=256)
+        ref = oracle.plan_compose(off, idx)
+        assert np.array_equal(got, ref), R
+
+
+def test_plan_dump_errors(lib):
+    o, o_p = offsets((0, 10, 5))
+    table = np.zeros((4, 5), dtype=np.int64)
+    t_p = table.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pic_plan_dump(0, 2, o_p, None, 5, t_p, 4) == EOFF
+    o, o_p = offsets((0, 10, 20))
+    assert lib.pic_plan_dump(0, 2, o_p, None, 21, t_p, 4) == EOFF   # last != n_tokens
+    assert lib.pic_plan_dump(0, 2, o_p, None, 20, t_p, 1) == EWS    # table too small
+    assert lib.pic_plan_dump(0, 2, o_p, None, 20, None, 4) == ENULL
+    assert lib.pic_plan_dump(0, 2, o_p, None, 20, t_p, 4) == OK
+    assert table[0].tolist() == [0, 0, 10, 1, 10] and table[1].tolist() == [1, 10, 10, 1, 10]
+    assert lib.pic_plan_dump(7, 2, o_p, None, 20, t_p, 4) == EUNSUP
+    i = np.array([0, 3], dtype=np.int32)
+    c, c_p = offsets((0, 2))
+    assert lib.pic_plan_dump(1, 1, c_p, i.ctypes.data_as(ctypes.c_void_p), 3, t_p, 4) == ECHAIN
 
 
 def test_validate_naive_add(lib):

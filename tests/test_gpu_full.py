@@ -8,7 +8,11 @@ per chain batch).
   sampled units (the oracle rebuilds them one by one from the same inputs)
   and sampled composed chains;
 * the slow-gate variants, where the carried term T(C2) S(C1) is a sizeable
-  part of the state, so composition really exercises T.
+  part of the state, so composition really exercises T;
+* composition-heavy reuse, 30 layers x 32 heads x d=128: a pool of 256
+  cached segments (512..8192 tokens) plus 512 fresh 2048-token segments,
+  64 requests composing 56-step chains, streamed layer by layer; sampled
+  units, chains and chain pairs against the oracle.
 """
 import numpy as np
 import pytest
@@ -150,6 +154,93 @@ def test_dense_slow_gates_full_length_sampled():
         return [(0, 0)]
 
     _dense_full("dense_30L_32x4096_slow", 2, samples, chains)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name,layers", [("reuse_256x30", None), ("reuse_256x30_slow", 2)])
+def test_reuse_workload_sampled(name, layers):
+    """At the base gates the carried term underflows (composition gives the
+    last segment's S0 exactly); the slow-gate variant makes it sizeable."""
+    import hybrid_caching_amd as pic
+    import torch
+    from oracle import DENSE
+    w = synth.WORKLOADS[name]
+    if layers is not None:
+        w = synth.scaled(w, layers=layers, name=w.name)
+    fw = synth.reuse_fresh_workload(w)
+    off, idx = synth.reuse_chains(w)
+    n_pool, n_fresh = w.n_seg, fw.n_seg
+    H, dk, dv = w.heads, w.dk, w.dv
+    dev = torch.device("cuda:0")
+    P = n_pool + n_fresh
+    buf = {"log_scale": torch.empty((P, 1, H), dtype=torch.float32, device=dev),
+           "T_hat": torch.empty((P, 1, H, dk, dk), dtype=torch.float32, device=dev),
+           "S0": torch.empty((P, 1, H, dk, dv), dtype=torch.float32, device=dev)}
+    pool_out = {key: t[:n_pool] for key, t in buf.items()}
+    fresh_out = {key: t[n_pool:] for key, t in buf.items()}
+    p_off, f_off = w.offsets(), fw.offsets()
+    rng = np.random.default_rng(105)
+    lens = np.diff(p_off)
+    sampled_layers = {0: [], min(17, w.layers - 1): [], w.layers - 1: []}
+    for layer in sampled_layers:
+        sampled_layers[layer] = {
+            "pool": [int(np.argmin(lens)), int(np.argmax(lens)), int(rng.integers(n_pool))],
+            "fresh": [int(rng.integers(n_fresh))],
+            "heads": [int(rng.integers(H)) for _ in range(3)],
+            "reqs": [int(rng.integers(w.extra["n_req"])) for _ in range(2)]}
+
+    def unit(x, offsets, s, h):
+        sl = slice(int(offsets[s]), int(offsets[s + 1]))
+        f = lambda t: t[sl, h].float().cpu().numpy()[None, :, None]
+        return f(x["k"]), f(x["v"]), f(x["alpha"]), f(x["beta"])
+
+    for layer in range(w.layers):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        pic.pic_segment_build(DENSE, x["k"][None], x["v"][None], x["alpha"][None],
+                              x["beta"][None], p_off, out=pool_out)
+        y = synth.torch_layer_inputs(fw, layer, dev)
+        pic.pic_segment_build(DENSE, y["k"][None], y["v"][None], y["alpha"][None],
+                              y["beta"][None], f_off, out=fresh_out)
+        want = layer in sampled_layers
+        res = pic.pic_compose(DENSE, buf["log_scale"], buf["T_hat"], buf["S0"], off, idx,
+                              want_pair=want)
+        torch.cuda.synchronize()
+        if not want:
+            del x, y
+            continue
+        S_out, lam_out, T_out = res
+        smp = sampled_layers[layer]
+        h = smp["heads"][0]
+        for s in smp["pool"]:
+            ref = oracle.build(DENSE, *unit(x, p_off, s, h), [0, int(lens[s])])
+            gpu = {key: t[s, 0, h].cpu().numpy()[None, None, None] for key, t in buf.items()}
+            report(f"{name} layer {layer}: pool unit {s} ({int(lens[s])} tokens), head {h}")
+            assert_pair_close(gpu, ref, DENSE, TOL_BF16)
+        for s in smp["fresh"]:
+            ref = oracle.build(DENSE, *unit(y, f_off, s, h), [0, fw.seg_lens[s]])
+            gpu = {key: t[n_pool + s, 0, h].cpu().numpy()[None, None, None]
+                   for key, t in buf.items()}
+            report(f"{name} layer {layer}: fresh unit {s}, head {h}")
+            assert_pair_close(gpu, ref, DENSE, TOL_BF16)
+        for r, hh in zip(smp["reqs"], smp["heads"][1:]):
+            ids = idx[off[r]:off[r + 1]]
+            sub = {key: t[torch.as_tensor(ids.astype(np.int64), device=dev), 0, hh]
+                   .cpu().numpy()[:, None, None] for key, t in buf.items()}
+            n = len(ids)
+            ref_S, ref_l, ref_T = oracle.compose(DENSE, sub["log_scale"], sub["T_hat"],
+                                                 sub["S0"], [0, n], list(range(n)),
+                                                 want_pair=True)
+            e = max_rel_units(S_out[r, 0, hh].cpu().numpy(), ref_S[0, 0, 0])
+            eT = max_rel_units(T_out[r, 0, hh].cpu().numpy(), ref_T[0, 0, 0])
+            el = lam_err(lam_out[r, 0, hh].cpu().numpy(), ref_l[0, 0, 0])
+            rho = rho_of(ref_S[0], sub["S0"][-1])
+            report(f"{name} layer {layer}: chain (req {r}, head {hh}, {n} steps): "
+                   f"compose err {e:.3e}, chain That err {eT:.3e}, lambda err {el:.1e}, "
+                   f"rho {rho:.3f}")
+            assert e <= 1e-4 and eT <= 1e-4 and el <= 1e-5
+            if name.endswith("_slow"):
+                assert rho >= 0.1
+        del x, y
 
 
 def test_all_segments_empty():

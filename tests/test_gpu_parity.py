@@ -219,6 +219,55 @@ def test_compose_matches_oracle(form, d, with_sin):
     assert max_rel_units(nv.cpu().numpy(), ref_nv) <= 1e-6
 
 
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("d", [32, 128])
+def test_chain_pair_matches_oracle(form, d):
+    """The chain's own pair (sum of log scales; That_pn ... That_p1 for the
+    dense form), including an empty chain (0, I) and repeated entries."""
+    import hybrid_caching_amd as pic
+    P, B, H = 10, 2, 3
+    lam, That, S = random_pool(form, P, B, H, d, d, seed=900 + d + form)
+    off, idx = CHAINS
+    S_out, lam_out, T_out = pic.pic_compose(form, to_dev(lam), to_dev(That), to_dev(S), off,
+                                            idx, want_pair=True)
+    ref_S, ref_lam, ref_T = oracle.compose(form, lam, That, S, off, idx, want_pair=True)
+    assert max_rel_units(S_out.cpu().numpy(), ref_S) <= TOL_F32
+    el = lam_err(lam_out.cpu().numpy(), ref_lam)
+    assert el <= 1e-5, el
+    assert np.all(lam_out.cpu().numpy()[1] == 0.0)  # empty chain: lambda = 0
+    if form == DENSE:
+        got_T = T_out.cpu().numpy()
+        e = max_rel_units(got_T, ref_T)
+        report(f"chain That err {e:.3e}")
+        assert e <= TOL_F32
+        assert np.array_equal(got_T[1], np.broadcast_to(np.eye(d, dtype=np.float32), got_T[1].shape))
+    else:
+        assert T_out is None
+
+
+def test_chain_pair_composes_like_its_chain():
+    """Folding a run of pairs into one pair and composing with it gives the
+    same state as composing the run (associativity, the merge a sharded build
+    would do)."""
+    import hybrid_caching_amd as pic
+    import torch
+    P, B, H, d = 8, 1, 4, 128
+    lam, That, S = random_pool(DENSE, P, B, H, d, d, seed=77, lam_range=(-0.05, 0.0))
+    S_in = synth.random_state((1, B, H, d, d), seed=8)
+    dl, dT, dS = to_dev(lam), to_dev(That), to_dev(S)
+    seq = pic.pic_compose(DENSE, dl, dT, dS, [0, 8], list(range(8)), to_dev(S_in))
+    S_a, l_a, T_a = pic.pic_compose(DENSE, dl, dT, dS, [0, 5], [0, 1, 2, 3, 4], want_pair=True)
+    pool_l = torch.cat([l_a, dl[5:]])
+    pool_T = torch.cat([T_a, dT[5:]])
+    pool_S = torch.cat([S_a, dS[5:]])
+    merged = pic.pic_compose(DENSE, pool_l, pool_T, pool_S, [0, 4], [0, 1, 2, 3], to_dev(S_in))
+    ref = oracle.compose(DENSE, lam, That, S, [0, 8], list(range(8)), S_in)
+    e_seq = max_rel_units(seq.cpu().numpy(), ref)
+    e_merged = max_rel_units(merged.cpu().numpy(), ref)
+    report(f"merged-chain err {e_merged:.3e} (sequential {e_seq:.3e})")
+    assert e_seq <= TOL_F32 and e_merged <= TOL_F32
+
+
 def test_compose_in_place_and_empty_chains():
     import hybrid_caching_amd as pic
     import torch
