@@ -38,7 +38,7 @@ CSRC = os.path.join(ROOT, "hybrid_caching_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # the source files each timed kernel is compiled from
 KERNEL_SOURCES = {
-    "build_dense_pipe_kernel": ["k_build_dense_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_dense_ws_kernel": ["k_build_dense_ws.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_sd_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
@@ -352,10 +352,10 @@ def main(argv=None):
         "composes_per_s": composes / t_comp,
         "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3,
                "step_events": t_step_ev * 1e3},
-        "roofline": {"kernel": "build_dense_pipe_kernel", "bound": "mfma", "achieved": achieved_tf,
+        "roofline": {"kernel": "build_dense_ws_kernel", "bound": "mfma", "achieved": achieved_tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tf / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("build_dense_pipe_kernel", w.name),
+                     "traffic": measured_traffic("build_dense_ws_kernel", w.name),
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes": build_bytes(N, B, H, dk, dv, n_seg)},
         "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",

@@ -415,8 +415,8 @@ hipError_t launch_dense_t(const BuildArgs& a, hipStream_t s) {
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s) {
   const int d = a.dk > a.dv ? a.dk : a.dv;
   const int dp = d <= 32 ? 32 : (d <= 64 ? 64 : 128);
-  // bf16 inputs take the software-pipelined kernel (k_build_dense_pipe.hip)
-  if (a.qkv_bf16) return launch_build_dense_pipe(a, s);
+  // bf16 inputs take the producer/consumer kernel (k_build_dense_ws.hip)
+  if (a.qkv_bf16) return launch_build_dense_ws(a, s);
   switch (dp) {
     case 32: return launch_dense_t<32, false>(a, s);
     case 64: return launch_dense_t<64, false>(a, s);
