@@ -1,47 +1,59 @@
 // k_build_dense_ws.hip -- build of the dense gated-delta pair
 // (lambda_C, That_C, S(C|0)) for bf16 k/v with producer and consumer waves.
 // Same chunked arithmetic as k_build_dense.hip, which serves fp32 inputs
-// (see the derivation there).
+// (see the derivation there), on sub-chunks of 32 tokens.
 // [xix.ai HYPIC article (French), paragraph on linear layers: T_C as the
 //  product of the segment's token transitions and S(C|0) from a zero start;
 //  dense delta-rule transitions are the heaviest family.]
 //
 // One workgroup per (segment, layer, head) with DP/32 consumer waves and four
-// producer waves (on a 128-wide head: one of each per SIMD).
+// producer waves (on a 128-wide head: one of each per SIMD).  The segment is
+// staged 64 tokens at a time (a "chunk"); the UT transform works on the two
+// 32-token halves of a chunk ("sub-chunks" s = 0, 1), which are independent
+// of each other, so their triangular systems are solved side by side and
+// each is only 32 x 32.
 //
 // Consumer wave c keeps columns [32c, 32c+32) of BOTH running matrices, S and
-// That, in MFMA accumulators for the whole segment, and only runs the chain
-// of a chunk (64 tokens):
-//   (A)  S <- gamma S;  N = -U That,  M = W - U S          (split-bf16 MFMA)
-//   (B)  That += K^T N,  S += K^T M                          (split-bf16 MFMA)
-//   (W)  W = A' V for the next chunk, as the seed of M       (MFMA)
+// That, in MFMA accumulators for the whole segment, and only runs the chain;
+// for sub-chunk s of a chunk:
+//   (A_s)  S <- gamma_s S;  N_s = -U_s That,  M_s = W_s - U_s S   (split-bf16 MFMA)
+//   (B_s)  That += K_s^T N_s,  S += K_s^T M_s                     (split-bf16 MFMA)
+//   (W)    W_s = A'_s V_s of the next chunk, as the seeds of M_s   (MFMA)
 // Producer waves prepare chunk ci+1 while the consumers chain chunk ci:
-//   stage K (row-major and transposed), V^T and the gates; L = diag(beta)
-//   strictly-lower(K K^T); X = (I + L)^{-1} (16x16 blocks by substitution,
-//   16x16 merges, one 32x32 merge); A = X diag(beta), A' = A diag(r) split
-//   into bf16 hi/lo; U^T = K^T A^T (MFMA).
-// so that S <- gamma S + K^T (W - gamma U S) and That <- That - K^T (U That).
+//   stage K (row-major and transposed), V^T and the gates; G_ss = K_s K_s^T;
+//   X_s = (I + diag(beta) strictly-lower(G_ss))^{-1} (16x16 blocks by
+//   substitution, one 16x16 merge); A_s = X_s diag(beta), A'_s = A_s diag(r)
+//   split into bf16 hi/lo; U_s^T = K_s^T A_s^T (MFMA).
+// so that S <- gamma S + K^T (W - gamma U S) and That <- That - K^T (U That)
+// per sub-chunk.
 //
-// Hand-over layouts.  The producers compute U^T tile by tile; an accumulator
-// of a U^T tile holds, in lane (g, token), exactly the A-operand fragment the
-// consumer lane (g, token) needs for U . state with the state fed from its own
-// accumulators (the permuted K order of mfma_util.hpp), so -U goes to LDS as
-// per-lane 16-byte hi/lo fragments and is read back with one b128 load each.
-// Token-indexed K dimensions (K^T, V^T, the columns of A and A') are stored
-// with positions 4-7 and 8-11 of every 16 tokens swapped: reading positions
-// 8g .. 8g+7 then yields tokens 4g + {0..3} and 4g + 8 + {0..3}, the order
-// of an accumulator half used as a B operand.
+// Hand-over layouts.  The producers compute U_s^T tile by tile; an
+// accumulator of a U^T tile holds, in lane (g, token), exactly the A-operand
+// fragment the consumer lane (g, token) needs for U . state with the state fed
+// from its own accumulators (the permuted K order of mfma_util.hpp), so -U
+// goes to LDS as per-lane 16-byte hi/lo fragments and is read back with one
+// b128 load each.  Token-indexed K dimensions (K^T, V^T, the columns of A and
+// A') are stored with positions 4-7 and 8-11 of every 16 tokens swapped:
+// reading positions 8g .. 8g+7 then yields tokens 4g + {0..3} and
+// 4g + 8 + {0..3}, the order of an accumulator half used as a B operand.
+// In K^T and V^T the eight 16-byte chunks of a row are also XOR-swizzled by
+// the row's 8-row group, so that the transposed writes of staging spread
+// over the LDS banks; readers apply the same swizzle.
+//
+// Coalesced loads: a load instruction of a producer wave reads whole 256-byte
+// head rows (16 lanes per token row, four token rows), each lane taking
+// tokens t and t+1 of one 8-channel group, so that it can write (t, t+1)
+// pairs into the transposed layouts.
 //
 // Both roles run their own loop over chunk cycles with the same sequence of
-// eight workgroup barriers per cycle:
-//   I0 stage K, V             | S *= gamma, (A) k-steps 0-1/4
-//   I1 G = K K^T; gates       | (A) 1/4-2/4
-//   I2 16x16 diagonal blocks  | (A) 2/4-3/4
-//   I3 Y = L X (merges, 1/2)  | (A) 3/4-4/4
-//   I4 X = -X Y (merges, 2/2) | (B) token k-step 0
-//   I5 32x32 merge            | (B) token k-steps 1, 2
-//   I6 split A, A'            | (B) token k-step 3
-//   I7 U^T = K^T A^T -> LDS   | W = A' V -> M seed, N seed 0
+// seven workgroup barriers per cycle:
+//   I0 stage K, V               | S *= gamma_0, (A_0) first half
+//   I1 G_00, G_11; gates        | (A_0) second half
+//   I2 16x16 diagonal blocks    | (B_0)
+//   I3 Y = L X (merge, 1/2)     | S *= gamma_1, (A_1) first half
+//   I4 X = -X Y (merge, 2/2)    | (A_1) second half
+//   I5 split A, A'              | (B_1)
+//   I6 U^T = K^T A^T -> LDS     | W = A' V -> M seeds, N seeds 0
 // Cycle ci prepares chunk ci and chains chunk ci-1 (n_chunks + 1 cycles).
 #include "mfma_util.hpp"
 #include "pic_internal.hpp"
@@ -72,15 +84,15 @@ struct WsLds {
   static constexpr int KT = XM + C * X_LD * 4;          // K^T, two buffers (chunk parity)
   static constexpr int VT = KT + 2 * DP * KT_LD * 2;    // V^T
   static constexpr int UF = VT + DP * KT_LD * 2;        // -U fragments
-  static constexpr int UF_BYTES = 2 * NT * 2 * 2 * 64 * 16;  // [mt][t][h][hi,lo][lane] x 16 B
+  static constexpr int UF_BYTES = 2 * NT * 2 * 2 * 64 * 16;  // [s][t][h][hi,lo][lane] x 16 B
   static constexpr int GB = UF + UF_BYTES;              // beta of the chunk's tokens
   static constexpr int GR = GB + C * 4;                 // r = gate ratio per token
-  static constexpr int GG = GR + C * 4;                 // gamma per chunk parity
+  static constexpr int GG = GR + C * 4;                 // gamma [chunk parity][sub-chunk]
   static constexpr int GA = GG + 16;                    // alpha, beta of the staged chunk
   static constexpr int GBT = GA + C * 4;
   static constexpr int TOTAL = GBT + C * 4;
   static_assert(KT % 16 == 0 && VT % 16 == 0 && UF % 16 == 0 && XM % 16 == 0, "alignment");
-  static_assert(A_BYTES % 16 == 0 && LM % 16 == 0, "alignment");
+  static_assert(A_BYTES % 16 == 0 && LM % 16 == 0 && GB % 16 == 0, "alignment");
 };
 
 // storage position of token t inside a K dimension (swap bits 2 and 3)
@@ -99,10 +111,35 @@ __device__ __forceinline__ uint4 ws_pick(bool ok, uint4 x) {
   return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
 }
 
-// byte offset of a -U fragment: tile (mt, t), half h, part (0 hi, 1 lo), lane
+// element offset of 16-byte chunk `chunk` of row `row` in a swizzled K^T / V^T
+template <int LD>
+__device__ __forceinline__ int kt_at(int row, int chunk) {
+  return row * LD + 8 * (chunk ^ ((row >> 3) & 7));
+}
+
+// The same offset for rows 32 t + cl read by lane (g, cl) at chunk
+// 4 s + 2 hh + g: the swizzle only flips bits of the chunk index, so it is
+// a per-lane base for each half hh plus a constant for (t, s).
+template <int LD>
+__device__ __forceinline__ int kt_lane_base(int cl, int g, int hh) {
+  return cl * LD + 8 * (g ^ ((cl >> 3) & 1)) + 16 * (hh ^ ((cl >> 4) & 1));
+}
+template <int LD>
+__device__ __forceinline__ int kt_tile(int t, int s) {
+  return 32 * t * LD + 32 * (s ^ (t & 1));
+}
+
+// a copy of v the compiler cannot see through: keeps per-lane address
+// arithmetic inside a loop instead of holding it in registers across it
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// byte offset of a -U fragment: sub-chunk s, channel tile t, half h, part (0 hi, 1 lo), lane
 template <int NT>
-__device__ __forceinline__ int uf_off(int mt, int t, int h, int part, int lane) {
-  return ((((mt * NT + t) * 2 + h) * 2 + part) * 64 + lane) * 16;
+__device__ __forceinline__ int uf_off(int s, int t, int h, int part, int lane) {
+  return ((((s * NT + t) * 2 + h) * 2 + part) * 64 + lane) * 16;
 }
 
 template <int DP>
@@ -153,88 +190,92 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
       for (int q = 0; q < 16; ++q) XT[t][q] = (t * 32 + acc_row(q, g) == c * 32 + cl) ? 1.f : 0.f;
     }
     PM[0] = PM[1] = PN[0] = PN[1] = zero16();
+    constexpr int NK = 2 * NT;  // channel k-steps of 16
 
-    // (A) over channel k-steps [k0, k1): N += (-U) That, M += (-U) S
-    auto chain_a = [&](int k0, int k1) {
+    // (A_s) over channel k-steps [k0, k1): N_s += (-U_s) That, M_s += (-U_s) S
+    auto chain_a = [&](int s, int k0, int k1) {
 #pragma unroll
-      for (int ks = 0; ks < 2 * NT; ++ks) {
+      for (int ks = 0; ks < NK; ++ks) {
         if (ks < k0 || ks >= k1) continue;
         const int t = ks >> 1, hh = ks & 1;
         bf16x8 th, tl, sh, sl;
         split_acc_half(XT[t], hh, th, tl);
         split_acc_half(XS[t], hh, sh, sl);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 uh = *reinterpret_cast<const bf16x8*>(Uf + uf_off<NT>(mt, t, hh, 0, lane));
-          const bf16x8 ul = *reinterpret_cast<const bf16x8*>(Uf + uf_off<NT>(mt, t, hh, 1, lane));
-          PN[mt] = mfma32(ul, th, PN[mt]);
-          PN[mt] = mfma32(uh, tl, PN[mt]);
-          PN[mt] = mfma32(uh, th, PN[mt]);
-          PM[mt] = mfma32(ul, sh, PM[mt]);
-          PM[mt] = mfma32(uh, sl, PM[mt]);
-          PM[mt] = mfma32(uh, sh, PM[mt]);
-        }
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(Uf + uf_off<NT>(s, t, hh, 0, lane));
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(Uf + uf_off<NT>(s, t, hh, 1, lane));
+        PN[s] = mfma32(ul, th, PN[s]);
+        PM[s] = mfma32(ul, sh, PM[s]);
+        PN[s] = mfma32(uh, tl, PN[s]);
+        PM[s] = mfma32(uh, sl, PM[s]);
+        PN[s] = mfma32(uh, th, PN[s]);
+        PM[s] = mfma32(uh, sh, PM[s]);
       }
     };
-    // (B) over token k-steps [k0, k1): That += K^T N, S += K^T M
-    auto chain_b = [&](int k0, int k1, const __bf16* Ktp) {
+    // (B_s): That += K_s^T N_s, S += K_s^T M_s over the sub-chunk's 32 tokens
+    auto chain_b = [&](int s, const __bf16* Ktp) {
+      const int ln = opaque(lane);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        if (kt < k0 || kt >= k1) continue;
-        const int mt = kt >> 1, hh = kt & 1;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kb = kt_lane_base<KT>(ln & 31, ln >> 5, hh);
         bf16x8 nh, nl, mh, ml;
-        split_acc_half(PN[mt], hh, nh, nl);
-        split_acc_half(PM[mt], hh, mh, ml);
+        split_acc_half(PN[s], hh, nh, nl);
+        split_acc_half(PM[s], hh, mh, ml);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const bf16x8 kf = lds_load8(Ktp + (t * 32 + cl) * KT + 32 * mt + 16 * hh + 8 * g);
+          const bf16x8 kf = lds_load8(Ktp + kb + kt_tile<KT>(t, s));
           XT[t] = mfma32(kf, nl, XT[t]);
-          XT[t] = mfma32(kf, nh, XT[t]);
           XS[t] = mfma32(kf, ml, XS[t]);
+          XT[t] = mfma32(kf, nh, XT[t]);
           XS[t] = mfma32(kf, mh, XS[t]);
         }
       }
+    };
+    auto scale_s = [&](float gam) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) XS[t] *= gam;
     };
 
 #pragma unroll 1
     for (int ci = 0; ci <= n_chunks; ++ci) {
       const bool chain = ci > 0, prep = ci < n_chunks;
       const __bf16* Ktp = Kt0 + ((ci - 1) & 1) * (DP * KT);
+      const float* gamma = gg + 2 * ((ci - 1) & 1);
       __syncthreads();  // I0: -U and gamma of chunk ci-1 are in LDS
       if (chain) {
-        const float gam = gg[(ci - 1) & 1];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) XS[t] *= gam;
-        chain_a(0, (2 * NT) / 4);
+        scale_s(gamma[0]);
+        chain_a(0, 0, NK / 2);
       }
       __syncthreads();  // I1
-      if (chain) chain_a((2 * NT) / 4, (2 * NT * 2) / 4);
+      if (chain) chain_a(0, NK / 2, NK);
       __syncthreads();  // I2
-      if (chain) chain_a((2 * NT * 2) / 4, (2 * NT * 3) / 4);
+      if (chain) chain_b(0, Ktp);
       __syncthreads();  // I3
-      if (chain) chain_a((2 * NT * 3) / 4, 2 * NT);
+      if (chain) {
+        scale_s(gamma[1]);
+        chain_a(1, 0, NK / 2);
+      }
       __syncthreads();  // I4
-      if (chain) chain_b(0, 1, Ktp);
+      if (chain) chain_a(1, NK / 2, NK);
       __syncthreads();  // I5
-      if (chain) chain_b(1, 3, Ktp);
-      __syncthreads();  // I6
-      if (chain) chain_b(3, 4, Ktp);
-      __syncthreads();  // I7: A' and V^T of chunk ci are in LDS
+      if (chain) chain_b(1, Ktp);
+      __syncthreads();  // I6: A' and V^T of chunk ci are in LDS
       if (prep) {
+        const int ln = opaque(lane);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int s = 0; s < 2; ++s) {
           f32x16 acc = zero16();
 #pragma unroll
-          for (int ks = 0; ks < C / 16; ++ks) {
-            const int kc = ks * 16 + 8 * g;
-            const bf16x8 ph = lds_load8(Bh + (mt * 32 + cl) * AL + kc);
-            const bf16x8 pl = lds_load8(Bl + (mt * 32 + cl) * AL + kc);
-            const bf16x8 vf = lds_load8(Vt + (c * 32 + cl) * KT + kc);
+          for (int kk = 0; kk < 2; ++kk) {
+            const int kc = 32 * s + 16 * kk + 8 * g;
+            const bf16x8 ph = lds_load8(Bh + (s * 32 + cl) * AL + kc);
+            const bf16x8 pl = lds_load8(Bl + (s * 32 + cl) * AL + kc);
+            const bf16x8 vf = lds_load8(Vt + kt_lane_base<KT>(ln & 31, ln >> 5, kk) +
+                                        kt_tile<KT>(c, s));
             acc = mfma32(pl, vf, acc);
             acc = mfma32(ph, vf, acc);
           }
-          PM[mt] = acc;
-          PN[mt] = zero16();
+          PM[s] = acc;
+          PN[s] = zero16();
         }
       }
     }
@@ -269,20 +310,20 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
     const int p = pw * 64 + lane;            // producer thread 0..255
     constexpr int NCG = DP / 8;              // 8-channel groups
     constexpr int NIT = (32 * NCG + kPT - 1) / kPT;  // staging items per thread
+    constexpr int PPI = kPT / NCG;                   // token pairs per item round
     float lam = 0.f;
 
-    // strictly upper 16x16 blocks of X stay zero for the whole segment
-    for (int e = p; e < 6 * 256; e += kPT) {
-      const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      const int bi = (blk < 3) ? 0 : ((blk < 5) ? 1 : 2);
-      const int bj = (blk < 3) ? blk + 1 : ((blk < 5) ? blk - 1 : 3);
-      Xm[(16 * bi + r) * XL + 16 * bj + cc] = 0.f;
+    // strictly upper 16x16 blocks of each sub-chunk's X stay zero for the
+    // whole segment (the blocks coupling the two sub-chunks are never read)
+    for (int e = p; e < 2 * 256; e += kPT) {
+      const int s = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+      Xm[(32 * s + r) * XL + 32 * s + 16 + cc] = 0.f;
     }
 
     // register prefetch of one chunk: item i of this thread is tokens
-    // (t0, t0+1) x channels [8 cg, 8 cg + 8), t0 = 2 (lane & 31),
-    // cg = 2 pw + lane / 32 + 8 i: the transposed LDS writes of a wave fall
-    // on consecutive banks.  Producer wave 0 also takes alpha, beta of token lane.
+    // (t0, t0+1) x channels [8 cg, 8 cg + 8) with cg = p % 16 and
+    // t0 = 2 (p / 16 + 16 i): each load instruction of a wave covers four
+    // whole 256-byte token rows.
     uint4 pk[NIT][2], pv[NIT][2];
     // alpha, beta of token lane, prefetched by every producer wave with the
     // k/v items: loads without a select on the loaded value, so that no wait
@@ -292,17 +333,17 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
     auto prefetch = [&](int ci) {
       const int64_t c0 = t_begin + int64_t(ci) * C;
       const int len = (t_end - c0 < C) ? int(t_end - c0) : C;
-      const int t0 = 2 * (lane & 31);
-      // clamped (in-segment, in-head) addresses; zeroing happens at staging
-      const int ta = min(t0, len - 1), tb = min(t0 + 1, len - 1);
-      const int64_t ra = (int64_t(b) * N + c0 + ta) * H + h;
-      const int64_t rb = (int64_t(b) * N + c0 + tb) * H + h;
       const __bf16* kp = static_cast<const __bf16*>(a.k);
       const __bf16* vp = static_cast<const __bf16*>(a.v);
+      const int cg = p % NCG;
+      const int ik = min(8 * cg, dk - 8), iv = min(8 * cg, dv - 8);
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        const int cg = 2 * pw + (lane >> 5) + 8 * i;
-        const int ik = min(8 * cg, dk - 8), iv = min(8 * cg, dv - 8);
+        const int t0 = 2 * (p / NCG + PPI * i);
+        // clamped (in-segment, in-head) addresses; zeroing happens at staging
+        const int ta = min(t0, len - 1), tb = min(t0 + 1, len - 1);
+        const int64_t ra = (int64_t(b) * N + c0 + ta) * H + h;
+        const int64_t rb = (int64_t(b) * N + c0 + tb) * H + h;
         pk[i][0] = *reinterpret_cast<const uint4*>(kp + ra * dk + ik);
         pk[i][1] = *reinterpret_cast<const uint4*>(kp + rb * dk + ik);
         pv[i][0] = *reinterpret_cast<const uint4*>(vp + ra * dv + iv);
@@ -324,13 +365,12 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
       // ---------------- I0: stage chunk ci; prefetch chunk ci+1
       __syncthreads();
       if (prep) {
-        const int t0 = 2 * (lane & 31);
-        const int pos = tpos(t0);
+        const int cg = p % NCG, i0 = 8 * cg;
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-          const int cg = 2 * pw + (lane >> 5) + 8 * i;
-          if (cg < NCG) {
-            const int i0 = 8 * cg;
+          const int t0 = 2 * (p / NCG + PPI * i);
+          if (t0 < C) {
+            const int pos = tpos(t0);
             const uint4 k0 = ws_pick(i0 < dk && t0 < len, pk[i][0]);
             const uint4 k1 = ws_pick(i0 < dk && t0 + 1 < len, pk[i][1]);
             const uint4 v0 = ws_pick(i0 < dv && t0 < len, pv[i][0]);
@@ -339,8 +379,9 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
             *reinterpret_cast<uint4*>(Kr + (t0 + 1) * KR + i0) = k1;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              *reinterpret_cast<unsigned*>(Kt + (i0 + j) * KT + pos) = ws_pair(k0, k1, j);
-              *reinterpret_cast<unsigned*>(Vt + (i0 + j) * KT + pos) = ws_pair(v0, v1, j);
+              const int at = kt_at<KT>(i0 + j, pos >> 3) + (pos & 7);
+              *reinterpret_cast<unsigned*>(Kt + at) = ws_pair(k0, k1, j);
+              *reinterpret_cast<unsigned*>(Vt + at) = ws_pair(v0, v1, j);
             }
           }
         }
@@ -351,36 +392,41 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
         if (ci + 1 < n_chunks) prefetch(ci + 1);
       }
 
-      // ---------------- I1: G = strictly-lower(K K^T) (waves 0-2; row r of L
-      // is beta_r times row r of G, applied where L is read); gates (wave 3)
+      // ---------------- I1: G_ss = strictly-lower(K_s K_s^T) (waves 0, 1; row
+      // r of L is beta_r times row r of G, applied where L is read); gates of
+      // both sub-chunks (wave 3, one sub-chunk per half wave)
       __syncthreads();
-      if (prep && pw < 3) {
-        const int mt = (pw == 0) ? 0 : 1, nt = (pw == 2) ? 1 : 0;
+      if (prep && pw < 2) {
+        const int s = pw;
         f32x16 acc0 = zero16(), acc1 = zero16();  // two chains of dependent MFMAs
 #pragma unroll
         for (int ks = 0; ks < DP / 16; ++ks) {
           const int kc = ks * 16 + 8 * g;
-          const bf16x8 ak = lds_load8(Kr + (mt * 32 + cl) * KR + kc);
-          const bf16x8 bk = lds_load8(Kr + (nt * 32 + cl) * KR + kc);
+          const bf16x8 ak = lds_load8(Kr + (s * 32 + cl) * KR + kc);
           if (ks & 1)
-            acc1 = mfma32(ak, bk, acc1);
+            acc1 = mfma32(ak, ak, acc1);
           else
-            acc0 = mfma32(ak, bk, acc0);
+            acc0 = mfma32(ak, ak, acc0);
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int r = mt * 32 + acc_row(q, g), cc = nt * 32 + cl;
-          Lm[r * XL + cc] = (cc < r) ? acc0[q] + acc1[q] : 0.f;
+          const int r = acc_row(q, g);
+          Lm[(s * 32 + r) * XL + s * 32 + cl] = (cl < r) ? acc0[q] + acc1[q] : 0.f;
         }
       }
       if (prep && pw == kProducers - 1) {
-        const float x = wave_inclusive_scan(lane < len ? log2f(ga[lane]) : 0.f);
-        const float bend =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+        const float x = half_wave_scan(lane < len ? log2f(ga[lane]) : 0.f);
+        const int xi = __builtin_bit_cast(int, x);
+        const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 31));
+        const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 63));
+        const float bend = g ? e1 : e0;
         gb[lane] = lane < len ? (a.beta ? gbt[lane] : 1.f) : 0.f;
         gr[lane] = exp2f(bend - x);
-        if (lane == 0) gg[ci & 1] = exp2f(bend);
-        lam += bend;
+        if (lane == 0) {
+          gg[2 * (ci & 1)] = exp2f(e0);
+          gg[2 * (ci & 1) + 1] = exp2f(e1);
+        }
+        lam += e0 + e1;
       }
 
       // ---------------- I2: 16x16 diagonal blocks of X by substitution
@@ -407,22 +453,22 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
         for (int j = 0; j < 4; ++j) xo[j] = (4 * pp + j == cc) ? 1.f : 0.f;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
-          float s = 0.f;
+          float sm = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s = fmaf(lv[r][j], xo[j], s);
-          s = group_sum<4>(s);
-          if (r > cc && pp == (r >> 2)) xo[r & 3] = -s;
+          for (int j = 0; j < 4; ++j) sm = fmaf(lv[r][j], xo[j], sm);
+          sm = group_sum<4>(sm);
+          if (r > cc && pp == (r >> 2)) xo[r & 3] = -sm;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) Xm[(o + 4 * pp + j) * XL + o + cc] = xo[j];
       }
 
-      // ---------------- I3: 16x16 merges, Y = L_10 X_00 and L_32 X_22
-      __syncthreads();
+      // ---------------- I3: 16x16 merges, Y = L_10 X_00 of each sub-chunk
       // (each thread: one row, two adjacent columns; vector LDS loads)
+      __syncthreads();
       if (prep) {
-        const int inst = p >> 7, r = (p >> 3) & 15, c2 = 2 * (p & 7);
-        const int orow = inst ? 48 : 16, ocol = inst ? 32 : 0;
+        const int s = p >> 7, r = (p >> 3) & 15, c2 = 2 * (p & 7);
+        const int orow = 32 * s + 16, ocol = 32 * s;
         float lrow[16];
 #pragma unroll
         for (int q = 0; q < 16; q += 4) {
@@ -437,14 +483,14 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
           s1 = fmaf(lrow[q], x.y, s1);
         }
         const float bw = gb[orow + r];
-        *reinterpret_cast<float2*>(Ym + inst * 256 + r * 16 + c2) = make_float2(bw * s0, bw * s1);
+        *reinterpret_cast<float2*>(Ym + s * 256 + r * 16 + c2) = make_float2(bw * s0, bw * s1);
       }
 
-      // ---------------- I4: X_10 = -X_11 Y, X_32 = -X_33 Y
+      // ---------------- I4: X_10 = -X_11 Y of each sub-chunk
       __syncthreads();
       if (prep) {
-        const int inst = p >> 7, r = (p >> 3) & 15, c2 = 2 * (p & 7);
-        const int orow = inst ? 48 : 16, ocol = inst ? 32 : 0;
+        const int s = p >> 7, r = (p >> 3) & 15, c2 = 2 * (p & 7);
+        const int orow = 32 * s + 16, ocol = 32 * s;
         float xrow[16];
 #pragma unroll
         for (int q = 0; q < 16; q += 4) {
@@ -454,100 +500,57 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const float2 y = *reinterpret_cast<const float2*>(Ym + inst * 256 + q * 16 + c2);
+          const float2 y = *reinterpret_cast<const float2*>(Ym + s * 256 + q * 16 + c2);
           s0 = fmaf(xrow[q], y.x, s0);
           s1 = fmaf(xrow[q], y.y, s1);
         }
         *reinterpret_cast<float2*>(Xm + (orow + r) * XL + ocol + c2) = make_float2(-s0, -s1);
       }
 
-      // ---------------- I5: 32x32 merge X_[2:4][0:2] = -X_22 L_21 X_11
-      // on split-bf16 MFMA (producer wave 0)
-      __syncthreads();
-      if (prep && pw == 0) {
-        const float b21 = gb[32 + cl];
-        f32x16 y = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float av[8], bv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            av[j] = b21 * Lm[(32 + cl) * XL + 16 * ks + 8 * g + j];
-            bv[j] = Xm[(16 * ks + 8 * g + j) * XL + cl];
-          }
-          bf16x8 ah, al, bh2, bl2;
-          split8(av, ah, al);
-          split8(bv, bh2, bl2);
-          y = mfma32(al, bh2, y);
-          y = mfma32(ah, bl2, y);
-          y = mfma32(ah, bh2, y);
-        }
-        f32x16 z = zero16();
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 yh, yl;
-          split_acc_half(y, hh, yh, yl);
-          float av[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) av[j] = Xm[(32 + cl) * XL + 32 + kperm(hh, g, j)];
-          bf16x8 ah, al;
-          split8(av, ah, al);
-          z = mfma32(al, yh, z);
-          z = mfma32(ah, yl, z);
-          z = mfma32(ah, yh, z);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) Xm[(32 + acc_row(q, g)) * XL + cl] = -z[q];
-      }
-
-      // ---------------- I6: A = X diag(beta), A' = A diag(r), split hi/lo,
-      // columns stored at permuted positions (region of K, L, Y is dead)
+      // ---------------- I5: A_s = X_s diag(beta), A'_s = A_s diag(r), split
+      // hi/lo, columns stored at permuted positions (region of K, L, Y is dead)
       __syncthreads();
       if (prep) {
+        const int s = p >> 7, row = 32 * s + ((p >> 2) & 31), c0 = 32 * s + 8 * (p & 3);
+        // positions c0 .. c0+7 hold tokens t4 + {0..3} and t4 + 8 + {0..3}
+        const int t4 = (c0 & ~15) + ((c0 & 8) ? 4 : 0);
+        float av[8], bv[8];
 #pragma unroll
-        for (int i = 0; i < C * C / 8 / kPT; ++i) {
-          const int e = p + i * kPT;
-          const int row = e >> 3, c0 = (e & 7) * 8;
-          // positions c0 .. c0+7 hold tokens t4 + {0..3} and t4 + 8 + {0..3}
-          const int t4 = (c0 & ~15) + ((c0 & 8) ? 4 : 0);
-          float av[8], bv[8];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int tk = t4 + 8 * hf;
-            const float4 x = *reinterpret_cast<const float4*>(Xm + row * XL + tk);
-            const float4 bb = *reinterpret_cast<const float4*>(gb + tk);
-            const float4 rr = *reinterpret_cast<const float4*>(gr + tk);
-            av[4 * hf] = x.x * bb.x; av[4 * hf + 1] = x.y * bb.y;
-            av[4 * hf + 2] = x.z * bb.z; av[4 * hf + 3] = x.w * bb.w;
-            bv[4 * hf] = av[4 * hf] * rr.x; bv[4 * hf + 1] = av[4 * hf + 1] * rr.y;
-            bv[4 * hf + 2] = av[4 * hf + 2] * rr.z; bv[4 * hf + 3] = av[4 * hf + 3] * rr.w;
-          }
-          bf16x8 h8, l8;
-          split8(av, h8, l8);
-          *reinterpret_cast<bf16x8*>(Ah + row * AL + c0) = h8;
-          *reinterpret_cast<bf16x8*>(Al + row * AL + c0) = l8;
-          split8(bv, h8, l8);
-          *reinterpret_cast<bf16x8*>(Bh + row * AL + c0) = h8;
-          *reinterpret_cast<bf16x8*>(Bl + row * AL + c0) = l8;
+        for (int hf = 0; hf < 2; ++hf) {
+          const int tk = t4 + 8 * hf;
+          const float4 x = *reinterpret_cast<const float4*>(Xm + row * XL + tk);
+          const float4 bb = *reinterpret_cast<const float4*>(gb + tk);
+          const float4 rr = *reinterpret_cast<const float4*>(gr + tk);
+          av[4 * hf] = x.x * bb.x; av[4 * hf + 1] = x.y * bb.y;
+          av[4 * hf + 2] = x.z * bb.z; av[4 * hf + 3] = x.w * bb.w;
+          bv[4 * hf] = av[4 * hf] * rr.x; bv[4 * hf + 1] = av[4 * hf + 1] * rr.y;
+          bv[4 * hf + 2] = av[4 * hf + 2] * rr.z; bv[4 * hf + 3] = av[4 * hf + 3] * rr.w;
         }
+        bf16x8 h8, l8;
+        split8(av, h8, l8);
+        *reinterpret_cast<bf16x8*>(Ah + row * AL + c0) = h8;
+        *reinterpret_cast<bf16x8*>(Al + row * AL + c0) = l8;
+        split8(bv, h8, l8);
+        *reinterpret_cast<bf16x8*>(Bh + row * AL + c0) = h8;
+        *reinterpret_cast<bf16x8*>(Bl + row * AL + c0) = l8;
       }
 
-      // ---------------- I7: U^T = K^T A^T tile by tile; -U fragments to LDS
-      // (the consumers finished reading the previous -U in I3)
+      // ---------------- I6: U_s^T = K_s^T A_s^T tile by tile; -U fragments to
+      // LDS (the consumers finished reading the previous -U in I4)
       __syncthreads();
       if (prep) {
 #pragma unroll
         for (int i = 0; i < (2 * NT + kProducers - 1) / kProducers; ++i) {
           const int tile = pw + i * kProducers;
           if (tile >= 2 * NT) break;
-          const int t = tile % NT, mt = tile / NT;
+          const int t = tile % NT, s = tile / NT;
           f32x16 acc = zero16();
 #pragma unroll
-          for (int ks = 0; ks < C / 16; ++ks) {
-            const int kc = ks * 16 + 8 * g;
-            const bf16x8 kf = lds_load8(Kt + (t * 32 + cl) * KT + kc);
-            const bf16x8 ah = lds_load8(Ah + (mt * 32 + cl) * AL + kc);
-            const bf16x8 al = lds_load8(Al + (mt * 32 + cl) * AL + kc);
+          for (int kk = 0; kk < 2; ++kk) {
+            const int kc = 32 * s + 16 * kk + 8 * g;
+            const bf16x8 kf = lds_load8(Kt + kt_lane_base<KT>(cl, g, kk) + kt_tile<KT>(t, s));
+            const bf16x8 ah = lds_load8(Ah + (s * 32 + cl) * AL + kc);
+            const bf16x8 al = lds_load8(Al + (s * 32 + cl) * AL + kc);
             acc = mfma32(kf, al, acc);
             acc = mfma32(kf, ah, acc);
           }
@@ -558,8 +561,8 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
             for (int j = 0; j < 8; ++j) x[j] = -acc[8 * hh + j];
             bf16x8 h8, l8;
             split8(x, h8, l8);
-            *reinterpret_cast<bf16x8*>(Uf + uf_off<NT>(mt, t, hh, 0, lane)) = h8;
-            *reinterpret_cast<bf16x8*>(Uf + uf_off<NT>(mt, t, hh, 1, lane)) = l8;
+            *reinterpret_cast<bf16x8*>(Uf + uf_off<NT>(s, t, hh, 0, lane)) = h8;
+            *reinterpret_cast<bf16x8*>(Uf + uf_off<NT>(s, t, hh, 1, lane)) = l8;
           }
         }
       }

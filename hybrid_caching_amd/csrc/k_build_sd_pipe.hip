@@ -49,16 +49,6 @@ __device__ __forceinline__ float bf_at(const uint4& a, int j) {
   return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// inclusive prefix sum inside each half-wave of 32 lanes (DPP)
-__device__ __forceinline__ float half_wave_scan(float x) {
-  x += dpp_f<0x111>(x);        // row_shr:1
-  x += dpp_f<0x112>(x);        // row_shr:2
-  x += dpp_f<0x114>(x);        // row_shr:4
-  x += dpp_f<0x118>(x);        // row_shr:8
-  x += dpp_f<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3 (not across halves)
-  return x;
-}
-
 __device__ __forceinline__ int opaque_i(int v) {
   asm volatile("" : "+v"(v));
   return v;

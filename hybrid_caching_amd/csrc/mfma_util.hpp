@@ -146,6 +146,17 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// Inclusive prefix sum inside each half wave (lanes 0-31 and 32-63): the
+// steps of wave_inclusive_scan without the broadcast across halves.
+__device__ __forceinline__ float half_wave_scan(float x) {
+  x += dpp_f<0x111>(x);        // row_shr:1
+  x += dpp_f<0x112>(x);        // row_shr:2
+  x += dpp_f<0x114>(x);        // row_shr:4
+  x += dpp_f<0x118>(x);        // row_shr:8
+  x += dpp_f<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  return x;
+}
+
 // 8 consecutive bf16 (16 bytes) from LDS
 __device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
