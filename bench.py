@@ -233,6 +233,124 @@ def bench_scalar_diag(w, args):
     return 0
 
 
+def _group_segments(lens, max_tokens):
+    """Consecutive runs of segments holding at most max_tokens tokens each."""
+    groups, cur, tot = [], [], 0
+    for i, n in enumerate(lens):
+        if cur and tot + n > max_tokens:
+            groups.append(cur)
+            cur, tot = [], 0
+        cur.append(i)
+        tot += n
+    if cur:
+        groups.append(cur)
+    return groups
+
+
+def bench_reuse(w, args):
+    """Composition-heavy reuse: build a pool of cached segments (all layers)
+    and the requests' fresh segments, then compose every request's chain of
+    pool and fresh pairs in one call.  Times the fresh builds (inputs resident
+    per group of segments) and the batched compose; one JSON line."""
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pic.load()
+    fw = synth.reuse_fresh_workload(w)
+    off, idx = synth.reuse_chains(w)
+    B, H, dk, dv = w.layers, w.heads, w.dk, w.dv
+    n_pool, n_fresh = w.n_seg, fw.n_seg
+    P = n_pool + n_fresh
+    R = len(off) - 1
+    pool = {"log_scale": torch.empty((P, B, H), dtype=torch.float32, device=dev),
+            "T_hat": torch.empty((P, B, H, dk, dk), dtype=torch.float32, device=dev),
+            "S0": torch.empty((P, B, H, dk, dv), dtype=torch.float32, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def build_groups(wl, base, seed_base, record):
+        lens = list(wl.seg_lens)
+        for gi, grp in enumerate(_group_segments(lens, 32768)):
+            gl = [lens[i] for i in grp]
+            gw = synth.scaled(wl, seg_lens=gl, name=wl.name)
+            Ng = sum(gl)
+            k = torch.empty((B, Ng, H, dk), dtype=torch.bfloat16, device=dev)
+            v = torch.empty((B, Ng, H, dv), dtype=torch.bfloat16, device=dev)
+            alpha = torch.empty((B, Ng, H), dtype=torch.float32, device=dev)
+            beta = torch.empty((B, Ng, H), dtype=torch.float32, device=dev)
+            for layer in range(B):
+                x = synth.torch_layer_inputs(gw, layer, dev, seed_offset=seed_base + 131 * gi)
+                k[layer].copy_(x["k"])
+                v[layer].copy_(x["v"])
+                alpha[layer].copy_(x["alpha"])
+                beta[layer].copy_(x["beta"])
+                del x
+            p0, p1 = base + grp[0], base + grp[-1] + 1
+            out = {key: t[p0:p1] for key, t in pool.items()}
+            goff = np.concatenate([[0], np.cumsum(gl)]).astype(np.int64)
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            pic.pic_segment_build(synth.DENSE, k, v, alpha, beta, goff, out=out)
+            e1.record(stream)
+            record.append((e0, e1, Ng))
+            del k, v, alpha, beta
+
+    pool_rec, fresh_rec = [], []
+    t0 = time.perf_counter()
+    build_groups(w, 0, 0, pool_rec)
+    build_groups(fw, n_pool, 7, fresh_rec)
+    torch.cuda.synchronize()
+    prep_s = time.perf_counter() - t0
+    fresh_ms = sum(a.elapsed_time(b) for a, b, _ in fresh_rec)
+    fresh_tokens = sum(n for _, _, n in fresh_rec)
+
+    S_out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def compose():
+        pic.pic_compose(synth.DENSE, pool["log_scale"], pool["T_hat"], pool["S0"], off, idx,
+                        None, out=S_out)
+
+    for _ in range(max(args.warmup, 1)):
+        compose()
+    torch.cuda.synchronize()
+    recs = []
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        compose()
+        e1.record(stream)
+        recs.append((e0, e1))
+    torch.cuda.synchronize()
+    t_comp = float(np.mean([a.elapsed_time(b) for a, b in recs])) / 1e3
+    steps_total = int(off[-1])
+    composes = steps_total * B                     # pair applications per layer, all heads
+    # every step reads its pair once; the states are written once (no S_in)
+    cb = compose_bytes(steps_total, B, H, dk, dv, n_req=0) + R * B * H * dk * dv * 4
+    gbs = cb / t_comp / 1e9
+    out = {"metric": "state composes/s (dense delta, H=32, d=128), composition-heavy reuse; "
+                     "% HBM roofline",
+           "value": composes / t_comp, "unit": "composes/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": t_comp * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, split-bf16 MFMA",
+           "data": "synthetic",
+           "config": {"workload": w.name, "form": "dense_gdn", "layers": B, "heads": H, "dk": dk,
+                      "dv": dv, "pool_segments": n_pool, "requests": R,
+                      "chain_steps": steps_total // R, "fresh_segments": n_fresh,
+                      "fresh_segment_tokens": int(fw.seg_lens[0])},
+           "roofline": {"kernel": "compose_dense_kernel", "bound": "hbm", "achieved": gbs,
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                        "traffic": measured_traffic("compose_dense_kernel", w.name),
+                        "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": cb},
+           "fresh_build": {"tokens_per_s": fresh_tokens / (fresh_ms / 1e3), "ms": fresh_ms,
+                           "segments": n_fresh, "layers": B},
+           "pool_and_input_preparation_s": prep_s}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +385,8 @@ def main(argv=None):
         w = synth.scaled(w, layers=args.layers, name=w.name)
     if w.form != synth.DENSE:
         return bench_scalar_diag(w, args)
+    if w.extra.get("pool_size"):
+        return bench_reuse(w, args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()

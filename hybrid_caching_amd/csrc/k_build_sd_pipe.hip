@@ -49,6 +49,15 @@ __device__ __forceinline__ float bf_at(const uint4& a, int j) {
   return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// element offset of 16-byte chunk `chunk` of row `row` of a transposed
+// operand.  With SWZ the chunk index is XOR-swizzled by the row's 8-row group,
+// so that transposed writes from rows 8 apart (the scalar form's staging
+// mapping) spread over the LDS banks.
+template <bool SWZ>
+__device__ __forceinline__ int sd_at(int row, int chunk, int ld) {
+  return row * ld + 8 * (SWZ ? (chunk ^ ((row >> 3) & 7)) : chunk);
+}
+
 __device__ __forceinline__ int opaque_i(int v) {
   asm volatile("" : "+v"(v));
   return v;
@@ -90,9 +99,25 @@ __global__ __launch_bounds__(4 * DP) void build_sd_pipe_kernel(BuildArgs a) {
 #pragma unroll
   for (int j = 0; j < (DIAG ? 8 : 1); ++j) lam[j] = 0.f;
 
+  // staging item of a thread: tokens (t0, t0+1) x channels [i0, i0+8).
+  // Scalar form: consecutive threads take consecutive channel groups of one
+  // token pair, so that a load instruction reads whole 256-byte token rows.
+  // Diagonal form: the 32 lanes of a half wave take the 32 token pairs of one
+  // channel group (the per-channel prefix is a half-wave scan).
+  auto item = [](int tid, int& t0, int& i0) {
+    if (DIAG) {
+      const int lane = tid & 63;
+      t0 = 2 * (lane & 31);
+      i0 = 8 * (2 * (tid >> 6) + (lane >> 5));
+    } else {
+      t0 = 2 * (tid / (DP / 8));
+      i0 = 8 * (tid % (DP / 8));
+    }
+  };
   auto load = [&](Stage<DIAG>& st, int ci) {
     const int tid = opaque_i(threadIdx.x), lane = tid & 63;
-    const int t0 = 2 * (lane & 31), i0 = 8 * (2 * (tid >> 6) + (lane >> 5));
+    int t0, i0;
+    item(tid, t0, i0);
     const int64_t c0 = t_begin + int64_t(ci) * C;
     const int len = (t_end - c0 < C) ? int(t_end - c0) : C;
     const int ta = min(t0, len - 1), tb = min(t0 + 1, len - 1);
@@ -121,7 +146,9 @@ __global__ __launch_bounds__(4 * DP) void build_sd_pipe_kernel(BuildArgs a) {
   // stage chunk ci from registers into LDS (Kw^T hi/lo, V^T, channel decays)
   auto stage = [&](const Stage<DIAG>& st, int ci) {
     const int tid = opaque_i(threadIdx.x), lane = tid & 63;
-    const int tp = lane & 31, t0 = 2 * tp, i0 = 8 * (2 * (tid >> 6) + (lane >> 5));
+    const int tp = lane & 31;
+    int t0, i0;
+    item(tid, t0, i0);
     const int64_t c0 = t_begin + int64_t(ci) * C;
     const int len = (t_end - c0 < C) ? int(t_end - c0) : C;
     const bool va = t0 < len, vb = t0 + 1 < len;
@@ -169,15 +196,18 @@ __global__ __launch_bounds__(4 * DP) void build_sd_pipe_kernel(BuildArgs a) {
       unsigned h0, l0, h1, l1;
       split2(ka0, kb0, h0, l0);
       split2(ka1, kb1, h1, l1);
-      *reinterpret_cast<unsigned*>(Kh + (i0 + j) * KT + t0) = h0;
-      *reinterpret_cast<unsigned*>(Kl + (i0 + j) * KT + t0) = l0;
-      *reinterpret_cast<unsigned*>(Kh + (i0 + j + 1) * KT + t0) = h1;
-      *reinterpret_cast<unsigned*>(Kl + (i0 + j + 1) * KT + t0) = l1;
+      const int at0 = sd_at<!DIAG>(i0 + j, t0 >> 3, KT) + (t0 & 7);
+      const int at1 = sd_at<!DIAG>(i0 + j + 1, t0 >> 3, KT) + (t0 & 7);
+      *reinterpret_cast<unsigned*>(Kh + at0) = h0;
+      *reinterpret_cast<unsigned*>(Kl + at0) = l0;
+      *reinterpret_cast<unsigned*>(Kh + at1) = h1;
+      *reinterpret_cast<unsigned*>(Kl + at1) = l1;
     }
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     const uint4 v0 = (okv && va) ? st.v0 : z, v1 = (okv && vb) ? st.v1 : z;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<unsigned*>(Vt + (i0 + j) * KT + t0) = pair_w(v0, v1, j);
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<unsigned*>(Vt + sd_at<!DIAG>(i0 + j, t0 >> 3, KT) + (t0 & 7)) = pair_w(v0, v1, j);
   };
 
   // S <- decay (.) S + Kw^T V for this wave's tiles
@@ -197,10 +227,11 @@ __global__ __launch_bounds__(4 * DP) void build_sd_pipe_kernel(BuildArgs a) {
         }
 #pragma unroll
         for (int ks = 0; ks < C / 16; ++ks) {
-          const int kc = ks * 16 + 8 * g;
-          const bf16x8 ah = lds_load8(Kh + (mt * 32 + cl) * KT + kc);
-          const bf16x8 al = lds_load8(Kl + (mt * 32 + cl) * KT + kc);
-          const bf16x8 vb = lds_load8(Vt + (nt * 32 + cl) * KT + kc);
+          const int kch = ks * 2 + g;  // 16-byte chunk of tokens 16 ks + 8 g ..
+          const int ka = sd_at<!DIAG>(mt * 32 + cl, kch, KT), va2 = sd_at<!DIAG>(nt * 32 + cl, kch, KT);
+          const bf16x8 ah = lds_load8(Kh + ka);
+          const bf16x8 al = lds_load8(Kl + ka);
+          const bf16x8 vb = lds_load8(Vt + va2);
           S[k] = mfma32(al, vb, S[k]);
           S[k] = mfma32(ah, vb, S[k]);
         }
