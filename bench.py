@@ -38,7 +38,10 @@ CSRC = os.path.join(ROOT, "hybrid_caching_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # the source files each timed kernel is compiled from
 KERNEL_SOURCES = {
-    "build_dense_ws_kernel": ["k_build_dense_ws.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_dense_ws_kernel": ["k_build_dense_ws.hip", "mfma_util.hpp", "pic_internal.hpp",
+                              "stage_util.hpp"],
+    "build_dense_h16_kernel": ["k_build_dense_h16.hip", "mfma_util.hpp", "pic_internal.hpp",
+                               "stage_util.hpp"],
     "build_sd_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
@@ -293,7 +296,8 @@ def bench_reuse(w, args):
             torch.cuda.synchronize()
             e0, e1 = ev(), ev()
             e0.record(stream)
-            pic.pic_segment_build(synth.DENSE, k, v, alpha, beta, goff, out=out)
+            pic.pic_segment_build(synth.DENSE, k, v, alpha, beta, goff, out=out,
+                                  precision=args.prec)
             e1.record(stream)
             record.append((e0, e1, Ng))
             del k, v, alpha, beta
@@ -337,7 +341,7 @@ def bench_reuse(w, args):
            "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, split-bf16 MFMA",
            "data": "synthetic",
            "config": {"workload": w.name, "form": "dense_gdn", "layers": B, "heads": H, "dk": dk,
-                      "dv": dv, "pool_segments": n_pool, "requests": R,
+                      "dv": dv, "build_precision": args.precision, "pool_segments": n_pool, "requests": R,
                       "chain_steps": steps_total // R, "fresh_segments": n_fresh,
                       "fresh_segment_tokens": int(fw.seg_lens[0])},
            "roofline": {"kernel": "compose_dense_kernel", "bound": "hbm", "achieved": gbs,
@@ -358,6 +362,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense_30L_32x4096")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--precision", choices=["fp32", "fp16"], default="fp32",
+                    help="operand precision of the dense build's matrix-core products: fp32 "
+                         "(split bf16) or fp16 (single fp16 operands); state is fp32 in both")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -366,6 +373,7 @@ def main(argv=None):
     ap.add_argument("--source-digest", action="store_true",
                     help="print the source digest of each timed kernel and exit")
     args = ap.parse_args(argv)
+    args.prec = 1 if args.precision == "fp16" else 0
     if args.source_digest:
         for kname in KERNEL_SOURCES:
             print(kname, source_digest(kname))
@@ -422,7 +430,8 @@ def main(argv=None):
     def step(record=None):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record(stream)
-        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs)
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs,
+                              precision=args.prec)
         e1.record(stream)
         pic.pic_compose(w.form, pairs["log_scale"], pairs["T_hat"], pairs["S0"], chain_off,
                         chain_idx, None, out=S_out)
@@ -450,6 +459,7 @@ def main(argv=None):
     flops = dense_build_flops_per_token_head(dk) * N * B * H
     achieved_tf = flops / t_build / 1e12
     composes = n_seg * B  # pairs applied to a running state, per layer (all heads)
+    build_kernel = "build_dense_h16_kernel" if args.prec else "build_dense_ws_kernel"
     cb = compose_bytes(n_seg, B, H, dk, dv)
     nb = naive_bytes(n_seg, B, H, dk, dv)
     out = {
@@ -463,19 +473,20 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state, bf16 k/v, split-bf16 MFMA",
+        "dtype": ("f32 state, bf16 k/v, fp16 MFMA operands" if args.prec else
+                  "f32 state, bf16 k/v, split-bf16 MFMA"),
         "data": "synthetic",
         "config": {"workload": w.name, "form": "dense_gdn", "layers": B, "heads": H, "dk": dk,
-                   "dv": dv, "segments": n_seg, "segment_tokens": int(w.seg_lens[0]),
+                   "dv": dv, "build_precision": args.precision, "segments": n_seg, "segment_tokens": int(w.seg_lens[0]),
                    "prompt_tokens": N, "chunk": CHUNK},
         "build_tokens_per_s": N / t_build,
         "composes_per_s": composes / t_comp,
         "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3,
                "step_events": t_step_ev * 1e3},
-        "roofline": {"kernel": "build_dense_ws_kernel", "bound": "mfma", "achieved": achieved_tf,
+        "roofline": {"kernel": build_kernel, "bound": "mfma", "achieved": achieved_tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tf / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("build_dense_ws_kernel", w.name),
+                     "traffic": measured_traffic(build_kernel, w.name),
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes": build_bytes(N, B, H, dk, dv, n_seg)},
         "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libpic.so")
 
 FORM_SCALAR, FORM_DIAG, FORM_DENSE = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
+PREC_FP32, PREC_FP16 = 0, 1
 
 STATUS = {0: "PIC_OK", -1: "PIC_ERR_NULL", -2: "PIC_ERR_DIMS", -3: "PIC_ERR_OFFSETS",
           -4: "PIC_ERR_CHAIN", -5: "PIC_ERR_WORKSPACE", -6: "PIC_ERR_UNSUPPORTED",
@@ -30,9 +31,9 @@ SIGNATURES = {
     "pic_status_string": (ctypes.c_char_p, [_i]),
     "pic_last_error": (ctypes.c_char_p, []),
     "pic_segment_build_workspace": (_sz, [_i, _i, _i, _i, _i, _i64, _i32]),
-    "pic_validate_build": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
+    "pic_validate_build": (_i, [_i, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
                                 _p, _p, _p, _sz]),
-    "pic_segment_build": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
+    "pic_segment_build": (_i, [_i, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
                                _p, _p, _p, _sz, _p]),
     "pic_compose_workspace": (_sz, [_i32, _i64]),
     "pic_validate_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
@@ -117,12 +118,14 @@ def _workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=None):
+def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=None,
+                      precision: int = PREC_FP32):
     """Cached pairs of every (segment, layer, head).
 
     k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
     [B, N, H] (diag: [B, N, H, dk]), beta: fp32 [B, N, H] or None (= 1; dense
-    only), seg_offsets: host ints [n_seg+1].  Returns dict(log_scale, T_hat
+    only), seg_offsets: host ints [n_seg+1].  precision: PREC_FP32 or
+    PREC_FP16 (dense with bf16 k/v only).  Returns dict(log_scale, T_hat
     (dense only), S0) of fp32 device tensors laid out [n_seg, B, H, ...].
     """
     lib = load()
@@ -145,7 +148,7 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
             out["T_hat"] = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
     ws_n = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
     ws = _workspace(ws_n, dev)
-    rc = lib.pic_segment_build(form, dt, B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+    rc = lib.pic_segment_build(form, dt, precision, B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                _ptr(beta), offs_p, n_seg, _ptr(out["log_scale"]),
                                _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
                                _stream(dev))

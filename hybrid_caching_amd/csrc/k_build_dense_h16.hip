@@ -1,0 +1,664 @@
+// k_build_dense_h16.hip -- build of the dense gated-delta pair
+// (lambda_C, That_C, S(C|0)) for bf16 k/v at fp16 operand precision
+// (PIC_PREC_FP16): every matrix-core product takes single fp16 operands and
+// accumulates in fp32; the running That and S stay fp32 in accumulators.
+// Same chunked arithmetic as k_build_dense.hip (derivation there), on
+// sub-chunks of 32 tokens:
+//   X_s = (I + diag(beta) strictly-lower(K_s K_s^T))^{-1}
+//   A_s = X_s diag(beta),  A'_s = X_s diag(beta r),  U_s = A_s K_s,  W_s = A'_s V_s
+//   That <- That - K_s^T (U_s That),   S <- gamma_s S + K_s^T (W_s - U_s (gamma_s S)).
+// [xix.ai HYPIC article (French), paragraph on linear layers: T_C as the
+//  product of the segment's token transitions and S(C|0) from a zero start;
+//  dense delta-rule transitions are the heaviest family.]
+//
+// Precision.  fp16 keeps 11 significant bits (bf16: 8), so one fp16 product
+// per operand pair replaces the three split-bf16 products of the fp32-accurate
+// kernels.  The ungated product That shrinks steadily along a segment (its
+// norm is ~1e-4 after 4096 tokens at the usual gates), far below fp16's
+// normal range, so each consumer wave keeps its columns of That scaled by a
+// power of two (a column scaling commutes with left multiplication, and a
+// power of two is exact) and re-normalises them once per chunk; the exponent
+// is applied when That is written.  S, U, W and the keys stay within fp16's
+// range for unit-norm keys and values of moderate size.
+//
+// One workgroup per (segment, layer, head): four consumer waves, each holding
+// columns [32c, 32c+32) of both That and S in MFMA accumulators for the whole
+// segment, and four producer waves.  Producer wave 0 ("solver") computes the
+// two 32x32 triangular inverses of a chunk by back substitution, one row of
+// X per lane (lanes 0-31 sub-chunk 0, lanes 32-63 sub-chunk 1), reading rows
+// of L as broadcast LDS loads a few steps ahead: no workgroup barrier inside
+// the solve.  Three helper waves stage k/v, form G = K K^T, the gates and
+// U^T = K^T A^T.
+//
+// LDS holds K and V row-major in fp16.  Every transposed operand fragment
+// (K^T for U^T and for K^T N, V^T for W) is read with ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives, for j = 0..3, 16-bit element
+// (i & 3) of the 8 bytes addressed by lane 4j + (i >> 2).  So when lane
+// 4j + q of the group addresses row r_j, columns c0 + 4q .. c0 + 4q + 3, lane
+// i receives rows r_0..r_3 of column c0 + i: a column of the tile, i.e. a
+// row of its transpose.  The row stride (288 bytes) puts the 16 addresses of
+// a group on distinct banks.
+//
+// Pipeline: cycle ci has two phases separated by workgroup barriers.
+//   phase A: consumers chain sub-chunk 1 of chunk ci-2
+//            helpers:  U^T of chunk ci-1 -> -U fragments (helpers 0, 1); V
+//                      rows of chunk ci-1 to LDS (helper 2)
+//            solver:   first part of the back substitution of chunk ci
+//   phase B: consumers: W seeds of chunk ci-1, chain sub-chunk 0 of ci-1
+//            helpers:  K rows of chunk ci+1 to LDS and G of chunk ci+1 (helper
+//                      s stages exactly the rows its G reads, so no other
+//                      wave waits for them); the gates of chunk ci+1 (helper 2)
+//            solver:   rest of the substitution of chunk ci -> A, A'
+// so a chunk is staged in cycle j-1, solved in cycle j, and chained in cycles
+// j+1 and j+2.  K is kept for four chunks; -U fragments, A/A', G and the
+// masked gates for two; V for one.  Every global load is issued a cycle
+// before its data is staged.  The solver applies beta to the rows of G
+// (L = diag(beta) strictly-lower(G)); G = K K^T is symmetric, so the helpers
+// write each accumulator column as a row with four 16-byte stores.
+#include <type_traits>
+
+#include "mfma_util.hpp"
+#include "pic_internal.hpp"
+
+namespace pic {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int DP = 128;        // padded head size
+constexpr int C = 64;          // tokens staged per chunk
+constexpr int NT = DP / 32;    // consumer waves = 32-row tiles
+constexpr int NHW = 3;         // helper producer waves
+constexpr int THREADS = (NT + 1 + NHW) * 64;
+constexpr int NKB = 4;         // K buffers (chunks alive at once)
+
+constexpr int RLD = DP + 16;   // row stride (halves) of K and V
+constexpr int A_LD = 40;       // A, A' rows (fp16, 32 tokens + pad)
+
+constexpr int ROWS_BYTES = C * RLD * 2;
+constexpr int L_K = 0;
+constexpr int L_V = L_K + NKB * ROWS_BYTES;
+constexpr int L_NM = L_V + ROWS_BYTES;
+constexpr int NM_FLOATS = 2 * 32 * 32;          // L of both sub-chunks
+constexpr int L_AB = L_NM + 2 * NM_FLOATS * 4;
+constexpr int AB_HALFS = 2 * 64 * A_LD;         // A rows then A' rows
+constexpr int L_UF = L_AB + 2 * AB_HALFS * 2;
+constexpr int UF_BYTES = 2 * NT * 2 * 64 * 16;  // [s][t][h][lane] x 16 B
+constexpr int L_GB = L_UF + 2 * UF_BYTES;       // beta (masked), two chunks
+constexpr int L_GBR = L_GB + 2 * C * 4;         // beta * r, two chunks
+constexpr int L_GG = L_GBR + 2 * C * 4;         // gamma ring [4][2]
+constexpr int LDS_TOTAL = L_GG + 8 * 4;
+static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of a CU");
+static_assert(L_V % 16 == 0 && L_NM % 16 == 0 && L_AB % 16 == 0 && L_UF % 16 == 0 &&
+              L_GB % 16 == 0 && L_GBR % 16 == 0 && (RLD * 2) % 16 == 0, "alignment");
+
+__device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned pk_h2(float x0, float x1) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, f16x2));
+}
+
+// accumulator registers 8h .. 8h+7 (times SGN) as an fp16 operand
+template <int SGN = 1>
+__device__ __forceinline__ f16x8 acc_h8(const f32x16& a, int h) {
+  u32x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = pk_h2(SGN * a[8 * h + 2 * j], SGN * a[8 * h + 2 * j + 1]);
+  return __builtin_bit_cast(f16x8, w);
+}
+
+// two bf16 values in a word -> two fp16 values in a word
+__device__ __forceinline__ unsigned bf2h_word(unsigned w) {
+  return pk_h2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+__device__ __forceinline__ uint4 bf2h(const uint4& x) {
+  return make_uint4(bf2h_word(x.x), bf2h_word(x.y), bf2h_word(x.z), bf2h_word(x.w));
+}
+__device__ __forceinline__ uint4 pick_u4(bool ok, const uint4& x) {
+  return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
+}
+
+__device__ __forceinline__ f16x8 lds_h8(const _Float16* p) {
+  return *reinterpret_cast<const f16x8*>(p);
+}
+
+// transposed read (see the header): 4 fp16 values
+__device__ __forceinline__ i16x4 lds_tr4(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+// an 8-value operand from two transposed reads
+__device__ __forceinline__ f16x8 tr_h8(const _Float16* p0, const _Float16* p1) {
+  const i16x4 lo = lds_tr4(p0), hi = lds_tr4(p1);
+  const i16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ __forceinline__ int uf_off(int s, int t, int h, int lane) {
+  return (((s * NT + t) * 2 + h) * 64 + lane) * 16;
+}
+
+// global-memory access through an explicitly global pointer (pointers that
+// reach a role function through memory would otherwise be accessed with flat
+// instructions, which also count against the LDS wait counter)
+template <class T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+template <class T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+  *(__attribute__((address_space(1))) T*)(p) = v;
+}
+__device__ __forceinline__ uint4 gload_u4(const void* p) {
+  const u32x4 w = *(const __attribute__((address_space(1))) u32x4*)(p);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// maximum over the 64 lanes (uniform result)
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // lane ^ 1
+  x = fmaxf(x, dpp_f<0x4E>(x));   // lane ^ 2
+  x = fmaxf(x, dpp_f<0x141>(x));  // half-row mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Back substitution of X (I + L) = I for the lane's row, steps i = HI .. LO
+// (descending): acc[r] -= X[row][i] L[i][r] for r < i, where L[i][r] =
+// beta_i G[i][r].  Row i of G is a broadcast read (every lane of the half
+// wave reads the same address), issued PF steps ahead of its use; bt holds
+// beta of the sub-chunk's 32 tokens (uniform per half wave).
+constexpr int PF = 3;
+template <int HI, int LO>
+__device__ __forceinline__ void subst_steps(float (&acc)[32], const float* nm, const float (&bt)[32]) {
+  float4 buf[PF + 1][8];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (HI - p >= LO) {
+#pragma unroll
+      for (int r4 = 0; r4 < (HI - p + 3) / 4; ++r4)
+        buf[p][r4] = *reinterpret_cast<const float4*>(nm + (HI - p) * 32 + 4 * r4);
+    }
+#pragma unroll
+  for (int i = HI; i >= LO; --i) {
+    const int slot = (HI - i) % (PF + 1);
+    const int ip = i - PF;  // row read now, used PF steps later
+    if (ip >= LO) {
+      const int ps = (HI - ip) % (PF + 1);
+#pragma unroll
+      for (int r4 = 0; r4 < (ip + 3) / 4; ++r4)
+        buf[ps][r4] = *reinterpret_cast<const float4*>(nm + ip * 32 + 4 * r4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float x = acc[i] * bt[i];
+#pragma unroll
+    for (int r4 = 0; r4 < (i + 3) / 4; ++r4) {
+      const float nv[4] = {buf[slot][r4].x, buf[slot][r4].y, buf[slot][r4].z, buf[slot][r4].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * r4 + e < i) acc[4 * r4 + e] = fmaf(-nv[e], x, acc[4 * r4 + e]);
+    }
+  }
+}
+
+// wave-uniform copies (values that reach a role through memory would
+// otherwise be treated as per-lane, turning uniform branches into exec masks)
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t rfl64(int64_t v) {
+  const uint32_t lo = uint32_t(rfl(int(uint32_t(v)))), hi = uint32_t(rfl(int(uint64_t(v) >> 32)));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* rflp(T* p) {
+  return reinterpret_cast<T*>(rfl64(reinterpret_cast<int64_t>(p)));
+}
+
+// Per-block values shared by the three roles.  Each role is its own
+// non-inlined function, so that the register allocator sees one role at a
+// time (inlined into one body, the three live-range sets interfere).
+struct Ctx {
+  int64_t t_begin, t_end, N, unit;
+  int n, b, h;
+};
+
+// the workgroup's LDS, at file scope so that every role function addresses
+// it directly (LDS instructions, not flat ones)
+__shared__ __attribute__((aligned(16))) char h16_smem[LDS_TOTAL];
+
+__device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x);
+__device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x);
+__device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x);
+
+__global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
+  const int BH = a.batch * a.heads;
+  const int seg = a.d_order[blockIdx.x / BH];
+  const int bh = blockIdx.x % BH;
+  Ctx x;
+  x.b = bh / a.heads;
+  x.h = bh % a.heads;
+  x.t_begin = a.d_offsets[seg];
+  x.t_end = a.d_offsets[seg + 1];
+  x.N = a.n_tokens;
+  x.n = int((x.t_end - x.t_begin + C - 1) / C);
+  x.unit = (int64_t(seg) * a.batch + x.b) * a.heads + x.h;
+  const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  if (wid < NT)
+    consumer_role(a, x);
+  else if (wid == NT)
+    solver_role(a, x);
+  else
+    helper_role(a, x);
+}
+
+#define PIC_H16_ROLE_PROLOGUE                                                   \
+  _Float16* Kb0 = reinterpret_cast<_Float16*>(h16_smem + L_K);                  \
+  _Float16* Vb = reinterpret_cast<_Float16*>(h16_smem + L_V);                   \
+  float* Nm0 = reinterpret_cast<float*>(h16_smem + L_NM);                       \
+  _Float16* AB0 = reinterpret_cast<_Float16*>(h16_smem + L_AB);                 \
+  char* Uf0 = h16_smem + L_UF;                                                  \
+  float* gb0 = reinterpret_cast<float*>(h16_smem + L_GB);                       \
+  float* gbr0 = reinterpret_cast<float*>(h16_smem + L_GBR);                     \
+  float* gg = reinterpret_cast<float*>(h16_smem + L_GG);                        \
+  const int H = rfl(a.heads), dk = rfl(a.dk), dv = rfl(a.dv);                   \
+  const int b = rfl(x.b), h = rfl(x.h), n = rfl(x.n);                           \
+  const int64_t t_begin = rfl64(x.t_begin), t_end = rfl64(x.t_end);             \
+  const int64_t N = rfl64(x.N), unit = rfl64(x.unit);                           \
+  const __bf16* kp = rflp(static_cast<const __bf16*>(a.k));                     \
+  const __bf16* vp = rflp(static_cast<const __bf16*>(a.v));                     \
+  const float* alpha = rflp(a.alpha);                                           \
+  const float* beta = rflp(a.beta);                                             \
+  float* out_lam = rflp(a.log_scale);                                           \
+  float* out_T = rflp(a.T_hat);                                                 \
+  float* out_S = rflp(a.S0);                                                    \
+  const int lane = threadIdx.x & 63, g = lane >> 5, cl = lane & 31;             \
+  const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));        \
+  /* transposed reads: group lane ti supplies row ti >> 2 of a 4-row block   */ \
+  /* and columns 4 (ti & 3) .. +3 of the group's 16-column half              */ \
+  const int ti = lane & 15, tg = lane >> 4;                                     \
+  const int tr_row = ti >> 2, tr_col = 16 * (tg & 1) + 4 * (ti & 3);            \
+  auto chunk_len = [&](int j) {                                                 \
+    const int64_t c0 = t_begin + int64_t(j) * C;                                \
+    return (t_end - c0 < C) ? int(t_end - c0) : C;                              \
+  };                                                                            \
+  (void)Kb0; (void)Vb; (void)Nm0; (void)AB0; (void)Uf0; (void)gb0;   \
+  (void)gbr0; (void)gg; (void)H; (void)dk; (void)dv; (void)b; (void)h; (void)N; \
+  (void)unit; (void)g; (void)cl; (void)wid; (void)chunk_len; (void)t_begin;     \
+  (void)t_end; (void)kp; (void)vp; (void)alpha; (void)beta; (void)out_lam;      \
+  (void)out_T; (void)out_S; (void)tr_row; (void)tr_col
+
+// ===========================================================================
+// consumer wave c: columns [32c, 32c+32) of That (scaled by 2^E) and S
+// ===========================================================================
+__device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
+  PIC_H16_ROLE_PROLOGUE;
+  const int c = wid;
+  f32x16 XT[NT], XS[NT], PM[2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    XS[t] = zero16();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = t * 32 + acc_row(q, g), col = c * 32 + cl;
+      XT[t][q] = (row == col && row < dk) ? 1.f : 0.f;
+    }
+  }
+  PM[0] = PM[1] = zero16();
+  int E = 0;
+
+  // sub-chunk s of chunk j: S *= gamma; N = -U That, M = W - U S;
+  // That += K^T N, S += K^T M
+  auto chain_sub = [&](int s, int j) {
+    const char* uf = Uf0 + (j & 1) * UF_BYTES;
+    const _Float16* kb = Kb0 + (j % NKB) * (C * RLD);
+    const float gam = gg[(j & 3) * 2 + s];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) XS[t] *= gam;
+    f32x16 PN = zero16(), P = PM[s];
+#pragma unroll
+    for (int ks = 0; ks < 2 * NT; ++ks) {
+      const int t = ks >> 1, hh = ks & 1;
+      // keep the scheduler from converting all k-steps up front (the
+      // converted operands would not fit next to the state)
+      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+      const f16x8 tb = acc_h8(XT[t], hh), sb = acc_h8(XS[t], hh);
+      const f16x8 u = *reinterpret_cast<const f16x8*>(uf + uf_off(s, t, hh, lane));
+      PN = mfma16(u, tb, PN);
+      P = mfma16(u, sb, P);
+    }
+    // K^T fragment of K-step hh, tile t: lane (g, m) needs K[token][32t + m]
+    // for tokens kperm(hh, g, 0..7) = 16 hh + 4 g + {0..3, 8..11} of the
+    // sub-chunk -- the row order of the N / M accumulator halves
+    const _Float16* kbase = kb + (32 * s + 4 * g + tr_row) * RLD + tr_col;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const f16x8 nb = acc_h8(PN, hh), mb = acc_h8(P, hh);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const _Float16* p0 = kbase + 16 * hh * RLD + 32 * t;
+        const f16x8 kf = tr_h8(p0, p0 + 8 * RLD);
+        XT[t] = mfma16(kf, nb, XT[t]);
+        XS[t] = mfma16(kf, mb, XS[t]);
+      }
+    }
+  };
+
+  // W seeds of both sub-chunks of chunk j: M_s = A'_s V_s (this wave's
+  // columns); then re-normalise this wave's columns of That by a power of
+  // two (branch-free, so that no copy of the state is made)
+  auto seeds_and_scale = [&](int j) {
+    const _Float16* Ap = AB0 + (j & 1) * AB_HALFS + 64 * A_LD;
+    // V^T fragment: lane (g, n) needs V[token 16 kk + 8 g + 0..7][32 c + n]
+    const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 32 * c + tr_col;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const f16x8 ph = lds_h8(Ap + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
+        const _Float16* p0 = vbase + (32 * s + 16 * kk) * RLD;
+        const f16x8 vf = tr_h8(p0, p0 + 4 * RLD);
+        acc = mfma16(ph, vf, acc);
+      }
+      PM[s] = acc;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(XT[t][q]));
+    m = wave_max(m);
+    int e;
+    (void)frexpf(m, &e);
+    e = (m > 0.f) ? (e < -120 ? -120 : e) : 0;
+    const float sc = ldexpf(1.f, -e);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) XT[t] *= sc;
+    E += e;
+  };
+
+  // Cycles -1 .. n+1 of the pipeline, peeled so that the steady-state loop
+  // has no branch around the chain (see the schedule at the top).
+  __syncthreads();  // cycle -1, phase A
+  __syncthreads();  //           phase B
+  __syncthreads();  // cycle 0,  phase A
+  __syncthreads();  //           phase B
+  if (n >= 1) {
+    __syncthreads();  // cycle 1, phase A
+    __syncthreads();  //          phase B
+    seeds_and_scale(0);
+    chain_sub(0, 0);
+#pragma unroll 1
+    for (int ci = 2; ci <= n; ++ci) {
+      __syncthreads();  // phase A
+      chain_sub(1, ci - 2);
+      __syncthreads();  // phase B
+      seeds_and_scale(ci - 1);
+      chain_sub(0, ci - 1);
+    }
+    __syncthreads();  // cycle n+1, phase A
+    chain_sub(1, n - 1);
+    __syncthreads();  //            phase B
+  } else {
+    __syncthreads();  // cycle 1, phase A
+    __syncthreads();  //          phase B
+  }
+
+  // write this wave's columns of S(C|0) and That_C
+  const int ncol = c * 32 + cl;
+  if (ncol < dv) {
+    float* out = out_S + unit * int64_t(dk) * dv;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = t * 32 + acc_row(q, g);
+        if (row < dk) gstore(out + int64_t(row) * dv + ncol, float(XS[t][q]));
+      }
+  }
+  if (ncol < dk) {
+    float* out = out_T + unit * int64_t(dk) * dk;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = t * 32 + acc_row(q, g);
+        if (row < dk) gstore(out + int64_t(row) * dk + ncol, ldexpf(XT[t][q], E));
+      }
+  }
+}
+
+// ===========================================================================
+// solver wave: X_s row by row, lanes 32 s + j own row j of sub-chunk s
+// ===========================================================================
+__device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
+  PIC_H16_ROLE_PROLOGUE;
+  const int s = g, jr = cl;
+  float acc[32], bt[32];
+  constexpr int IMID = 20;  // steps 31..IMID in phase A, the rest in phase B
+#pragma unroll 1
+  for (int ci = -1; ci <= n + 1; ++ci) {
+    const bool solve = ci >= 0 && ci < n;
+    const float* nm = Nm0 + (ci & 1) * NM_FLOATS + s * 1024;
+    __syncthreads();  // phase A
+    if (solve) {
+      // beta of the sub-chunk's tokens (masked: 0 past the chunk's end)
+      const float* bp = gb0 + (ci & 1) * C + 32 * s;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bp + 4 * q);
+        bt[4 * q] = b4.x; bt[4 * q + 1] = b4.y; bt[4 * q + 2] = b4.z; bt[4 * q + 3] = b4.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 32; ++r) acc[r] = (r == jr) ? 1.f : 0.f;
+      subst_steps<31, IMID>(acc, nm, bt);
+    }
+    __syncthreads();  // phase B
+    if (solve) {
+      subst_steps<IMID - 1, 1>(acc, nm, bt);
+      // A[jr][k] = X[jr][k] beta_k, A'[jr][k] = A[jr][k] r_k (natural order)
+      const float* brp = gbr0 + (ci & 1) * C + 32 * s;
+      _Float16* arow = AB0 + (ci & 1) * AB_HALFS + (32 * s + jr) * A_LD;
+      _Float16* brow = arow + 64 * A_LD;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 r0 = *reinterpret_cast<const float4*>(brp + 8 * q);
+        const float4 r1 = *reinterpret_cast<const float4*>(brp + 8 * q + 4);
+        const float* x8 = acc + 8 * q;
+        const float* b8 = bt + 8 * q;
+        uint4 wa, wb;
+        wa.x = pk_h2(x8[0] * b8[0], x8[1] * b8[1]);
+        wa.y = pk_h2(x8[2] * b8[2], x8[3] * b8[3]);
+        wa.z = pk_h2(x8[4] * b8[4], x8[5] * b8[5]);
+        wa.w = pk_h2(x8[6] * b8[6], x8[7] * b8[7]);
+        wb.x = pk_h2(x8[0] * r0.x, x8[1] * r0.y);
+        wb.y = pk_h2(x8[2] * r0.z, x8[3] * r0.w);
+        wb.z = pk_h2(x8[4] * r1.x, x8[5] * r1.y);
+        wb.w = pk_h2(x8[6] * r1.z, x8[7] * r1.w);
+        *reinterpret_cast<uint4*>(arow + 8 * q) = wa;
+        *reinterpret_cast<uint4*>(brow + 8 * q) = wb;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// helper waves: staging, G, gates, U^T
+// ===========================================================================
+__device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
+  PIC_H16_ROLE_PROLOGUE;
+  const int pw = wid - NT - 1;  // 0 .. NHW-1
+  const float* bsrc = beta ? beta : alpha;
+  const int HDk = H * dk, HDv = H * dv;  // element stride between tokens
+
+  // K rows: helper s (< 2) stages rows [32 s, 32 s + 32) of each chunk --
+  // exactly the rows its G product reads -- 8 items of 16 bytes per lane:
+  // item i = row 32 s + (lane >> 4) + 4 i, channels 8 (lane & 15) .. +7.
+  // V rows: the last helper, 16 items: row (lane >> 4) + 4 i, same channels.
+  // Tokens past the chunk's end read its last token (a valid address) and
+  // are zeroed when staged.
+  constexpr int NKI = 8, NVI = C / 4;
+  const int cg = lane & 15;
+  const int kch = min(8 * cg, dk - 8), vch = min(8 * cg, dv - 8);
+  // prefetch registers: K rows (helpers 0, 1) or V rows (helper 2)
+  uint4 pr[NVI > NKI ? NVI : NKI];
+  // alpha, beta of lane's token for two chunks (helper NHW-1), indexed by
+  // chunk parity, so that no register holding a pending load is copied
+  float pa[2] = {1.f, 1.f}, pb[2] = {0.f, 0.f};
+  float lam = 0.f;
+  // element offset of the first token of chunk j of this (layer, head)
+  auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
+  auto load_k = [&](int j) {
+    const int len = chunk_len(j);
+    const __bf16* base = kp + row0(j) * dk + kch;
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+      const int t = min(32 * pw + (lane >> 4) + 4 * i, len - 1);
+      pr[i] = gload_u4(base + t * HDk);
+    }
+  };
+  auto load_v = [&](int j) {
+    const int len = chunk_len(j);
+    const __bf16* base = vp + row0(j) * dv + vch;
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) pr[i] = gload_u4(base + min((lane >> 4) + 4 * i, len - 1) * HDv);
+  };
+  auto load_gates = [&](int j, float& ra, float& rb) {
+    const int64_t gi = row0(j) + int64_t(min(lane, chunk_len(j) - 1)) * H;
+    ra = gload(alpha + gi);
+    rb = gload(bsrc + gi);
+  };
+
+  // one pipeline cycle; P = parity of chunk ci+1 (compile-time register slot)
+  auto cycle = [&](int ci, auto par) {
+    constexpr int P = decltype(par)::value;
+    // ---------------- phase A
+    __syncthreads();
+    if (ci - 1 >= 0 && ci - 1 < n) {
+      const int j = ci - 1;
+      // U^T of chunk j, tile by tile -> -U fragments.  K^T fragment: lane
+      // (g, m) needs K[token 32 s + 16 kk + 8 g + 0..7][32 t + m].
+      const _Float16* kb = Kb0 + (j % NKB) * (C * RLD);
+      const _Float16* Ah = AB0 + (j & 1) * AB_HALFS;
+      char* uf = Uf0 + (j & 1) * UF_BYTES;
+      const _Float16* kbase = kb + (8 * g + tr_row) * RLD + tr_col;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const int tile = pw + 2 * i;
+        if (pw < 2) {
+          const int t = tile % NT, s = tile / NT;
+          f32x16 acc = zero16();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 32 * t;
+            const f16x8 kf = tr_h8(p0, p0 + 4 * RLD);
+            const f16x8 ah = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
+            acc = mfma16(kf, ah, acc);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            *reinterpret_cast<f16x8*>(uf + uf_off(s, t, hh, lane)) = acc_h8<-1>(acc, hh);
+        }
+      }
+      if (pw == NHW - 1) {
+        // V rows of chunk j (loaded a cycle ago)
+        const int len = chunk_len(j);
+        const bool okc = 8 * cg < dv;
+#pragma unroll
+        for (int i = 0; i < NVI; ++i) {
+          const int t = (lane >> 4) + 4 * i;
+          *reinterpret_cast<uint4*>(Vb + t * RLD + 8 * cg) = pick_u4(okc && t < len, bf2h(pr[i]));
+        }
+      }
+    }
+    if (pw == NHW - 1 && ci >= 0 && ci < n) load_v(ci);
+
+    // ---------------- phase B
+    __syncthreads();
+    if (ci + 1 < n) {
+      const int jn = ci + 1;
+      const int len = chunk_len(jn);
+      if (pw < 2) {
+        // K rows [32 s, 32 s + 32) of chunk jn (loaded a cycle ago), then
+        // G_ss = K_s K_s^T from those rows; L = diag(beta) strictly-lower(G)
+        const int s = pw;
+        _Float16* kb = Kb0 + (jn % NKB) * (C * RLD);
+        const bool okc = 8 * cg < dk;
+#pragma unroll
+        for (int i = 0; i < NKI; ++i) {
+          const int t = 32 * s + (lane >> 4) + 4 * i;
+          *reinterpret_cast<uint4*>(kb + t * RLD + 8 * cg) = pick_u4(okc && t < len, bf2h(pr[i]));
+        }
+        if (jn + 1 < n) load_k(jn + 1);
+        f32x16 acc0 = zero16(), acc1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < DP / 16; ++ks) {
+          const f16x8 ak = lds_h8(kb + (32 * s + cl) * RLD + 16 * ks + 8 * g);
+          if (ks & 1)
+            acc1 = mfma16(ak, ak, acc1);
+          else
+            acc0 = mfma16(ak, ak, acc0);
+        }
+        // G is symmetric: the lane's accumulator column cl is also row cl,
+        // with entries 8 k + 4 g + {0..3} in registers 4k .. 4k+3
+        float* nm = Nm0 + (jn & 1) * NM_FLOATS + s * 1024 + cl * 32 + 4 * g;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          *reinterpret_cast<float4*>(nm + 8 * k4) =
+              make_float4(acc0[4 * k4] + acc1[4 * k4], acc0[4 * k4 + 1] + acc1[4 * k4 + 1],
+                          acc0[4 * k4 + 2] + acc1[4 * k4 + 2], acc0[4 * k4 + 3] + acc1[4 * k4 + 3]);
+      } else {
+        // gates of chunk jn: log2 prefix per sub-chunk (one per half wave)
+        const float x2 = half_wave_scan(lane < len ? log2f(pa[P]) : 0.f);
+        const int xi = __builtin_bit_cast(int, x2);
+        const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 31));
+        const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 63));
+        const float bend = g ? e1 : e0;
+        const float bt = lane < len ? (beta ? pb[P] : 1.f) : 0.f;  // masked beta
+        gb0[(jn & 1) * C + lane] = bt;
+        gbr0[(jn & 1) * C + lane] = bt * exp2f(bend - x2);
+        if (lane == 0) {
+          gg[(jn & 3) * 2] = exp2f(e0);
+          gg[(jn & 3) * 2 + 1] = exp2f(e1);
+        }
+        lam += e0 + e1;
+        // the slot of chunk jn now takes chunk jn + 2
+        if (jn + 2 < n) load_gates(jn + 2, pa[P], pb[P]);
+      }
+    }
+  };
+
+  if (n > 0) {
+    if (pw < 2) load_k(0);
+    if (pw == NHW - 1) load_gates(0, pa[0], pb[0]);
+  }
+  if (n > 1 && pw == NHW - 1) load_gates(1, pa[1], pb[1]);
+  // chunk ci+1 has parity (ci+1) & 1: cycles -1, 1, 3, ... use slot 0
+#pragma unroll 1
+  for (int ci = -1; ci <= n + 1; ci += 2) {
+    cycle(ci, std::integral_constant<int, 0>{});
+    if (ci + 1 <= n + 1) cycle(ci + 1, std::integral_constant<int, 1>{});
+  }
+  if (pw == NHW - 1 && lane == 0) gstore(out_lam + unit, lam * kLn2);
+}
+
+}  // namespace
+
+hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s) {
+  const int64_t blocks = int64_t(a.n_seg) * a.batch * a.heads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(build_dense_h16_kernel, dim3(unsigned(blocks)), dim3(THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pic

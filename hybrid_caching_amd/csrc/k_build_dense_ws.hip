@@ -57,6 +57,7 @@
 // Cycle ci prepares chunk ci and chains chunk ci-1 (n_chunks + 1 cycles).
 #include "mfma_util.hpp"
 #include "pic_internal.hpp"
+#include "stage_util.hpp"
 
 namespace pic {
 namespace {
@@ -94,47 +95,6 @@ struct WsLds {
   static_assert(KT % 16 == 0 && VT % 16 == 0 && UF % 16 == 0 && XM % 16 == 0, "alignment");
   static_assert(A_BYTES % 16 == 0 && LM % 16 == 0 && GB % 16 == 0, "alignment");
 };
-
-// storage position of token t inside a K dimension (swap bits 2 and 3)
-__device__ __forceinline__ int tpos(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
-
-// (element j of token a, element j of token b) as one packed pair
-__device__ __forceinline__ unsigned ws_pair(const uint4& a, const uint4& b, int j) {
-  const unsigned wa = (j < 2) ? a.x : (j < 4) ? a.y : (j < 6) ? a.z : a.w;
-  const unsigned wb = (j < 2) ? b.x : (j < 4) ? b.y : (j < 6) ? b.z : b.w;
-  return __builtin_amdgcn_perm(wb, wa, (j & 1) ? 0x07060302u : 0x05040100u);
-}
-
-__device__ __forceinline__ uint4 ws_pick(bool ok, uint4 x) {
-  return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
-}
-
-// element offset of 16-byte chunk `chunk` of row `row` in a swizzled K^T / V^T
-template <int LD>
-__device__ __forceinline__ int kt_at(int row, int chunk) {
-  return row * LD + 8 * (chunk ^ ((row >> 3) & 7));
-}
-
-// The same offset for rows 32 t + cl read by lane (g, cl) at chunk
-// 4 s + 2 hh + g: the swizzle only flips bits of the chunk index, so it is
-// a per-lane base for each half hh plus a constant for (t, s).
-template <int LD>
-__device__ __forceinline__ int kt_lane_base(int cl, int g, int hh) {
-  return cl * LD + 8 * (g ^ ((cl >> 3) & 1)) + 16 * (hh ^ ((cl >> 4) & 1));
-}
-template <int LD>
-__device__ __forceinline__ int kt_tile(int t, int s) {
-  return 32 * t * LD + 32 * (s ^ (t & 1));
-}
-
-// a copy of v the compiler cannot see through: keeps per-lane address
-// arithmetic inside a loop instead of holding it in registers across it
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 
 // byte offset of a -U fragment: sub-chunk s, channel tile t, half h, part (0 hi, 1 lo), lane
 template <int NT>

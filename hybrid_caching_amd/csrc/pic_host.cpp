@@ -158,7 +158,7 @@ size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int d
   return build_ws_bytes(n_seg);
 }
 
-int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
                        int64_t n_tokens, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int64_t* seg_offsets,
                        int32_t n_seg, const float* log_scale, const float* T_hat,
@@ -169,6 +169,10 @@ int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, in
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
     return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
+  if (precision != PIC_PREC_FP32 && precision != PIC_PREC_FP16)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown precision %d", precision);
+  if (precision == PIC_PREC_FP16 && (form != PIC_FORM_DENSE || qkv_dtype != PIC_DT_BF16))
+    return fail(PIC_ERR_UNSUPPORTED, "PIC_PREC_FP16 needs the dense form with bf16 k/v");
   if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
   if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
   if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
@@ -194,12 +198,12 @@ int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, in
   return ok();
 }
 
-int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
                       int64_t n_tokens, const void* q, const void* k, const void* v,
                       const float* alpha, const float* beta, const int64_t* seg_offsets,
                       int32_t n_seg, float* log_scale, float* T_hat, float* S0,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = pic_validate_build(form, qkv_dtype, batch, heads, dk, dv, n_tokens, q, k, v,
+  if (int rc = pic_validate_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q, k, v,
                                   alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0,
                                   workspace, workspace_bytes))
     return rc;
@@ -216,8 +220,11 @@ int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int
   if (e != hipSuccess) return hip_fail(e, "copying segment order");
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
                    k, v, alpha, beta, d_off, d_order, log_scale, T_hat, S0};
-  e = (form == PIC_FORM_DENSE) ? pic::launch_build_dense(a, s)
-                               : pic::launch_build_scalar_diag(a, s);
+  if (form == PIC_FORM_DENSE)
+    e = (precision == PIC_PREC_FP16) ? pic::launch_build_dense_h16(a, s)
+                                     : pic::launch_build_dense(a, s);
+  else
+    e = pic::launch_build_scalar_diag(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the build kernel");
   return ok();
 }

@@ -50,6 +50,8 @@ hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_ws(const BuildArgs& a, hipStream_t s);
+// fp16 operand precision (bf16 inputs, any dk, dv <= 128)
+hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
 // chain pair: log_scale_out (all forms) and That_out = That_pn ... That_p1 (dense)

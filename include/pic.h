@@ -75,10 +75,24 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 2
+#define PIC_ABI_VERSION 3
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
+
+/* Arithmetic of the build's matrix-core products (the state and every
+ * accumulation are fp32 in both):
+ *   PIC_PREC_FP32  fp32-accurate: an fp32 operand is split into two bf16
+ *                  terms and a product takes up to three bf16 products
+ *                  (~2^-16 relative per product); all forms and dtypes.
+ *   PIC_PREC_FP16  one fp16 product per operand pair (11 significant bits);
+ *                  dense form with bf16 k/v only.  The ungated product That
+ *                  is kept at a power-of-two column scale internally, so its
+ *                  decay along a segment does not leave fp16's range; keys
+ *                  are assumed unit-norm (beta |k|^2 <= 2) and |v|, |S| well
+ *                  below 6e4.  Typical relative Frobenius error against fp64
+ *                  at 4096-8192 tokens: ~2e-3 on That, ~3e-4 on S(C|0). */
+enum pic_precision { PIC_PREC_FP32 = 0, PIC_PREC_FP16 = 1 };
 
 enum pic_status {
   PIC_OK = 0,
@@ -108,6 +122,8 @@ const char* pic_last_error(void);
  *
  * form        PIC_FORM_*
  * qkv_dtype   storage type of q, k, v: PIC_DT_BF16 or PIC_DT_F32
+ * precision   PIC_PREC_FP32, or PIC_PREC_FP16 (dense form with bf16 k/v only;
+ *             any other combination returns PIC_ERR_UNSUPPORTED)
  * batch, heads, dk, dv, n_tokens   sizes (see layouts above)
  * q           may be NULL; never read: the pair does not depend on queries
  * k, v        device, qkv_dtype
@@ -126,13 +142,13 @@ const char* pic_last_error(void);
 size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int dv,
                                    int64_t n_tokens, int32_t n_seg);
 
-int pic_validate_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
                        int64_t n_tokens, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, const int64_t* seg_offsets,
                        int32_t n_seg, const float* log_scale, const float* T_hat,
                        const float* S0, const void* workspace, size_t workspace_bytes);
 
-int pic_segment_build(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
                       int64_t n_tokens, const void* q, const void* k, const void* v,
                       const float* alpha, const float* beta, const int64_t* seg_offsets,
                       int32_t n_seg, float* log_scale, float* T_hat, float* S0,

@@ -56,13 +56,14 @@ def lam_err(got, ref):
     return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref)))) if ref.size else 0.0
 
 
-def build_both(form, k, v, alpha, beta, offsets, bf16, q=None):
+def build_both(form, k, v, alpha, beta, offsets, bf16, q=None, precision=0):
     """Run the HIP build and the oracle on the same (numpy, fp32-exact) inputs."""
     import hybrid_caching_amd as pic
     import torch
     dt = qkv_dtype(bf16)
     out = pic.pic_segment_build(form, to_dev(k, dt), to_dev(v, dt), to_dev(alpha),
-                                to_dev(beta), offsets, q=None if q is None else to_dev(q, dt))
+                                to_dev(beta), offsets, q=None if q is None else to_dev(q, dt),
+                                precision=precision)
     torch.cuda.synchronize()
     gpu = {key: val.cpu().numpy() for key, val in out.items()}
     ref = oracle.build(form, k, v, alpha, beta, offsets)

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 2
+    assert lib.pic_abi_version() == 3
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -68,11 +68,11 @@ def offsets(x):
 
 
 def vbuild(lib, form=DENSE, dt=BF16, B=1, H=2, dk=128, dv=128, N=100, offs=(0, 40, 100),
-           That=True, ws_bytes=None, k=None, alpha=None, S0=None, ws=None):
+           That=True, ws_bytes=None, k=None, alpha=None, S0=None, ws=None, prec=0):
     off, off_p = offsets(offs)
     n_seg = len(off) - 1
     need = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
-    return lib.pic_validate_build(form, dt, B, H, dk, dv, N, None, k or P(0), P(1),
+    return lib.pic_validate_build(form, dt, prec, B, H, dk, dv, N, None, k or P(0), P(1),
                                   alpha or P(2), P(3), off_p, n_seg, P(4),
                                   P(5) if That else None, S0 or P(6), ws or P(7),
                                   need if ws_bytes is None else ws_bytes)
@@ -83,11 +83,15 @@ def test_validate_build_accepts_good_arguments(lib):
     assert vbuild(lib, form=SCALAR, That=False) == OK
     assert vbuild(lib, form=DIAG, That=False, dt=F32, dk=16, dv=48) == OK
     assert vbuild(lib, offs=(0, 0, 100, 100)) == OK  # empty segments are allowed
+    assert vbuild(lib, prec=1) == OK  # fp16 operands: dense with bf16 k/v
+    assert vbuild(lib, prec=1, dk=16, dv=48) == OK
     assert lib.pic_last_error().decode() == ""
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"form": 7}, EUNSUP), ({"dt": 5}, EUNSUP),
+    ({"form": 7}, EUNSUP), ({"dt": 5}, EUNSUP), ({"prec": 2}, EUNSUP), ({"prec": -1}, EUNSUP),
+    ({"prec": 1, "dt": F32}, EUNSUP), ({"prec": 1, "form": SCALAR, "That": False}, EUNSUP),
+    ({"prec": 1, "form": DIAG, "That": False}, EUNSUP),
     ({"dk": 8}, EDIMS), ({"dv": 144}, EDIMS), ({"dk": 24}, EDIMS), ({"B": 0}, EDIMS),
     ({"H": 0}, EDIMS),
     ({"offs": (1, 40, 100)}, EOFF), ({"offs": (0, 50, 40, 100)}, EOFF),
@@ -104,10 +108,10 @@ def test_validate_build_rejects(lib, kw, code):
 def test_validate_build_null_pointers(lib):
     off, off_p = offsets((0, 10))
     ws = lib.pic_segment_build_workspace(DENSE, 1, 1, 16, 16, 10, 1)
-    args = [DENSE, BF16, 1, 1, 16, 16, 10, None, P(0), P(1), P(2), None, off_p, 1, P(4), P(5),
-            P(6), P(7), ws]
+    args = [DENSE, BF16, 0, 1, 1, 16, 16, 10, None, P(0), P(1), P(2), None, off_p, 1, P(4),
+            P(5), P(6), P(7), ws]
     assert lib.pic_validate_build(*args) == OK
-    for i in (8, 9, 10, 12, 14, 15, 16, 17):  # k, v, alpha, offsets, lam, That, S0, workspace
+    for i in (9, 10, 11, 13, 15, 16, 17, 18):  # k, v, alpha, offsets, lam, That, S0, workspace
         bad = list(args)
         bad[i] = None
         rc = lib.pic_validate_build(*bad)

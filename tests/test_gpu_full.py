@@ -69,7 +69,7 @@ def test_scalar_diag_full_workload(name):
     assert max_rel_units(naive.cpu().numpy(), ref_n) <= TOL_BF16
 
 
-def _dense_full(name, layers, samples, chains):
+def _dense_full(name, layers, samples, chains, precision=0):
     """Build the dense stack on the GPU from device-drawn inputs, then check
     sampled (layer, head, segment) units and sampled composed (layer, head)
     chains against the oracle run on the same input values."""
@@ -91,7 +91,7 @@ def _dense_full(name, layers, samples, chains):
         alpha[layer].copy_(x["alpha"])
         beta[layer].copy_(x["beta"])
     offsets = w.offsets()
-    pair = pic.pic_segment_build(w.form, k, v, alpha, beta, offsets)
+    pair = pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, precision=precision)
     comp = pic.pic_compose(w.form, pair["log_scale"], pair["T_hat"], pair["S0"], [0, n_seg],
                            list(range(n_seg)))
     naive = pic.pic_naive_add(pair["S0"], [0, n_seg], list(range(n_seg)))
@@ -110,7 +110,7 @@ def _dense_full(name, layers, samples, chains):
         gpu = {"S0": pair["S0"][seg, layer, head].cpu().numpy()[None, None, None],
                "T_hat": pair["T_hat"][seg, layer, head].cpu().numpy()[None, None, None],
                "log_scale": pair["log_scale"][seg, layer, head].cpu().numpy()[None, None, None]}
-        report(f"{name} unit (layer {layer}, head {head}, seg {seg}):")
+        report(f"{name} precision {precision} unit (layer {layer}, head {head}, seg {seg}):")
         assert_pair_close(gpu, ref, w.form, TOL_BF16)
     for (layer, head) in chains(rng, B, H):
         kk, vv, aa, bb = unit_inputs(layer, head, 0, n_seg)
@@ -123,7 +123,8 @@ def _dense_full(name, layers, samples, chains):
         rho = rho_of(ref_c[0], ref["S"][-1])
         en = max_rel_units(naive[0, layer, head].cpu().numpy(),
                            oracle.naive_add(ref["S"], [0, n_seg], list(range(n_seg)))[0, 0, 0])
-        report(f"{name} chain (layer {layer}, head {head}): compose err {e:.3e}, rho {rho:.3f}, "
+        report(f"{name} precision {precision} chain (layer {layer}, head {head}): "
+               f"compose err {e:.3e}, rho {rho:.3f}, "
                f"naive-add err {en:.3e}")
         assert e <= TOL_BF16 and en <= TOL_BF16
         if name.endswith("_slow"):
@@ -131,7 +132,8 @@ def _dense_full(name, layers, samples, chains):
     return pair
 
 
-def test_dense_full_workload_sampled():
+@pytest.mark.parametrize("precision", [0, 1])
+def test_dense_full_workload_sampled(precision):
     def samples(rng, B, H, n_seg):
         fixed = [(0, 0, 0), (B - 1, H - 1, n_seg - 1), (B // 2, 7, n_seg // 2)]
         extra = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_seg)))
@@ -141,10 +143,11 @@ def test_dense_full_workload_sampled():
     def chains(rng, B, H):
         return [(B - 1, 3)]
 
-    _dense_full("dense_30L_32x4096", None, samples, chains)
+    _dense_full("dense_30L_32x4096", None, samples, chains, precision)
 
 
-def test_dense_slow_gates_full_length_sampled():
+@pytest.mark.parametrize("precision", [0, 1])
+def test_dense_slow_gates_full_length_sampled(precision):
     """Slow gates at the full 32 x 4096 prompt (2 layers): composition of 32
     built segments must match the oracle with a sizeable carried term."""
     def samples(rng, B, H, n_seg):
@@ -153,7 +156,7 @@ def test_dense_slow_gates_full_length_sampled():
     def chains(rng, B, H):
         return [(0, 0)]
 
-    _dense_full("dense_30L_32x4096_slow", 2, samples, chains)
+    _dense_full("dense_30L_32x4096_slow", 2, samples, chains, precision)
 
 
 @pytest.mark.timeout(400)
