@@ -17,18 +17,18 @@
 // norm is ~1e-4 after 4096 tokens at the usual gates), far below fp16's
 // normal range, so each consumer wave keeps its columns of That scaled by a
 // power of two (a column scaling commutes with left multiplication, and a
-// power of two is exact) and re-normalises them once per chunk; the exponent
-// is applied when That is written.  S, U, W and the keys stay within fp16's
+// power of two is exact) and re-normalises them every other chunk; the
+// exponent is applied when That is written.  S, U, W and the keys stay within fp16's
 // range for unit-norm keys and values of moderate size.
 //
 // One workgroup per (segment, layer, head): four consumer waves, each holding
 // columns [32c, 32c+32) of both That and S in MFMA accumulators for the whole
 // segment, and four producer waves.  Producer wave 0 ("solver") computes the
-// two 32x32 triangular inverses of a chunk by back substitution, one row of
-// X per lane (lanes 0-31 sub-chunk 0, lanes 32-63 sub-chunk 1), reading rows
-// of L as broadcast LDS loads a few steps ahead: no workgroup barrier inside
-// the solve.  Three helper waves stage k/v, form G = K K^T, the gates and
-// U^T = K^T A^T.
+// two 32x32 triangular inverses of a chunk: the 16x16 diagonal blocks by back
+// substitution, one row per lane, reading rows of L as broadcast LDS loads a
+// few steps ahead, then the off-diagonal blocks X_10 = -X_11 L_10 X_00 with
+// 16x16x16 matrix-core products: no workgroup barrier inside the solve.
+// Three helper waves stage k/v, form G = K K^T, the gates and U^T = K^T A^T.
 //
 // LDS holds K and V row-major in fp16.  Every transposed operand fragment
 // (K^T for U^T and for K^T N, V^T for W) is read with ds_read_b64_tr_b16: in
@@ -41,20 +41,19 @@
 //
 // Pipeline: cycle ci has two phases separated by workgroup barriers.
 //   phase A: consumers chain sub-chunk 1 of chunk ci-2
-//            helpers:  U^T of chunk ci-1 -> -U fragments (helpers 0, 1); V
-//                      rows of chunk ci-1 to LDS (helper 2)
-//            solver:   first part of the back substitution of chunk ci
+//            helpers:  K rows of chunk ci+1 to LDS (helpers 0, 1), V rows
+//                      32..63 of chunk ci-1 (helper 2); U^T of chunk ci-1 ->
+//                      -U fragments (all three)
+//            solver:   V rows 0..31 of chunk ci-1; diagonal blocks of chunk ci
 //   phase B: consumers: W seeds of chunk ci-1, chain sub-chunk 0 of ci-1
-//            helpers:  K rows of chunk ci+1 to LDS and G of chunk ci+1 (helper
-//                      s stages exactly the rows its G reads, so no other
-//                      wave waits for them); the gates of chunk ci+1 (helper 2)
-//            solver:   rest of the substitution of chunk ci -> A, A'
+//            helpers:  the gates of chunk ci+1 (helper 2)
+//            solver:   off-diagonal blocks of chunk ci -> A, A'; G of chunk ci+1
 // so a chunk is staged in cycle j-1, solved in cycle j, and chained in cycles
 // j+1 and j+2.  K is kept for four chunks; -U fragments, A/A', G and the
 // masked gates for two; V for one.  Every global load is issued a cycle
 // before its data is staged.  The solver applies beta to the rows of G
-// (L = diag(beta) strictly-lower(G)); G = K K^T is symmetric, so the helpers
-// write each accumulator column as a row with four 16-byte stores.
+// (L = diag(beta) strictly-lower(G)); G = K K^T is symmetric, so each lane
+// writes its accumulator column as a row with four 16-byte stores.
 #include <type_traits>
 
 #include "mfma_util.hpp"
@@ -174,31 +173,28 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// Back substitution of X (I + L) = I for the lane's row, steps i = HI .. LO
-// (descending): acc[r] -= X[row][i] L[i][r] for r < i, where L[i][r] =
-// beta_i G[i][r].  Row i of G is a broadcast read (every lane of the half
-// wave reads the same address), issued PF steps ahead of its use; bt holds
-// beta of the sub-chunk's 32 tokens (uniform per half wave).
+// Back substitution of X_bb (I + L_bb) = I for one row of a 16x16 diagonal
+// block, steps i = 15 .. 1: acc[r] -= X[row][i] L[i][r] for r < i, where
+// L[i][r] = beta_i G[i][r].  Row i of the block of G is a broadcast read
+// (the 16 lanes of a block read the same address), issued PF steps ahead of
+// its use; bt holds beta of the block's 16 tokens.
 constexpr int PF = 3;
-template <int HI, int LO>
-__device__ __forceinline__ void subst_steps(float (&acc)[32], const float* nm, const float (&bt)[32]) {
-  float4 buf[PF + 1][8];
+__device__ __forceinline__ void subst16(float (&acc)[16], const float* grow0, const float (&bt)[16]) {
+  float4 buf[PF + 1][4];
 #pragma unroll
   for (int p = 0; p < PF; ++p)
-    if (HI - p >= LO) {
 #pragma unroll
-      for (int r4 = 0; r4 < (HI - p + 3) / 4; ++r4)
-        buf[p][r4] = *reinterpret_cast<const float4*>(nm + (HI - p) * 32 + 4 * r4);
-    }
+    for (int r4 = 0; r4 < (15 - p + 3) / 4; ++r4)
+      buf[p][r4] = *reinterpret_cast<const float4*>(grow0 + (15 - p) * 32 + 4 * r4);
 #pragma unroll
-  for (int i = HI; i >= LO; --i) {
-    const int slot = (HI - i) % (PF + 1);
+  for (int i = 15; i >= 1; --i) {
+    const int slot = (15 - i) % (PF + 1);
     const int ip = i - PF;  // row read now, used PF steps later
-    if (ip >= LO) {
-      const int ps = (HI - ip) % (PF + 1);
+    if (ip >= 1) {
+      const int ps = (15 - ip) % (PF + 1);
 #pragma unroll
       for (int r4 = 0; r4 < (ip + 3) / 4; ++r4)
-        buf[ps][r4] = *reinterpret_cast<const float4*>(nm + ip * 32 + 4 * r4);
+        buf[ps][r4] = *reinterpret_cast<const float4*>(grow0 + ip * 32 + 4 * r4);
     }
     __builtin_amdgcn_sched_barrier(0);
     const float x = acc[i] * bt[i];
@@ -209,6 +205,68 @@ __device__ __forceinline__ void subst_steps(float (&acc)[32], const float* nm, c
       for (int e = 0; e < 4; ++e)
         if (4 * r4 + e < i) acc[4 * r4 + e] = fmaf(-nv[e], x, acc[4 * r4 + e]);
     }
+  }
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 h4(float x0, float x1, float x2, float x3) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = {pk_h2(x0, x1), pk_h2(x2, x3)};
+  return __builtin_bit_cast(f16x4, w);
+}
+
+// Staging of K / V rows: 16 items of 16 bytes per lane cover a chunk --
+// item i is row (lane >> 4) + 4 i, channels 8 (lane & 15) .. +7 -- so each
+// load instruction reads four whole 256-byte rows.  Rows past the chunk's end
+// read its last row (a valid address) and are zeroed when staged; channels
+// past the head size read a valid group and are zeroed too.
+template <int NI>
+__device__ __forceinline__ void load_rows(uint4 (&pr)[NI], const __bf16* base, int HD, int len,
+                                          int i0, int ni, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (i < ni) pr[i] = gload_u4(base + min((lane >> 4) + 4 * (i0 + i), len - 1) * HD);
+}
+template <int NI>
+__device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI], int len, int d,
+                                           int i0, int ni, int lane) {
+  const int cg = lane & 15;
+  const bool full = len == C && d == DP, okc = 8 * cg < d;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (i < ni) {
+      const int t = (lane >> 4) + 4 * (i0 + i);
+      const uint4 w = bf2h(pr[i]);
+      *reinterpret_cast<uint4*>(dst + t * RLD + 8 * cg) = full ? w : pick_u4(okc && t < len, w);
+    }
+}
+
+// G_ss = K_s K_s^T for both sub-chunks from the K rows of a chunk (fp32).  G
+// is symmetric: the lane's accumulator column cl is also row cl, with entries
+// 8 k + 4 g + {0..3} in registers 4k .. 4k+3, so each lane writes its row
+// with four 16-byte stores.
+__device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane) {
+  const int g = lane >> 5, cl = lane & 31;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    f32x16 acc0 = zero16(), acc1 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) {
+      const f16x8 ak = lds_h8(kb + (32 * s + cl) * RLD + 16 * ks + 8 * g);
+      if (ks & 1)
+        acc1 = mfma16(ak, ak, acc1);
+      else
+        acc0 = mfma16(ak, ak, acc0);
+    }
+    float* row = gm + s * 1024 + cl * 32 + 4 * g;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      *reinterpret_cast<float4*>(row + 8 * k4) =
+          make_float4(acc0[4 * k4] + acc1[4 * k4], acc0[4 * k4 + 1] + acc1[4 * k4 + 1],
+                      acc0[4 * k4 + 2] + acc1[4 * k4 + 2], acc0[4 * k4 + 3] + acc1[4 * k4 + 3]);
   }
 }
 
@@ -328,9 +386,6 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
 #pragma unroll
     for (int ks = 0; ks < 2 * NT; ++ks) {
       const int t = ks >> 1, hh = ks & 1;
-      // keep the scheduler from converting all k-steps up front (the
-      // converted operands would not fit next to the state)
-      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
       const f16x8 tb = acc_h8(XT[t], hh), sb = acc_h8(XS[t], hh);
       const f16x8 u = *reinterpret_cast<const f16x8*>(uf + uf_off(s, t, hh, lane));
       PN = mfma16(u, tb, PN);
@@ -354,9 +409,9 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
   };
 
   // W seeds of both sub-chunks of chunk j: M_s = A'_s V_s (this wave's
-  // columns); then re-normalise this wave's columns of That by a power of
-  // two (branch-free, so that no copy of the state is made)
-  auto seeds_and_scale = [&](int j) {
+  // columns); then (every other chunk) re-normalise this wave's columns of
+  // That by a power of two -- branch-free, so that no copy of the state is made
+  auto seeds_and_scale = [&](int j, auto rescale) {
     const _Float16* Ap = AB0 + (j & 1) * AB_HALFS + 64 * A_LD;
     // V^T fragment: lane (g, n) needs V[token 16 kk + 8 g + 0..7][32 c + n]
     const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 32 * c + tr_col;
@@ -372,6 +427,7 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
       }
       PM[s] = acc;
     }
+    if (!decltype(rescale)::value) return;
     float m = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -396,14 +452,27 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
   if (n >= 1) {
     __syncthreads();  // cycle 1, phase A
     __syncthreads();  //          phase B
-    seeds_and_scale(0);
+    seeds_and_scale(0, std::true_type{});
     chain_sub(0, 0);
+    int ci = 2;
 #pragma unroll 1
-    for (int ci = 2; ci <= n; ++ci) {
+    for (; ci + 1 <= n; ci += 2) {
       __syncthreads();  // phase A
       chain_sub(1, ci - 2);
       __syncthreads();  // phase B
-      seeds_and_scale(ci - 1);
+      seeds_and_scale(ci - 1, std::false_type{});
+      chain_sub(0, ci - 1);
+      __syncthreads();  // phase A
+      chain_sub(1, ci - 1);
+      __syncthreads();  // phase B
+      seeds_and_scale(ci, std::true_type{});
+      chain_sub(0, ci);
+    }
+    if (ci <= n) {
+      __syncthreads();  // phase A
+      chain_sub(1, ci - 2);
+      __syncthreads();  // phase B
+      seeds_and_scale(ci - 1, std::false_type{});
       chain_sub(0, ci - 1);
     }
     __syncthreads();  // cycle n+1, phase A
@@ -439,100 +508,154 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
 }
 
 // ===========================================================================
-// solver wave: X_s row by row, lanes 32 s + j own row j of sub-chunk s
+// solver wave: X_s = (I + L_s)^{-1} of both sub-chunks.  Phase A: the four
+// 16x16 diagonal blocks by back substitution, lane 32 s + 16 b + j owning
+// row j of block b of sub-chunk s; the rows go to a scratch tile (fp16).
+// Phase B: the off-diagonal block X_10 = -X_11 L_10 X_00 of each sub-chunk
+// with two 16x16x16 matrix-core products (their B operands are read
+// transposed from the scratch tile; the first product's accumulators are
+// already the second one's B operand), then A = X diag(beta) and
+// A' = X diag(beta r) to LDS; then G of the next chunk.  The scratch is the
+// A/A' buffer of the chunk being solved: its previous chunk was last read in
+// the cycle before.  The solver also stages the first half of V.
 // ===========================================================================
+constexpr int XS_LD = 48;  // scratch row stride (halves): 96 bytes, so that the
+                           // four rows of a transposed read hit distinct banks
 __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
-  const int s = g, jr = cl;
-  float acc[32], bt[32];
-  constexpr int IMID = 20;  // steps 31..IMID in phase A, the rest in phase B
+  const int s = lane >> 5, blk = (lane >> 4) & 1, jr = lane & 15;
+  const int HDv = H * dv;
+  const int vch = min(8 * (lane & 15), dv - 8);
+  float acc[16], bt[16];
+  uint4 pv[8];  // V rows 0..31 of the next chunk to stage (items 0..7)
 #pragma unroll 1
   for (int ci = -1; ci <= n + 1; ++ci) {
     const bool solve = ci >= 0 && ci < n;
-    const float* nm = Nm0 + (ci & 1) * NM_FLOATS + s * 1024;
+    const float* gm = Nm0 + (ci & 1) * NM_FLOATS;          // G of both sub-chunks
+    const float* gbp = gb0 + (ci & 1) * C;                 // masked beta
+    const float* grp = gbr0 + (ci & 1) * C;                // beta * r
+    _Float16* ab = AB0 + (ci & 1) * AB_HALFS;              // scratch, then A / A'
     __syncthreads();  // phase A
+    // V rows 0..31 of chunk ci-1 (loaded a cycle ago), then load chunk ci's
+    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pv, chunk_len(ci - 1), dv, 0, 8, lane);
+    if (solve)
+      load_rows(pv, vp + ((int64_t(b) * N + t_begin + int64_t(ci) * C) * H + h) * dv + vch, HDv,
+                chunk_len(ci), 0, 8, lane);
     if (solve) {
-      // beta of the sub-chunk's tokens (masked: 0 past the chunk's end)
-      const float* bp = gb0 + (ci & 1) * C + 32 * s;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 b4 = *reinterpret_cast<const float4*>(bp + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const float4 b4 = *reinterpret_cast<const float4*>(gbp + 32 * s + 16 * blk + 4 * q);
         bt[4 * q] = b4.x; bt[4 * q + 1] = b4.y; bt[4 * q + 2] = b4.z; bt[4 * q + 3] = b4.w;
       }
 #pragma unroll
-      for (int r = 0; r < 32; ++r) acc[r] = (r == jr) ? 1.f : 0.f;
-      subst_steps<31, IMID>(acc, nm, bt);
+      for (int r = 0; r < 16; ++r) acc[r] = (r == jr) ? 1.f : 0.f;
+      subst16(acc, gm + s * 1024 + (16 * blk) * 32 + 16 * blk, bt);
+      // row jr of block blk -> scratch tile (s, blk)
+      _Float16* xr = ab + ((2 * s + blk) * 16 + jr) * XS_LD;
+      *reinterpret_cast<uint4*>(xr) = make_uint4(pk_h2(acc[0], acc[1]), pk_h2(acc[2], acc[3]),
+                                                 pk_h2(acc[4], acc[5]), pk_h2(acc[6], acc[7]));
+      *reinterpret_cast<uint4*>(xr + 8) = make_uint4(pk_h2(acc[8], acc[9]), pk_h2(acc[10], acc[11]),
+                                                     pk_h2(acc[12], acc[13]), pk_h2(acc[14], acc[15]));
     }
     __syncthreads();  // phase B
     if (solve) {
-      subst_steps<IMID - 1, 1>(acc, nm, bt);
-      // A[jr][k] = X[jr][k] beta_k, A'[jr][k] = A[jr][k] r_k (natural order)
-      const float* brp = gbr0 + (ci & 1) * C + 32 * s;
-      _Float16* arow = AB0 + (ci & 1) * AB_HALFS + (32 * s + jr) * A_LD;
+      // off-diagonal blocks; 16x16x16 layouts: lane l holds A[l%16][4(l/16)+e],
+      // B[4(l/16)+e][l%16], D[4(l/16)+e][l%16], e = 0..3
+      const int m = lane & 15, kq = lane >> 4;
+      f32x4 X10[2];
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gm + ss * 1024 + (16 + m) * 32 + 4 * kq);
+        const float bm = gbp[32 * ss + 16 + m];
+        const f16x4 l10 = h4(bm * g4.x, bm * g4.y, bm * g4.z, bm * g4.w);
+        const _Float16* t00 = ab + (2 * ss) * 16 * XS_LD;
+        const _Float16* t11 = ab + (2 * ss + 1) * 16 * XS_LD;
+        const f16x4 x00 = __builtin_bit_cast(f16x4, lds_tr4(t00 + (4 * kq + (m >> 2)) * XS_LD + 4 * (m & 3)));
+        const f16x4 x11 = *reinterpret_cast<const f16x4*>(t11 + m * XS_LD + 4 * kq);
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        y = mfma16x16(l10, x00, y);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        X10[ss] = mfma16x16(x11, h4(y[0], y[1], y[2], y[3]), z);
+      }
+      // rows of the diagonal blocks (this lane's row of block blk), the other
+      // half of the row: zeros (block 0) or the off-diagonal block (block 1,
+      // written below)
+      const int row = 32 * s + 16 * blk + jr;
+      _Float16* arow = ab + row * A_LD;
       _Float16* brow = arow + 64 * A_LD;
+      const float* bk = bt;  // beta of the block's tokens (phase A)
+      float rk[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 r0 = *reinterpret_cast<const float4*>(brp + 8 * q);
-        const float4 r1 = *reinterpret_cast<const float4*>(brp + 8 * q + 4);
-        const float* x8 = acc + 8 * q;
-        const float* b8 = bt + 8 * q;
-        uint4 wa, wb;
-        wa.x = pk_h2(x8[0] * b8[0], x8[1] * b8[1]);
-        wa.y = pk_h2(x8[2] * b8[2], x8[3] * b8[3]);
-        wa.z = pk_h2(x8[4] * b8[4], x8[5] * b8[5]);
-        wa.w = pk_h2(x8[6] * b8[6], x8[7] * b8[7]);
-        wb.x = pk_h2(x8[0] * r0.x, x8[1] * r0.y);
-        wb.y = pk_h2(x8[2] * r0.z, x8[3] * r0.w);
-        wb.z = pk_h2(x8[4] * r1.x, x8[5] * r1.y);
-        wb.w = pk_h2(x8[6] * r1.z, x8[7] * r1.w);
-        *reinterpret_cast<uint4*>(arow + 8 * q) = wa;
-        *reinterpret_cast<uint4*>(brow + 8 * q) = wb;
+        const float4 r4 = *reinterpret_cast<const float4*>(grp + 32 * s + 16 * blk + 4 * q);
+        rk[4 * q] = r4.x; rk[4 * q + 1] = r4.y; rk[4 * q + 2] = r4.z; rk[4 * q + 3] = r4.w;
+      }
+      uint4 wa[2], wb[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int k = 8 * h8;
+        wa[h8] = make_uint4(pk_h2(acc[k] * bk[k], acc[k + 1] * bk[k + 1]),
+                            pk_h2(acc[k + 2] * bk[k + 2], acc[k + 3] * bk[k + 3]),
+                            pk_h2(acc[k + 4] * bk[k + 4], acc[k + 5] * bk[k + 5]),
+                            pk_h2(acc[k + 6] * bk[k + 6], acc[k + 7] * bk[k + 7]));
+        wb[h8] = make_uint4(pk_h2(acc[k] * rk[k], acc[k + 1] * rk[k + 1]),
+                            pk_h2(acc[k + 2] * rk[k + 2], acc[k + 3] * rk[k + 3]),
+                            pk_h2(acc[k + 4] * rk[k + 4], acc[k + 5] * rk[k + 5]),
+                            pk_h2(acc[k + 6] * rk[k + 6], acc[k + 7] * rk[k + 7]));
+      }
+      // (the scratch reads above precede these stores in the wave's LDS
+      // order, so they see the scratch before it is overwritten)
+      *reinterpret_cast<uint4*>(arow + 16 * blk) = wa[0];
+      *reinterpret_cast<uint4*>(arow + 16 * blk + 8) = wa[1];
+      *reinterpret_cast<uint4*>(brow + 16 * blk) = wb[0];
+      *reinterpret_cast<uint4*>(brow + 16 * blk + 8) = wb[1];
+      if (blk == 0) {
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(arow + 16) = z4;
+        *reinterpret_cast<uint4*>(arow + 24) = z4;
+        *reinterpret_cast<uint4*>(brow + 16) = z4;
+        *reinterpret_cast<uint4*>(brow + 24) = z4;
+      }
+      // off-diagonal blocks: lane l holds X10[4 kq + e][m] of each sub-chunk
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const float bn = gbp[32 * ss + m], rn = grp[32 * ss + m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 32 * ss + 16 + 4 * kq + e;
+          ab[r * A_LD + m] = _Float16(-X10[ss][e] * bn);
+          ab[(64 + r) * A_LD + m] = _Float16(-X10[ss][e] * rn);
+        }
       }
     }
+    // G of chunk ci+1 (its K rows were staged in phase A)
+    if (ci + 1 < n) gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane);
   }
 }
 
 // ===========================================================================
-// helper waves: staging, G, gates, U^T
+// helper waves: K rows (helpers 0, 1), the second half of V and the gates
+// (helper 2), U^T
 // ===========================================================================
 __device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const int pw = wid - NT - 1;  // 0 .. NHW-1
   const float* bsrc = beta ? beta : alpha;
   const int HDk = H * dk, HDv = H * dv;  // element stride between tokens
-
-  // K rows: helper s (< 2) stages rows [32 s, 32 s + 32) of each chunk --
-  // exactly the rows its G product reads -- 8 items of 16 bytes per lane:
-  // item i = row 32 s + (lane >> 4) + 4 i, channels 8 (lane & 15) .. +7.
-  // V rows: the last helper, 16 items: row (lane >> 4) + 4 i, same channels.
-  // Tokens past the chunk's end read its last token (a valid address) and
-  // are zeroed when staged.
-  constexpr int NKI = 8, NVI = C / 4;
   const int cg = lane & 15;
   const int kch = min(8 * cg, dk - 8), vch = min(8 * cg, dv - 8);
-  // prefetch registers: K rows (helpers 0, 1) or V rows (helper 2)
-  uint4 pr[NVI > NKI ? NVI : NKI];
+  // K rows: helper s (< 2) stages rows [32 s, 32 s + 32) of each chunk
+  // (items 8 s .. 8 s + 7); helper 2 stages V rows 32..63 (items 8..15).
+  const int i0 = pw < 2 ? 8 * pw : 8;
+  uint4 pr[8];
+  // U^T tiles of each chunk: helper 0: 0-2, helper 1: 3-5, helper 2: 6-7
+  const int tile0 = 3 * pw, ntile = pw < 2 ? 3 : 2;
   // alpha, beta of lane's token for two chunks (helper NHW-1), indexed by
   // chunk parity, so that no register holding a pending load is copied
   float pa[2] = {1.f, 1.f}, pb[2] = {0.f, 0.f};
   float lam = 0.f;
   // element offset of the first token of chunk j of this (layer, head)
   auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
-  auto load_k = [&](int j) {
-    const int len = chunk_len(j);
-    const __bf16* base = kp + row0(j) * dk + kch;
-#pragma unroll
-    for (int i = 0; i < NKI; ++i) {
-      const int t = min(32 * pw + (lane >> 4) + 4 * i, len - 1);
-      pr[i] = gload_u4(base + t * HDk);
-    }
-  };
-  auto load_v = [&](int j) {
-    const int len = chunk_len(j);
-    const __bf16* base = vp + row0(j) * dv + vch;
-#pragma unroll
-    for (int i = 0; i < NVI; ++i) pr[i] = gload_u4(base + min((lane >> 4) + 4 * i, len - 1) * HDv);
-  };
   auto load_gates = [&](int j, float& ra, float& rb) {
     const int64_t gi = row0(j) + int64_t(min(lane, chunk_len(j) - 1)) * H;
     ra = gload(alpha + gi);
@@ -544,102 +667,76 @@ __device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
     constexpr int P = decltype(par)::value;
     // ---------------- phase A
     __syncthreads();
+    if (pw < 2) {
+      // K rows of chunk ci+1 (loaded a cycle ago), then load chunk ci+2's
+      if (ci + 1 < n)
+        stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, chunk_len(ci + 1), dk, i0, 8, lane);
+      if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, 8, lane);
+    } else {
+      // V rows 32..63 of chunk ci-1 (loaded a cycle ago), then chunk ci's
+      if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, chunk_len(ci - 1), dv, i0, 8, lane);
+      if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), i0, 8, lane);
+    }
     if (ci - 1 >= 0 && ci - 1 < n) {
+      // U^T of chunk j -> -U fragments.  K^T fragment: lane (g, m) needs
+      // K[token 32 s + 16 kk + 8 g + 0..7][32 t + m].  All operands are read
+      // before the products, so the reads of the tiles overlap.
       const int j = ci - 1;
-      // U^T of chunk j, tile by tile -> -U fragments.  K^T fragment: lane
-      // (g, m) needs K[token 32 s + 16 kk + 8 g + 0..7][32 t + m].
       const _Float16* kb = Kb0 + (j % NKB) * (C * RLD);
       const _Float16* Ah = AB0 + (j & 1) * AB_HALFS;
       char* uf = Uf0 + (j & 1) * UF_BYTES;
       const _Float16* kbase = kb + (8 * g + tr_row) * RLD + tr_col;
+      f16x8 kf[3][2], ah[3][2];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const int tile = pw + 2 * i;
-        if (pw < 2) {
-          const int t = tile % NT, s = tile / NT;
-          f32x16 acc = zero16();
+      for (int i = 0; i < 3; ++i)
+        if (i < ntile) {
+          const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
             const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 32 * t;
-            const f16x8 kf = tr_h8(p0, p0 + 4 * RLD);
-            const f16x8 ah = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
-            acc = mfma16(kf, ah, acc);
+            kf[i][kk] = tr_h8(p0, p0 + 4 * RLD);
+            ah[i][kk] = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
           }
+        }
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (i < ntile) {
+          const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
+          f32x16 acc = zero16();
+          acc = mfma16(kf[i][0], ah[i][0], acc);
+          acc = mfma16(kf[i][1], ah[i][1], acc);
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
             *reinterpret_cast<f16x8*>(uf + uf_off(s, t, hh, lane)) = acc_h8<-1>(acc, hh);
         }
-      }
-      if (pw == NHW - 1) {
-        // V rows of chunk j (loaded a cycle ago)
-        const int len = chunk_len(j);
-        const bool okc = 8 * cg < dv;
-#pragma unroll
-        for (int i = 0; i < NVI; ++i) {
-          const int t = (lane >> 4) + 4 * i;
-          *reinterpret_cast<uint4*>(Vb + t * RLD + 8 * cg) = pick_u4(okc && t < len, bf2h(pr[i]));
-        }
-      }
     }
-    if (pw == NHW - 1 && ci >= 0 && ci < n) load_v(ci);
 
     // ---------------- phase B
     __syncthreads();
-    if (ci + 1 < n) {
+    if (pw == NHW - 1 && ci + 1 < n) {
+      // gates of chunk jn: log2 prefix per sub-chunk (one per half wave)
       const int jn = ci + 1;
       const int len = chunk_len(jn);
-      if (pw < 2) {
-        // K rows [32 s, 32 s + 32) of chunk jn (loaded a cycle ago), then
-        // G_ss = K_s K_s^T from those rows; L = diag(beta) strictly-lower(G)
-        const int s = pw;
-        _Float16* kb = Kb0 + (jn % NKB) * (C * RLD);
-        const bool okc = 8 * cg < dk;
-#pragma unroll
-        for (int i = 0; i < NKI; ++i) {
-          const int t = 32 * s + (lane >> 4) + 4 * i;
-          *reinterpret_cast<uint4*>(kb + t * RLD + 8 * cg) = pick_u4(okc && t < len, bf2h(pr[i]));
-        }
-        if (jn + 1 < n) load_k(jn + 1);
-        f32x16 acc0 = zero16(), acc1 = zero16();
-#pragma unroll
-        for (int ks = 0; ks < DP / 16; ++ks) {
-          const f16x8 ak = lds_h8(kb + (32 * s + cl) * RLD + 16 * ks + 8 * g);
-          if (ks & 1)
-            acc1 = mfma16(ak, ak, acc1);
-          else
-            acc0 = mfma16(ak, ak, acc0);
-        }
-        // G is symmetric: the lane's accumulator column cl is also row cl,
-        // with entries 8 k + 4 g + {0..3} in registers 4k .. 4k+3
-        float* nm = Nm0 + (jn & 1) * NM_FLOATS + s * 1024 + cl * 32 + 4 * g;
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-          *reinterpret_cast<float4*>(nm + 8 * k4) =
-              make_float4(acc0[4 * k4] + acc1[4 * k4], acc0[4 * k4 + 1] + acc1[4 * k4 + 1],
-                          acc0[4 * k4 + 2] + acc1[4 * k4 + 2], acc0[4 * k4 + 3] + acc1[4 * k4 + 3]);
-      } else {
-        // gates of chunk jn: log2 prefix per sub-chunk (one per half wave)
-        const float x2 = half_wave_scan(lane < len ? log2f(pa[P]) : 0.f);
-        const int xi = __builtin_bit_cast(int, x2);
-        const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 31));
-        const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 63));
-        const float bend = g ? e1 : e0;
-        const float bt = lane < len ? (beta ? pb[P] : 1.f) : 0.f;  // masked beta
-        gb0[(jn & 1) * C + lane] = bt;
-        gbr0[(jn & 1) * C + lane] = bt * exp2f(bend - x2);
-        if (lane == 0) {
-          gg[(jn & 3) * 2] = exp2f(e0);
-          gg[(jn & 3) * 2 + 1] = exp2f(e1);
-        }
-        lam += e0 + e1;
-        // the slot of chunk jn now takes chunk jn + 2
-        if (jn + 2 < n) load_gates(jn + 2, pa[P], pb[P]);
+      const float x2 = half_wave_scan(lane < len ? log2f(pa[P]) : 0.f);
+      const int xi = __builtin_bit_cast(int, x2);
+      const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 31));
+      const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 63));
+      const float bend = g ? e1 : e0;
+      const float bt = lane < len ? (beta ? pb[P] : 1.f) : 0.f;  // masked beta
+      gb0[(jn & 1) * C + lane] = bt;
+      gbr0[(jn & 1) * C + lane] = bt * exp2f(bend - x2);
+      if (lane == 0) {
+        gg[(jn & 3) * 2] = exp2f(e0);
+        gg[(jn & 3) * 2 + 1] = exp2f(e1);
       }
+      lam += e0 + e1;
+      // the slot of chunk jn now takes chunk jn + 2
+      if (jn + 2 < n) load_gates(jn + 2, pa[P], pb[P]);
     }
   };
 
   if (n > 0) {
-    if (pw < 2) load_k(0);
+    if (pw < 2) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, 8, lane);
     if (pw == NHW - 1) load_gates(0, pa[0], pb[0]);
   }
   if (n > 1 && pw == NHW - 1) load_gates(1, pa[1], pb[1]);
