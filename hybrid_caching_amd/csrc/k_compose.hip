@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // One workgroup per chain unit (request, layer, head).  Wave w owns columns
 // [32w, 32w+32) of the running state S (dk x dv) in MFMA accumulators, as
 // DKP/32 row tiles.  Each chain step stages That_p in LDS as hi/lo bf16 rows
-// (padded stride to spread LDS banks) and forms That_p * S with split-bf16
+// (padded stride to spread LDS banks; columns stored in the permuted K order
+// of the products) and forms That_p * S with split-bf16
 // MFMAs (3 per 32x32x16 block), taking the B operand straight from the
 // accumulators of the old S (K order permuted to match, see mfma_util.hpp).
 // Then S <- e^lambda * (That S) + S0_p.  The next step's operator is loaded
@@ -88,23 +89,29 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // PROD = true forms the chain's operator instead: the "state" is dk x dk,
 // starts at I, and each step is X <- That_p X (no scale, no additive term);
 // the launcher passes dv = dk and S_out = the That output.
-template <int DKP, bool PROD>
+// FULL = true when dk = dv = DKP: no padding, so every operator and S0
+// access is an unconditional load at a loop-invariant offset from the step's
+// (uniform) base address.
+template <int DKP, bool PROD, bool FULL>
 __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   constexpr int NT = DKP / 32;
-  constexpr int LDR = DKP + 4;        // row stride of the staged operator, in bf16
+  // row stride of the staged operator (bf16): 16-byte aligned rows whose
+  // 16-byte reads from 32 consecutive rows spread evenly over the banks
+  constexpr int LDR = DKP + 8;
   constexpr int F4 = DKP * DKP / 4;   // float4 items of one operator
   __shared__ __attribute__((aligned(16))) __bf16 th_hi[DKP * LDR];
   __shared__ __attribute__((aligned(16))) __bf16 th_lo[DKP * LDR];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, cl = lane & 31;
-  const int nthr = blockDim.x;
+  // with FULL the block is 64 * DKP / 32 threads (one wave per 32 columns)
+  const int nthr = FULL ? 64 * NT : int(blockDim.x);
   const int dk = a.dk, dv = a.dv;
   const int64_t BH = int64_t(a.batch) * a.heads;
   const int64_t unit = blockIdx.x;
   const int64_t r = unit / BH, bh = unit % BH;
   const int n = wave * 32 + cl;  // state column of this lane
-  const bool ncol = n < dv;
+  const bool ncol = FULL || n < dv;
   const int64_t sdd = int64_t(dk) * dv;
   const int per_thr = (F4 + nthr - 1) / nthr;  // <= 16 (DKP = 128, 256 threads)
 
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
       if (PROD)
         S[t][q] = (row == n && row < dk) ? 1.f : 0.f;
       else
-        S[t][q] = (a.S_in && ncol && row < dk) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
+        S[t][q] = (a.S_in && ncol && (FULL || row < dk)) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
     }
   }
 
@@ -125,6 +132,13 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   float4 pre[16];
   auto load_op = [&](int64_t pu) {
     const float* Tp = a.pool_T_hat + pu * int64_t(dk) * dk;
+    if (FULL) {
+      // item e is float4 e of the row-major operator
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        if (it < per_thr) pre[it] = reinterpret_cast<const float4*>(Tp)[threadIdx.x + it * nthr];
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int e = threadIdx.x + it * nthr;
@@ -144,13 +158,16 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int e = threadIdx.x + it * nthr;
-      if (it < per_thr && e < F4) {
+      if (it < per_thr && (FULL || e < F4)) {
         const int row = (e * 4) / DKP, col = (e * 4) % DKP;
         unsigned h0, l0, h1, l1;
         split2(pre[it].x, pre[it].y, h0, l0);
         split2(pre[it].z, pre[it].w, h1, l1);
-        *reinterpret_cast<uint2*>(th_hi + row * LDR + col) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(th_lo + row * LDR + col) = make_uint2(l0, l1);
+        // column positions permuted within each 16 (bits 2 and 3 swapped), so
+        // that the 8 columns of a permuted K-step are contiguous
+        const int pcol = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+        *reinterpret_cast<uint2*>(th_hi + row * LDR + pcol) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(th_lo + row * LDR + pcol) = make_uint2(l0, l1);
       }
     }
     if (c + 1 < c1) load_op(int64_t(a.d_chain_idx[c + 1]) * BH + bh);
@@ -164,7 +181,10 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = t * 32 + acc_row(q, g);
-          s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+          if (FULL)
+            s0[t][q] = S0p[row * DKP + n];
+          else
+            s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
       scale = expf(a.pool_log_scale[pu]);
     }
@@ -178,12 +198,13 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
       const int t = ks >> 1, h = ks & 1;
       bf16x8 bhi, blo;
       split_acc_half(S[t], h, bhi, blo);
-      const int kc = 32 * t + 16 * h + 4 * g;
+      // K indices kperm(h, g, 0..7) sit at positions 16h + 8g .. +7
+      const int kc = 32 * t + 16 * h + 8 * g;
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
         const int arow = mt * 32 + cl;
-        const bf16x8 ahi = lds_perm8(th_hi + arow * LDR, kc);
-        const bf16x8 alo = lds_perm8(th_lo + arow * LDR, kc);
+        const bf16x8 ahi = lds_load8(th_hi + arow * LDR + kc);
+        const bf16x8 alo = lds_load8(th_lo + arow * LDR + kc);
         acc[mt] = mfma32(alo, bhi, acc[mt]);
         acc[mt] = mfma32(ahi, blo, acc[mt]);
         acc[mt] = mfma32(ahi, bhi, acc[mt]);
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) a.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
+        if (FULL || row < dk) a.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
       }
     }
   }
@@ -267,6 +288,14 @@ hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStrea
   return hipGetLastError();
 }
 
+template <int DKP, bool PROD>
+void launch_dense_t(const ComposeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.dk == DKP && a.dv == DKP)
+    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, false>), grid, block, 0, s, a);
+}
+
 template <bool PROD>
 hipError_t launch_dense_chain(const ComposeArgs& a, hipStream_t s) {
   const int64_t units = int64_t(a.n_req) * a.batch * a.heads;
@@ -277,10 +306,10 @@ hipError_t launch_dense_chain(const ComposeArgs& a, hipStream_t s) {
   const dim3 block{unsigned(64 * waves), 1, 1};
   const int dkp = (a.dk + 31) / 32 * 32;
   switch (dkp) {
-    case 32: hipLaunchKernelGGL((compose_dense_kernel<32, PROD>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((compose_dense_kernel<64, PROD>), grid, block, 0, s, a); break;
-    case 96: hipLaunchKernelGGL((compose_dense_kernel<96, PROD>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((compose_dense_kernel<128, PROD>), grid, block, 0, s, a); break;
+    case 32: launch_dense_t<32, PROD>(a, grid, block, s); break;
+    case 64: launch_dense_t<64, PROD>(a, grid, block, s); break;
+    case 96: launch_dense_t<96, PROD>(a, grid, block, s); break;
+    case 128: launch_dense_t<128, PROD>(a, grid, block, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
