@@ -40,8 +40,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "build_dense_ws_kernel": ["k_build_dense_ws.hip", "mfma_util.hpp", "pic_internal.hpp",
                               "stage_util.hpp"],
-    "build_dense_h16_kernel": ["k_build_dense_h16.hip", "mfma_util.hpp", "pic_internal.hpp",
-                               "stage_util.hpp"],
+    "build_dense_h16_kernel": ["k_build_dense_h16.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_sd_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
@@ -180,15 +179,25 @@ def bench_scalar_diag(w, args):
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    # Each kernel here runs for well under a millisecond, so a step enqueues
+    # `reps` passes of each operation back to back and the events bracket each
+    # group: the per-launch time is the group's time / reps, with the queue kept
+    # full (a single launch between two events would also time the host's
+    # enqueue latency).
+    reps = args.reps
+
     def step(rec=None):
         e = [ev() for _ in range(4)]
         e[0].record(stream)
-        pic.pic_segment_build(w.form, k, v, alpha, None, offsets, out=pairs)
+        for _ in range(reps):
+            pic.pic_segment_build(w.form, k, v, alpha, None, offsets, out=pairs)
         e[1].record(stream)
-        pic.pic_compose(w.form, pairs["log_scale"], None, pairs["S0"], chain_off, chain_idx,
-                        None, out=S_out)
+        for _ in range(reps):
+            pic.pic_compose(w.form, pairs["log_scale"], None, pairs["S0"], chain_off, chain_idx,
+                            None, out=S_out)
         e[2].record(stream)
-        pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
+        for _ in range(reps):
+            pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
         e[3].record(stream)
         if rec is not None:
             rec.append(e)
@@ -201,8 +210,8 @@ def bench_scalar_diag(w, args):
     for _ in range(args.steps):
         step(recs)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
-    ms = [np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]) for i in range(3)]
+    wall = (time.perf_counter() - t0) / (args.steps * reps)
+    ms = [np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]) / reps for i in range(3)]
     gate_bytes = 4 * (dk if w.form == synth.DIAG else 1)
     lam_out = 4 * (dk if w.form == synth.DIAG else 1)
     qb = 2 if w.qkv_bf16 else 4
@@ -218,7 +227,8 @@ def bench_scalar_diag(w, args):
            "data": "synthetic",
            "config": {"workload": w.name, "form": synth.FORM_NAMES[w.form], "layers": B,
                       "heads": H, "dk": dk, "dv": dv, "segments": n_seg,
-                      "segment_tokens": int(w.seg_lens[0]), "prompt_tokens": N},
+                      "segment_tokens": int(w.seg_lens[0]), "prompt_tokens": N,
+                      "passes_per_step": reps},
            "ms": {"build": ms[0], "compose": ms[1], "naive_add": ms[2]},
            "roofline": {"kernel": "build_sd_pipe_kernel", "bound": "hbm",
                         "achieved": gbs(bb, ms[0]), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -312,6 +322,8 @@ def bench_reuse(w, args):
     fresh_tokens = sum(n for _, _, n in fresh_rec)
 
     S_out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration)
 
     def compose():
         pic.pic_compose(synth.DENSE, pool["log_scale"], pool["T_hat"], pool["S0"], off, idx,
@@ -362,9 +374,15 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense_30L_32x4096")
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
-    ap.add_argument("--precision", choices=["fp32", "fp16"], default="fp32",
-                    help="operand precision of the dense build's matrix-core products: fp32 "
-                         "(split bf16) or fp16 (single fp16 operands); state is fp32 in both")
+    ap.add_argument("--precision", choices=["fp32", "fp16"], default="fp16",
+                    help="operand precision of the dense build's matrix-core products: fp16 "
+                         "(single fp16 operands, the default; relative error ~2e-3 against the "
+                         "fp64 oracle) or fp32 (split bf16, ~2e-5); state and accumulation are "
+                         "fp32 in both")
+    ap.add_argument("--no-fp32-build", action="store_true",
+                    help="skip the secondary timing of the dense build at fp32 operand precision")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="scalar/diagonal workloads: passes of each operation per timed step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -458,6 +476,24 @@ def main(argv=None):
 
     flops = dense_build_flops_per_token_head(dk) * N * B * H
     achieved_tf = flops / t_build / 1e12
+    # the same build at the other operand precision, for reference (not in `value`)
+    other = None
+    if not args.no_fp32_build and args.prec == 1:
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs, precision=0)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(3):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs, precision=0)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t_other = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs])) / 1e3
+        other = {"precision": "fp32 (split bf16)", "kernel": "build_dense_ws_kernel",
+                 "ms": t_other * 1e3, "build_tokens_per_s": N / t_other,
+                 "achieved_tflops": flops / t_other / 1e12,
+                 "frac_of_bf16_peak": flops / t_other / 1e12 / PEAK_BF16_TFLOPS}
     composes = n_seg * B  # pairs applied to a running state, per layer (all heads)
     build_kernel = "build_dense_h16_kernel" if args.prec else "build_dense_ws_kernel"
     cb = compose_bytes(n_seg, B, H, dk, dv)
@@ -499,6 +535,8 @@ def main(argv=None):
                                "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
         "build_hbm_gbs": build_bytes(N, B, H, dk, dv, n_seg) / t_build / 1e9,
     }
+    if other is not None:
+        out["build_other_precision"] = other
     if not args.no_cpu_baseline:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))
