@@ -38,6 +38,12 @@ namespace pic {
 namespace {
 
 constexpr int kCs = 64;  // tokens per chunk
+#ifndef SD_DEPTH_SCALAR
+#define SD_DEPTH_SCALAR 2
+#endif
+#ifndef SD_DEPTH_DIAG
+#define SD_DEPTH_DIAG 2
+#endif
 
 __device__ __forceinline__ int opaque_i(int v) {
   asm volatile("" : "+v"(v));
@@ -106,37 +112,45 @@ __device__ __forceinline__ int64_t row0(const BuildArgs& a, const Unit& u, int d
   return ((int64_t(u.b) * a.n_tokens + a.d_offsets[u.seg]) * a.heads + u.h) * d;
 }
 
-// Runs the two-chunk-deep pipeline: load(set, chunk) issues the loads of a
-// chunk into register set `set` (a std::integral_constant), stage(set, chunk,
-// buffer) stages it, frags(chunk, buffer) reads a chunk's operand fragments
-// into a value that contract(value, chunk) consumes.
-template <class LoadF, class StageF, class FragF, class ContractF>
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Runs the pipeline with DEPTH register sets: load(set, chunk) issues the
+// loads of a chunk into register set `set` (a std::integral_constant; chunk
+// j lives in set j % DEPTH), stage(set, chunk, buffer) stages it,
+// frags(chunk, buffer) reads a chunk's operand fragments into a value that
+// contract(value, chunk) consumes.  Step j: frags of chunk j (buffer j & 1),
+// stage chunk j+1 (buffer (j+1) & 1), load chunk j+1+DEPTH into the set just
+// staged, contract chunk j, barrier.
+template <int DEPTH, class LoadF, class StageF, class FragF, class ContractF>
 __device__ __forceinline__ void run_pipeline(int n_chunks, LoadF&& load, StageF&& stage,
                                              FragF&& frags, ContractF&& contract) {
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   if (n_chunks <= 0) return;
   const int last = n_chunks - 1;
-  load(S0(), 0);
-  load(S1(), min(1, last));
-  stage(S0(), 0, 0);
-  load(S0(), min(2, last));
+  static_for<0, DEPTH>([&](auto S) { load(S, min(decltype(S)::value, last)); });
+  stage(std::integral_constant<int, 0>(), 0, 0);
+  load(std::integral_constant<int, 0>(), min(DEPTH, last));
   __syncthreads();
   auto step = [&](auto D, int cj) __attribute__((always_inline)) {
-    using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
+    using DN = std::integral_constant<int, (decltype(D)::value + 1) % DEPTH>;
     auto fr = frags(cj, cj & 1);
     if (cj + 1 < n_chunks) stage(DN(), cj + 1, (cj + 1) & 1);
-    load(DN(), min(cj + 3, last));
+    load(DN(), min(cj + 1 + DEPTH, last));
     contract(fr, cj);
     __syncthreads();
   };
   int cj = 0;
 #pragma unroll 1
-  for (; cj + 1 < n_chunks; cj += 2) {
-    step(S0(), cj);
-    step(S1(), cj + 1);
-  }
-  if (cj < n_chunks) step(S0(), cj);
+  for (; cj + DEPTH <= n_chunks; cj += DEPTH)
+    static_for<0, DEPTH>([&](auto D) { step(D, cj + decltype(D)::value); });
+  static_for<0, DEPTH - 1>([&](auto D) {
+    if (cj + decltype(D)::value < n_chunks) step(D, cj + decltype(D)::value);
+  });
 }
 
 // write this wave's tiles of S (rows mt*32.., columns (nt0+k)*32..)
@@ -159,162 +173,302 @@ __device__ __forceinline__ void write_tiles(const f32x16 (&S)[TPW], float* out, 
 
 // ============================================================ scalar decay
 //
-// Thread mapping: lanes along channels, DP/8 lanes per token row, each thread
-// tokens t0 = 2 * (tid / (DP/8)) and t0+1, channels i0 .. i0+7.  The weights
-// of the chunk's 64 tokens come from one 64-lane scan that every wave does
-// for itself (lane = token), and reach the threads by ds_bpermute.  Kw (hi,
-// lo) and V are staged token-major (16-byte pieces of rows); the contraction
-// reads its transposed operand fragments with ds_read_b64_tr_b16.
+// Producer and consumer waves.  DP/32 consumer waves each hold one row of
+// 32x32 tiles of S (all DP/32 column tiles) in MFMA registers for the whole
+// segment; they read operand fragments and issue MFMAs.  Consumer wave 0
+// also turns the gates into the chunk's token weights, two chunks ahead
+// (a 64-lane scan, lane = token; it has the time, the MFMA waves wait on
+// the staging), and leaves them in a small LDS table.  As many producer
+// waves load and stage: producer thread (R, i0) takes the four consecutive
+// tokens 4R .. 4R+3 of the chunk, channels i0 .. i0+7; load instruction p
+// reads token 4R+p of every R, i.e. whole token rows.  A producer reads its
+// four weights with one broadcast LDS load, stages Kw (hi, lo) and V
+// token-major, and issues the loads of a later chunk into each token's
+// registers as soon as that token is staged.  The consumers read their
+// transposed operand fragments with ds_read_b64_tr_b16.
+//
+// Step j (one barrier): consumers contract chunk j (buffer j & 1, table
+// j % 3); consumer wave 0 writes the weights of chunk j+2 (table (j+2) % 3);
+// producers stage chunk j+1 (buffer (j+1) & 1, weights from table
+// (j+1) % 3) and load chunk j+3.
+#ifndef SD_SCALAR_T
+#define SD_SCALAR_T 0
+#endif
+// element offset of tokens t .. of channel row `row` (t a multiple of 4); the
+// 16-byte chunks of a row are XOR-swizzled by the row's 8-row group
+template <int KT>
+__device__ __forceinline__ int ch_at(int row, int t) {
+  return row * KT + 8 * ((t >> 3) ^ ((row >> 3) & 7)) + (t & 7);
+}
 template <int DP>
 struct ScalarLds {
-  static constexpr int RLD = DP + 16;              // row stride (bf16): the 16 addresses of a
-                                                   // transposed read's lane group hit distinct banks
-  static constexpr int KH = 0;                     // Kw hi [C][RLD]
-  static constexpr int KL = KH + kCs * RLD * 2;    // Kw lo
-  static constexpr int VR = KL + kCs * RLD * 2;    // V
-  static constexpr int TOTAL = VR + kCs * RLD * 2;
-};
-
-struct ScalarRegs {
-  uint4 k0, k1, v0, v1;
-  float a;  // gate of token `lane` of the chunk
+  static constexpr bool T = SD_SCALAR_T;     // channel rows (else token rows)
+  static constexpr int KT = kCs + 8;         // channel rows: bf16 stride
+  static constexpr int RLD = DP + 16;        // token rows: bf16 stride; the 16 addresses of a
+                                             // transposed read's lane group hit distinct banks
+  static constexpr int TILE = T ? DP * KT * 2 : kCs * RLD * 2;
+  static constexpr int KH = 0;               // Kw hi [C][RLD]
+  static constexpr int KL = KH + TILE;       // Kw lo
+  static constexpr int VR = KL + TILE;       // V
+  static constexpr int TOTAL = VR + TILE;    // one of two buffers
+  static constexpr int WT = 2 * TOTAL;       // weight tables [3][C + 4]
+  static constexpr int ALL = WT + 3 * (kCs + 4) * 4;
 };
 
 template <int DP>
 __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) {
   using L = ScalarLds<DP>;
-  constexpr int C = kCs, NTH = 4 * DP, NW = NTH / 64, RLD = L::RLD;
-  constexpr int NTC = DP / 32, TILES = NTC * NTC, TPW = (TILES + NW - 1) / NW;
-  constexpr int GPR = DP / 8;  // threads per token row
-  static_assert((C / 2) * GPR == NTH, "two tokens x 8 channels per thread");
-  static_assert(NTC % TPW == 0, "the tiles of a wave share one row of tiles");
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::TOTAL];
+  constexpr int C = kCs, RLD = L::RLD;
+  constexpr int NC = DP / 32;     // consumer waves = rows of tiles
+  constexpr int GPR = DP / 8;     // producer threads per token row
+  static_assert(NC * 64 / GPR * 4 == C, "the producers cover the chunk");
+  static_assert(2 * NC * 64 == 4 * DP, "block size");
+  __shared__ __attribute__((aligned(16))) char smem[L::ALL];
+  float* wtab = reinterpret_cast<float*>(smem + L::WT);
 
   const Unit u = unit_of(a);
   const int H = a.heads, dk = a.dk, dv = a.dv;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int n = u.n_chunks, last = n - 1;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  if (wave < NC) {
+    // ---------------- consumers
+    const int mt = wave, lane = threadIdx.x & 63;
+    const bool scan_wave = wave == 0;
+    const float* abase = a.alpha + row0(a, u, 1);
+    float areg[2] = {1.f, 1.f}, lam = 0.f;
+    // gate of token `lane` of chunk ci (clamped inside the segment)
+    auto load_gate = [&](auto SET, int ci) __attribute__((always_inline)) {
+      const int len = chunk_len(u, ci);
+      const char* ac = reinterpret_cast<const char*>(abase + int64_t(ci) * C * H);
+      areg[decltype(SET)::value] =
+          *reinterpret_cast<const float*>(ac + unsigned(min(lane, len - 1)) * unsigned(H) * 4u);
+    };
+    // weights of chunk ci into table ci & 1: w_t = product of the gates after
+    // t in the chunk (0 past its end), then the chunk's decay
+    // Lazy decay: the consumers hold S' = S / 2^G, G the log2 decay since a
+    // reference point, so a chunk needs no rescaling of S: its token weights
+    // become 2^(-G_prev - prefix_t) (prefix_t: log2 gates of the chunk through
+    // token t).  When G_prev + (the chunk's decay) would drop below -kLazy,
+    // the reference moves to the chunk's end: S' is scaled once by
+    // 2^(G_prev + decay) before the chunk and the weights are the plain
+    // 2^(decay - prefix_t) <= 1.  Weights stay below 2^kLazy.
+    constexpr float kLazy = 32.f;
+    float Gref = 0.f;
+    // weights of chunk ci (gates from register set SET) into table `tab`:
+    // [0, C) token weights (0 past the chunk's end), [C] the factor to scale
+    // S' by before the chunk, [C+1] G after the chunk.  Chunks past the last
+    // (ci >= n) are computed but leave G and lambda unchanged.
+    auto weights = [&](auto SET, int ci, int tab) __attribute__((always_inline)) {
+      const bool real = ci < n;
+      ci = min(ci, last);
+      const int len = chunk_len(u, ci);
+      const bool ok = lane < len;
+      const float incl = wave_inclusive_scan(ok ? log2_gate(areg[decltype(SET)::value]) : 0.f);
+      const float tot =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+      const bool move = Gref + tot < -kLazy;
+      const float e0 = move ? tot : -Gref;  // weight exponent = e0 - prefix_t
+      float* wt = wtab + tab * (C + 4);
+      wt[lane] = ok ? exp2_w(e0 - incl) : 0.f;
+      const float Gnew = move ? 0.f : Gref + tot;
+      if (lane == 0) {
+        wt[C] = move ? exp2_w(Gref + tot) : 1.f;
+        wt[C + 1] = Gnew;
+      }
+      if (real) {
+        Gref = Gnew;
+        lam += tot;
+      }
+    };
+
+    f32x16 S[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) S[k] = zero16();
+    float Gs = 0.f;  // S = 2^Gs S' after the chunks contracted so far
+    if (n > 0) {
+      if (scan_wave) {
+        load_gate(I0(), 0);
+        load_gate(I1(), min(1, last));
+        weights(I0(), 0, 0);
+        load_gate(I0(), min(2, last));
+        weights(I1(), 1, 1);
+        load_gate(I1(), min(3, last));
+      }
+      __syncthreads();  // weights of chunks 0 and 1
+      __syncthreads();  // chunk 0 staged
+      auto step = [&](auto D, int cj) __attribute__((always_inline)) {
+        const char* sb = smem + (cj & 1) * L::TOTAL;
+        const __bf16* Kh = reinterpret_cast<const __bf16*>(sb + L::KH);
+        const __bf16* Kl = reinterpret_cast<const __bf16*>(sb + L::KL);
+        const __bf16* Vr = reinterpret_cast<const __bf16*>(sb + L::VR);
+        const float pre = wtab[(cj % 3) * (C + 4) + C];
+        Gs = wtab[(cj % 3) * (C + 4) + C + 1];
+        // lane 4j + q of a 16-lane group addresses token row r0 + j, columns c0 + 4q
+        const int l = opaque_i(threadIdx.x) & 63;
+        const int rsub = (l & 15) >> 2, csub = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+        bf16x8 ah[C / 16], al[C / 16], vb[NC][C / 16];
+        if (L::T) {
+          const int cl = l & 31, t8 = 8 * (l >> 5);
+#pragma unroll
+          for (int ks = 0; ks < C / 16; ++ks) {
+            const int ka = ch_at<L::KT>(mt * 32 + cl, 16 * ks + t8);
+            ah[ks] = lds_load8(Kh + ka);
+            al[ks] = lds_load8(Kl + ka);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) vb[k][ks] = lds_load8(Vr + ch_at<L::KT>(k * 32 + cl, 16 * ks + t8));
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < C / 16; ++ks) {
+            const int r0 = 16 * ks + 8 * (l >> 5) + rsub;
+            const int ca = r0 * RLD + mt * 32 + csub;
+            ah[ks] = tr_bf8(Kh + ca, Kh + ca + 4 * RLD);
+            al[ks] = tr_bf8(Kl + ca, Kl + ca + 4 * RLD);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+              const int cv = r0 * RLD + k * 32 + csub;
+              vb[k][ks] = tr_bf8(Vr + cv, Vr + cv + 4 * RLD);
+            }
+          }
+        }
+        if (__builtin_amdgcn_readfirstlane(__float_as_int(pre)) != __float_as_int(1.f)) {
+#pragma unroll
+          for (int k = 0; k < NC; ++k) S[k] *= pre;
+        }
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+#pragma unroll
+          for (int k = 0; k < NC; ++k) {
+            S[k] = mfma32(al[ks], vb[k][ks], S[k]);
+            S[k] = mfma32(ah[ks], vb[k][ks], S[k]);
+          }
+        if (scan_wave) {
+          weights(D, cj + 2, (cj + 2) % 3);
+          load_gate(D, min(cj + 4, last));
+        }
+        __syncthreads();
+      };
+      int cj = 0;
+#pragma unroll 1
+      for (; cj + 2 <= n; cj += 2) {
+        step(I0(), cj);
+        step(I1(), cj + 1);
+      }
+      if (cj < n) step(I0(), cj);
+    }
+    const float fin = exp2_w(Gs);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) S[k] *= fin;
+    write_tiles<NC>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, 0, dk, dv);
+    if (threadIdx.x == 0) a.log_scale[u.unit] = lam * kLn2;
+    return;
+  }
+
+  // ---------------- producers
+  const int ptid = int(threadIdx.x) - NC * 64;
+  const int R = ptid / GPR, i0 = 8 * (ptid % GPR);
   const int sk = H * dk, sv = H * dv;
+  const unsigned ik = unsigned(min(i0, dk - 8)), iv = unsigned(min(i0, dv - 8));
   const __bf16* kbase = static_cast<const __bf16*>(a.k) + row0(a, u, dk);
   const __bf16* vbase = static_cast<const __bf16*>(a.v) + row0(a, u, dv);
-  const float* abase = a.alpha + row0(a, u, 1);
-
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const bool has_tiles = wave * TPW < TILES;
-  const int mt = (wave * TPW) / NTC, nt0 = (wave * TPW) % NTC;
-
-  f32x16 S[TPW];
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) S[k] = zero16();
-  float lam = 0.f, gnext = 1.f;
-  ScalarRegs regs[2];
+  struct Set {
+    uint4 k[4], v[4];  // tokens 4R+p of a chunk
+  };
+  Set regs[2];
 
   // Tokens past the end of the segment read its last token (a valid
-  // address) and get weight 0; channels past dk / dv read the last channels
-  // and only feed rows / columns of S that are not written.
-  auto load = [&](auto SET, int ci) __attribute__((always_inline)) {
-    ScalarRegs& st = regs[decltype(SET)::value];
-    const int tid = opaque_i(threadIdx.x), lane = tid & 63;
-    const int t0 = 2 * (tid / GPR), i0 = 8 * (tid % GPR);
+  // address; their weight is 0); channels past dk / dv read the last
+  // channels and only feed rows / columns of S that are not written.
+  auto load_tok = [&](auto SET, int ci, auto P) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
     const int len = chunk_len(u, ci);
-    const unsigned ta = unsigned(min(t0, len - 1)), tb = unsigned(min(t0 + 1, len - 1));
-    const unsigned ik = unsigned(min(i0, dk - 8)), iv = unsigned(min(i0, dv - 8));
+    const unsigned t = unsigned(min(4 * R + p, len - 1));
     const int64_t off = int64_t(ci) * C;
     const char* kc = reinterpret_cast<const char*>(kbase + off * sk);
     const char* vc = reinterpret_cast<const char*>(vbase + off * sv);
-    const char* ac = reinterpret_cast<const char*>(abase + off * H);
-    st.k0 = *reinterpret_cast<const uint4*>(kc + (ta * unsigned(sk) + ik) * 2u);
-    st.k1 = *reinterpret_cast<const uint4*>(kc + (tb * unsigned(sk) + ik) * 2u);
-    st.v0 = *reinterpret_cast<const uint4*>(vc + (ta * unsigned(sv) + iv) * 2u);
-    st.v1 = *reinterpret_cast<const uint4*>(vc + (tb * unsigned(sv) + iv) * 2u);
-    st.a = *reinterpret_cast<const float*>(ac + unsigned(min(lane, len - 1)) * unsigned(H) * 4u);
+    Set& rs = regs[decltype(SET)::value];
+    rs.k[p] = *reinterpret_cast<const uint4*>(kc + (t * unsigned(sk) + ik) * 2u);
+    rs.v[p] = *reinterpret_cast<const uint4*>(vc + (t * unsigned(sv) + iv) * 2u);
   };
-
-  auto stage_t = [&](auto TAIL, const ScalarRegs& st, int ci, char* sb) __attribute__((always_inline)) {
-    constexpr bool tail = decltype(TAIL)::value;
+  // stage chunk cs from register set SET into buffer cs & 1, reloading each
+  // token's registers with chunk cl as soon as the token is staged
+  auto stage = [&](auto SET, int cs, int cl) __attribute__((always_inline)) {
+    constexpr int st = decltype(SET)::value;
+    char* sb = smem + (cs & 1) * L::TOTAL;
     __bf16* Kh = reinterpret_cast<__bf16*>(sb + L::KH);
     __bf16* Kl = reinterpret_cast<__bf16*>(sb + L::KL);
     __bf16* Vr = reinterpret_cast<__bf16*>(sb + L::VR);
-    const int tid = opaque_i(threadIdx.x), lane = tid & 63;
-    const int t0 = 2 * (tid / GPR), i0 = 8 * (tid % GPR);
-    const int len = chunk_len(u, ci);
-    const bool ok = !tail || lane < len;
-    const float incl = wave_inclusive_scan(ok ? log2_gate(st.a) : 0.f);
-    const float tot =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
-    const float wt = ok ? exp2_w(tot - incl) : 0.f;  // product of the later gates of the chunk
-    const float w0 = __shfl(wt, t0, 64), w1 = __shfl(wt, t0 + 1, 64);
-    lam += tot;
-    gnext = exp2_w(tot);
-    float x0[8], x1[8];
+    const float4 w4 = *reinterpret_cast<const float4*>(wtab + (cs % 3) * (C + 4) + 4 * R);
+    if (L::T) {
+      const Set& rs = regs[st];
+      const float w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x0[j] = w0 * bf_at(st.k0, j);
-      x1[j] = w1 * bf_at(st.k1, j);
-    }
-    bf16x8 h0, l0, h1, l1;
-    split8(x0, h0, l0);
-    split8(x1, h1, l1);
-    *reinterpret_cast<bf16x8*>(Kh + t0 * RLD + i0) = h0;
-    *reinterpret_cast<bf16x8*>(Kl + t0 * RLD + i0) = l0;
-    *reinterpret_cast<bf16x8*>(Kh + (t0 + 1) * RLD + i0) = h1;
-    *reinterpret_cast<bf16x8*>(Kl + (t0 + 1) * RLD + i0) = l1;
-    *reinterpret_cast<uint4*>(Vr + t0 * RLD + i0) = st.v0;
-    *reinterpret_cast<uint4*>(Vr + (t0 + 1) * RLD + i0) = st.v1;
-  };
-  auto stage = [&](auto SET, int ci, int buf) __attribute__((always_inline)) {
-    char* sb = smem + buf * L::TOTAL;
-    if (chunk_len(u, ci) == C)
-      stage_t(std::false_type(), regs[decltype(SET)::value], ci, sb);
-    else
-      stage_t(std::true_type(), regs[decltype(SET)::value], ci, sb);
-  };
-
-  struct Frags {
-    bf16x8 ah[C / 16], al[C / 16], vb[TPW][C / 16];
-    float g;
-  };
-  auto frags = [&](int, int buf) __attribute__((always_inline)) {
-    Frags fr;
-    fr.g = gnext;  // decay of the chunk being contracted (staged one step ago)
-    if (has_tiles) {
-      const char* sb = smem + buf * L::TOTAL;
-      const __bf16* Kh = reinterpret_cast<const __bf16*>(sb + L::KH);
-      const __bf16* Kl = reinterpret_cast<const __bf16*>(sb + L::KL);
-      const __bf16* Vr = reinterpret_cast<const __bf16*>(sb + L::VR);
-      const int lane = opaque_i(threadIdx.x) & 63;
-      // lane 4j + q of a 16-lane group addresses token row r0 + j, columns c0 + 4q
-      const int rsub = (lane & 15) >> 2, csub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      for (int j = 0; j < 8; ++j) {
+        // channel i0 + j, tokens 4R .. 4R+3
+        float x[4];
 #pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        const int r0 = 16 * ks + 8 * (lane >> 5) + rsub;
-        const int ca = r0 * RLD + mt * 32 + csub;
-        fr.ah[ks] = tr_bf8(Kh + ca, Kh + ca + 4 * RLD);
-        fr.al[ks] = tr_bf8(Kl + ca, Kl + ca + 4 * RLD);
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          const int cv = r0 * RLD + (nt0 + k) * 32 + csub;
-          fr.vb[k][ks] = tr_bf8(Vr + cv, Vr + cv + 4 * RLD);
-        }
+        for (int q = 0; q < 4; ++q) x[q] = w[q] * bf_at(rs.k[q], j);
+        unsigned h01, l01, h23, l23;
+        split2(x[0], x[1], h01, l01);
+        split2(x[2], x[3], h23, l23);
+        const int at = ch_at<L::KT>(i0 + j, 4 * R);
+        *reinterpret_cast<uint2*>(Kh + at) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(Kl + at) = make_uint2(l01, l23);
+        const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        auto dw = [&](const uint4& v) { return (j < 2) ? v.x : (j < 4) ? v.y : (j < 6) ? v.z : v.w; };
+        const unsigned v01 = __builtin_amdgcn_perm(dw(rs.v[1]), dw(rs.v[0]), sel);
+        const unsigned v23 = __builtin_amdgcn_perm(dw(rs.v[3]), dw(rs.v[2]), sel);
+        *reinterpret_cast<uint2*>(Vr + at) = make_uint2(v01, v23);
       }
+      static_for<0, 4>([&](auto P) __attribute__((always_inline)) { load_tok(SET, cl, P); });
+      return;
     }
-    return fr;
+    static_for<0, 4>([&](auto P) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      const int t = 4 * R + p;
+      const float wp = p == 0 ? w4.x : p == 1 ? w4.y : p == 2 ? w4.z : w4.w;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = wp * bf_at(regs[st].k[p], j);
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      *reinterpret_cast<bf16x8*>(Kh + t * RLD + i0) = hi;
+      *reinterpret_cast<bf16x8*>(Kl + t * RLD + i0) = lo;
+      *reinterpret_cast<uint4*>(Vr + t * RLD + i0) = regs[st].v[p];
+      load_tok(SET, cl, P);
+    });
   };
-  auto contract = [&](const Frags& fr, int) __attribute__((always_inline)) {
-    if (!has_tiles) return;
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) S[k] *= fr.g;
-#pragma unroll
-    for (int ks = 0; ks < C / 16; ++ks)
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        S[k] = mfma32(fr.al[ks], fr.vb[k][ks], S[k]);
-        S[k] = mfma32(fr.ah[ks], fr.vb[k][ks], S[k]);
+  auto load_all = [&](auto SET, int ci) __attribute__((always_inline)) {
+    static_for<0, 4>([&](auto P) __attribute__((always_inline)) { load_tok(SET, ci, P); });
+  };
+
+  if (n > 0) {
+    load_all(I0(), 0);
+    load_all(I1(), min(1, last));
+    __syncthreads();  // weights of chunks 0 and 1
+    stage(I0(), 0, min(2, last));
+    __syncthreads();  // chunk 0 staged
+    auto step = [&](auto D, int cj) __attribute__((always_inline)) {
+      using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
+      if (cj + 1 < n) {
+        stage(DN(), cj + 1, min(cj + 3, last));
+      } else {
+        // keep the load sequence of every step the same (see the header)
+        load_all(DN(), last);
       }
-  };
-
-  run_pipeline(u.n_chunks, load, stage, frags, contract);
-
-  if (has_tiles) write_tiles<TPW>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, nt0, dk, dv);
-  if (threadIdx.x == 0) a.log_scale[u.unit] = lam * kLn2;
+      __syncthreads();
+    };
+    int cj = 0;
+#pragma unroll 1
+    for (; cj + 2 <= n; cj += 2) {
+      step(I0(), cj);
+      step(I1(), cj + 1);
+    }
+    if (cj < n) step(I0(), cj);
+  }
 }
 
 // ============================================================ diagonal gates
@@ -384,7 +538,7 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
 #pragma unroll
   for (int k = 0; k < TPW; ++k) S[k] = zero16();
   float lam[4] = {0.f, 0.f, 0.f, 0.f};
-  DiagRegs regs[2];
+  DiagRegs regs[SD_DEPTH_DIAG];
 
   // lane -> (row r, channels c0 .. c0+3, first token t4 of the lane in the chunk)
   auto lane_map = [&](int& r, int& c0, int& t4) __attribute__((always_inline)) {
@@ -539,7 +693,7 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     }
   };
 
-  run_pipeline(u.n_chunks, load, stage, frags, contract);
+  run_pipeline<SD_DEPTH_DIAG>(u.n_chunks, load, stage, frags, contract);
 
   if (has_tiles) write_tiles<TPW>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, nt0, dk, dv);
   // lambda: rows r == 0 hold their block's totals; the TG blocks of each
