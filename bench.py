@@ -87,6 +87,44 @@ def copy_calibration(torch, dev, nbytes: int) -> None:
     del src, dst
 
 
+def hold_cycles(torch, stream, seconds: float) -> int:
+    """Argument of torch.cuda._sleep that holds the stream for about
+    `seconds` (calibrated once here); 0 if this torch has no _sleep."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return 0
+    probe = 1 << 20
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(probe)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_cycle = max(e0.elapsed_time(e1) / 1e3, 1e-6) / probe
+    return int(min(seconds / per_cycle, 1 << 34))
+
+
+def hbm_copy_reference(torch, dev, nbytes: int = 1 << 30) -> dict:
+    """The rate of a plain device copy (torch's copy of `nbytes`, best of
+    three): what this part sustains for a simple streaming read + write, as
+    context for the HBM roofline fractions (which use the 8 TB/s peak)."""
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(4):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    gbs = 2 * nbytes / best / 1e9
+    return {"copy_bytes": nbytes, "copy_gbs": gbs, "copy_frac_of_peak": gbs / PEAK_HBM_GBS}
+
+
 def dense_build_flops_per_token_head(d: int, c: int = CHUNK) -> float:
     """Algorithmic flops of the chunked dense build per token and head:
     the chunk's UT work 6*c*d (K K^T, U = A K, W = A V, each 2*c*d per token)
@@ -179,26 +217,31 @@ def bench_scalar_diag(w, args):
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    # Each kernel here runs for well under a millisecond, so a step enqueues
-    # `reps` passes of each operation back to back and the events bracket each
-    # group: the per-launch time is the group's time / reps, with the queue kept
-    # full (a single launch between two events would also time the host's
-    # enqueue latency).
+    # Each kernel here runs for well under a millisecond, less than the host
+    # needs to marshal and enqueue one call.  So each operation is timed as a
+    # group of `reps` back-to-back launches that the host enqueues while the
+    # stream is held by a spin kernel (torch.cuda._sleep) issued before the
+    # group's first event: the events then see the launches run back to back
+    # on the device, and the per-launch time is the group's time / reps.
     reps = args.reps
+    hold = hold_cycles(torch, stream, reps * 150e-6)
+
+    def group(fn, e0, e1):
+        if hold:
+            torch.cuda._sleep(hold)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
 
     def step(rec=None):
-        e = [ev() for _ in range(4)]
-        e[0].record(stream)
-        for _ in range(reps):
-            pic.pic_segment_build(w.form, k, v, alpha, None, offsets, out=pairs)
-        e[1].record(stream)
-        for _ in range(reps):
-            pic.pic_compose(w.form, pairs["log_scale"], None, pairs["S0"], chain_off, chain_idx,
-                            None, out=S_out)
-        e[2].record(stream)
-        for _ in range(reps):
-            pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
-        e[3].record(stream)
+        e = [ev() for _ in range(6)]
+        group(lambda: pic.pic_segment_build(w.form, k, v, alpha, None, offsets, out=pairs),
+              e[0], e[1])
+        group(lambda: pic.pic_compose(w.form, pairs["log_scale"], None, pairs["S0"], chain_off,
+                                      chain_idx, None, out=S_out), e[2], e[3])
+        group(lambda: pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive),
+              e[4], e[5])
         if rec is not None:
             rec.append(e)
 
@@ -206,12 +249,10 @@ def bench_scalar_diag(w, args):
         step()
     torch.cuda.synchronize()
     recs = []
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         step(recs)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / (args.steps * reps)
-    ms = [np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]) / reps for i in range(3)]
+    ms = [np.mean([r[2 * i].elapsed_time(r[2 * i + 1]) for r in recs]) / reps for i in range(3)]
     gate_bytes = 4 * (dk if w.form == synth.DIAG else 1)
     lam_out = 4 * (dk if w.form == synth.DIAG else 1)
     qb = 2 if w.qkv_bf16 else 4
@@ -222,7 +263,7 @@ def bench_scalar_diag(w, args):
     gbs = lambda nbytes, t: nbytes / (t / 1e3) / 1e9
     out = {"metric": f"{synth.FORM_NAMES[w.form]} segment build tokens/s; % HBM roofline",
            "value": N / (ms[0] / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": wall * 1e3, "higher_is_better": True,
+           "warmup": args.warmup, "ms_per_step": float(sum(ms)), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, bf16 k/v",
            "data": "synthetic",
            "config": {"workload": w.name, "form": synth.FORM_NAMES[w.form], "layers": B,
@@ -241,7 +282,8 @@ def bench_scalar_diag(w, args):
                                 "frac": gbs(cb, ms[1]) / PEAK_HBM_GBS},
            "roofline_naive_add": {"bound": "hbm", "achieved": gbs(nb, ms[2]),
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": gbs(nb, ms[2]) / PEAK_HBM_GBS}}
+                                  "frac": gbs(nb, ms[2]) / PEAK_HBM_GBS},
+           "hbm_reference": hbm_copy_reference(torch, dev)}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -362,7 +404,8 @@ def bench_reuse(w, args):
                         "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": cb},
            "fresh_build": {"tokens_per_s": fresh_tokens / (fresh_ms / 1e3), "ms": fresh_ms,
                            "segments": n_fresh, "layers": B},
-           "pool_and_input_preparation_s": prep_s}
+           "pool_and_input_preparation_s": prep_s,
+           "hbm_reference": hbm_copy_reference(torch, dev)}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -537,6 +580,7 @@ def main(argv=None):
     }
     if other is not None:
         out["build_other_precision"] = other
+    out["hbm_reference"] = hbm_copy_reference(torch, dev)
     if not args.no_cpu_baseline:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -35,6 +36,120 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+// ---------------------------------------------------------------- staging
+// The small per-call tables (segment offsets and order, chain tables) reach
+// the device through pinned host slots: the caller's arrays are copied into
+// a slot and the slot is copied to the workspace with hipMemcpyAsync, which
+// is then asynchronous, so back-to-back calls queue on the stream without
+// waiting for the device.  A slot is reused after the copy that last read it
+// has completed (one event per slot; with 64 slots that wait is normally
+// already over).  Tables larger than a slot (or when pinned memory cannot be
+// had) are copied from the caller's memory and the call waits for the
+// stream, so the source may be released on return.  Slots
+// are per device and shared by all threads (a mutex guards the choice of
+// slot).  Not usable under stream capture: a captured copy would read a slot
+// that later calls overwrite.
+struct Piece {
+  void* dst;
+  const void* src;
+  size_t bytes;
+};
+
+class Staging {
+ public:
+  static constexpr int kSlots = 64;
+  static constexpr size_t kSlotBytes = 64 * 1024;
+
+  hipError_t copy(std::initializer_list<Piece> pieces, hipStream_t s) {
+    size_t total = 0;
+    for (const Piece& p : pieces) total += p.bytes + kSlack;
+    if (total == 0) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (total > kSlotBytes || dev < 0 || dev >= kMaxDevices) return copy_pageable(pieces, s);
+    std::lock_guard<std::mutex> lock(mu_);
+    Pool& pool = pools_[dev];
+    if (!pool.host) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&pool.host), kSlots * kSlotBytes,
+                        hipHostMallocDefault);
+      if (e != hipSuccess) {
+        pool.host = nullptr;
+        return copy_pageable(pieces, s);
+      }
+      for (int i = 0; i < kSlots; ++i) {
+        e = hipEventCreateWithFlags(&pool.ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+        pool.pending[i] = false;
+      }
+    }
+    const int i = pool.next;
+    pool.next = (pool.next + 1) % kSlots;
+    if (pool.pending[i]) {
+      e = hipEventSynchronize(pool.ev[i]);
+      if (e != hipSuccess) return e;
+    }
+    // The pieces go to ascending places of one workspace: lay them out in
+    // the slot as they lie there and move the whole span with one copy.
+    char* slot = pool.host + size_t(i) * kSlotBytes;
+    char* base = nullptr;
+    size_t span = 0;
+    for (const Piece& p : pieces) {
+      if (p.bytes == 0) continue;
+      char* d = static_cast<char*>(p.dst);
+      if (!base) base = d;
+      if (d < base + span || size_t(d - base) + p.bytes > kSlotBytes) {
+        base = nullptr;  // not laid out as expected: one copy per piece
+        break;
+      }
+      span = size_t(d - base) + p.bytes;
+    }
+    if (base) {
+      for (const Piece& p : pieces)
+        if (p.bytes) std::memcpy(slot + (static_cast<char*>(p.dst) - base), p.src, p.bytes);
+      e = hipMemcpyAsync(base, slot, span, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return e;
+    } else {
+      size_t at = 0;
+      for (const Piece& p : pieces) {
+        if (p.bytes == 0) continue;
+        std::memcpy(slot + at, p.src, p.bytes);
+        e = hipMemcpyAsync(p.dst, slot + at, p.bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+        at += p.bytes;
+      }
+    }
+    e = hipEventRecord(pool.ev[i], s);
+    pool.pending[i] = e == hipSuccess;
+    return e;
+  }
+
+ private:
+  static constexpr int kMaxDevices = 64;
+  static constexpr size_t kSlack = 256;  // alignment gaps between the pieces
+  struct Pool {
+    char* host = nullptr;
+    hipEvent_t ev[kSlots];
+    bool pending[kSlots];
+    int next = 0;
+  };
+  static hipError_t copy_pageable(std::initializer_list<Piece> pieces, hipStream_t s) {
+    for (const Piece& p : pieces) {
+      if (p.bytes == 0) continue;
+      const hipError_t e = hipMemcpyAsync(p.dst, p.src, p.bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipStreamSynchronize(s);
+  }
+  std::mutex mu_;
+  Pool pools_[kMaxDevices];
+};
+
+Staging& staging() {
+  static Staging* st = new Staging();  // never destroyed: pinned memory lives until exit
+  return *st;
+}
 
 // product of non-negative sizes, or -1 on int64 overflow
 int64_t mul_sizes(std::initializer_list<int64_t> xs) {
@@ -212,12 +327,11 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
   char* ws = static_cast<char*>(workspace);
   int64_t* d_off = reinterpret_cast<int64_t*>(ws);
   int32_t* d_order = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
-  hipError_t e = hipMemcpyAsync(d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1),
-                                hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "copying segment offsets");
-  e = hipMemcpyAsync(d_order, order.data(), sizeof(int32_t) * size_t(n_seg),
-                     hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "copying segment order");
+  hipError_t e = staging().copy(
+      {{d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1)},
+       {d_order, order.data(), sizeof(int32_t) * size_t(n_seg)}},
+      s);
+  if (e != hipSuccess) return hip_fail(e, "copying the segment plan");
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
                    k, v, alpha, beta, d_off, d_order, log_scale, T_hat, S0};
   if (form == PIC_FORM_DENSE)
@@ -299,14 +413,12 @@ static int enqueue_chains(int32_t n_req, const int64_t* off, const int32_t* idx,
   char* ws = static_cast<char*>(workspace);
   int64_t* o = reinterpret_cast<int64_t*>(ws);
   int32_t* i = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_req) + 1)));
-  hipError_t e = hipMemcpyAsync(o, off, sizeof(int64_t) * (size_t(n_req) + 1),
-                                hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "copying chain offsets");
   const int64_t total = off[n_req];
-  if (total > 0) {
-    e = hipMemcpyAsync(i, idx, sizeof(int32_t) * size_t(total), hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "copying chain indices");
-  }
+  const hipError_t e = staging().copy(
+      {{o, off, sizeof(int64_t) * (size_t(n_req) + 1)},
+       {i, idx, total > 0 ? sizeof(int32_t) * size_t(total) : size_t(0)}},
+      s);
+  if (e != hipSuccess) return hip_fail(e, "copying the chain tables");
   *d_off = o;
   *d_idx = i;
   return PIC_OK;

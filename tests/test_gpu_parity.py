@@ -363,3 +363,35 @@ def test_errors_leave_outputs_untouched():
     assert ei.value.code == -4
     torch.cuda.synchronize()
     assert torch.isnan(S_out).all()
+
+
+def test_back_to_back_calls_with_changing_tables():
+    """150 builds and 150 composes with different plans are enqueued without
+    synchronising (more calls than the library's pinned staging slots, so
+    slots are reused while earlier copies may still be pending); every result
+    matches the oracle for its own plan."""
+    import torch
+    import hybrid_caching_amd as pic
+    form, B, H, d = SCALAR, 1, 2, 32
+    plans = [[0, 64, 100], [0, 10, 100], [0, 100, 100], [0, 1, 50, 99, 100]]
+    k, v, a, _ = rand_case(form, B, H, d, d, [0, 100], seed=77)
+    kd, vd, ad = to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(a)
+    lam, _, S = random_pool(form, 6, B, H, d, d, seed=78)
+    lam_d, S_d = to_dev(lam), to_dev(S)
+    chains = [([0, 2, 5], [0, 1, 2, 3, 4]), ([0, 1], [5]), ([0, 0, 3], [2, 2, 2]),
+              ([0, 6], [5, 4, 3, 2, 1, 0]), ([0, 1, 2, 3], [1, 3, 5])]
+    builds, composes = [], []
+    for i in range(150):
+        off = plans[i % len(plans)]
+        builds.append((off, pic.pic_segment_build(form, kd, vd, ad, None, off)))
+        coff, cidx = chains[i % len(chains)]
+        composes.append((coff, cidx, pic.pic_compose(form, lam_d, None, S_d, coff, cidx, None)))
+    torch.cuda.synchronize()
+    ref_b = {tuple(p): oracle.build(form, k, v, a, None, p) for p in plans}
+    for off, out in builds:
+        ref = ref_b[tuple(off)]
+        assert max_rel_units(out["S0"].cpu().numpy(), ref["S"]) <= TOL_BF16
+        assert lam_err(out["log_scale"].cpu().numpy(), ref["lam"]) <= 1e-4
+    ref_c = {i: oracle.compose(form, lam, None, S, c[0], c[1], None) for i, c in enumerate(chains)}
+    for i, (coff, cidx, out) in enumerate(composes):
+        assert max_rel_units(out.cpu().numpy(), ref_c[i % len(chains)]) <= TOL_F32
