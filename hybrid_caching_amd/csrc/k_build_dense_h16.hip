@@ -46,8 +46,9 @@
 //                      -U fragments (all three)
 //            solver:   V rows 0..31 of chunk ci-1; diagonal blocks of chunk ci
 //   phase B: consumers: W seeds of chunk ci-1, chain sub-chunk 0 of ci-1
-//            helpers:  the gates of chunk ci+1 (helper 2)
-//            solver:   off-diagonal blocks of chunk ci -> A, A'; G of chunk ci+1
+//            helpers:  G of chunk ci+1 (helper s: sub-chunk s), the gates of
+//                      chunk ci+1 (helper 2)
+//            solver:   off-diagonal blocks of chunk ci -> A, A'
 // so a chunk is staged in cycle j-1, solved in cycle j, and chained in cycles
 // j+1 and j+2.  K is kept for four chunks; -U fragments, A/A', G and the
 // masked gates for two; V for one.  Every global load is issued a cycle
@@ -244,14 +245,13 @@ __device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI],
     }
 }
 
-// G_ss = K_s K_s^T for both sub-chunks from the K rows of a chunk (fp32).  G
-// is symmetric: the lane's accumulator column cl is also row cl, with entries
+// G_ss = K_s K_s^T of sub-chunk s from the K rows of a chunk (fp32).  G is
+// symmetric: the lane's accumulator column cl is also row cl, with entries
 // 8 k + 4 g + {0..3} in registers 4k .. 4k+3, so each lane writes its row
 // with four 16-byte stores.
-__device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane) {
+__device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane, int s) {
   const int g = lane >> 5, cl = lane & 31;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  {
     f32x16 acc0 = zero16(), acc1 = zero16();
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks) {
@@ -628,8 +628,6 @@ __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
         }
       }
     }
-    // G of chunk ci+1 (its K rows were staged in phase A)
-    if (ci + 1 < n) gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane);
   }
 }
 
@@ -713,6 +711,9 @@ __device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
 
     // ---------------- phase B
     __syncthreads();
+    // G of sub-chunk pw of chunk ci+1 (its K rows were staged in phase A)
+    if (pw < 2 && ci + 1 < n)
+      gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane, pw);
     if (pw == NHW - 1 && ci + 1 < n) {
       // gates of chunk jn: log2 prefix per sub-chunk (one per half wave)
       const int jn = ci + 1;
