@@ -27,8 +27,11 @@
 // two 32x32 triangular inverses of a chunk: the 16x16 diagonal blocks by back
 // substitution, one row per lane, reading rows of L as broadcast LDS loads a
 // few steps ahead, then the off-diagonal blocks X_10 = -X_11 L_10 X_00 with
-// 16x16x16 matrix-core products: no workgroup barrier inside the solve.
-// Three helper waves stage k/v, form G = K K^T, the gates and U^T = K^T A^T.
+// 16x16x16 matrix-core products: no workgroup barrier inside the solve; it
+// also forms two of the eight U^T = K^T A^T tiles.  Two K waves stage the K
+// rows (half each), form the other six U^T tiles and G = K K^T (one
+// sub-chunk each); the last wave stages V and turns the gates into the
+// masked beta, beta * r and the sub-chunk decays.
 //
 // LDS holds K and V row-major in fp16.  Every transposed operand fragment
 // (K^T for U^T and for K^T N, V^T for W) is read with ds_read_b64_tr_b16: in
@@ -41,13 +44,13 @@
 //
 // Pipeline: cycle ci has two phases separated by workgroup barriers.
 //   phase A: consumers chain sub-chunk 1 of chunk ci-2
-//            helpers:  K rows of chunk ci+1 to LDS (helpers 0, 1), V rows
-//                      32..63 of chunk ci-1 (helper 2); U^T of chunk ci-1 ->
-//                      -U fragments (all three)
-//            solver:   V rows 0..31 of chunk ci-1; diagonal blocks of chunk ci
+//            K waves:  K rows of chunk ci+1 to LDS; U^T tiles 0-5 of chunk
+//                      ci-1 -> -U fragments
+//            V wave:   V rows of chunk ci-1
+//            solver:   diagonal blocks of chunk ci; U^T tiles 6, 7 of ci-1
 //   phase B: consumers: W seeds of chunk ci-1, chain sub-chunk 0 of ci-1
-//            helpers:  G of chunk ci+1 (helper s: sub-chunk s), the gates of
-//                      chunk ci+1 (helper 2)
+//            K waves:  G of chunk ci+1 (wave s: sub-chunk s)
+//            V wave:   the gates of chunk ci+1
 //            solver:   off-diagonal blocks of chunk ci -> A, A'
 // so a chunk is staged in cycle j-1, solved in cycle j, and chained in cycles
 // j+1 and j+2.  K is kept for four chunks; -U fragments, A/A', G and the
@@ -72,7 +75,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int DP = 128;        // padded head size
 constexpr int C = 64;          // tokens staged per chunk
 constexpr int NT = DP / 32;    // consumer waves = 32-row tiles
-constexpr int NHW = 3;         // helper producer waves
+constexpr int NHW = 3;         // producer waves besides the solver (two K, one V)
 constexpr int THREADS = (NT + 1 + NHW) * 64;
 constexpr int NKB = 4;         // K buffers (chunks alive at once)
 
@@ -270,6 +273,40 @@ __device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane, in
   }
 }
 
+// U^T tiles tile0 .. tile0+NTL-1 of chunk j -> -U fragments.  Tile i covers
+// sub-chunk i / NT, columns 32 (i % NT) ..  K^T fragment: lane (g, m) needs
+// K[token 32 s + 16 kk + 8 g + 0..7][32 t + m].  All operands are read before
+// the products, so the reads of the tiles overlap.
+template <int NTL>
+__device__ __forceinline__ void ut_tiles(const _Float16* kb, const _Float16* Ah, char* uf, int tile0,
+                                         int lane) {
+  const int g = lane >> 5, cl = lane & 31;
+  const int ti = lane & 15, tg = lane >> 4;
+  const int tr_row = ti >> 2, tr_col = 16 * (tg & 1) + 4 * (ti & 3);
+  const _Float16* kbase = kb + (8 * g + tr_row) * RLD + tr_col;
+  f16x8 kf[NTL][2], ah[NTL][2];
+#pragma unroll
+  for (int i = 0; i < NTL; ++i) {
+    const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 32 * t;
+      kf[i][kk] = tr_h8(p0, p0 + 4 * RLD);
+      ah[i][kk] = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NTL; ++i) {
+    const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
+    f32x16 acc = zero16();
+    acc = mfma16(kf[i][0], ah[i][0], acc);
+    acc = mfma16(kf[i][1], ah[i][1], acc);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<f16x8*>(uf + uf_off(s, t, hh, lane)) = acc_h8<-1>(acc, hh);
+  }
+}
+
 // wave-uniform copies (values that reach a role through memory would
 // otherwise be treated as per-lane, turning uniform branches into exec masks)
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -296,7 +333,8 @@ __shared__ __attribute__((aligned(16))) char h16_smem[LDS_TOTAL];
 
 __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x);
 __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x);
-__device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x);
+__device__ __noinline__ void kstage_role(const BuildArgs& a, const Ctx& x);
+__device__ __noinline__ void vstage_role(const BuildArgs& a, const Ctx& x);
 
 __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
   const int BH = a.batch * a.heads;
@@ -315,8 +353,10 @@ __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
     consumer_role(a, x);
   else if (wid == NT)
     solver_role(a, x);
+  else if (wid < NT + NHW)
+    kstage_role(a, x);
   else
-    helper_role(a, x);
+    vstage_role(a, x);
 }
 
 #define PIC_H16_ROLE_PROLOGUE                                                   \
@@ -524,10 +564,7 @@ constexpr int XS_LD = 48;  // scratch row stride (halves): 96 bytes, so that the
 __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const int s = lane >> 5, blk = (lane >> 4) & 1, jr = lane & 15;
-  const int HDv = H * dv;
-  const int vch = min(8 * (lane & 15), dv - 8);
   float acc[16], bt[16];
-  uint4 pv[8];  // V rows 0..31 of the next chunk to stage (items 0..7)
 #pragma unroll 1
   for (int ci = -1; ci <= n + 1; ++ci) {
     const bool solve = ci >= 0 && ci < n;
@@ -536,11 +573,6 @@ __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
     const float* grp = gbr0 + (ci & 1) * C;                // beta * r
     _Float16* ab = AB0 + (ci & 1) * AB_HALFS;              // scratch, then A / A'
     __syncthreads();  // phase A
-    // V rows 0..31 of chunk ci-1 (loaded a cycle ago), then load chunk ci's
-    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pv, chunk_len(ci - 1), dv, 0, 8, lane);
-    if (solve)
-      load_rows(pv, vp + ((int64_t(b) * N + t_begin + int64_t(ci) * C) * H + h) * dv + vch, HDv,
-                chunk_len(ci), 0, 8, lane);
     if (solve) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -556,6 +588,12 @@ __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
                                                  pk_h2(acc[4], acc[5]), pk_h2(acc[6], acc[7]));
       *reinterpret_cast<uint4*>(xr + 8) = make_uint4(pk_h2(acc[8], acc[9]), pk_h2(acc[10], acc[11]),
                                                      pk_h2(acc[12], acc[13]), pk_h2(acc[14], acc[15]));
+    }
+    // U^T tiles 6, 7 of chunk ci-1
+    if (ci - 1 >= 0 && ci - 1 < n) {
+      const int j = ci - 1;
+      ut_tiles<2>(Kb0 + (j % NKB) * (C * RLD), AB0 + (j & 1) * AB_HALFS, Uf0 + (j & 1) * UF_BYTES,
+                  6, lane);
     }
     __syncthreads();  // phase B
     if (solve) {
@@ -632,27 +670,50 @@ __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
 }
 
 // ===========================================================================
-// helper waves: K rows (helpers 0, 1), the second half of V and the gates
-// (helper 2), U^T
+// K waves: K rows (half each), U^T tiles, G; V wave: V rows and the gates
 // ===========================================================================
-__device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
+__device__ __noinline__ void kstage_role(const BuildArgs& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
-  const int pw = wid - NT - 1;  // 0 .. NHW-1
-  const float* bsrc = beta ? beta : alpha;
-  const int HDk = H * dk, HDv = H * dv;  // element stride between tokens
-  const int cg = lane & 15;
-  const int kch = min(8 * cg, dk - 8), vch = min(8 * cg, dv - 8);
-  // K rows: helper s (< 2) stages rows [32 s, 32 s + 32) of each chunk
-  // (items 8 s .. 8 s + 7); helper 2 stages V rows 32..63 (items 8..15).
-  const int i0 = pw < 2 ? 8 * pw : 8;
+  const int pw = wid - NT - 1;  // 0 or 1
+  const int HDk = H * dk;       // element stride between tokens
+  const int kch = min(8 * (lane & 15), dk - 8);
+  // K rows: K wave pw stages rows [32 pw, 32 pw + 32) of each chunk (items
+  // 8 pw .. 8 pw + 7), loaded a cycle ahead
+  const int i0 = 8 * pw;
   uint4 pr[8];
-  // U^T tiles of each chunk: helper 0: 0-2, helper 1: 3-5, helper 2: 6-7
-  const int tile0 = 3 * pw, ntile = pw < 2 ? 3 : 2;
-  // alpha, beta of lane's token for two chunks (helper NHW-1), indexed by
-  // chunk parity, so that no register holding a pending load is copied
+  auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
+  if (n > 0) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, 8, lane);
+#pragma unroll 1
+  for (int ci = -1; ci <= n + 1; ++ci) {
+    // ---------------- phase A: K rows of chunk ci+1, load chunk ci+2's;
+    // U^T tiles 3 pw .. 3 pw + 2 of chunk ci-1
+    __syncthreads();
+    if (ci + 1 < n)
+      stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, chunk_len(ci + 1), dk, i0, 8, lane);
+    if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, 8, lane);
+    if (ci - 1 >= 0 && ci - 1 < n) {
+      const int j = ci - 1;
+      ut_tiles<3>(Kb0 + (j % NKB) * (C * RLD), AB0 + (j & 1) * AB_HALFS, Uf0 + (j & 1) * UF_BYTES,
+                  3 * pw, lane);
+    }
+    // ---------------- phase B: G of sub-chunk pw of chunk ci+1
+    __syncthreads();
+    if (ci + 1 < n)
+      gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane, pw);
+  }
+}
+
+// V rows and gates (the last wave)
+__device__ __noinline__ void vstage_role(const BuildArgs& a, const Ctx& x) {
+  PIC_H16_ROLE_PROLOGUE;
+  const float* bsrc = beta ? beta : alpha;
+  const int HDv = H * dv;  // element stride between tokens
+  const int vch = min(8 * (lane & 15), dv - 8);
+  uint4 pr[16];  // V rows of a chunk (items 0..15), loaded a cycle ahead
+  // alpha, beta of lane's token for two chunks, indexed by chunk parity, so
+  // that no register holding a pending load is copied
   float pa[2] = {1.f, 1.f}, pb[2] = {0.f, 0.f};
   float lam = 0.f;
-  // element offset of the first token of chunk j of this (layer, head)
   auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
   auto load_gates = [&](int j, float& ra, float& rb) {
     const int64_t gi = row0(j) + int64_t(min(lane, chunk_len(j) - 1)) * H;
@@ -663,59 +724,14 @@ __device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
   // one pipeline cycle; P = parity of chunk ci+1 (compile-time register slot)
   auto cycle = [&](int ci, auto par) {
     constexpr int P = decltype(par)::value;
-    // ---------------- phase A
+    // ---------------- phase A: V rows of chunk ci-1, then load chunk ci's
     __syncthreads();
-    if (pw < 2) {
-      // K rows of chunk ci+1 (loaded a cycle ago), then load chunk ci+2's
-      if (ci + 1 < n)
-        stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, chunk_len(ci + 1), dk, i0, 8, lane);
-      if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, 8, lane);
-    } else {
-      // V rows 32..63 of chunk ci-1 (loaded a cycle ago), then chunk ci's
-      if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, chunk_len(ci - 1), dv, i0, 8, lane);
-      if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), i0, 8, lane);
-    }
-    if (ci - 1 >= 0 && ci - 1 < n) {
-      // U^T of chunk j -> -U fragments.  K^T fragment: lane (g, m) needs
-      // K[token 32 s + 16 kk + 8 g + 0..7][32 t + m].  All operands are read
-      // before the products, so the reads of the tiles overlap.
-      const int j = ci - 1;
-      const _Float16* kb = Kb0 + (j % NKB) * (C * RLD);
-      const _Float16* Ah = AB0 + (j & 1) * AB_HALFS;
-      char* uf = Uf0 + (j & 1) * UF_BYTES;
-      const _Float16* kbase = kb + (8 * g + tr_row) * RLD + tr_col;
-      f16x8 kf[3][2], ah[3][2];
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        if (i < ntile) {
-          const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 32 * t;
-            kf[i][kk] = tr_h8(p0, p0 + 4 * RLD);
-            ah[i][kk] = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
-          }
-        }
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        if (i < ntile) {
-          const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
-          f32x16 acc = zero16();
-          acc = mfma16(kf[i][0], ah[i][0], acc);
-          acc = mfma16(kf[i][1], ah[i][1], acc);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            *reinterpret_cast<f16x8*>(uf + uf_off(s, t, hh, lane)) = acc_h8<-1>(acc, hh);
-        }
-    }
-
-    // ---------------- phase B
+    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, chunk_len(ci - 1), dv, 0, 16, lane);
+    if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), 0, 16, lane);
+    // ---------------- phase B: gates of chunk ci+1
     __syncthreads();
-    // G of sub-chunk pw of chunk ci+1 (its K rows were staged in phase A)
-    if (pw < 2 && ci + 1 < n)
-      gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane, pw);
-    if (pw == NHW - 1 && ci + 1 < n) {
-      // gates of chunk jn: log2 prefix per sub-chunk (one per half wave)
+    if (ci + 1 < n) {
+      // log2 prefix per sub-chunk (one per half wave)
       const int jn = ci + 1;
       const int len = chunk_len(jn);
       const float x2 = half_wave_scan(lane < len ? log2f(pa[P]) : 0.f);
@@ -736,18 +752,15 @@ __device__ __noinline__ void helper_role(const BuildArgs& a, const Ctx& x) {
     }
   };
 
-  if (n > 0) {
-    if (pw < 2) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, 8, lane);
-    if (pw == NHW - 1) load_gates(0, pa[0], pb[0]);
-  }
-  if (n > 1 && pw == NHW - 1) load_gates(1, pa[1], pb[1]);
+  if (n > 0) load_gates(0, pa[0], pb[0]);
+  if (n > 1) load_gates(1, pa[1], pb[1]);
   // chunk ci+1 has parity (ci+1) & 1: cycles -1, 1, 3, ... use slot 0
 #pragma unroll 1
   for (int ci = -1; ci <= n + 1; ci += 2) {
     cycle(ci, std::integral_constant<int, 0>{});
     if (ci + 1 <= n + 1) cycle(ci + 1, std::integral_constant<int, 1>{});
   }
-  if (pw == NHW - 1 && lane == 0) gstore(out_lam + unit, lam * kLn2);
+  if (lane == 0) gstore(out_lam + unit, lam * kLn2);
 }
 
 }  // namespace
