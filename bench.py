@@ -41,7 +41,8 @@ KERNEL_SOURCES = {
     "build_dense_ws_kernel": ["k_build_dense_ws.hip", "mfma_util.hpp", "pic_internal.hpp",
                               "stage_util.hpp"],
     "build_dense_h16_kernel": ["k_build_dense_h16.hip", "mfma_util.hpp", "pic_internal.hpp"],
-    "build_sd_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_scalar_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_diag_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
 
@@ -253,6 +254,7 @@ def bench_scalar_diag(w, args):
         step(recs)
     torch.cuda.synchronize()
     ms = [np.mean([r[2 * i].elapsed_time(r[2 * i + 1]) for r in recs]) / reps for i in range(3)]
+    kname = "build_diag_pipe_kernel" if w.form == synth.DIAG else "build_scalar_pipe_kernel"
     gate_bytes = 4 * (dk if w.form == synth.DIAG else 1)
     lam_out = 4 * (dk if w.form == synth.DIAG else 1)
     qb = 2 if w.qkv_bf16 else 4
@@ -271,10 +273,10 @@ def bench_scalar_diag(w, args):
                       "segment_tokens": int(w.seg_lens[0]), "prompt_tokens": N,
                       "passes_per_step": reps},
            "ms": {"build": ms[0], "compose": ms[1], "naive_add": ms[2]},
-           "roofline": {"kernel": "build_sd_pipe_kernel", "bound": "hbm",
+           "roofline": {"kernel": kname, "bound": "hbm",
                         "achieved": gbs(bb, ms[0]), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": gbs(bb, ms[0]) / PEAK_HBM_GBS,
-                        "traffic": measured_traffic("build_sd_pipe_kernel", w.name),
+                        "traffic": measured_traffic(kname, w.name),
                         "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
                         "tflops": flops / (ms[0] / 1e3) / 1e12},
            "roofline_compose": {"bound": "hbm", "achieved": gbs(cb, ms[1]),

@@ -327,36 +327,51 @@ struct Ctx {
   int n, b, h;
 };
 
+// The fields of the call that the roles read.  The roles take this (not the
+// kernel's argument block, which also carries the plan tables) so that the
+// per-lane copy the calls make stays small.
+struct Core {
+  int heads, dk, dv;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  float* log_scale;
+  float* T_hat;
+  float* S0;
+};
+
 // the workgroup's LDS, at file scope so that every role function addresses
 // it directly (LDS instructions, not flat ones)
 __shared__ __attribute__((aligned(16))) char h16_smem[LDS_TOTAL];
 
-__device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x);
-__device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x);
-__device__ __noinline__ void kstage_role(const BuildArgs& a, const Ctx& x);
-__device__ __noinline__ void vstage_role(const BuildArgs& a, const Ctx& x);
+__device__ __noinline__ void consumer_role(const Core& a, const Ctx& x);
+__device__ __noinline__ void solver_role(const Core& a, const Ctx& x);
+__device__ __noinline__ void kstage_role(const Core& a, const Ctx& x);
+__device__ __noinline__ void vstage_role(const Core& a, const Ctx& x);
 
 __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
   const int BH = a.batch * a.heads;
-  const int seg = a.d_order[blockIdx.x / BH];
+  const int seg = seg_in_order(a, blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
   Ctx x;
   x.b = bh / a.heads;
   x.h = bh % a.heads;
-  x.t_begin = a.d_offsets[seg];
-  x.t_end = a.d_offsets[seg + 1];
+  x.t_begin = seg_offset(a, seg);
+  x.t_end = seg_offset(a, seg + 1);
   x.N = a.n_tokens;
   x.n = int((x.t_end - x.t_begin + C - 1) / C);
   x.unit = (int64_t(seg) * a.batch + x.b) * a.heads + x.h;
+  const Core core{a.heads, a.dk, a.dv, a.k, a.v, a.alpha, a.beta, a.log_scale, a.T_hat, a.S0};
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (wid < NT)
-    consumer_role(a, x);
+    consumer_role(core, x);
   else if (wid == NT)
-    solver_role(a, x);
+    solver_role(core, x);
   else if (wid < NT + NHW)
-    kstage_role(a, x);
+    kstage_role(core, x);
   else
-    vstage_role(a, x);
+    vstage_role(core, x);
 }
 
 #define PIC_H16_ROLE_PROLOGUE                                                   \
@@ -398,7 +413,7 @@ __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
 // ===========================================================================
 // consumer wave c: columns [32c, 32c+32) of That (scaled by 2^E) and S
 // ===========================================================================
-__device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
+__device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const int c = wid;
   f32x16 XT[NT], XS[NT], PM[2];
@@ -561,7 +576,7 @@ __device__ __noinline__ void consumer_role(const BuildArgs& a, const Ctx& x) {
 // ===========================================================================
 constexpr int XS_LD = 48;  // scratch row stride (halves): 96 bytes, so that the
                            // four rows of a transposed read hit distinct banks
-__device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
+__device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const int s = lane >> 5, blk = (lane >> 4) & 1, jr = lane & 15;
   float acc[16], bt[16];
@@ -672,7 +687,7 @@ __device__ __noinline__ void solver_role(const BuildArgs& a, const Ctx& x) {
 // ===========================================================================
 // K waves: K rows (half each), U^T tiles, G; V wave: V rows and the gates
 // ===========================================================================
-__device__ __noinline__ void kstage_role(const BuildArgs& a, const Ctx& x) {
+__device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const int pw = wid - NT - 1;  // 0 or 1
   const int HDk = H * dk;       // element stride between tokens
@@ -704,7 +719,7 @@ __device__ __noinline__ void kstage_role(const BuildArgs& a, const Ctx& x) {
 }
 
 // V rows and gates (the last wave)
-__device__ __noinline__ void vstage_role(const BuildArgs& a, const Ctx& x) {
+__device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
   const float* bsrc = beta ? beta : alpha;
   const int HDv = H * dv;  // element stride between tokens

@@ -127,9 +127,9 @@ __global__ __launch_bounds__((DP / 32 + kProducers) * 64) void build_dense_ws_ke
 
   const int H = a.heads, dk = a.dk, dv = a.dv;
   const int BH = a.batch * H;
-  const int seg = a.d_order[blockIdx.x / BH];
+  const int seg = seg_in_order(a, blockIdx.x / BH);
   const int bh = blockIdx.x % BH, b = bh / H, h = bh % H;
-  const int64_t t_begin = a.d_offsets[seg], t_end = a.d_offsets[seg + 1];
+  const int64_t t_begin = seg_offset(a, seg), t_end = seg_offset(a, seg + 1);
   const int64_t N = a.n_tokens;
   const int n_chunks = int((t_end - t_begin + C - 1) / C);
   const int64_t unit = (int64_t(seg) * a.batch + b) * H + h;

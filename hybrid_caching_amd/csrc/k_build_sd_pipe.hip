@@ -93,12 +93,12 @@ struct Unit {
 __device__ __forceinline__ Unit unit_of(const BuildArgs& a) {
   Unit u;
   const int H = a.heads, BH = a.batch * H;
-  u.seg = a.d_order[blockIdx.x / BH];
+  u.seg = seg_in_order(a, blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
   u.b = bh / H;
   u.h = bh % H;
-  const int64_t t_begin = a.d_offsets[u.seg];
-  u.n_tok = a.d_offsets[u.seg + 1] - t_begin;
+  const int64_t t_begin = seg_offset(a, u.seg);
+  u.n_tok = seg_offset(a, u.seg + 1) - t_begin;
   u.n_chunks = int((u.n_tok + kCs - 1) / kCs);
   u.unit = (int64_t(u.seg) * a.batch + u.b) * H + u.h;
   return u;
@@ -109,7 +109,7 @@ __device__ __forceinline__ int chunk_len(const Unit& u, int ci) {
 }
 // element offset of token t_begin of this (layer, head) in a [B][N][H][d] tensor
 __device__ __forceinline__ int64_t row0(const BuildArgs& a, const Unit& u, int d) {
-  return ((int64_t(u.b) * a.n_tokens + a.d_offsets[u.seg]) * a.heads + u.h) * d;
+  return ((int64_t(u.b) * a.n_tokens + seg_offset(a, u.seg)) * a.heads + u.h) * d;
 }
 
 template <int I, int N, class F>

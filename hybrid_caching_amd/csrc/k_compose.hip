@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (a.S_in) s = reinterpret_cast<const float4*>(a.S_in)[unit * nelem4 + e4];
   const float4* S0 = reinterpret_cast<const float4*>(a.pool_S0);
-  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
+  const int64_t c0 = chain_offset(a, r), c1 = chain_offset(a, r + 1);
   int64_t c = c0;
   // four steps at a time: issue the loads together, then fold in order
   for (; c + 4 <= c1; c += 4) {
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
     float sc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t pu = int64_t(a.d_chain_idx[c + u]) * BH + bh;
+      const int64_t pu = int64_t(chain_entry(a, c + u)) * BH + bh;
       x[u] = S0[pu * nelem4 + e4];
       if (!NAIVE) sc[u] = DIAG ? a.pool_log_scale[pu * a.dk + row] : a.pool_log_scale[pu];
     }
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
     }
   }
   for (; c < c1; ++c) {
-    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+    const int64_t pu = int64_t(chain_entry(a, c)) * BH + bh;
     const float4 x = S0[pu * nelem4 + e4];
     if (NAIVE) {
       s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
@@ -150,10 +150,10 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
     }
   };
 
-  const int64_t c0 = a.d_chain_off[r], c1 = a.d_chain_off[r + 1];
-  if (c0 < c1) load_op(int64_t(a.d_chain_idx[c0]) * BH + bh);
+  const int64_t c0 = chain_offset(a, r), c1 = chain_offset(a, r + 1);
+  if (c0 < c1) load_op(int64_t(chain_entry(a, c0)) * BH + bh);
   for (int64_t c = c0; c < c1; ++c) {
-    const int64_t pu = int64_t(a.d_chain_idx[c]) * BH + bh;
+    const int64_t pu = int64_t(chain_entry(a, c)) * BH + bh;
     __syncthreads();  // every wave is done reading the previous operator
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
         *reinterpret_cast<uint2*>(th_lo + row * LDR + pcol) = make_uint2(l0, l1);
       }
     }
-    if (c + 1 < c1) load_op(int64_t(a.d_chain_idx[c + 1]) * BH + bh);
+    if (c + 1 < c1) load_op(int64_t(chain_entry(a, c + 1)) * BH + bh);
     // this step's S0 strip, loaded ahead of the products
     f32x16 s0[NT];
     float scale = 1.f;
@@ -240,8 +240,8 @@ __global__ void chain_log_scale_kernel(ComposeArgs a, int per) {
   if (e >= total) return;
   const int64_t r = e / (BH * per), rest = e % (BH * per);
   float acc = 0.f;
-  for (int64_t c = a.d_chain_off[r]; c < a.d_chain_off[r + 1]; ++c)
-    acc += a.pool_log_scale[int64_t(a.d_chain_idx[c]) * BH * per + rest];
+  for (int64_t c = chain_offset(a, r); c < chain_offset(a, r + 1); ++c)
+    acc += a.pool_log_scale[int64_t(chain_entry(a, c)) * BH * per + rest];
   a.log_scale_out[e] = acc;
 }
 

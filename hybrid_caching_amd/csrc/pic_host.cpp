@@ -324,16 +324,24 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const std::vector<int32_t> order = build_order(seg_offsets, n_seg);
-  char* ws = static_cast<char*>(workspace);
-  int64_t* d_off = reinterpret_cast<int64_t*>(ws);
-  int32_t* d_order = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
-  hipError_t e = staging().copy(
-      {{d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1)},
-       {d_order, order.data(), sizeof(int32_t) * size_t(n_seg)}},
-      s);
-  if (e != hipSuccess) return hip_fail(e, "copying the segment plan");
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
-                   k, v, alpha, beta, d_off, d_order, log_scale, T_hat, S0};
+                   k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
+  hipError_t e = hipSuccess;
+  if (n_seg <= pic::kInlineSeg) {
+    std::copy(seg_offsets, seg_offsets + n_seg + 1, a.inl_off);
+    std::copy(order.begin(), order.end(), a.inl_order);
+  } else {
+    char* ws = static_cast<char*>(workspace);
+    int64_t* d_off = reinterpret_cast<int64_t*>(ws);
+    int32_t* d_order =
+        reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
+    e = staging().copy({{d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1)},
+                        {d_order, order.data(), sizeof(int32_t) * size_t(n_seg)}},
+                       s);
+    if (e != hipSuccess) return hip_fail(e, "copying the segment plan");
+    a.d_offsets = d_off;
+    a.d_order = d_order;
+  }
   if (form == PIC_FORM_DENSE)
     e = (precision == PIC_PREC_FP16) ? pic::launch_build_dense_h16(a, s)
                                      : pic::launch_build_dense(a, s);
@@ -408,19 +416,26 @@ int pic_validate_naive_add(int batch, int heads, int dk, int dv, int64_t pool_si
   return ok();
 }
 
+// chain tables into the arguments (small) or the workspace (copied)
 static int enqueue_chains(int32_t n_req, const int64_t* off, const int32_t* idx, void* workspace,
-                          hipStream_t s, const int64_t** d_off, const int32_t** d_idx) {
+                          hipStream_t s, pic::ComposeArgs& a) {
+  const int64_t total = off[n_req];
+  a.inl = n_req <= pic::kInlineReq && total <= pic::kInlineIdx;
+  if (a.inl) {
+    std::copy(off, off + n_req + 1, a.inl_off);
+    if (total > 0) std::copy(idx, idx + total, a.inl_idx);
+    return PIC_OK;
+  }
   char* ws = static_cast<char*>(workspace);
   int64_t* o = reinterpret_cast<int64_t*>(ws);
   int32_t* i = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_req) + 1)));
-  const int64_t total = off[n_req];
   const hipError_t e = staging().copy(
       {{o, off, sizeof(int64_t) * (size_t(n_req) + 1)},
        {i, idx, total > 0 ? sizeof(int32_t) * size_t(total) : size_t(0)}},
       s);
   if (e != hipSuccess) return hip_fail(e, "copying the chain tables");
-  *d_off = o;
-  *d_idx = i;
+  a.d_chain_off = o;
+  a.d_chain_idx = i;
   return PIC_OK;
 }
 
@@ -435,13 +450,10 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
     return rc;
   if (n_req == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t* d_off;
-  const int32_t* d_idx;
-  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
-    return rc;
-  pic::ComposeArgs a{form,   batch, heads, dk, dv, pool_size, pool_log_scale, pool_T_hat,
-                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out,
-                     log_scale_out, T_hat_out};
+  pic::ComposeArgs a{form,    batch,    heads,    dk,     dv,       pool_size,
+                     pool_log_scale, pool_T_hat, pool_S0, n_req, nullptr, nullptr,
+                     chain_offsets[n_req], S_in, S_out, log_scale_out, T_hat_out, false, {}, {}};
+  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, a)) return rc;
   hipError_t e = (form == PIC_FORM_DENSE) ? pic::launch_compose_dense(a, s)
                                           : pic::launch_compose_elementwise(a, false, s);
   if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
@@ -466,13 +478,10 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
     return rc;
   if (n_req == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t* d_off;
-  const int32_t* d_idx;
-  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, &d_off, &d_idx))
-    return rc;
-  pic::ComposeArgs a{PIC_FORM_SCALAR, batch, heads, dk, dv, pool_size, nullptr, nullptr,
-                     pool_S0, n_req, d_off, d_idx, chain_offsets[n_req], S_in, S_out,
-                     nullptr, nullptr};
+  pic::ComposeArgs a{PIC_FORM_SCALAR, batch,   heads,   dk,    dv,      pool_size,
+                     nullptr,         nullptr, pool_S0, n_req, nullptr, nullptr,
+                     chain_offsets[n_req], S_in, S_out, nullptr, nullptr, false, {}, {}};
+  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, a)) return rc;
   hipError_t e = pic::launch_compose_elementwise(a, true, s);
   if (e != hipSuccess) return hip_fail(e, "launching the naive-add kernel");
   return ok();

@@ -10,6 +10,14 @@ namespace pic {
 
 enum Form : int { kScalar = 0, kDiag = 1, kDense = 2 };
 
+// Small plans travel inside the kernel arguments, so a call needs no
+// host-to-device copy before its kernel: up to kInlineSeg segments for a
+// build, up to kInlineReq requests with kInlineIdx chain entries for a
+// compose.  Larger plans go through the caller's workspace.
+constexpr int kInlineSeg = 32;
+constexpr int kInlineReq = 16;
+constexpr int kInlineIdx = 64;
+
 // Sizes of one build call, after validation.
 struct BuildArgs {
   int form;
@@ -26,7 +34,17 @@ struct BuildArgs {
   float* log_scale;
   float* T_hat;
   float* S0;
+  int64_t inl_off[kInlineSeg + 1];  // the offsets and order when n_seg <= kInlineSeg
+  int32_t inl_order[kInlineSeg];
 };
+
+// segment offset i and the i-th segment of the visiting order
+__device__ __forceinline__ int64_t seg_offset(const BuildArgs& a, int i) {
+  return a.n_seg <= kInlineSeg ? a.inl_off[i] : a.d_offsets[i];
+}
+__device__ __forceinline__ int seg_in_order(const BuildArgs& a, int i) {
+  return a.n_seg <= kInlineSeg ? a.inl_order[i] : a.d_order[i];
+}
 
 // One compose / naive-add call, after validation.
 struct ComposeArgs {
@@ -44,7 +62,18 @@ struct ComposeArgs {
   float* S_out;
   float* log_scale_out;        // chain pair: sum of log scales, may be null
   float* T_hat_out;            // chain pair: product of That (dense), may be null
+  bool inl;                    // chain tables inline (the fields below)
+  int64_t inl_off[kInlineReq + 1];
+  int32_t inl_idx[kInlineIdx];
 };
+
+// chain offset r and chain entry c
+__device__ __forceinline__ int64_t chain_offset(const ComposeArgs& a, int64_t r) {
+  return a.inl ? a.inl_off[r] : a.d_chain_off[r];
+}
+__device__ __forceinline__ int chain_entry(const ComposeArgs& a, int64_t c) {
+  return a.inl ? a.inl_idx[c] : a.d_chain_idx[c];
+}
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);

@@ -395,3 +395,43 @@ def test_back_to_back_calls_with_changing_tables():
     ref_c = {i: oracle.compose(form, lam, None, S, c[0], c[1], None) for i, c in enumerate(chains)}
     for i, (coff, cidx, out) in enumerate(composes):
         assert max_rel_units(out.cpu().numpy(), ref_c[i % len(chains)]) <= TOL_F32
+
+
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("n_seg", [32, 33, 70])
+def test_plan_in_arguments_and_in_workspace(form, n_seg):
+    """Plans of up to 32 segments travel in the kernel arguments, larger ones
+    through the workspace: both sides of the boundary match the oracle
+    (ragged lengths, empty segments included)."""
+    rng = np.random.default_rng(900 + n_seg)
+    lens = rng.integers(0, 90, size=n_seg)
+    lens[::7] = 0
+    offsets = [0] + list(np.cumsum(lens).astype(int))
+    k, v, a, b = rand_case(form, 1, 2, 32, 32, offsets, seed=901 + form)
+    gpu, ref = build_both(form, k, v, a, b, offsets, True)
+    assert_pair_close(gpu, ref, form, TOL_BF16)
+    if form == DENSE:
+        gpu16, _ = build_both(form, k, v, a, b, offsets, True, precision=1)
+        assert_pair_close(gpu16, ref, form, TOL_BF16)
+
+
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("n_req,steps", [(16, 4), (17, 3), (4, 40)])
+def test_chain_tables_in_arguments_and_in_workspace(form, n_req, steps):
+    """Chain tables of up to 16 requests and 64 entries travel in the kernel
+    arguments, larger ones through the workspace."""
+    import hybrid_caching_amd as pic
+    P, B, H, d = 9, 1, 2, 32
+    lam, That, S = random_pool(form, P, B, H, d, d, seed=910 + n_req)
+    rng = np.random.default_rng(911 + steps)
+    off = [0]
+    idx = []
+    for r in range(n_req):
+        n = int(rng.integers(0, steps + 1)) if r % 3 else steps
+        idx += list(rng.integers(0, P, size=n))
+        off.append(len(idx))
+    out = pic.pic_compose(form, to_dev(lam), to_dev(That), to_dev(S), off, idx, None)
+    ref = oracle.compose(form, lam, That, S, off, idx, None)
+    assert max_rel_units(out.cpu().numpy(), ref) <= TOL_F32
+    nv = pic.pic_naive_add(to_dev(S), off, idx, None)
+    assert max_rel_units(nv.cpu().numpy(), oracle.naive_add(S, off, idx, None)) <= 1e-6
