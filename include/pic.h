@@ -47,9 +47,16 @@
  *     T_hat [P][batch][heads][dk][dk] (dense), S0 [P][batch][heads][dk][dv].
  *     The build writes segment s of the call at pool index s.
  *   - States: S_in, S_out [n_req][batch][heads][dk][dv], fp32.
- *   - Ownership: every buffer belongs to the caller.  The library keeps no
- *     state between calls and allocates no device memory; scratch goes into
- *     the caller's workspace (size from the *_workspace query).
+ *   - Ownership: every buffer belongs to the caller.  The library allocates
+ *     no device memory; the per-call tables (segment offsets and order,
+ *     chain tables) go into the caller's workspace (size from the
+ *     *_workspace query).  Small tables (builds of up to 32 segments,
+ *     composes of up to 16 requests and 64 chain entries) travel in the
+ *     kernel arguments instead and leave the workspace untouched.  Larger
+ *     ones are copied through a pool of pinned host buffers that the library
+ *     allocates on first use (per device, 4 MiB, kept until the process
+ *     ends), so that the copy does not wait for the stream.  Calls are not
+ *     safe under stream capture.
  *   - Asynchrony: a return of PIC_OK means the work is validated and
  *     enqueued on `stream` (a hipStream_t; NULL = the null stream).  Results
  *     are ready once the stream is synchronised.  Host arrays may be reused
