@@ -473,24 +473,30 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
 
 // ============================================================ diagonal gates
 //
-// Thread mapping: a wave covers PL lanes x 4 channels of a token row and RW
-// rows of 4 consecutive tokens (lane = PL * r + p: tokens 4r .. 4r+3 of the
-// wave's block, channels 4p .. 4p+3 of its channel part); the waves split
-// the head's channels into CP parts and the chunk into TG blocks of 4 * RW
-// tokens.  Per channel, the log2 gates are summed over a lane's 4 tokens,
-// then over the later rows of the block by ds_bpermute; a lane's weights are
-// one exp2 of the sum over later rows times its own later gates.  Kw^T (hi,
-// lo) and V^T go to LDS as channel rows (8 bytes per channel and lane); the
-// block decays go to a small table that the contraction applies to S
-// between the blocks.
+// Producer and consumer waves, as for the scalar form.  DP/32 consumer waves
+// each hold one row of 32x32 tiles of S and contract the chunk block by
+// block, scaling S's rows by each block's decay first.  As many producer
+// waves stage: a producer wave covers PL lanes x 4 channels of a token row
+// and RW rows of 8 consecutive tokens (lane = PL * r + p: tokens 8r .. 8r+7
+// of the wave's block, channels 4p .. 4p+3 of its channel part); the waves
+// split the channels into CP parts and the chunk into TG blocks of 8 * RW
+// tokens, so a channel's suffix sums of log2 alpha stay in one wave: serial
+// over a lane's 8 tokens, then over the later rows by ds_bpermute.  A lane's
+// weights are one exp2 of the sum over the later rows times its own later
+// gates.  Kw^T (hi, lo) and V^T go to LDS as channel rows, one 16-byte store
+// (8 tokens) per channel and array; the 16-byte pieces of a row are
+// XOR-swizzled by the row's 8-row group.  Loads: 16 lanes x 8 bytes of k or
+// v or 16 lanes x 16 bytes of gates per token row (whole 128-byte lines);
+// each register set is reloaded as soon as the staging step is done with it.
 template <int DP>
 struct DiagShape {
+  static constexpr int NC = DP / 32;                    // consumer waves
+  static constexpr int NP = DP / 32;                    // producer waves
   static constexpr int PL = DP / 4 < 16 ? DP / 4 : 16;  // lanes per token row
-  static constexpr int RW = 64 / PL;                    // token quads per wave
+  static constexpr int RW = 64 / PL;                    // rows of 8 tokens per wave
   static constexpr int CP = DP / (4 * PL);              // channel parts
-  static constexpr int NW = DP / 16;                    // waves
-  static constexpr int TG = NW / CP;                    // token blocks per chunk
-  static constexpr int BT = 4 * RW;                     // tokens per block
+  static constexpr int TG = NP / CP;                    // token blocks per chunk
+  static constexpr int BT = 8 * RW;                     // tokens per block
   static_assert(TG * BT == kCs, "the blocks cover the chunk");
   static_assert(BT % 16 == 0, "a block is a whole number of MFMA K-steps");
 };
@@ -506,204 +512,267 @@ struct DiagLds {
 };
 
 struct DiagRegs {
-  uint2 k[4], v[4];
-  float4 a[4];
+  uint2 k[8], v[8];
+  float4 a[8];
 };
 
 template <int DP>
 __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
   using L = DiagLds<DP>;
   using Sh = DiagShape<DP>;
-  constexpr int C = kCs, NTH = 4 * DP, NW = NTH / 64, KT = L::KT;
-  constexpr int PL = Sh::PL, RW = Sh::RW, CP = Sh::CP, TG = Sh::TG, BT = Sh::BT;
-  constexpr int NTC = DP / 32, TILES = NTC * NTC, TPW = (TILES + NW - 1) / NW;
-  static_assert(NW == Sh::NW, "wave count");
-  static_assert(NTC % TPW == 0, "the tiles of a wave share one row of tiles");
-  static_assert(TG * DP * 4 <= 2 * DiagLds<DP>::TOTAL, "lambda table fits the LDS buffers");
+  constexpr int C = kCs, KT = L::KT;
+  constexpr int NC = Sh::NC, PL = Sh::PL, RW = Sh::RW, CP = Sh::CP, TG = Sh::TG, BT = Sh::BT;
+  static_assert((NC + Sh::NP) * 64 == 4 * DP, "block size");
+  static_assert(TG * DP * 4 <= 2 * L::TOTAL, "lambda table fits the LDS buffers");
   __shared__ __attribute__((aligned(16))) char smem[2 * L::TOTAL];
 
   const Unit u = unit_of(a);
   const int H = a.heads, dk = a.dk, dv = a.dv;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int n = u.n_chunks, last = n - 1;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  if (wave < NC) {
+    // ---------------- consumers: tiles (mt = wave, nt = 0 .. NC-1)
+    const int mt = wave;
+    f32x16 S[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) S[k] = zero16();
+    if (n > 0) {
+      __syncthreads();  // chunk 0 staged
+#pragma unroll 1
+      for (int cj = 0; cj < n; ++cj) {
+        const char* sb = smem + (cj & 1) * L::TOTAL;
+        const __bf16* Kh = reinterpret_cast<const __bf16*>(sb + L::KH);
+        const __bf16* Kl = reinterpret_cast<const __bf16*>(sb + L::KL);
+        const __bf16* Vt = reinterpret_cast<const __bf16*>(sb + L::VT);
+        const float* gm = reinterpret_cast<const float*>(sb + L::GM);
+        const int l = opaque_i(threadIdx.x) & 63, g = l >> 5, cl = l & 31;
+        bf16x8 ah[C / 16], al[C / 16], vb[NC][C / 16];
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) {
+          const int ka = ch_at<KT>(mt * 32 + cl, 16 * ks + 8 * g);
+          ah[ks] = lds_load8(Kh + ka);
+          al[ks] = lds_load8(Kl + ka);
+#pragma unroll
+          for (int k = 0; k < NC; ++k) vb[k][ks] = lds_load8(Vt + ch_at<KT>(k * 32 + cl, 16 * ks + 8 * g));
+        }
+#pragma unroll
+        for (int bi = 0; bi < TG; ++bi) {
+          float f[16];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const float4 x = *reinterpret_cast<const float4*>(gm + bi * DP + mt * 32 + 8 * qq + 4 * g);
+            f[4 * qq] = x.x; f[4 * qq + 1] = x.y; f[4 * qq + 2] = x.z; f[4 * qq + 3] = x.w;
+          }
+#pragma unroll
+          for (int k = 0; k < NC; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[k][r] *= f[r];
+#pragma unroll
+          for (int ks = bi * (BT / 16); ks < (bi + 1) * (BT / 16); ++ks)
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+              S[k] = mfma32(al[ks], vb[k][ks], S[k]);
+              S[k] = mfma32(ah[ks], vb[k][ks], S[k]);
+            }
+        }
+        __syncthreads();
+      }
+    }
+    write_tiles<NC>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, 0, dk, dv);
+    __syncthreads();  // lambda table
+    __syncthreads();
+    return;
+  }
+
+  // ---------------- producers
+  const int ptid = int(threadIdx.x) - NC * 64;
+  const int pw = __builtin_amdgcn_readfirstlane(ptid >> 6);
+  const int part = pw % CP, tb = pw / CP;
   const int sk = H * dk, sv = H * dv;
   const __bf16* kbase = static_cast<const __bf16*>(a.k) + row0(a, u, dk);
   const __bf16* vbase = static_cast<const __bf16*>(a.v) + row0(a, u, dv);
   const float* abase = a.alpha + row0(a, u, dk);
-
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const bool has_tiles = wave * TPW < TILES;
-  const int mt = (wave * TPW) / NTC, nt0 = (wave * TPW) % NTC;
-  const int part = wave % CP, tg = wave / CP;
-
-  f32x16 S[TPW];
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) S[k] = zero16();
   float lam[4] = {0.f, 0.f, 0.f, 0.f};
-  DiagRegs regs[SD_DEPTH_DIAG];
+  DiagRegs regs[2];
 
-  // lane -> (row r, channels c0 .. c0+3, first token t4 of the lane in the chunk)
-  auto lane_map = [&](int& r, int& c0, int& t4) __attribute__((always_inline)) {
+  // lane -> (row r, channels c0 .. c0+3, first token t0 of the lane in the chunk)
+  auto lane_map = [&](int& r, int& c0, int& t0) __attribute__((always_inline)) {
     const int lane = opaque_i(threadIdx.x) & 63;
-    const int p = lane % PL;
     r = lane / PL;
-    c0 = 4 * (PL * part + p);
-    t4 = BT * tg + 4 * r;
+    c0 = 4 * (PL * part + lane % PL);
+    t0 = BT * tb + 8 * r;
   };
-
-  auto load = [&](auto SET, int ci) __attribute__((always_inline)) {
-    DiagRegs& st = regs[decltype(SET)::value];
-    int r, c0, t4;
-    lane_map(r, c0, t4);
+  // Tokens past the end of the segment read its last token (a valid
+  // address; their weight is 0 and their gate counts as 1); channels past
+  // dk / dv read the last channels and only feed rows / columns of S that
+  // are not written.
+  auto tok_ptrs = [&](int ci, int q, const char*& kp, const char*& vp, const char*& ap)
+      __attribute__((always_inline)) {
+    int r, c0, t0;
+    lane_map(r, c0, t0);
     const int len = chunk_len(u, ci);
+    const unsigned t = unsigned(min(t0 + q, len - 1));
     const unsigned ck = unsigned(min(c0, dk - 4)), cv = unsigned(min(c0, dv - 4));
     const int64_t off = int64_t(ci) * C;
-    const char* kc = reinterpret_cast<const char*>(kbase + off * sk);
-    const char* vc = reinterpret_cast<const char*>(vbase + off * sv);
-    const char* ac = reinterpret_cast<const char*>(abase + off * sk);
+    kp = reinterpret_cast<const char*>(kbase + off * sk) + (t * unsigned(sk) + ck) * 2u;
+    vp = reinterpret_cast<const char*>(vbase + off * sv) + (t * unsigned(sv) + cv) * 2u;
+    ap = reinterpret_cast<const char*>(abase + off * sk) + (t * unsigned(sk) + ck) * 4u;
+  };
+  auto load_a = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const unsigned t = unsigned(min(t4 + q, len - 1));
-      st.k[q] = *reinterpret_cast<const uint2*>(kc + (t * unsigned(sk) + ck) * 2u);
-      st.v[q] = *reinterpret_cast<const uint2*>(vc + (t * unsigned(sv) + cv) * 2u);
-      st.a[q] = *reinterpret_cast<const float4*>(ac + (t * unsigned(sk) + ck) * 4u);
+    for (int q = 0; q < 8; ++q) {
+      const char *kp, *vp, *ap;
+      tok_ptrs(ci, q, kp, vp, ap);
+      st.a[q] = *reinterpret_cast<const float4*>(ap);
     }
   };
+  auto load_k = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const char *kp, *vp, *ap;
+      tok_ptrs(ci, q, kp, vp, ap);
+      st.k[q] = *reinterpret_cast<const uint2*>(kp);
+    }
+  };
+  auto load_v = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const char *kp, *vp, *ap;
+      tok_ptrs(ci, q, kp, vp, ap);
+      st.v[q] = *reinterpret_cast<const uint2*>(vp);
+    }
+  };
+  auto load_all = [&](auto SET, int ci) __attribute__((always_inline)) {
+    DiagRegs& st = regs[decltype(SET)::value];
+    load_a(st, ci);
+    load_k(st, ci);
+    load_v(st, ci);
+  };
 
-  auto stage_t = [&](auto TAIL, const DiagRegs& st, int ci, char* sb) __attribute__((always_inline)) {
+  // stage chunk cs from register set SET into buffer cs & 1, reloading the
+  // set with chunk cl as each part of it is used up
+  auto stage_t = [&](auto TAIL, auto SET, int cs, int cl) __attribute__((always_inline)) {
     constexpr bool tail = decltype(TAIL)::value;
+    DiagRegs& st = regs[decltype(SET)::value];
+    char* sb = smem + (cs & 1) * L::TOTAL;
     __bf16* Kh = reinterpret_cast<__bf16*>(sb + L::KH);
     __bf16* Kl = reinterpret_cast<__bf16*>(sb + L::KL);
     __bf16* Vt = reinterpret_cast<__bf16*>(sb + L::VT);
     float* gm = reinterpret_cast<float*>(sb + L::GM);
-    int r, c0, t4;
-    lane_map(r, c0, t4);
+    int r, c0, t0;
+    lane_map(r, c0, t0);
     const int lane = opaque_i(threadIdx.x) & 63;
-    const int len = chunk_len(u, ci);
+    const int len = chunk_len(u, cs);
+    float w[4][8];
     float gv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float gg[4], l[4];
+      float gg[8], l[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = !tail || t4 + q < len;
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = !tail || t0 + q < len;
         const float x = st.a[q][j];
         gg[q] = ok ? x : 1.f;
         l[q] = ok ? log2_gate(x) : 0.f;
       }
-      const float quad = (l[0] + l[1]) + (l[2] + l[3]);
+      const float tot = ((l[0] + l[1]) + (l[2] + l[3])) + ((l[4] + l[5]) + (l[6] + l[7]));
       // sum over the rows r' >= r of the block (same lane position)
-      float incl = quad;
+      float incl = tot;
 #pragma unroll
-      for (int s = 1; s < RW; s <<= 1) {
-        const float o = __shfl(incl, lane + s * PL, 64);
-        incl += (r + s < RW) ? o : 0.f;
+      for (int s2 = 1; s2 < RW; s2 <<= 1) {
+        const float o = __shfl(incl, lane + s2 * PL, 64);
+        incl += (r + s2 < RW) ? o : 0.f;
       }
-      const float base = exp2_w(incl - quad);  // product of the gates of later rows
-      float w[4];
-      w[3] = base;
-      w[2] = base * gg[3];
-      w[1] = w[2] * gg[2];
-      w[0] = w[1] * gg[1];
+      w[j][7] = exp2_w(incl - tot);  // product of the gates of later rows
+#pragma unroll
+      for (int q = 6; q >= 0; --q) w[j][q] = w[j][q + 1] * gg[q + 1];
       if (tail) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (t4 + q >= len) w[q] = 0.f;
+        for (int q = 0; q < 8; ++q)
+          if (t0 + q >= len) w[j][q] = 0.f;
       }
       lam[j] += incl;  // the block total on rows r == 0, which hold lambda
       gv[j] = exp2_w(incl);
-      // channel c0 + j: Kw hi / lo and V of tokens t4 .. t4+3
-      float kw[4];
+    }
+    if (r == 0) *reinterpret_cast<float4*>(gm + tb * DP + c0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+    load_a(st, cl);
+    // channel c0 + j: Kw hi / lo of tokens t0 .. t0+7
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned word = (j < 2) ? st.k[q].x : st.k[q].y;
-        kw[q] = w[q] * ((j & 1) ? bf_hi(word) : bf_lo(word));
+    for (int j = 0; j < 4; ++j) {
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const unsigned w0 = (j < 2) ? st.k[q].x : st.k[q].y;
+        const unsigned w1 = (j < 2) ? st.k[q + 1].x : st.k[q + 1].y;
+        const float x0 = w[j][q] * ((j & 1) ? bf_hi(w0) : bf_lo(w0));
+        const float x1 = w[j][q + 1] * ((j & 1) ? bf_hi(w1) : bf_lo(w1));
+        split2(x0, x1, hi[q / 2], lo[q / 2]);
       }
-      unsigned h01, l01, h23, l23;
-      split2(kw[0], kw[1], h01, l01);
-      split2(kw[2], kw[3], h23, l23);
-      const int at = (c0 + j) * KT + t4;
-      *reinterpret_cast<uint2*>(Kh + at) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2*>(Kl + at) = make_uint2(l01, l23);
+      const int at = ch_at<KT>(c0 + j, t0);
+      *reinterpret_cast<uint4*>(Kh + at) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(Kl + at) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    load_k(st, cl);
+    // channel c0 + j: V of tokens t0 .. t0+7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const unsigned v01 = (j < 2) ? __builtin_amdgcn_perm(st.v[1].x, st.v[0].x, sel)
-                                   : __builtin_amdgcn_perm(st.v[1].y, st.v[0].y, sel);
-      const unsigned v23 = (j < 2) ? __builtin_amdgcn_perm(st.v[3].x, st.v[2].x, sel)
-                                   : __builtin_amdgcn_perm(st.v[3].y, st.v[2].y, sel);
-      *reinterpret_cast<uint2*>(Vt + at) = make_uint2(v01, v23);
+      unsigned pv[4];
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const unsigned v0 = (j < 2) ? st.v[q].x : st.v[q].y;
+        const unsigned v1 = (j < 2) ? st.v[q + 1].x : st.v[q + 1].y;
+        pv[q / 2] = __builtin_amdgcn_perm(v1, v0, sel);
+      }
+      *reinterpret_cast<uint4*>(Vt + ch_at<KT>(c0 + j, t0)) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
     }
-    if (r == 0) *reinterpret_cast<float4*>(gm + tg * DP + c0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+    load_v(st, cl);
   };
-  auto stage = [&](auto SET, int ci, int buf) __attribute__((always_inline)) {
-    char* sb = smem + buf * L::TOTAL;
-    if (chunk_len(u, ci) == C)
-      stage_t(std::false_type(), regs[decltype(SET)::value], ci, sb);
+  auto stage = [&](auto SET, int cs, int cl) __attribute__((always_inline)) {
+    if (chunk_len(u, cs) == C)
+      stage_t(std::false_type(), SET, cs, cl);
     else
-      stage_t(std::true_type(), regs[decltype(SET)::value], ci, sb);
+      stage_t(std::true_type(), SET, cs, cl);
   };
 
-  struct Frags {
-    bf16x8 ah[C / 16], al[C / 16], vb[TPW][C / 16];
-    int buf;
-  };
-  auto frags = [&](int, int buf) __attribute__((always_inline)) {
-    Frags fr;
-    fr.buf = buf;
-    if (has_tiles) {
-      const char* sb = smem + buf * L::TOTAL;
-      const __bf16* Kh = reinterpret_cast<const __bf16*>(sb + L::KH);
-      const __bf16* Kl = reinterpret_cast<const __bf16*>(sb + L::KL);
-      const __bf16* Vt = reinterpret_cast<const __bf16*>(sb + L::VT);
-      const int lane = opaque_i(threadIdx.x) & 63;
-      const int g = lane >> 5, cl = lane & 31;
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        const int ka = (mt * 32 + cl) * KT + 16 * ks + 8 * g;
-        fr.ah[ks] = lds_load8(Kh + ka);
-        fr.al[ks] = lds_load8(Kl + ka);
-#pragma unroll
-        for (int k = 0; k < TPW; ++k)
-          fr.vb[k][ks] = lds_load8(Vt + ((nt0 + k) * 32 + cl) * KT + 16 * ks + 8 * g);
+  if (n > 0) {
+    load_all(I0(), 0);
+    load_all(I1(), min(1, last));
+    stage(I0(), 0, min(2, last));
+    __syncthreads();  // chunk 0 staged
+    // step j: stage chunk j+1 (register set (j+1) & 1, buffer (j+1) & 1),
+    // reloading the set with chunk j+3; one barrier
+    auto step = [&](auto D, int cj) __attribute__((always_inline)) {
+      using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
+      if (cj + 1 < n) {
+        stage(DN(), cj + 1, min(cj + 3, last));
+      } else {
+        // keep the load sequence of every step the same (see the header)
+        load_all(DN(), last);
       }
+      __syncthreads();
+    };
+    int cj = 0;
+#pragma unroll 1
+    for (; cj + 2 <= n; cj += 2) {
+      step(I0(), cj);
+      step(I1(), cj + 1);
     }
-    return fr;
-  };
-  // per block: S <- gamma_block (.) S (rows), then the block's K-steps
-  auto contract = [&](const Frags& fr, int) __attribute__((always_inline)) {
-    if (!has_tiles) return;
-    const float* gm = reinterpret_cast<const float*>(smem + fr.buf * L::TOTAL + L::GM);
-    const int g = (opaque_i(threadIdx.x) & 63) >> 5;
-#pragma unroll
-    for (int bi = 0; bi < TG; ++bi) {
-      float f[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const float4 x = *reinterpret_cast<const float4*>(gm + bi * DP + mt * 32 + 8 * qq + 4 * g);
-        f[4 * qq] = x.x; f[4 * qq + 1] = x.y; f[4 * qq + 2] = x.z; f[4 * qq + 3] = x.w;
-      }
-#pragma unroll
-      for (int k = 0; k < TPW; ++k)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[k][r] *= f[r];
-#pragma unroll
-      for (int ks = bi * (BT / 16); ks < (bi + 1) * (BT / 16); ++ks)
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          S[k] = mfma32(fr.al[ks], fr.vb[k][ks], S[k]);
-          S[k] = mfma32(fr.ah[ks], fr.vb[k][ks], S[k]);
-        }
-    }
-  };
-
-  run_pipeline<SD_DEPTH_DIAG>(u.n_chunks, load, stage, frags, contract);
-
-  if (has_tiles) write_tiles<TPW>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, nt0, dk, dv);
+    if (cj < n) step(I0(), cj);
+  }
   // lambda: rows r == 0 hold their block's totals; the TG blocks of each
   // channel are summed through LDS (free after the pipeline's last barrier)
-  int r, c0, t4;
-  lane_map(r, c0, t4);
+  int r, c0, t0;
+  lane_map(r, c0, t0);
+  (void)t0;
   float* lb = reinterpret_cast<float*>(smem);
-  if (r == 0) *reinterpret_cast<float4*>(lb + tg * DP + c0) = make_float4(lam[0], lam[1], lam[2], lam[3]);
   __syncthreads();
-  if (r == 0 && tg == 0 && c0 < dk) {
+  if (r == 0) *reinterpret_cast<float4*>(lb + tb * DP + c0) = make_float4(lam[0], lam[1], lam[2], lam[3]);
+  __syncthreads();
+  if (r == 0 && tb == 0 && c0 < dk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float s = 0.f;
