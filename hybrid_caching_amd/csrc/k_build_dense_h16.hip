@@ -225,27 +225,36 @@ __device__ __forceinline__ f16x4 h4(float x0, float x1, float x2, float x3) {
 // Staging of K / V rows: 16 items of 16 bytes per lane cover a chunk --
 // item i is row (lane >> 4) + 4 i, channels 8 (lane & 15) .. +7 -- so each
 // load instruction reads four whole 256-byte rows.  Rows past the chunk's end
-// read its last row (a valid address) and are zeroed when staged; channels
-// past the head size read a valid group and are zeroed too.
+// read its last row (a valid address) and are staged as they are: beta is
+// zero on them, so their rows and columns of A, A', U and W, and their rows of
+// N and M, are exactly zero, and a finite key or value row only ever meets
+// zero coefficients.  Channels past the head size read a valid group and are
+// zeroed (they would enter K K^T and the products over channels).
 template <int NI>
 __device__ __forceinline__ void load_rows(uint4 (&pr)[NI], const __bf16* base, int HD, int len,
-                                          int i0, int ni, int lane) {
+                                          int i0, int lane) {
+  if (len == C) {  // whole chunk: one row address, item offsets are uniform
+    const __bf16* p = base + (lane >> 4) * HD;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    if (i < ni) pr[i] = gload_u4(base + min((lane >> 4) + 4 * (i0 + i), len - 1) * HD);
+    for (int i = 0; i < NI; ++i) pr[i] = gload_u4(p + 4 * (i0 + i) * HD);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) pr[i] = gload_u4(base + min((lane >> 4) + 4 * (i0 + i), len - 1) * HD);
+  }
 }
 template <int NI>
-__device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI], int len, int d,
-                                           int i0, int ni, int lane) {
+__device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI], int d, int i0, int lane) {
   const int cg = lane & 15;
-  const bool full = len == C && d == DP, okc = 8 * cg < d;
+  _Float16* row = dst + (lane >> 4) * RLD + 8 * cg;
+  if (d == DP) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    if (i < ni) {
-      const int t = (lane >> 4) + 4 * (i0 + i);
-      const uint4 w = bf2h(pr[i]);
-      *reinterpret_cast<uint4*>(dst + t * RLD + 8 * cg) = full ? w : pick_u4(okc && t < len, w);
-    }
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4*>(row + 4 * (i0 + i) * RLD) = bf2h(pr[i]);
+  } else {
+    const bool okc = 8 * cg < d;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<uint4*>(row + 4 * (i0 + i) * RLD) = pick_u4(okc, bf2h(pr[i]));
+  }
 }
 
 // G_ss = K_s K_s^T of sub-chunk s from the K rows of a chunk (fp32).  G is
@@ -464,9 +473,8 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   };
 
   // W seeds of both sub-chunks of chunk j: M_s = A'_s V_s (this wave's
-  // columns); then (every other chunk) re-normalise this wave's columns of
-  // That by a power of two -- branch-free, so that no copy of the state is made
-  auto seeds_and_scale = [&](int j, auto rescale) {
+  // columns)
+  auto seeds = [&](int j) {
     const _Float16* Ap = AB0 + (j & 1) * AB_HALFS + 64 * A_LD;
     // V^T fragment: lane (g, n) needs V[token 16 kk + 8 g + 0..7][32 c + n]
     const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 32 * c + tr_col;
@@ -482,7 +490,10 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
       }
       PM[s] = acc;
     }
-    if (!decltype(rescale)::value) return;
+  };
+  // re-normalise this wave's columns of That by a power of two -- branch-free,
+  // so that no copy of the state is made
+  auto renorm = [&]() {
     float m = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -507,27 +518,32 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   if (n >= 1) {
     __syncthreads();  // cycle 1, phase A
     __syncthreads();  //          phase B
-    seeds_and_scale(0, std::true_type{});
+    seeds(0);
+    renorm();
     chain_sub(0, 0);
     int ci = 2;
+    // (the re-normalisation every other chunk sits at the end of phase A:
+    // between the same two chain steps as at the start of phase B, but in
+    // the phase where the consumers have the shorter part of the work)
 #pragma unroll 1
     for (; ci + 1 <= n; ci += 2) {
       __syncthreads();  // phase A
       chain_sub(1, ci - 2);
       __syncthreads();  // phase B
-      seeds_and_scale(ci - 1, std::false_type{});
+      seeds(ci - 1);
       chain_sub(0, ci - 1);
       __syncthreads();  // phase A
       chain_sub(1, ci - 1);
+      renorm();
       __syncthreads();  // phase B
-      seeds_and_scale(ci, std::true_type{});
+      seeds(ci);
       chain_sub(0, ci);
     }
     if (ci <= n) {
       __syncthreads();  // phase A
       chain_sub(1, ci - 2);
       __syncthreads();  // phase B
-      seeds_and_scale(ci - 1, std::false_type{});
+      seeds(ci - 1);
       chain_sub(0, ci - 1);
     }
     __syncthreads();  // cycle n+1, phase A
@@ -697,15 +713,15 @@ __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
   const int i0 = 8 * pw;
   uint4 pr[8];
   auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
-  if (n > 0) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, 8, lane);
+  if (n > 0) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, lane);
 #pragma unroll 1
   for (int ci = -1; ci <= n + 1; ++ci) {
     // ---------------- phase A: K rows of chunk ci+1, load chunk ci+2's;
     // U^T tiles 3 pw .. 3 pw + 2 of chunk ci-1
     __syncthreads();
     if (ci + 1 < n)
-      stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, chunk_len(ci + 1), dk, i0, 8, lane);
-    if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, 8, lane);
+      stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, dk, i0, lane);
+    if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, lane);
     if (ci - 1 >= 0 && ci - 1 < n) {
       const int j = ci - 1;
       ut_tiles<3>(Kb0 + (j % NKB) * (C * RLD), AB0 + (j & 1) * AB_HALFS, Uf0 + (j & 1) * UF_BYTES,
@@ -741,8 +757,8 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
     constexpr int P = decltype(par)::value;
     // ---------------- phase A: V rows of chunk ci-1, then load chunk ci's
     __syncthreads();
-    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, chunk_len(ci - 1), dv, 0, 16, lane);
-    if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), 0, 16, lane);
+    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, dv, 0, lane);
+    if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), 0, lane);
     // ---------------- phase B: gates of chunk ci+1
     __syncthreads();
     if (ci + 1 < n) {
