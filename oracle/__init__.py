@@ -15,6 +15,12 @@ module only marshals numpy arrays into it.  What each call computes:
 * ``compose``    -- S <- T_C S + S(C|0) along a chain of cached pairs.
   [same paragraph: left-multiply by T_C, then add]
 * ``naive_add``  -- S_in + sum S(C|0), the ablation.  [same paragraph]
+* ``seam_compose`` -- reuse with seam windows: before each cached pair, the
+  entry's seam tokens advance the state one token at a time and each emits
+  o_t = S_t^T q_t.  [xix.ai, paragraph on full-attention layers: the first w
+  tokens of every inner segment are left out of the cache and recomputed on
+  reuse; linear layers advance the running state through them and pass each
+  token's output up]
 * ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
   its definition: segments as token ranges cut into 64-token chunks, visited
   longest first; chains applied entry by entry.
@@ -64,6 +70,11 @@ def _bind(lib):
     lib.oracle_compose.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, ctypes.c_int,
                                    _i64p, _i32p, _dp, _dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_seam_compose.restype = ctypes.c_int
+    lib.oracle_seam_compose.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp,
+                                        ctypes.c_int, _i64p, _i32p, _i64p, ctypes.c_int64, _dp,
+                                        _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.oracle_naive_add.restype = ctypes.c_int
     lib.oracle_naive_add.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int64, _dp, ctypes.c_int, _i64p, _i32p, _dp, _dp,
@@ -204,6 +215,39 @@ def naive_add(S, chain_offsets, chain_idx, S_in=None, *, threads=None, lib=None)
     if rc != 0:
         raise ValueError("oracle_naive_add rejected its arguments")
     return S_out
+
+
+def seam_compose(form, lam, That, S, chain_offsets, chain_idx, seam_offsets, q, k, v, alpha,
+                 beta, S_in=None, *, literal=False, threads=None, lib=None):
+    """Reuse with seam windows.
+
+    Pool as in ``compose``.  Chain entry c (over all requests, in order) has
+    the seam tokens [seam_offsets[c], seam_offsets[c+1]) of q, k: [B, NS, H, dk],
+    v: [B, NS, H, dv], alpha: [B, NS, H] (diag: [B, NS, H, dk]), beta: [B, NS, H]
+    or None.  Each entry advances the state through its seam tokens (emitting
+    o_t = S_t^T q_t) and then applies its pair.  Returns (S_out [R, B, H, dk, dv],
+    O [B, NS, H, dv]).
+    """
+    lib = lib or load()
+    lam, S = _f64(lam), _f64(S)
+    That = _f64(That) if form == DENSE else None
+    q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
+    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    P, B, H, dk, dv = S.shape
+    NS = k.shape[1]
+    off, idx = _chains(chain_offsets, chain_idx)
+    soff = np.ascontiguousarray(np.asarray(seam_offsets, dtype=np.int64))
+    R = len(off) - 1
+    S_in = _f64(S_in)
+    S_out = np.zeros((R, B, H, dk, dv))
+    O = np.zeros((B, NS, H, dv))
+    rc = lib.oracle_seam_compose(form, int(bool(literal)), B, H, dk, dv, P, _ptr(lam), _ptr(That),
+                                 _ptr(S), R, _ptr(off, _i64p), _ptr(idx, _i32p), _ptr(soff, _i64p),
+                                 NS, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(S_in), _ptr(S_out), _ptr(O), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_seam_compose rejected its arguments")
+    return S_out, O
 
 
 CHUNK = 64

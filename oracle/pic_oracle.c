@@ -43,6 +43,12 @@
  *     remio.ai (Japanese), same section: naive addition cannot reproduce
  *     the sequential state.]
  *
+ *  - Reuse with seam windows: the first tokens of an inner segment are
+ *    kept out of its cached pair and, on reuse, run from the running state
+ *    one by one, each emitting its output o_t = S_t^T q_t, before the pair
+ *    of the rest of the segment is applied (oracle_seam_compose, below).
+ *    [xix.ai, paragraph on full-attention layers: seam windows of w tokens.]
+ *
  *  Because T_C underflows fp32 at realistic gate values, the pair is also
  *  given in split form: lambda_C = sum_t ln(alpha_t) (per head for scalar
  *  and dense, per key channel for diagonal) and, for the dense form,
@@ -468,5 +474,147 @@ int oracle_naive_add(int B, int H, int dk, int dv, int64_t P, const double *S, i
   comp_ctx c = {ORACLE_SCALAR, B,         H,         dk,   dv,    1,    NULL, NULL,
                 S,             chain_off, chain_idx, S_in, S_out, NULL, NULL};
   run_items(compose_unit, &c, (int64_t)n_req * B * H, n_threads);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* reuse with seam windows                                             */
+/* ------------------------------------------------------------------ */
+/* On reuse, the first few tokens of a cached segment (its seam window) are
+ * not part of the cached pair: they are run again from the running state,
+ * token by token, and each of them emits its layer output; then the pair of
+ * the rest of the segment is applied.
+ *   [xix.ai HYPIC article (French), paragraph on full-attention layers: a
+ *    window of w tokens (8 by default) at the start of every inner segment is
+ *    left out of the cache and recomputed under the full prefix on reuse;
+ *    the linear layers advance the running state through these tokens and
+ *    pass each token's per-layer output up to the attention layer above.]
+ * The output of a token is read from the state after its own update (the
+ * usual linear-attention readout):  o_t = S_t^T q_t,  o_t in R^{dv}.
+ *
+ * Chain entry c of request r: first its seam tokens
+ * [seam_off[c], seam_off[c+1]) of the seam arrays, then pool pair idx[c].
+ * Seam inputs use the build layout with N = NS (the seam token count):
+ * q, k [B][NS][H][dk], v [B][NS][H][dv], alpha, beta as in the build.
+ * O [B][NS][H][dv].  literal = 1 applies each seam token as an explicit
+ * transition matrix; 0 uses the family's structure (as in the build). */
+typedef struct {
+  comp_ctx cc;
+  build_ctx tok; /* the seam inputs (offsets unused) */
+  int literal;
+  const int64_t *seam_off;
+  const double *q;
+  double *O;
+} seam_ctx;
+
+static void seam_token(const seam_ctx *sc, int b, int h, int64_t t, double *S, double *Tt,
+                       double *tmp) {
+  const build_ctx *c = &sc->tok;
+  const int dk = c->dk, dv = c->dv, form = c->form;
+  const double *kt = k_at(c, b, t, h), *vt = v_at(c, b, t, h), *at = a_at(c, b, t, h);
+  const double bt = b_at(c, b, t, h);
+  if (sc->literal) {
+    token_transition(form, dk, kt, at, bt, Tt, NULL);
+    matmul(dk, dk, dv, Tt, S, tmp);
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[i * dv + j] = tmp[i * dv + j] + bt * kt[i] * vt[j];
+  } else if (form == ORACLE_DENSE) {
+    /* S <- a (S - b k (k^T S)) + b k v^T */
+    for (int j = 0; j < dv; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < dk; ++i) s += kt[i] * S[i * dv + j];
+      tmp[j] = s;
+    }
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j)
+        S[i * dv + j] = at[0] * (S[i * dv + j] - bt * kt[i] * tmp[j]) + bt * kt[i] * vt[j];
+  } else {
+    /* scalar: every row decays by a[0]; diagonal: row i by a[i] */
+    for (int i = 0; i < dk; ++i) {
+      const double ai = (form == ORACLE_DIAG) ? at[i] : at[0];
+      for (int j = 0; j < dv; ++j) S[i * dv + j] = ai * S[i * dv + j] + kt[i] * vt[j];
+    }
+  }
+  /* o_t = S_t^T q_t */
+  const double *qt = sc->q + (((int64_t)b * c->N + t) * c->H + h) * dk;
+  double *ot = sc->O + (((int64_t)b * c->N + t) * c->H + h) * dv;
+  for (int j = 0; j < dv; ++j) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += qt[i] * S[i * dv + j];
+    ot[j] = s;
+  }
+}
+
+static void seam_unit(void *vctx, int64_t item) {
+  const seam_ctx *sc = (const seam_ctx *)vctx;
+  const comp_ctx *c = &sc->cc;
+  const int dk = c->dk, dv = c->dv, form = c->form;
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int64_t r = item / BH, bh = item % BH;
+  const int b = (int)(bh / c->H), h = (int)(bh % c->H);
+  double *S = c->S_out + item * dk * dv;
+  if (c->S_in)
+    memcpy(S, c->S_in + item * dk * dv, sizeof(double) * dk * dv);
+  else
+    memset(S, 0, sizeof(double) * dk * dv);
+  const int dmax = dk > dv ? dk : dv;
+  double *Tt = (double *)malloc(sizeof(double) * dk * dk);
+  double *tmp = (double *)malloc(sizeof(double) * dk * dmax);
+  double *Tp = (double *)malloc(sizeof(double) * dk * dk);
+  for (int64_t e = c->off[r]; e < c->off[r + 1]; ++e) {
+    for (int64_t t = sc->seam_off[e]; t < sc->seam_off[e + 1]; ++t)
+      seam_token(sc, b, h, t, S, Tt, tmp);
+    /* then the cached pair of the rest of the segment: S <- T_p S + S_p */
+    const int64_t unit = (int64_t)c->idx[e] * BH + bh;
+    const int nlam = (form == ORACLE_DIAG) ? dk : 1;
+    const double *lp = c->lam + unit * nlam;
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dk; ++j) {
+        const double ungated = (form == ORACLE_DENSE) ? c->That[unit * dk * dk + i * dk + j]
+                                                      : (double)(i == j);
+        Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;
+      }
+    matmul(dk, dk, dv, Tp, S, tmp);
+    const double *Sp = c->S + unit * dk * dv;
+    for (int i = 0; i < dk * dv; ++i) S[i] = tmp[i] + Sp[i];
+  }
+  free(Tt);
+  free(tmp);
+  free(Tp);
+}
+
+int oracle_seam_compose(int form, int literal, int B, int H, int dk, int dv, int64_t P,
+                        const double *lam, const double *That, const double *S, int n_req,
+                        const int64_t *chain_off, const int32_t *chain_idx,
+                        const int64_t *seam_off, int64_t NS, const double *q, const double *k,
+                        const double *v, const double *alpha, const double *beta,
+                        const double *S_in, double *S_out, double *O, int n_threads) {
+  if (form < 0 || form > 2 || dk <= 0 || dv <= 0 || check_chains(P, n_req, chain_off, chain_idx))
+    return -1;
+  if (form == ORACLE_DENSE && That == NULL) return -1;
+  const int64_t total = chain_off[n_req];
+  if (seam_off[0] != 0 || seam_off[total] != NS) return -1;
+  for (int64_t e = 0; e < total; ++e)
+    if (seam_off[e + 1] < seam_off[e]) return -1;
+  seam_ctx sc;
+  memset(&sc, 0, sizeof(sc));
+  comp_ctx cc = {form,      B,         H,    dk,    dv,   0,    lam, That,
+                 S,         chain_off, chain_idx, S_in, S_out, NULL, NULL};
+  sc.cc = cc;
+  sc.tok.form = form;
+  sc.tok.B = B;
+  sc.tok.H = H;
+  sc.tok.dk = dk;
+  sc.tok.dv = dv;
+  sc.tok.N = NS;
+  sc.tok.k = k;
+  sc.tok.v = v;
+  sc.tok.alpha = alpha;
+  sc.tok.beta = beta;
+  sc.literal = literal;
+  sc.seam_off = seam_off;
+  sc.q = q;
+  sc.O = O;
+  run_items(seam_unit, &sc, (int64_t)n_req * B * H, n_threads);
   return 0;
 }

@@ -11,6 +11,22 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_seam_pins as seam_pins
+
+_SEAM_OUT = """  /* o_t = S_t^T q_t */
+  const double *qt = sc->q + (((int64_t)b * c->N + t) * c->H + h) * dk;
+  double *ot = sc->O + (((int64_t)b * c->N + t) * c->H + h) * dv;
+  for (int j = 0; j < dv; ++j) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += qt[i] * S[i * dv + j];
+    ot[j] = s;
+  }
+"""
+_SEAM_UPDATE_START = "  if (sc->literal) {\n    token_transition(form, dk, kt, at, bt, Tt, NULL);"
+_SEAM_LOOP = """    for (int64_t t = sc->seam_off[e]; t < sc->seam_off[e + 1]; ++t)
+      seam_token(sc, b, h, t, S, Tt, tmp);
+"""
+_SEAM_PAIR_END = "    for (int i = 0; i < dk * dv; ++i) S[i] = tmp[i] + Sp[i];\n  }\n  free(Tt);"
 
 MUTANTS = [
     ("dense: gate dropped from the state update",
@@ -58,6 +74,33 @@ MUTANTS = [
     ("value rows read with the key stride",
      "return c->v + (((int64_t)b * c->N + t) * c->H + h) * c->dv;",
      "return c->v + (((int64_t)b * c->N + t) * c->H + h) * c->dk;"),
+    ("seam: output read before the token's update",
+     [_SEAM_OUT, _SEAM_UPDATE_START],
+     ["", _SEAM_OUT.replace("  const double *qt", "  {\n  const double *qt") + "  }\n"
+      + _SEAM_UPDATE_START]),
+    ("seam: window applied after the entry's pair",
+     [_SEAM_LOOP, _SEAM_PAIR_END],
+     ["", "    for (int i = 0; i < dk * dv; ++i) S[i] = tmp[i] + Sp[i];\n" + _SEAM_LOOP
+      + "  }\n  free(Tt);"]),
+    ("seam: output transposed",
+     "for (int i = 0; i < dk; ++i) s += qt[i] * S[i * dv + j];",
+     "for (int i = 0; i < dk; ++i) s += qt[i] * S[(j * dk + i) % (dk * dv)];"),
+    ("seam: queries read with the value stride",
+     "const double *qt = sc->q + (((int64_t)b * c->N + t) * c->H + h) * dk;",
+     "const double *qt = sc->q + (((int64_t)b * c->N + t) * c->H + h) * dv;"),
+    ("seam: first token of each window skipped",
+     "for (int64_t t = sc->seam_off[e]; t < sc->seam_off[e + 1]; ++t)",
+     "for (int64_t t = sc->seam_off[e] + (sc->seam_off[e + 1] > sc->seam_off[e]);"
+     " t < sc->seam_off[e + 1]; ++t)"),
+    ("seam: dense erase term dropped",
+     "S[i * dv + j] = at[0] * (S[i * dv + j] - bt * kt[i] * tmp[j]) + bt * kt[i] * vt[j];",
+     "S[i * dv + j] = at[0] * S[i * dv + j] + bt * kt[i] * vt[j];"),
+    ("seam: diagonal gate of channel 0 for every row",
+     "const double ai = (form == ORACLE_DIAG) ? at[i] : at[0];",
+     "const double ai = at[0];"),
+    ("seam: pair gate scale dropped",
+     "Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;",
+     "Tp[i * dk + j] = ungated;"),
 ]
 
 
@@ -79,6 +122,16 @@ def _pin_calls():
               pins.test_p5_diag_closed_form, pins.test_p9_delta_rule_retrieval,
               pins.test_p11_one_hot_closed_form, pins.test_p12_permutation_chain,
               lambda: pins.test_p2_identity_dense(False)]
+    for form in (pins.SCALAR, pins.DIAG, pins.DENSE):
+        calls += [
+            lambda f=form: seam_pins.test_seam_split_equals_unsplit(f, False, [7, 9, 5], [0, 3, 3]),
+            lambda f=form: seam_pins.test_seam_split_equals_unsplit(f, True, [4, 10, 3, 8],
+                                                                    [0, 8, 8, 2]),
+            lambda f=form: seam_pins.test_seam_exact_rational(f, 0),
+            lambda f=form: seam_pins.test_seam_empty_windows_equal_compose(f),
+            lambda f=form: seam_pins.test_seam_queries_only_reach_outputs(f),
+        ]
+    calls.append(seam_pins.test_seam_delta_rule_retrieval)
     return calls
 
 
@@ -103,8 +156,11 @@ def test_real_oracle_passes_every_pin():
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, old, new, tmp_path):
     src = open(oracle._SRC, encoding="utf-8").read()
-    assert src.count(old) >= 1, f"mutation target not found: {name}"
-    mutated = src.replace(old, new, 1)
+    olds, news = (old, new) if isinstance(old, list) else ([old], [new])
+    mutated = src
+    for o, n in zip(olds, news):
+        assert mutated.count(o) == 1, f"mutation target not found once: {name}"
+        mutated = mutated.replace(o, n, 1)
     path = tmp_path / "mutant.c"
     path.write_text(mutated, encoding="utf-8")
     so = str(tmp_path / "libmutant.so")
