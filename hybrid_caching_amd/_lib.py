@@ -42,6 +42,11 @@ SIGNATURES = {
                          _sz, _p]),
     "pic_validate_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz]),
     "pic_naive_add": (_i, [_i, _i, _i, _i, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "pic_compose_seams_workspace": (_sz, [_i32, _i64]),
+    "pic_validate_compose_seams": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p,
+                                        _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "pic_compose_seams": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _i64,
+                               _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "pic_materialize_T": (_i, [_i, _i64, _i, _p, _p, _p, _p]),
     "pic_plan_dump": (_i, [_i, _i32, _p, _p, _i64, _p, _i64]),
 }
@@ -209,6 +214,47 @@ def pic_naive_add(pool_S0, chain_offsets, chain_idx, S_in=None, *, out=None):
                            _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "pic_naive_add")
     return out
+
+
+def pic_compose_seams(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, chain_idx,
+                      seam_offsets, q, k, v, alpha, beta=None, S_in=None, *, out=None,
+                      out_O=None):
+    """Reuse with seam windows: each chain entry first runs its seam tokens
+    [seam_offsets[c], seam_offsets[c+1]) through the state (writing
+    O[t] = S^T q_t after each token), then applies its pair.
+
+    Pool and chains as in ``pic_compose``; q, k: [B, NS, H, dk], v: [B, NS, H, dv]
+    (all bf16 or all fp32); alpha fp32 [B, NS, H] (diag [B, NS, H, dk]); beta
+    fp32 [B, NS, H] or None (dense only).  Returns (S_out [R, B, H, dk, dv],
+    O [B, NS, H, dv])."""
+    lib = load()
+    P, B, H, dk, dv = pool_S0.shape
+    for t, n in ((pool_log_scale, "pool_log_scale"), (pool_T_hat, "pool_T_hat"),
+                 (pool_S0, "pool_S0"), (S_in, "S_in"), (out, "out"), (alpha, "alpha"),
+                 (beta, "beta"), (out_O, "out_O")):
+        _need(t, n, torch.float32)
+    if not (q.dtype == k.dtype == v.dtype) or k.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k and v must all be bfloat16 or all float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, None)
+    dt = DT_BF16 if k.dtype == torch.bfloat16 else DT_F32
+    NS = k.shape[1]
+    off, off_p = _host_i64(chain_offsets)
+    idx, idx_p = _host_i32(chain_idx)
+    soff, soff_p = _host_i64(seam_offsets)
+    R = len(off) - 1
+    dev = pool_S0.device
+    if out is None:
+        out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    if out_O is None:
+        out_O = torch.empty((B, NS, H, dv), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.pic_compose_seams_workspace(R, int(off[-1])), dev)
+    rc = lib.pic_compose_seams(form, dt, B, H, dk, dv, P, _ptr(pool_log_scale),
+                               _ptr(pool_T_hat), _ptr(pool_S0), R, off_p, idx_p, soff_p, NS,
+                               _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S_in),
+                               _ptr(out), _ptr(out_O), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "pic_compose_seams")
+    return out, out_O
 
 
 def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):

@@ -183,6 +183,14 @@ size_t compose_ws_bytes(int32_t n_req, int64_t total) {
          align_up(sizeof(int32_t) * size_t(std::max<int64_t>(total, 1)));
 }
 
+// Reuse with seams: the compose tables, then the seam offsets (int64 each).
+static_assert(pic::kMaxSeam == PIC_MAX_SEAM, "seam window limit of the header");
+
+size_t compose_seams_ws_bytes(int32_t n_req, int64_t total) {
+  if (n_req < 0 || total < 0) return 0;
+  return compose_ws_bytes(n_req, total) + align_up(sizeof(int64_t) * (size_t(total) + 1));
+}
+
 int check_chains(int64_t pool_size, int32_t n_req, const int64_t* off, const int32_t* idx) {
   if (n_req < 0) return fail(PIC_ERR_DIMS, "n_req (%d) must be >= 0", n_req);
   if (pool_size < 0) return fail(PIC_ERR_DIMS, "pool_size must be >= 0");
@@ -484,6 +492,119 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
   if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, a)) return rc;
   hipError_t e = pic::launch_compose_elementwise(a, true, s);
   if (e != hipSuccess) return hip_fail(e, "launching the naive-add kernel");
+  return ok();
+}
+
+/* ------------------------------------------------------ compose with seams */
+
+size_t pic_compose_seams_workspace(int32_t n_req, int64_t chain_total) {
+  return compose_seams_ws_bytes(n_req, chain_total);
+}
+
+int pic_validate_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                               int64_t pool_size, const float* pool_log_scale,
+                               const float* pool_T_hat, const float* pool_S0, int32_t n_req,
+                               const int64_t* chain_offsets, const int32_t* chain_idx,
+                               const int64_t* seam_offsets, int64_t n_seam, const void* q,
+                               const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* S_in, const float* S_out,
+                               const float* O_out, const void* workspace,
+                               size_t workspace_bytes) {
+  (void)S_in;
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
+  if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (n_seam < 0) return fail(PIC_ERR_DIMS, "n_seam must be >= 0");
+  if (mul_sizes({pool_size, batch, heads, dk, std::max(dk, dv)}) < 0 ||
+      mul_sizes({n_req, batch, heads, dk, dv}) < 0 ||
+      mul_sizes({batch, n_seam, heads, std::max(dk, dv)}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (int rc = check_chains(pool_size, n_req, chain_offsets, chain_idx)) return rc;
+  const int64_t total = chain_offsets[n_req];
+  if (!seam_offsets) return fail(PIC_ERR_NULL, "seam_offsets is NULL");
+  if (seam_offsets[0] != 0)
+    return fail(PIC_ERR_OFFSETS, "seam_offsets[0] = %lld, must be 0", (long long)seam_offsets[0]);
+  for (int64_t c = 0; c < total; ++c) {
+    const int64_t w = seam_offsets[c + 1] - seam_offsets[c];
+    if (w < 0) return fail(PIC_ERR_OFFSETS, "seam_offsets decrease at chain entry %lld", (long long)c);
+    if (w > pic::kMaxSeam)
+      return fail(PIC_ERR_DIMS, "seam window of chain entry %lld has %lld tokens (at most %d)",
+                  (long long)c, (long long)w, pic::kMaxSeam);
+  }
+  if (seam_offsets[total] != n_seam)
+    return fail(PIC_ERR_OFFSETS, "seam_offsets[chain_total] = %lld, must equal n_seam = %lld",
+                (long long)seam_offsets[total], (long long)n_seam);
+  if (n_req > 0 && !S_out) return fail(PIC_ERR_NULL, "S_out is required");
+  if (total > 0 && (!pool_S0 || !pool_log_scale))
+    return fail(PIC_ERR_NULL, "pool_S0 and pool_log_scale are required");
+  if (total > 0 && form == PIC_FORM_DENSE && !pool_T_hat)
+    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense form");
+  if (form != PIC_FORM_DENSE && pool_T_hat)
+    return fail(PIC_ERR_UNSUPPORTED, "pool_T_hat must be NULL for scalar and diagonal forms");
+  if (n_seam > 0 && (!q || !k || !v || !alpha || !O_out))
+    return fail(PIC_ERR_NULL, "q, k, v, alpha and O_out are required when there are seam tokens");
+  if (int rc = check_align({pool_log_scale, pool_T_hat, pool_S0, S_in, S_out, q, k, v, alpha,
+                            beta, O_out, workspace}))
+    return rc;
+  const size_t need = compose_seams_ws_bytes(n_req, total);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                      int64_t pool_size, const float* pool_log_scale, const float* pool_T_hat,
+                      const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                      const int32_t* chain_idx, const int64_t* seam_offsets, int64_t n_seam,
+                      const void* q, const void* k, const void* v, const float* alpha,
+                      const float* beta, const float* S_in, float* S_out, float* O_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_compose_seams(form, qkv_dtype, batch, heads, dk, dv, pool_size,
+                                          pool_log_scale, pool_T_hat, pool_S0, n_req,
+                                          chain_offsets, chain_idx, seam_offsets, n_seam, q, k,
+                                          v, alpha, beta, S_in, S_out, O_out, workspace,
+                                          workspace_bytes))
+    return rc;
+  if (n_req == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = chain_offsets[n_req];
+  pic::SeamArgs a{};
+  a.c = pic::ComposeArgs{form,    batch,    heads,    dk,     dv,       pool_size,
+                         pool_log_scale, pool_T_hat, pool_S0, n_req, nullptr, nullptr,
+                         total, S_in, S_out, nullptr, nullptr, false, {}, {}};
+  a.qkv_bf16 = qkv_dtype == PIC_DT_BF16;
+  a.n_seam = n_seam;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = (form == PIC_FORM_DENSE) ? beta : nullptr;
+  a.O = O_out;
+  a.c.inl = n_req <= pic::kInlineReq && total <= pic::kInlineIdx;
+  if (a.c.inl) {
+    std::copy(chain_offsets, chain_offsets + n_req + 1, a.c.inl_off);
+    if (total > 0) std::copy(chain_idx, chain_idx + total, a.c.inl_idx);
+    std::copy(seam_offsets, seam_offsets + total + 1, a.inl_seam_off);
+  } else {
+    char* ws = static_cast<char*>(workspace);
+    int64_t* o = reinterpret_cast<int64_t*>(ws);
+    int32_t* i = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_req) + 1)));
+    int64_t* so = reinterpret_cast<int64_t*>(ws + compose_ws_bytes(n_req, total));
+    const hipError_t e = staging().copy(
+        {{o, chain_offsets, sizeof(int64_t) * (size_t(n_req) + 1)},
+         {i, chain_idx, total > 0 ? sizeof(int32_t) * size_t(total) : size_t(0)},
+         {so, seam_offsets, sizeof(int64_t) * (size_t(total) + 1)}},
+        s);
+    if (e != hipSuccess) return hip_fail(e, "copying the chain and seam tables");
+    a.c.d_chain_off = o;
+    a.c.d_chain_idx = i;
+    a.d_seam_off = so;
+  }
+  const hipError_t e = pic::launch_compose_seams(a, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the seam compose kernel");
   return ok();
 }
 

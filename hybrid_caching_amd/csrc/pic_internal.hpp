@@ -75,6 +75,28 @@ __device__ __forceinline__ int chain_entry(const ComposeArgs& a, int64_t c) {
   return a.inl ? a.inl_idx[c] : a.d_chain_idx[c];
 }
 
+// One reuse-with-seams call, after validation: a compose whose chain entries
+// each first run a window of seam tokens through the state.
+constexpr int kMaxSeam = 64;  // tokens in one seam window
+struct SeamArgs {
+  ComposeArgs c;               // pool, chains, states (the chain-pair outputs are unused)
+  bool qkv_bf16;
+  int64_t n_seam;              // seam tokens of the call (the token axis of q, k, v, ...)
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;           // dense only, may be null (= 1)
+  float* O;                    // outputs [batch][n_seam][heads][dv]
+  const int64_t* d_seam_off;   // device [chain_total + 1]
+  int64_t inl_seam_off[kInlineIdx + 1];  // when c.inl
+};
+
+// first seam token of chain entry c (c = chain_total gives the end)
+__device__ __forceinline__ int64_t seam_offset(const SeamArgs& a, int64_t c) {
+  return a.c.inl ? a.inl_seam_off[c] : a.d_seam_off[c];
+}
+
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
@@ -83,6 +105,7 @@ hipError_t launch_build_dense_ws(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
+hipError_t launch_compose_seams(const SeamArgs& a, hipStream_t s);
 // chain pair: log_scale_out (all forms) and That_out = That_pn ... That_p1 (dense)
 hipError_t launch_chain_log_scale(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_chain_T_hat(const ComposeArgs& a, hipStream_t s);

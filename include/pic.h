@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 3
+#define PIC_ABI_VERSION 4
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -228,6 +228,61 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
                   int32_t n_req, const int64_t* chain_offsets, const int32_t* chain_idx,
                   const float* S_in, float* S_out, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* ----------------------------------------------------------------------
+ * Compose with seam windows: reuse in which each cached segment's first
+ * tokens are kept out of its pair and run again from the running state.
+ *   [xix.ai HYPIC article, paragraph on full-attention layers: a window of w
+ *    tokens (8 by default) at the start of every inner segment is left out of
+ *    the cache and recomputed on reuse under the full prefix; the linear
+ *    layers advance the running state through these tokens and pass each
+ *    token's per-layer output up to the attention layer above.]
+ *
+ * For request r and each of its chain entries c (in order, as in
+ * pic_compose): first the entry's seam tokens
+ * t = seam_offsets[c] .. seam_offsets[c+1]-1, one at a time,
+ *     S <- T_t S + beta_t k_t v_t^T       (the form's token transition)
+ *     O[t] = S^T q_t                      (read after the token's update)
+ * then the entry's pair, S <- e^{log_scale_p} That_p S + S0_p.  The pair of a
+ * segment with a seam window is the pair of the tokens after the window.
+ *
+ * Arguments as for pic_compose, and:
+ * qkv_dtype     storage type of q, k, v: PIC_DT_BF16 or PIC_DT_F32
+ * seam_offsets  HOST int64[chain_total + 1], chain_total = chain_offsets[n_req]:
+ *               seam_offsets[0] = 0, non-decreasing, last = n_seam; a window
+ *               holds at most PIC_MAX_SEAM tokens (PIC_ERR_DIMS otherwise);
+ *               an empty window is allowed
+ * n_seam        number of seam tokens of the call (the token axis below)
+ * q, k          device [batch][n_seam][heads][dk] (qkv_dtype)
+ * v             device [batch][n_seam][heads][dv] (qkv_dtype)
+ * alpha         device fp32 gates [batch][n_seam][heads] (diag: [..][dk])
+ * beta          device fp32 [batch][n_seam][heads], dense only, NULL = 1
+ * O_out         device fp32 out [batch][n_seam][heads][dv]
+ * q, k, v, alpha and O_out may be NULL only when n_seam = 0.  The chain's own
+ * pair is not produced.  The state and all updates are fp32 (seam tokens on
+ * the vector units; the pairs as in pic_compose).
+ * -------------------------------------------------------------------- */
+#define PIC_MAX_SEAM 64
+
+size_t pic_compose_seams_workspace(int32_t n_req, int64_t chain_total);
+
+int pic_validate_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                               int64_t pool_size, const float* pool_log_scale,
+                               const float* pool_T_hat, const float* pool_S0, int32_t n_req,
+                               const int64_t* chain_offsets, const int32_t* chain_idx,
+                               const int64_t* seam_offsets, int64_t n_seam, const void* q,
+                               const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* S_in, const float* S_out,
+                               const float* O_out, const void* workspace,
+                               size_t workspace_bytes);
+
+int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int dv,
+                      int64_t pool_size, const float* pool_log_scale, const float* pool_T_hat,
+                      const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                      const int32_t* chain_idx, const int64_t* seam_offsets, int64_t n_seam,
+                      const void* q, const void* k, const void* v, const float* alpha,
+                      const float* beta, const float* S_in, float* S_out, float* O_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Plain operator: T_out[u] = e^{log_scale[u]} * That[u] (dense), e^{lambda} I

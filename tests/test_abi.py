@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("pic_segment_build", "pic_compose", "pic_naive_add", "pic_validate_build",
               "pic_validate_compose", "pic_validate_naive_add", "pic_materialize_T",
               "pic_last_error", "pic_status_string", "pic_abi_version",
-              "pic_segment_build_workspace", "pic_compose_workspace", "pic_plan_dump"):
+              "pic_segment_build_workspace", "pic_compose_workspace", "pic_plan_dump",
+              "pic_compose_seams", "pic_validate_compose_seams", "pic_compose_seams_workspace"):
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 3
+    assert lib.pic_abi_version() == 4
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -245,3 +246,51 @@ def test_product_path_does_not_import_the_oracle():
                 assert "pic_oracle" not in text, f
     src = open(os.path.join(ROOT, "oracle", "pic_oracle.c"), encoding="utf-8").read()
     assert "pic.h" not in src and "hybrid_caching_amd" not in src
+
+
+def vseams(lib, form=DENSE, dt=BF16, B=1, H=2, dk=128, dv=128, pool=5, off=(0, 3, 3, 5),
+           idx=(4, 0, 1, 2, 3), seam=(0, 0, 8, 16, 16, 20), That=True, ws_bytes=None,
+           q=None, O=None, beta=None, n_seam=None):
+    o, o_p = offsets(off)
+    i = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    i_p = i.ctypes.data_as(ctypes.c_void_p) if i.size else None
+    so, so_p = offsets(seam)
+    R = len(o) - 1
+    ns = int(so[-1]) if n_seam is None else n_seam
+    need = lib.pic_compose_seams_workspace(R, int(o[-1]))
+    return lib.pic_validate_compose_seams(
+        form, dt, B, H, dk, dv, pool, P(0), P(1) if That else None, P(2), R, o_p, i_p, so_p, ns,
+        P(6) if q is None else q, P(7), P(8), P(9), beta, P(3), P(4),
+        P(10) if O is None else O, P(5),
+        need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_compose_seams(lib):
+    assert vseams(lib) == OK
+    assert vseams(lib, form=SCALAR, That=False, dt=F32) == OK
+    assert vseams(lib, form=DIAG, That=False, dk=16, dv=64) == OK
+    assert vseams(lib, beta=P(11)) == OK
+    assert vseams(lib, seam=(0, 0, 0, 0, 0, 0)) == OK  # no seam tokens at all
+    assert vseams(lib, seam=(0, 0, 0, 0, 0, 0), q=ctypes.c_void_p(0), O=ctypes.c_void_p(0)) == OK
+    assert vseams(lib, off=(0,), idx=(), seam=(0,)) == OK
+    assert vseams(lib, seam=(0, 64, 64, 64, 64, 64)) == OK  # the largest window
+    assert lib.pic_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"form": 3}, EUNSUP), ({"dt": 2}, EUNSUP), ({"dk": 8}, EDIMS),
+    ({"seam": (1, 1, 8, 16, 16, 20)}, EOFF), ({"seam": (0, 8, 4, 16, 16, 20)}, EOFF),
+    ({"seam": (0, 0, 8, 16, 16, 20), "n_seam": 21}, EOFF),
+    ({"seam": (0, 65, 65, 65, 65, 65)}, EDIMS), ({"n_seam": -1}, EDIMS),
+    ({"idx": (4, 0, 1, 2, 9)}, ECHAIN), ({"That": False}, ENULL),
+    ({"form": SCALAR, "That": True}, EUNSUP),
+    ({"q": ctypes.c_void_p(0)}, ENULL), ({"O": ctypes.c_void_p(0)}, ENULL),
+    ({"ws_bytes": 8}, EWS), ({"q": ctypes.c_void_p(A + 2)}, EALIGN),
+])
+def test_validate_compose_seams_rejects(lib, kw, code):
+    assert vseams(lib, **kw) == code
+    assert lib.pic_last_error().decode() != ""
+
+
+def test_compose_seams_workspace_grows_with_the_chain(lib):
+    assert lib.pic_compose_seams_workspace(4, 100) >= lib.pic_compose_workspace(4, 100) + 8 * 101
