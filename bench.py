@@ -44,7 +44,9 @@ KERNEL_SOURCES = {
     "build_scalar_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_diag_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
+PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
 
 
 def source_digest(kernel: str) -> str:
@@ -366,12 +368,24 @@ def bench_reuse(w, args):
     fresh_tokens = sum(n for _, _, n in fresh_rec)
 
     S_out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    seam_w = int(w.extra.get("seam", 0))
+    if seam_w:
+        seam_off = synth.reuse_seam_offsets(off, seam_w)
+        n_seam = int(seam_off[-1])
+        si = synth.torch_seam_inputs(w, n_seam, dev)
+        O = torch.empty((B, n_seam, H, dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration)
 
     def compose():
-        pic.pic_compose(synth.DENSE, pool["log_scale"], pool["T_hat"], pool["S0"], off, idx,
-                        None, out=S_out)
+        if seam_w:
+            pic.pic_compose_seams(synth.DENSE, pool["log_scale"], pool["T_hat"], pool["S0"], off,
+                                  idx, seam_off, si["q"], si["k"], si["v"], si["alpha"],
+                                  si["beta"], None, out=S_out, out_O=O)
+        else:
+            pic.pic_compose(synth.DENSE, pool["log_scale"], pool["T_hat"], pool["S0"], off, idx,
+                            None, out=S_out)
 
     for _ in range(max(args.warmup, 1)):
         compose()
@@ -389,9 +403,22 @@ def bench_reuse(w, args):
     composes = steps_total * B                     # pair applications per layer, all heads
     # every step reads its pair once; the states are written once (no S_in)
     cb = compose_bytes(steps_total, B, H, dk, dv, n_req=0) + R * B * H * dk * dv * 4
+    kname, seam_info = "compose_dense_kernel", None
+    if seam_w:
+        # each seam token reads q, k, v (bf16), alpha, beta and writes its output
+        # (fp32); its update u = S^T k, S <- a S + k c^T, o = S^T q is 7 dk dv flops
+        tok_bytes = B * H * ((2 * dk + dv) * 2 + 8 + dv * 4)
+        cb += n_seam * tok_bytes
+        seam_flops = 7.0 * dk * dv * n_seam * B * H
+        t_valu = seam_flops / (PEAK_FP32_VALU_TFLOPS * 1e12)
+        kname = "compose_seam_kernel"
+        seam_info = {"window": seam_w, "seam_tokens": n_seam, "seam_flops": seam_flops,
+                     "valu_time_at_peak_ms": t_valu * 1e3,
+                     "hbm_time_at_peak_ms": cb / (PEAK_HBM_GBS * 1e9) * 1e3,
+                     "output_tokens_per_s": n_seam * B / t_comp}
     gbs = cb / t_comp / 1e9
-    out = {"metric": "state composes/s (dense delta, H=32, d=128), composition-heavy reuse; "
-                     "% HBM roofline",
+    out = {"metric": "state composes/s (dense delta, H=32, d=128), composition-heavy reuse"
+                     + (" with seam windows" if seam_w else "") + "; % HBM roofline",
            "value": composes / t_comp, "unit": "composes/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": t_comp * 1e3, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, split-bf16 MFMA",
@@ -400,12 +427,13 @@ def bench_reuse(w, args):
                       "dv": dv, "build_precision": args.precision, "pool_segments": n_pool, "requests": R,
                       "chain_steps": steps_total // R, "fresh_segments": n_fresh,
                       "fresh_segment_tokens": int(fw.seg_lens[0])},
-           "roofline": {"kernel": "compose_dense_kernel", "bound": "hbm", "achieved": gbs,
+           "roofline": {"kernel": kname, "bound": "hbm", "achieved": gbs,
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                        "traffic": measured_traffic("compose_dense_kernel", w.name),
+                        "traffic": measured_traffic(kname, w.name),
                         "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": cb},
            "fresh_build": {"tokens_per_s": fresh_tokens / (fresh_ms / 1e3), "ms": fresh_ms,
                            "segments": n_fresh, "layers": B},
+           "seam": seam_info,
            "pool_and_input_preparation_s": prep_s,
            "hbm_reference": hbm_copy_reference(torch, dev)}
     print(json.dumps(out), flush=True)

@@ -18,10 +18,29 @@
 //   dense     u = S^T k,  S <- a S + k (b (v - a u))^T
 //   scalar    S <- a S + k v^T
 //   diagonal  S <- Diag(a) S + k v^T
-// A lane holds half of each of its column's rows, so the column sums S^T k
-// and S^T q take a partial sum over its 64 rows and one exchange with lane
-// l ^ 32.  Seam tokens are staged in LDS a few at a time (fp32, zero padded
-// to 128 channels), each lane reading its 64 key entries once per token.
+// Dense and scalar forms with bf16 inputs take a window of up to eight tokens
+// at once (chunked form, products on the matrix cores).  With S0 the state
+// before the window, g_t the product of the window's gates up to token t and
+// r(t,s) = a_{s+1} ... a_t:
+//   S_t = g_t S0 + sum_{s<=t} r(t,s) k_s c_s^T
+//   c_t = b_t (v_t - g_t S0^T k_t - sum_{s<t} r(t,s) (k_s . k_t) c_s)   (dense;
+//         scalar: c_t = v_t)
+//   o_t = g_t S0^T q_t + sum_{s<=t} r(t,s) (k_s . q_t) c_s
+// so one product [K; Q] S0 (16 rows, split-bf16 B from the accumulators; k and
+// q are exact in bf16) gives every column sum, one product on wave 0 gives the
+// 8x8 products k_s . k_t and k_s . q_t, each lane runs the short recurrence for
+// its column in fp32, and S <- g S0 + K^T C~ is one more product per tile.
+// The diagonal form and fp32 inputs update token by token on the vector
+// units: a lane holds half of each of its column's rows, so the column sums
+// S^T k and S^T q take a partial sum over its 64 rows and one exchange with
+// lane l ^ 32.  Seam tokens are staged in LDS eight at a time, zero padded to
+// 128 channels.  The
+// first eight tokens of the next entry's window are loaded into registers as
+// soon as the current window is staged (one 8- or 16-byte piece of k, q and v
+// per thread, token indices clamped into the call's range so that no load is
+// conditional), so they arrive while the current tokens and pair are applied.
+#include <type_traits>
+
 #include "mfma_util.hpp"
 #include "pic_internal.hpp"
 
@@ -30,21 +49,21 @@ namespace {
 
 constexpr int SP = 128;        // padded head size (state rows and columns)
 constexpr int SNT = SP / 32;   // 32-row tiles of a column strip
-constexpr int STW = 4;         // seam tokens staged per round
+constexpr int STW = 8;         // seam tokens staged per round
 constexpr int SLDR = SP + 8;   // row stride of the staged operator (bf16)
-
-template <bool BF16>
-__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
-  if (BF16) return static_cast<float>(static_cast<const __bf16*>(p)[i]);
-  return static_cast<const float*>(p)[i];
-}
 
 template <int FORM, bool BF16>
 __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   __shared__ __attribute__((aligned(16))) __bf16 th_hi[FORM == kDense ? SP * SLDR : 8];
   __shared__ __attribute__((aligned(16))) __bf16 th_lo[FORM == kDense ? SP * SLDR : 8];
-  __shared__ __attribute__((aligned(16))) float sk[STW][SP];
-  __shared__ __attribute__((aligned(16))) float sq[STW][SP];
+  // window path: dense / scalar forms with bf16 inputs
+  constexpr bool WIN = BF16 && FORM != kDiag;
+  __shared__ __attribute__((aligned(16))) float sk[WIN ? 1 : STW][SP];
+  __shared__ __attribute__((aligned(16))) float sq[WIN ? 1 : STW][SP];
+  __shared__ __attribute__((aligned(16))) __bf16 skb[WIN ? STW : 1][SP];   // k rows
+  __shared__ __attribute__((aligned(16))) __bf16 sqb[WIN ? STW : 1][SP];   // q rows
+  __shared__ __attribute__((aligned(16))) __bf16 skT[WIN ? SP : 1][STW];   // k columns
+  __shared__ __attribute__((aligned(16))) float skk[WIN ? 2 * STW : 1][STW];  // k.k, q.k
   __shared__ __attribute__((aligned(16))) float sv[STW][SP];
   __shared__ __attribute__((aligned(16))) float sg[STW][FORM == kDiag ? SP : 4];  // gates
   __shared__ float sb[STW];                                                       // beta
@@ -84,23 +103,64 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     }
   };
 
-  // stage seam tokens t0 .. t0+m-1 (m <= STW) into LDS
-  auto stage = [&](int64_t t0, int m) {
+  // One round of up to STW seam tokens in registers: thread e holds channels
+  // 4 (e % 32) .. +3 of token e / 32 of k, q and v (and of the diagonal gates);
+  // threads 0 .. STW-1 hold the scalar gate and beta of token e.
+  const int rt = threadIdx.x >> 5, rc = 4 * (threadIdx.x & 31);
+  typedef typename std::conditional<BF16, uint2, float4>::type Piece;
+  Piece pk, pq, pv;
+  float4 pa = make_float4(1.f, 1.f, 1.f, 1.f);
+  float pa1 = 1.f, pb1 = 1.f;
+  auto piece = [&](const void* base, int64_t off) -> Piece {
+    if constexpr (BF16)
+      return *reinterpret_cast<const uint2*>(static_cast<const __bf16*>(base) + off);
+    else
+      return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+  };
+  // load the round starting at seam token t0 (tokens past the call's end are
+  // clamped to its last one; they are loaded but never used)
+  auto load_round = [&](int64_t t0) {
+    const int64_t tl = t0 + rt < NS ? t0 + rt : NS - 1;
+    const int64_t tok = (int64_t(b) * NS + tl) * H + h;
+    const int ck = rc < dk ? rc : 0, cv = rc < dv ? rc : 0;
+    pk = piece(sa.k, tok * dk + ck);
+    pq = piece(sa.q, tok * dk + ck);
+    pv = piece(sa.v, tok * dv + cv);
+    if (FORM == kDiag) pa = *reinterpret_cast<const float4*>(sa.alpha + tok * dk + ck);
+    if (FORM != kDiag) {
+      const int64_t ts = t0 + (threadIdx.x & (STW - 1)) < NS ? t0 + (threadIdx.x & (STW - 1)) : NS - 1;
+      const int64_t tk = (int64_t(b) * NS + ts) * H + h;
+      pa1 = sa.alpha[tk];
+      if (FORM == kDense && sa.beta) pb1 = sa.beta[tk];
+    }
+  };
+  auto as4 = [&](const Piece& x) -> float4 {
+    if constexpr (BF16)
+      return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                         __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    else
+      return x;
+  };
+  // write the round held in registers to LDS (zero padded past dk / dv)
+  auto store_round = [&]() {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (WIN) {
+      const uint2 kz = rc < dk ? pk : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(&skb[rt][rc]) = kz;
+      *reinterpret_cast<uint2*>(&sqb[rt][rc]) = rc < dk ? pq : make_uint2(0u, 0u);
+      const unsigned short* kh = reinterpret_cast<const unsigned short*>(&kz);
 #pragma unroll
-    for (int i = 0; i < STW * SP / 256; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int tt = e / SP, ch = e % SP;
-      if (tt < m) {
-        const int64_t tok = (int64_t(b) * NS + t0 + tt) * H + h;
-        sk[tt][ch] = ch < dk ? ld_in<BF16>(sa.k, tok * dk + ch) : 0.f;
-        sq[tt][ch] = ch < dk ? ld_in<BF16>(sa.q, tok * dk + ch) : 0.f;
-        sv[tt][ch] = ch < dv ? ld_in<BF16>(sa.v, tok * dv + ch) : 0.f;
-        if (FORM == kDiag) sg[tt][ch] = ch < dk ? sa.alpha[tok * dk + ch] : 1.f;
-        if (FORM != kDiag && ch == 0) {
-          sg[tt][0] = sa.alpha[tok];
-          sb[tt] = (FORM == kDense && sa.beta) ? sa.beta[tok] : 1.f;
-        }
-      }
+      for (int j = 0; j < 4; ++j) reinterpret_cast<unsigned short*>(&skT[rc + j][0])[rt] = kh[j];
+    } else {
+      *reinterpret_cast<float4*>(&sk[rt][rc]) = rc < dk ? as4(pk) : z;
+      *reinterpret_cast<float4*>(&sq[rt][rc]) = rc < dk ? as4(pq) : z;
+    }
+    *reinterpret_cast<float4*>(&sv[rt][rc]) = rc < dv ? as4(pv) : z;
+    if (FORM == kDiag)
+      *reinterpret_cast<float4*>(&sg[rt][rc]) = rc < dk ? pa : make_float4(1.f, 1.f, 1.f, 1.f);
+    if (FORM != kDiag && threadIdx.x < STW) {
+      sg[threadIdx.x][0] = pa1;
+      sb[threadIdx.x] = pb1;
     }
   };
 
@@ -116,11 +176,12 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       }
     const float vn = sv[tt][n];
     if (FORM == kDense) {
-      float u = 0.f;
+      float up[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
       for (int t4 = 0; t4 < SNT; ++t4)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) u = fmaf(kr[t4][q], S[t4][q], u);
+        for (int q = 0; q < 16; ++q) up[q & 3] = fmaf(kr[t4][q], S[t4][q], up[q & 3]);
+      float u = (up[0] + up[1]) + (up[2] + up[3]);
       u += __shfl_xor(u, 32);
       const float a = sg[tt][0];
       const float cc = sb[tt] * (vn - a * u);
@@ -146,33 +207,172 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
             S[t4][4 * i + e] = fmaf(kr[t4][4 * i + e], vn, gv[e] * S[t4][4 * i + e]);
         }
     }
-    float o = 0.f;
+    float op[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t4 = 0; t4 < SNT; ++t4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 x = *reinterpret_cast<const float4*>(&sq[tt][32 * t4 + 8 * i + 4 * g]);
-        o = fmaf(x.x, S[t4][4 * i], o);
-        o = fmaf(x.y, S[t4][4 * i + 1], o);
-        o = fmaf(x.z, S[t4][4 * i + 2], o);
-        o = fmaf(x.w, S[t4][4 * i + 3], o);
+        op[0] = fmaf(x.x, S[t4][4 * i], op[0]);
+        op[1] = fmaf(x.y, S[t4][4 * i + 1], op[1]);
+        op[2] = fmaf(x.z, S[t4][4 * i + 2], op[2]);
+        op[3] = fmaf(x.w, S[t4][4 * i + 3], op[3]);
       }
+    float o = (op[0] + op[1]) + (op[2] + op[3]);
     o += __shfl_xor(o, 32);
     if (g == 0 && ncol) sa.O[((int64_t(b) * NS + t) * H + h) * dv + n] = o;
   };
 
+  // the m (<= STW) tokens staged in LDS, from seam token t_lo, in chunked form
+  auto window = [&](int m, int64_t t_lo) {
+    const int cl = lane & 31;
+    // A rows: k_0..k_7, q_0..q_7, then copies of k rows (finite, unused)
+    const __bf16* arow = cl < STW ? skb[cl] : (cl < 2 * STW ? sqb[cl - STW] : skb[cl & (STW - 1)]);
+    if (wave == 0) {  // k_s . k_t (rows 0..7) and q_t . k_s (rows 8..15), column s or t
+      const __bf16* brow = skb[cl & (STW - 1)];
+      f32x16 gacc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < SP / 16; ++ks)
+        gacc = mfma32(lds_load8(arow + 16 * ks + 8 * g), lds_load8(brow + 16 * ks + 8 * g), gacc);
+      if (cl < STW) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          skk[4 * g + e][cl] = gacc[e];
+          skk[STW + 4 * g + e][cl] = gacc[4 + e];
+        }
+      }
+    }
+    // column sums S0^T k_t (rows 0..7) and S0^T q_t (rows 8..15) of this
+    // lane's column; the B operand comes from the accumulators (permuted K)
+    f32x16 racc = zero16();
+#pragma unroll
+    for (int t4 = 0; t4 < SNT; ++t4)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 bhi, blo;
+        split_acc_half(S[t4], hh, bhi, blo);
+        const bf16x8 af = lds_perm8(arow, 32 * t4 + 16 * hh + 4 * g);
+        racc = mfma32(af, bhi, racc);
+        racc = mfma32(af, blo, racc);
+      }
+    // lane half g holds tokens 4g .. 4g+3; take the other half's from l ^ 32
+    float a[STW], bq[STW];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float xa = __shfl_xor(racc[e], 32), xb = __shfl_xor(racc[4 + e], 32);
+      a[e] = g ? xa : racc[e];
+      a[4 + e] = g ? racc[e] : xa;
+      bq[e] = g ? xb : racc[4 + e];
+      bq[4 + e] = g ? racc[4 + e] : xb;
+    }
+    __syncthreads();  // the 8x8 products are in LDS
+    float al[STW], cc[STW];
+#pragma unroll
+    for (int t = 0; t < STW; ++t) al[t] = sg[t][0];
+    float gt = 1.f;
+#pragma unroll
+    for (int t = 0; t < STW; ++t) {
+      cc[t] = 0.f;
+      if (t < m) {
+        gt *= al[t];
+        float kk[STW], qk[STW];
+#pragma unroll
+        for (int s4 = 0; s4 < STW / 4; ++s4) {
+          const float4 x = *reinterpret_cast<const float4*>(&skk[t][4 * s4]);
+          const float4 y = *reinterpret_cast<const float4*>(&skk[STW + t][4 * s4]);
+          kk[4 * s4] = x.x; kk[4 * s4 + 1] = x.y; kk[4 * s4 + 2] = x.z; kk[4 * s4 + 3] = x.w;
+          qk[4 * s4] = y.x; qk[4 * s4 + 1] = y.y; qk[4 * s4 + 2] = y.z; qk[4 * s4 + 3] = y.w;
+        }
+        const float vt = sv[t][n];
+        if (FORM == kDense) {
+          float acc = 0.f, rr = 1.f;
+#pragma unroll
+          for (int s = t - 1; s >= 0; --s) {
+            rr *= al[s + 1];
+            acc = fmaf(rr * kk[s], cc[s], acc);
+          }
+          cc[t] = sb[t] * (vt - gt * a[t] - acc);
+        } else {
+          cc[t] = vt;
+        }
+        float o = fmaf(qk[t], cc[t], gt * bq[t]);
+        float rr = 1.f;
+#pragma unroll
+        for (int s = t - 1; s >= 0; --s) {
+          rr *= al[s + 1];
+          o = fmaf(rr * qk[s], cc[s], o);
+        }
+        if (g == 0 && ncol) sa.O[((int64_t(b) * NS + t_lo + t) * H + h) * dv + n] = o;
+      }
+    }
+    // S <- g S0 + sum_s r(m-1, s) k_s c_s^T: scale, then K^T C~ per row tile
+    float ct[STW];
+    float rr = 1.f;
+#pragma unroll
+    for (int s = STW - 1; s >= 0; --s) {
+      ct[s] = 0.f;
+      if (s < m) {
+        ct[s] = rr * cc[s];
+        rr *= al[s];
+      }
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < SNT; ++t4) S[t4] *= gt;
+    bf16x8 chi, clo;
+    split8(ct, chi, clo);
+    if (g) {  // tokens 8..15 of the K step are zero
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { chi[j] = __bf16(0.f); clo[j] = __bf16(0.f); }
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < SNT; ++t4) {
+      bf16x8 kt = lds_load8(&skT[32 * t4 + cl][0]);
+      if (g) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kt[j] = __bf16(0.f);
+      }
+      S[t4] = mfma32(kt, chi, S[t4]);
+      S[t4] = mfma32(kt, clo, S[t4]);
+    }
+  };
+
   const int64_t c0 = chain_offset(sa.c, r), c1 = chain_offset(sa.c, r + 1);
   if (FORM == kDense && c0 < c1) load_op(int64_t(chain_entry(sa.c, c0)) * BH + bh);
+  const bool seams = NS > 0;
+  if (seams && c0 < c1) load_round(seam_offset(sa, c0));
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t pu = int64_t(chain_entry(sa.c, c)) * BH + bh;
-    // the entry's seam window
+    // the entry's seam window: its first round is in registers already
     const int64_t t_lo = seam_offset(sa, c), t_hi = seam_offset(sa, c + 1);
-    for (int64_t t0 = t_lo; t0 < t_hi; t0 += STW) {
-      const int m = int(t_hi - t0 < STW ? t_hi - t0 : STW);
+    const bool next = seams && c + 1 < c1;
+    if (t_hi > t_lo) {
+      const bool one_round = t_hi - t_lo <= STW;
       __syncthreads();  // the previous round's tokens are no longer read
-      stage(t0, m);
+      store_round();
+      if (one_round && next) load_round(seam_offset(sa, c + 1));
       __syncthreads();
-      for (int tt = 0; tt < m; ++tt) token(tt, t0 + tt);
+      const int m0 = int(one_round ? t_hi - t_lo : STW);
+      if constexpr (WIN) {
+        window(m0, t_lo);
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < STW; ++tt)  // unrolled, so that reads run ahead
+          if (tt < m0) token(tt, t_lo + tt);
+      }
+      for (int64_t t0 = t_lo + STW; t0 < t_hi; t0 += STW) {  // windows longer than a round
+        const int m = int(t_hi - t0 < STW ? t_hi - t0 : STW);
+        load_round(t0);
+        __syncthreads();
+        store_round();
+        __syncthreads();
+        if constexpr (WIN)
+          window(m, t0);
+        else
+          for (int tt = 0; tt < m; ++tt) token(tt, t0 + tt);
+      }
+      if (!one_round && next) load_round(seam_offset(sa, c + 1));
+    } else if (next) {
+      load_round(seam_offset(sa, c + 1));
     }
     // then the entry's pair
     const float* S0p = sa.c.pool_S0 + pu * sdd;

@@ -141,6 +141,52 @@ WORKLOADS["reuse_256x30_slow"] = replace(WORKLOADS["reuse_256x30"], name="reuse_
                                          beta=("uniform", 0.0, 0.02))
 
 
+# the same reuse with seam windows: every chain entry after a request's first
+# starts with an 8-token window that is not in its cached pair and is run from
+# the running state on reuse (the pages' default w = 8)
+WORKLOADS["reuse_seam_256x30"] = replace(WORKLOADS["reuse_256x30"], name="reuse_seam_256x30",
+                                         extra=dict(REUSE, seam=8))
+
+
+def reuse_seam_offsets(chain_offsets, w: int) -> np.ndarray:
+    """Seam offsets of a reuse call: w tokens for every chain entry except
+    the first of each request.  Returns int64 [chain_total + 1]."""
+    off = np.asarray(chain_offsets, dtype=np.int64)
+    lens = np.full(int(off[-1]), w, dtype=np.int64)
+    lens[off[:-1][off[:-1] < off[1:]]] = 0
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def torch_seam_inputs(w: Workload, n_seam: int, device, seed_offset: int = 0):
+    """Seam tokens of a reuse call for all layers, drawn on the device with
+    the workload's distributions: q, k, v [layers, n_seam, heads, d] (k rows
+    L2-normalised as configured, q ~ N(0, 1/dk)), alpha, beta fp32."""
+    import torch
+
+    B, H, dk, dv = w.layers, w.heads, w.dk, w.dv
+    sdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    out = {"q": torch.empty((B, n_seam, H, dk), dtype=sdt, device=device),
+           "k": torch.empty((B, n_seam, H, dk), dtype=sdt, device=device),
+           "v": torch.empty((B, n_seam, H, dv), dtype=sdt, device=device),
+           "alpha": torch.empty((B, n_seam, H, dk) if w.form == DIAG else (B, n_seam, H),
+                                dtype=torch.float32, device=device),
+           "beta": torch.empty((B, n_seam, H), dtype=torch.float32, device=device)}
+    seam_w = replace(w, seg_lens=(int(n_seam),))
+    for layer in range(B):
+        x = torch_layer_inputs(seam_w, layer, device, seed_offset=seed_offset + 7)
+        out["k"][layer].copy_(x["k"])
+        out["v"][layer].copy_(x["v"])
+        out["alpha"][layer].copy_(x["alpha"])
+        if x["beta"] is not None:
+            out["beta"][layer].copy_(x["beta"])
+        del x
+        g = torch.Generator(device=device)
+        g.manual_seed(int(w.seed) * 1000003 + layer * 7919 + seed_offset + 11)
+        out["q"][layer].copy_((torch.randn((n_seam, H, dk), generator=g, device=device)
+                               * (1.0 / np.sqrt(dk))).to(sdt))
+    return out
+
+
 def reuse_fresh_workload(w: Workload) -> Workload:
     """The fresh segments of a reuse workload (n_req x fresh_per_req of
     fresh_len tokens), same distributions, its own seed stream."""
