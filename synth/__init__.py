@@ -148,6 +148,11 @@ WORKLOADS["reuse_seam_256x30"] = replace(WORKLOADS["reuse_256x30"], name="reuse_
                                          extra=dict(REUSE, seam=8))
 
 
+WORKLOADS["reuse_seam_256x30_slow"] = replace(WORKLOADS["reuse_256x30_slow"],
+                                              name="reuse_seam_256x30_slow",
+                                              extra=dict(REUSE, seam=8))
+
+
 def reuse_seam_offsets(chain_offsets, w: int) -> np.ndarray:
     """Seam offsets of a reuse call: w tokens for every chain entry except
     the first of each request.  Returns int64 [chain_total + 1]."""

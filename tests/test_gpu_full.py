@@ -12,7 +12,8 @@ per chain batch).
 * composition-heavy reuse, 30 layers x 32 heads x d=128: a pool of 256
   cached segments (512..8192 tokens) plus 512 fresh 2048-token segments,
   64 requests composing 56-step chains, streamed layer by layer; sampled
-  units, chains and chain pairs against the oracle.
+  units, chains and chain pairs against the oracle; the same with 8-token
+  seam windows on every inner chain entry (final states and seam outputs).
 """
 import numpy as np
 import pytest
@@ -244,6 +245,66 @@ def test_reuse_workload_sampled(name, layers):
             if name.endswith("_slow"):
                 assert rho >= 0.1
         del x, y
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name,layers", [("reuse_seam_256x30", 3), ("reuse_seam_256x30_slow", 2)])
+def test_reuse_seam_workload_sampled(name, layers):
+    """Reuse with 8-token seam windows on every inner chain entry, at the
+    benchmark's per-layer launch size (768 pool and fresh segments, 64 requests
+    x 56-entry chains, 32 heads, d = 128), layer by layer; sampled chains
+    against the oracle: final state and every seam output."""
+    import hybrid_caching_amd as pic
+    import torch
+    from oracle import DENSE
+    w = synth.scaled(synth.WORKLOADS[name], layers=layers, name=synth.WORKLOADS[name].name)
+    fw = synth.reuse_fresh_workload(w)
+    off, idx = synth.reuse_chains(w)
+    seam_off = synth.reuse_seam_offsets(off, w.extra["seam"])
+    NS = int(seam_off[-1])
+    n_pool, n_fresh = w.n_seg, fw.n_seg
+    H, dk, dv = w.heads, w.dk, w.dv
+    dev = torch.device("cuda:0")
+    P = n_pool + n_fresh
+    buf = {"log_scale": torch.empty((P, 1, H), dtype=torch.float32, device=dev),
+           "T_hat": torch.empty((P, 1, H, dk, dk), dtype=torch.float32, device=dev),
+           "S0": torch.empty((P, 1, H, dk, dv), dtype=torch.float32, device=dev)}
+    pool_out = {key: t[:n_pool] for key, t in buf.items()}
+    fresh_out = {key: t[n_pool:] for key, t in buf.items()}
+    one = synth.scaled(w, layers=1, name=w.name)
+    rng = np.random.default_rng(205)
+    for layer in range(w.layers):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        pic.pic_segment_build(DENSE, x["k"][None], x["v"][None], x["alpha"][None],
+                              x["beta"][None], w.offsets(), out=pool_out)
+        y = synth.torch_layer_inputs(fw, layer, dev)
+        pic.pic_segment_build(DENSE, y["k"][None], y["v"][None], y["alpha"][None],
+                              y["beta"][None], fw.offsets(), out=fresh_out)
+        del x, y
+        si = synth.torch_seam_inputs(one, NS, dev, seed_offset=1000 * layer)
+        S_out, O = pic.pic_compose_seams(DENSE, buf["log_scale"], buf["T_hat"], buf["S0"], off,
+                                         idx, seam_off, si["q"], si["k"], si["v"], si["alpha"],
+                                         si["beta"])
+        torch.cuda.synchronize()
+        for r, hh in [(int(rng.integers(w.extra["n_req"])), int(rng.integers(H))) for _ in range(2)]:
+            ids = idx[off[r]:off[r + 1]]
+            n = len(ids)
+            sub = {key: t[torch.as_tensor(ids.astype(np.int64), device=dev), 0, hh]
+                   .cpu().numpy()[:, None, None] for key, t in buf.items()}
+            t0, t1 = int(seam_off[off[r]]), int(seam_off[off[r + 1]])
+            so = seam_off[off[r]:off[r + 1] + 1] - t0
+            tok = lambda key: si[key][0, t0:t1, hh].float().cpu().numpy()[None, :, None]
+            ref_S, ref_O = oracle.seam_compose(DENSE, sub["log_scale"], sub["T_hat"], sub["S0"],
+                                               [0, n], list(range(n)), so, tok("q"), tok("k"),
+                                               tok("v"), tok("alpha"), tok("beta"))
+            es = max_rel_units(S_out[r, 0, hh].cpu().numpy(), ref_S[0, 0, 0])
+            eo = max_rel_units(O[0, t0:t1, hh].cpu().numpy(), ref_O[0, :, 0])
+            rho = rho_of(ref_S[0], sub["S0"][-1])
+            report(f"{name} layer {layer}: chain (req {r}, head {hh}, {n} entries, {t1 - t0} "
+                   f"seam tokens): state err {es:.3e}, output err {eo:.3e}, rho {rho:.3f}")
+            assert es <= 1e-4 and eo <= 1e-4
+            if name.endswith("_slow"):
+                assert rho >= 0.1
 
 
 def test_all_segments_empty():
