@@ -52,7 +52,9 @@ constexpr int SNT = SP / 32;   // 32-row tiles of a column strip
 constexpr int STW = 8;         // seam tokens staged per round
 constexpr int SLDR = SP + 8;   // row stride of the staged operator (bf16)
 
-template <int FORM, bool BF16>
+// FULL: dk = dv = 128, so every operator, S0 and state access is an
+// unconditional load at a loop-invariant offset from the step's base address
+template <int FORM, bool BF16, bool FULL>
 __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   __shared__ __attribute__((aligned(16))) __bf16 th_hi[FORM == kDense ? SP * SLDR : 8];
   __shared__ __attribute__((aligned(16))) __bf16 th_lo[FORM == kDense ? SP * SLDR : 8];
@@ -70,13 +72,13 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5;
-  const int dk = sa.c.dk, dv = sa.c.dv, H = sa.c.heads;
+  const int dk = FULL ? SP : sa.c.dk, dv = FULL ? SP : sa.c.dv, H = sa.c.heads;
   const int64_t BH = int64_t(sa.c.batch) * H;
   const int64_t unit = blockIdx.x;
   const int64_t r = unit / BH, bh = unit % BH;
   const int b = int(bh / H), h = int(bh % H);
   const int n = wave * 32 + (lane & 31);  // state column of this lane
-  const bool ncol = n < dv;
+  const bool ncol = FULL || n < dv;
   const int64_t sdd = int64_t(dk) * dv;
   const int64_t NS = sa.n_seam;
 
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = t * 32 + acc_row(q, g);
-      S[t][q] = (sa.c.S_in && ncol && row < dk) ? sa.c.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
+      S[t][q] = (sa.c.S_in && (FULL || (ncol && row < dk))) ? sa.c.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
     }
 
   // operator of one chain step (dense), this thread's float4 items, zero padded
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       const int e = threadIdx.x + it * 256;
       const int row = (e * 4) / SP, col = (e * 4) % SP;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row < dk && col < dk) x = *reinterpret_cast<const float4*>(Tp + row * dk + col);
+      if (FULL || (row < dk && col < dk)) x = *reinterpret_cast<const float4*>(Tp + row * dk + col);
       pre[it] = x;
     }
   };
@@ -340,17 +342,36 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   if (FORM == kDense && c0 < c1) load_op(int64_t(chain_entry(sa.c, c0)) * BH + bh);
   const bool seams = NS > 0;
   if (seams && c0 < c1) load_round(seam_offset(sa, c0));
+  // One chain step: after a barrier the entry's operator (dense) and the first
+  // round of its window go to LDS and the next operator and window are
+  // loaded (they arrive while this step's window and product run); after a
+  // second barrier the window, then the pair.
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t pu = int64_t(chain_entry(sa.c, c)) * BH + bh;
-    // the entry's seam window: its first round is in registers already
     const int64_t t_lo = seam_offset(sa, c), t_hi = seam_offset(sa, c + 1);
     const bool next = seams && c + 1 < c1;
-    if (t_hi > t_lo) {
-      const bool one_round = t_hi - t_lo <= STW;
-      __syncthreads();  // the previous round's tokens are no longer read
-      store_round();
-      if (one_round && next) load_round(seam_offset(sa, c + 1));
-      __syncthreads();
+    const bool win = t_hi > t_lo, one_round = t_hi - t_lo <= STW;
+    __syncthreads();  // the previous step's operator and tokens are no longer read
+    if (FORM == kDense) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int e = threadIdx.x + it * 256;
+        const int row = (e * 4) / SP, col = (e * 4) % SP;
+        unsigned h0, l0, h1, l1;
+        split2(pre[it].x, pre[it].y, h0, l0);
+        split2(pre[it].z, pre[it].w, h1, l1);
+        // columns permuted within each 16 (bits 2 and 3 swapped) so that the
+        // 8 columns of a permuted K-step are contiguous
+        const int pcol = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+        *reinterpret_cast<uint2*>(th_hi + row * SLDR + pcol) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(th_lo + row * SLDR + pcol) = make_uint2(l0, l1);
+      }
+      if (c + 1 < c1) load_op(int64_t(chain_entry(sa.c, c + 1)) * BH + bh);
+    }
+    if (win) store_round();  // the window's first round was loaded ahead
+    if (next && (!win || one_round)) load_round(seam_offset(sa, c + 1));
+    __syncthreads();
+    if (win) {
       const int m0 = int(one_round ? t_hi - t_lo : STW);
       if constexpr (WIN) {
         window(m0, t_lo);
@@ -371,37 +392,19 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
           for (int tt = 0; tt < m; ++tt) token(tt, t0 + tt);
       }
       if (!one_round && next) load_round(seam_offset(sa, c + 1));
-    } else if (next) {
-      load_round(seam_offset(sa, c + 1));
     }
-    // then the entry's pair
+    // then the entry's pair (its operator is in LDS)
     const float* S0p = sa.c.pool_S0 + pu * sdd;
     if (FORM == kDense) {
-      __syncthreads();  // every wave is done reading the previous operator
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int row = (e * 4) / SP, col = (e * 4) % SP;
-        unsigned h0, l0, h1, l1;
-        split2(pre[it].x, pre[it].y, h0, l0);
-        split2(pre[it].z, pre[it].w, h1, l1);
-        // columns permuted within each 16 (bits 2 and 3 swapped) so that the
-        // 8 columns of a permuted K-step are contiguous
-        const int pcol = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-        *reinterpret_cast<uint2*>(th_hi + row * SLDR + pcol) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(th_lo + row * SLDR + pcol) = make_uint2(l0, l1);
-      }
-      if (c + 1 < c1) load_op(int64_t(chain_entry(sa.c, c + 1)) * BH + bh);
       f32x16 s0[SNT];
 #pragma unroll
       for (int t = 0; t < SNT; ++t)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = t * 32 + acc_row(q, g);
-          s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+          s0[t][q] = (FULL || (ncol && row < dk)) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
       const float scale = expf(sa.c.pool_log_scale[pu]);
-      __syncthreads();
       f32x16 acc[SNT];
 #pragma unroll
       for (int t = 0; t < SNT; ++t) acc[t] = zero16();
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = t * 32 + acc_row(q, g);
-          const bool in = ncol && row < dk;
+          const bool in = FULL || (ncol && row < dk);
           const float rs = (FORM == kDiag) ? (row < dk ? expf(sa.c.pool_log_scale[pu * dk + row]) : 1.f) : sc;
           S[t][q] = fmaf(rs, S[t][q], in ? S0p[int64_t(row) * dv + n] : 0.f);
         }
@@ -445,17 +448,25 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) sa.c.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
+        if (FULL || row < dk) sa.c.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
       }
   }
+}
+
+template <int FORM, bool BF16>
+void launch_seam_f(const SeamArgs& a, dim3 grid, hipStream_t s) {
+  if (a.c.dk == SP && a.c.dv == SP)
+    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, false>), grid, dim3(256), 0, s, a);
 }
 
 template <int FORM>
 void launch_seam_t(const SeamArgs& a, dim3 grid, hipStream_t s) {
   if (a.qkv_bf16)
-    hipLaunchKernelGGL((compose_seam_kernel<FORM, true>), grid, dim3(256), 0, s, a);
+    launch_seam_f<FORM, true>(a, grid, s);
   else
-    hipLaunchKernelGGL((compose_seam_kernel<FORM, false>), grid, dim3(256), 0, s, a);
+    launch_seam_f<FORM, false>(a, grid, s);
 }
 
 }  // namespace
