@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // FULL = true when dk = dv = DKP: no padding, so every operator and S0
 // access is an unconditional load at a loop-invariant offset from the step's
 // (uniform) base address.
-template <int DKP, bool PROD, bool FULL>
+// INL: the chain tables travel in the kernel arguments
+template <int DKP, bool PROD, bool FULL, bool INL>
 __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   constexpr int NT = DKP / 32;
   // row stride of the staged operator (bf16): 16-byte aligned rows whose
@@ -150,10 +151,35 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
     }
   };
 
-  const int64_t c0 = chain_offset(a, r), c1 = chain_offset(a, r + 1);
-  if (c0 < c1) load_op(int64_t(chain_entry(a, c0)) * BH + bh);
+  const int64_t c0 = chain_offset_t<INL>(a, r), c1 = chain_offset_t<INL>(a, r + 1);
+  // The chain's pool indices and log scales, 64 entries at a time, one per
+  // lane (one vector load each); a step takes its own with readlane, so no
+  // step issues a scalar or table load (those share the LDS wait counter and
+  // would hold up the next barrier for a memory round trip).
+  int64_t cb = c0;
+  int ent_l = 0;
+  float lam_l = 0.f;
+  auto fetch = [&](int64_t base) {
+    cb = base;
+    const int64_t cc = base + lane;
+    int e = 0;
+    float l = 0.f;
+    if (cc < c1) {
+      e = chain_entry_t<INL>(a, cc);
+      if (!PROD) l = table_at(a.pool_log_scale, int64_t(e) * BH + bh);
+    }
+    ent_l = e;
+    lam_l = l;
+  };
+  auto entry_at = [&](int64_t c) { return __builtin_amdgcn_readlane(ent_l, int(c - cb)); };
+  if (c0 < c1) {
+    fetch(c0);
+    load_op(int64_t(entry_at(c0)) * BH + bh);
+  }
   for (int64_t c = c0; c < c1; ++c) {
-    const int64_t pu = int64_t(chain_entry(a, c)) * BH + bh;
+    const int64_t pu = int64_t(entry_at(c)) * BH + bh;
+    const float lam = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam_l), int(c - cb)));
     __syncthreads();  // every wave is done reading the previous operator
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -170,7 +196,10 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
         *reinterpret_cast<uint2*>(th_lo + row * LDR + pcol) = make_uint2(l0, l1);
       }
     }
-    if (c + 1 < c1) load_op(int64_t(chain_entry(a, c + 1)) * BH + bh);
+    if (c + 1 < c1) {
+      if (c + 1 - cb >= 64) fetch(c + 1);
+      load_op(int64_t(entry_at(c + 1)) * BH + bh);
+    }
     // this step's S0 strip, loaded ahead of the products
     f32x16 s0[NT];
     float scale = 1.f;
@@ -186,7 +215,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
           else
             s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
-      scale = expf(a.pool_log_scale[pu]);
+      scale = expf(lam);
     }
     __syncthreads();
 
@@ -288,12 +317,19 @@ hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStrea
   return hipGetLastError();
 }
 
+template <int DKP, bool PROD, bool INL>
+void launch_dense_i(const ComposeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.dk == DKP && a.dv == DKP)
+    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, true, INL>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, false, INL>), grid, block, 0, s, a);
+}
 template <int DKP, bool PROD>
 void launch_dense_t(const ComposeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.dk == DKP && a.dv == DKP)
-    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, true>), grid, block, 0, s, a);
+  if (a.inl)
+    launch_dense_i<DKP, PROD, true>(a, grid, block, s);
   else
-    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, false>), grid, block, 0, s, a);
+    launch_dense_i<DKP, PROD, false>(a, grid, block, s);
 }
 
 template <bool PROD>

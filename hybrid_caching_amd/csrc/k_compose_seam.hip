@@ -54,7 +54,8 @@ constexpr int SLDR = SP + 8;   // row stride of the staged operator (bf16)
 
 // FULL: dk = dv = 128, so every operator, S0 and state access is an
 // unconditional load at a loop-invariant offset from the step's base address
-template <int FORM, bool BF16, bool FULL>
+// INL: the chain and seam tables travel in the kernel arguments
+template <int FORM, bool BF16, bool FULL, bool INL>
 __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   __shared__ __attribute__((aligned(16))) __bf16 th_hi[FORM == kDense ? SP * SLDR : 8];
   __shared__ __attribute__((aligned(16))) __bf16 th_lo[FORM == kDense ? SP * SLDR : 8];
@@ -338,18 +339,57 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     }
   };
 
-  const int64_t c0 = chain_offset(sa.c, r), c1 = chain_offset(sa.c, r + 1);
-  if (FORM == kDense && c0 < c1) load_op(int64_t(chain_entry(sa.c, c0)) * BH + bh);
+  const int64_t c0 = chain_offset_t<INL>(sa.c, r), c1 = chain_offset_t<INL>(sa.c, r + 1);
+  // The chain's pool indices, log scales (scalar / dense) and window bounds,
+  // 64 entries at a time, one per lane (vector loads); a step takes its own
+  // with readlane, so no step issues a scalar or table load (those share the
+  // LDS wait counter and would hold up the next barrier for a memory round
+  // trip).
+  int64_t cb = c0;
+  int ent_l = 0;
+  float lam_l = 0.f;
+  int64_t so0_l = 0, so1_l = 0;
+  auto fetch = [&](int64_t base) {
+    cb = base;
+    const int64_t cc = base + lane;
+    int e = 0;
+    float l = 0.f;
+    int64_t x0 = 0, x1 = 0;
+    if (cc < c1) {
+      e = chain_entry_t<INL>(sa.c, cc);
+      if (FORM != kDiag) l = table_at(sa.c.pool_log_scale, int64_t(e) * BH + bh);
+      x0 = seam_offset_t<INL>(sa, cc);
+      x1 = seam_offset_t<INL>(sa, cc + 1);
+    }
+    ent_l = e;
+    lam_l = l;
+    so0_l = x0;
+    so1_l = x1;
+  };
+  auto rl64 = [&](int64_t x, int64_t c) {
+    const int i = int(c - cb);
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x)), i));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint64_t(x) >> 32), i));
+    return int64_t((uint64_t(hi) << 32) | lo);
+  };
+  auto entry_at = [&](int64_t c) { return __builtin_amdgcn_readlane(ent_l, int(c - cb)); };
   const bool seams = NS > 0;
-  if (seams && c0 < c1) load_round(seam_offset(sa, c0));
+  if (c0 < c1) {
+    fetch(c0);
+    if (FORM == kDense) load_op(int64_t(entry_at(c0)) * BH + bh);
+    if (seams) load_round(rl64(so0_l, c0));
+  }
   // One chain step: after a barrier the entry's operator (dense) and the first
   // round of its window go to LDS and the next operator and window are
   // loaded (they arrive while this step's window and product run); after a
   // second barrier the window, then the pair.
   for (int64_t c = c0; c < c1; ++c) {
-    const int64_t pu = int64_t(chain_entry(sa.c, c)) * BH + bh;
-    const int64_t t_lo = seam_offset(sa, c), t_hi = seam_offset(sa, c + 1);
+    const int64_t pu = int64_t(entry_at(c)) * BH + bh;
+    const float lam = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam_l), int(c - cb)));
+    const int64_t t_lo = rl64(so0_l, c), t_hi = rl64(so1_l, c);
     const bool next = seams && c + 1 < c1;
+    if (c + 1 < c1 && c + 1 - cb >= 64) fetch(c + 1);  // entries c+1 .. c+64
     const bool win = t_hi > t_lo, one_round = t_hi - t_lo <= STW;
     __syncthreads();  // the previous step's operator and tokens are no longer read
     if (FORM == kDense) {
@@ -366,10 +406,10 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
         *reinterpret_cast<uint2*>(th_hi + row * SLDR + pcol) = make_uint2(h0, h1);
         *reinterpret_cast<uint2*>(th_lo + row * SLDR + pcol) = make_uint2(l0, l1);
       }
-      if (c + 1 < c1) load_op(int64_t(chain_entry(sa.c, c + 1)) * BH + bh);
+      if (c + 1 < c1) load_op(int64_t(entry_at(c + 1)) * BH + bh);
     }
     if (win) store_round();  // the window's first round was loaded ahead
-    if (next && (!win || one_round)) load_round(seam_offset(sa, c + 1));
+    if (next && (!win || one_round)) load_round(t_hi);
     __syncthreads();
     if (win) {
       const int m0 = int(one_round ? t_hi - t_lo : STW);
@@ -391,7 +431,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
         else
           for (int tt = 0; tt < m; ++tt) token(tt, t0 + tt);
       }
-      if (!one_round && next) load_round(seam_offset(sa, c + 1));
+      if (!one_round && next) load_round(t_hi);
     }
     // then the entry's pair (its operator is in LDS)
     const float* S0p = sa.c.pool_S0 + pu * sdd;
@@ -404,7 +444,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
           const int row = t * 32 + acc_row(q, g);
           s0[t][q] = (FULL || (ncol && row < dk)) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
-      const float scale = expf(sa.c.pool_log_scale[pu]);
+      const float scale = expf(lam);
       f32x16 acc[SNT];
 #pragma unroll
       for (int t = 0; t < SNT; ++t) acc[t] = zero16();
@@ -429,7 +469,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) S[t][q] = fmaf(scale, acc[t][q], s0[t][q]);
     } else {
-      const float sc = (FORM == kScalar) ? expf(sa.c.pool_log_scale[pu]) : 1.f;
+      const float sc = (FORM == kScalar) ? expf(lam) : 1.f;
 #pragma unroll
       for (int t = 0; t < SNT; ++t)
 #pragma unroll
@@ -453,12 +493,19 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   }
 }
 
+template <int FORM, bool BF16, bool INL>
+void launch_seam_i(const SeamArgs& a, dim3 grid, hipStream_t s) {
+  if (a.c.dk == SP && a.c.dv == SP)
+    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, true, INL>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, false, INL>), grid, dim3(256), 0, s, a);
+}
 template <int FORM, bool BF16>
 void launch_seam_f(const SeamArgs& a, dim3 grid, hipStream_t s) {
-  if (a.c.dk == SP && a.c.dv == SP)
-    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, true>), grid, dim3(256), 0, s, a);
+  if (a.c.inl)
+    launch_seam_i<FORM, BF16, true>(a, grid, s);
   else
-    hipLaunchKernelGGL((compose_seam_kernel<FORM, BF16, false>), grid, dim3(256), 0, s, a);
+    launch_seam_i<FORM, BF16, false>(a, grid, s);
 }
 
 template <int FORM>

@@ -38,12 +38,23 @@ struct BuildArgs {
   int32_t inl_order[kInlineSeg];
 };
 
+// a plan table entry in device memory, read as global memory: a pointer that
+// may point either into the kernel arguments or into device memory would be
+// read with a flat load, which also counts on the LDS wait counter, so every
+// later LDS wait (e.g. before a barrier) would wait for the memory round trip
+template <class T>
+__device__ __forceinline__ T table_at(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(1))) T*)(p))[i];
+}
+
 // segment offset i and the i-th segment of the visiting order
 __device__ __forceinline__ int64_t seg_offset(const BuildArgs& a, int i) {
-  return a.n_seg <= kInlineSeg ? a.inl_off[i] : a.d_offsets[i];
+  if (a.n_seg <= kInlineSeg) return a.inl_off[i];
+  return table_at(a.d_offsets, i);
 }
 __device__ __forceinline__ int seg_in_order(const BuildArgs& a, int i) {
-  return a.n_seg <= kInlineSeg ? a.inl_order[i] : a.d_order[i];
+  if (a.n_seg <= kInlineSeg) return a.inl_order[i];
+  return table_at(a.d_order, i);
 }
 
 // One compose / naive-add call, after validation.
@@ -69,10 +80,24 @@ struct ComposeArgs {
 
 // chain offset r and chain entry c
 __device__ __forceinline__ int64_t chain_offset(const ComposeArgs& a, int64_t r) {
-  return a.inl ? a.inl_off[r] : a.d_chain_off[r];
+  if (a.inl) return a.inl_off[r];
+  return table_at(a.d_chain_off, r);
 }
 __device__ __forceinline__ int chain_entry(const ComposeArgs& a, int64_t c) {
-  return a.inl ? a.inl_idx[c] : a.d_chain_idx[c];
+  if (a.inl) return a.inl_idx[c];
+  return table_at(a.d_chain_idx, c);
+}
+// the same with the table's place known at compile time (a runtime choice is
+// turned into a select between the two addresses, i.e. a flat load)
+template <bool INL>
+__device__ __forceinline__ int64_t chain_offset_t(const ComposeArgs& a, int64_t r) {
+  if constexpr (INL) return a.inl_off[r];
+  else return table_at(a.d_chain_off, r);
+}
+template <bool INL>
+__device__ __forceinline__ int chain_entry_t(const ComposeArgs& a, int64_t c) {
+  if constexpr (INL) return a.inl_idx[c];
+  else return table_at(a.d_chain_idx, c);
 }
 
 // One reuse-with-seams call, after validation: a compose whose chain entries
@@ -93,8 +118,10 @@ struct SeamArgs {
 };
 
 // first seam token of chain entry c (c = chain_total gives the end)
-__device__ __forceinline__ int64_t seam_offset(const SeamArgs& a, int64_t c) {
-  return a.c.inl ? a.inl_seam_off[c] : a.d_seam_off[c];
+template <bool INL>
+__device__ __forceinline__ int64_t seam_offset_t(const SeamArgs& a, int64_t c) {
+  if constexpr (INL) return a.inl_seam_off[c];
+  else return table_at(a.d_seam_off, c);
 }
 
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
