@@ -25,7 +25,8 @@ module only marshals numpy arrays into it.  What each call computes:
   its definition: segments as token ranges cut into 64-token chunks, visited
   longest first; chains applied entry by entry.
 
-Forms: 0 = scalar decay, 1 = diagonal gate, 2 = dense gated delta (GDN form).
+Forms: 0 = scalar decay, 1 = diagonal gate, 2 = dense gated delta (GDN form),
+3 = dense delta with per-channel gates (KDA form, T_t = (I - b k k^T) Diag(a)).
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ import threading
 
 import numpy as np
 
-SCALAR, DIAG, DENSE = 0, 1, 2
+SCALAR, DIAG, DENSE, KDA = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pic_oracle.c")
@@ -126,13 +127,13 @@ def build(form, k, v, alpha, beta, offsets, *, literal=False, want_T=False, thre
     """
     lib = lib or load()
     k, v, alpha = _f64(k), _f64(v), _f64(alpha)
-    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    beta = _f64(beta) if (beta is not None and form in (DENSE, KDA)) else None
     B, N, H, dk = k.shape
     dv = v.shape[3]
     offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     n_seg = len(offs) - 1
     lam = np.zeros((n_seg, B, H, dk) if form == DIAG else (n_seg, B, H))
-    That = np.zeros((n_seg, B, H, dk, dk)) if form == DENSE else None
+    That = np.zeros((n_seg, B, H, dk, dk)) if form in (DENSE, KDA) else None
     T = np.zeros((n_seg, B, H, dk, dk)) if (want_T or literal) else None
     S = np.zeros((n_seg, B, H, dk, dv))
     rc = lib.oracle_build(form, int(bool(literal)), B, H, dk, dv, N, _ptr(k), _ptr(v),
@@ -152,7 +153,7 @@ def recurrence(form, k, v, alpha, beta, S_in=None, *, threads=None, lib=None):
     """Unsplit literal recurrence over all N tokens from S_in: returns [B, H, dk, dv]."""
     lib = lib or load()
     k, v, alpha = _f64(k), _f64(v), _f64(alpha)
-    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    beta = _f64(beta) if (beta is not None and form in (DENSE, KDA)) else None
     B, N, H, dk = k.shape
     dv = v.shape[3]
     S_in = _f64(S_in)
@@ -183,14 +184,14 @@ def compose(form, lam, That, S, chain_offsets, chain_idx, S_in=None, *, want_pai
     """
     lib = lib or load()
     lam, S = _f64(lam), _f64(S)
-    That = _f64(That) if form == DENSE else None
+    That = _f64(That) if form in (DENSE, KDA) else None
     P, B, H, dk, dv = S.shape
     off, idx = _chains(chain_offsets, chain_idx)
     R = len(off) - 1
     S_in = _f64(S_in)
     S_out = np.zeros((R, B, H, dk, dv))
     lam_out = np.zeros((R,) + lam.shape[1:]) if want_pair else None
-    That_out = np.zeros((R, B, H, dk, dk)) if (want_pair and form == DENSE) else None
+    That_out = np.zeros((R, B, H, dk, dk)) if (want_pair and form in (DENSE, KDA)) else None
     rc = lib.oracle_compose(form, B, H, dk, dv, P, _ptr(lam), _ptr(That), _ptr(S), R,
                             _ptr(off, _i64p), _ptr(idx, _i32p), _ptr(S_in), _ptr(S_out),
                             _ptr(lam_out), _ptr(That_out), threads or default_threads())

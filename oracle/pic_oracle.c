@@ -24,6 +24,7 @@
  *        scalar decay   T_t = alpha_t * I              (beta = 1)
  *        diagonal gate  T_t = Diag(alpha_t)            (beta = 1)
  *        dense GDN      T_t = alpha_t * (I - beta_t k_t k_t^T)
+ *        dense KDA      T_t = (I - beta_t k_t k_t^T) Diag(alpha_t)
  *
  *  - A segment C = tokens [o, o+L) started from the zero state yields the
  *    pair (T_C, S(C|0)): T_C is the product of all token transitions of the
@@ -53,6 +54,10 @@
  *  given in split form: lambda_C = sum_t ln(alpha_t) (per head for scalar
  *  and dense, per key channel for diagonal) and, for the dense form,
  *  That_C = prod_t (I - beta_t k_t k_t^T), so that T_C = e^{lambda_C}*That_C.
+ *  For the KDA form the gate does not factor out of the product; lambda_C =
+ *  sum_t ln m_t with m_t the token's largest gate, and That_C is the product
+ *  of (I - beta_t k_t k_t^T) Diag(alpha_t / m_t): the same split when all
+ *  channels share one gate, and That_C stays bounded (norm <= 1).
  *  The oracle computes both factors directly (not by dividing T_C).
  *
  *  Two build paths are offered:
@@ -68,11 +73,11 @@
  *
  *  Layouts (row-major, last index fastest):
  *    k      [B][N][H][dk]        v    [B][N][H][dv]
- *    alpha  [B][N][H]  (scalar, dense)   or [B][N][H][dk]  (diagonal)
- *    beta   [B][N][H]  (dense; NULL means 1; ignored for scalar/diagonal)
+ *    alpha  [B][N][H]  (scalar, dense)   or [B][N][H][dk]  (diagonal, KDA)
+ *    beta   [B][N][H]  (dense, KDA; NULL means 1; ignored for scalar/diagonal)
  *    offsets[n_seg+1]  token offsets of the segments, offsets[0] = 0
- *    lam    [n_seg][B][H]     (scalar, dense)  or [n_seg][B][H][dk] (diag)
- *    That   [n_seg][B][H][dk][dk]   (dense only)
+ *    lam    [n_seg][B][H]     (scalar, dense, KDA)  or [n_seg][B][H][dk] (diag)
+ *    That   [n_seg][B][H][dk][dk]   (dense and KDA)
  *    T      [n_seg][B][H][dk][dk]   plain T_C, all forms (optional)
  *    S      [n_seg][B][H][dk][dv]
  */
@@ -85,6 +90,15 @@
 #define ORACLE_SCALAR 0
 #define ORACLE_DIAG 1
 #define ORACLE_DENSE 2
+#define ORACLE_KDA 3
+
+/* largest gate of a token (the KDA form's per-token scale) */
+static double max_gate(const double *at, int dk) {
+  double m = at[0];
+  for (int i = 1; i < dk; ++i)
+    if (at[i] > m) m = at[i];
+  return m;
+}
 
 /* ------------------------------------------------------------------ */
 /* a tiny thread pool: run fn(ctx, i) for i in [0, n)                  */
@@ -137,7 +151,9 @@ static void run_items(item_fn fn, void *ctx, int64_t n, int n_threads) {
  * and Th (dk x dk, may be NULL) with its ungated factor:
  *   scalar: T_t = a*I,            ungated I
  *   diag:   T_t = Diag(a[0..dk)), ungated I
- *   dense:  T_t = a*(I - b k k^T), ungated I - b k k^T                  */
+ *   dense:  T_t = a*(I - b k k^T), ungated I - b k k^T
+ *   KDA:    T_t = (I - b k k^T) Diag(a[0..dk)), ungated factor the same
+ *           with a divided by its largest entry m_t (lambda adds ln m_t) */
 static void token_transition(int form, int dk, const double *kt, const double *at, double bt,
                              double *Tt, double *Th) {
   for (int i = 0; i < dk; ++i) {
@@ -150,6 +166,10 @@ static void token_transition(int form, int dk, const double *kt, const double *a
       } else if (form == ORACLE_DIAG) {
         t = at[i] * eye;
         h = eye;
+      } else if (form == ORACLE_KDA) {
+        const double e = eye - bt * kt[i] * kt[j];
+        t = e * at[j];
+        h = e * (at[j] / max_gate(at, dk));
       } else {
         h = eye - bt * kt[i] * kt[j];
         t = at[0] * h;
@@ -190,11 +210,11 @@ static inline const double *v_at(const build_ctx *c, int b, int64_t t, int h) {
   return c->v + (((int64_t)b * c->N + t) * c->H + h) * c->dv;
 }
 static inline const double *a_at(const build_ctx *c, int b, int64_t t, int h) {
-  int64_t per = (c->form == ORACLE_DIAG) ? c->dk : 1;
+  int64_t per = (c->form == ORACLE_DIAG || c->form == ORACLE_KDA) ? c->dk : 1;
   return c->alpha + (((int64_t)b * c->N + t) * c->H + h) * per;
 }
 static inline double b_at(const build_ctx *c, int b, int64_t t, int h) {
-  if (c->form != ORACLE_DENSE || c->beta == NULL) return 1.0;
+  if ((c->form != ORACLE_DENSE && c->form != ORACLE_KDA) || c->beta == NULL) return 1.0;
   return c->beta[((int64_t)b * c->N + t) * c->H + h];
 }
 
@@ -231,7 +251,10 @@ static void build_unit(void *vctx, int64_t item) {
   for (int64_t t = t0; t < t1; ++t) {
     const double *kt = k_at(c, b, t, h), *vt = v_at(c, b, t, h), *at = a_at(c, b, t, h);
     const double bt = b_at(c, b, t, h);
-    for (int i = 0; i < nlam; ++i) lam[i] += log(at[i]);
+    if (form == ORACLE_KDA)
+      lam[0] += log(max_gate(at, dk));
+    else
+      for (int i = 0; i < nlam; ++i) lam[i] += log(at[i]);
     if (c->literal) {
       /* S <- T_t S + bt * k v^T ; T <- T_t T ; That <- That_t That */
       token_transition(form, dk, kt, at, bt, Tt, Tht);
@@ -254,6 +277,31 @@ static void build_unit(void *vctx, int64_t item) {
         for (int j = 0; j < dv; ++j) S[i * dv + j] = at[i] * S[i * dv + j] + kt[i] * vt[j];
         for (int j = 0; j < dk; ++j) T[i * dk + j] *= at[i];
       }
+    } else if (form == ORACLE_KDA) {
+      /* T_t = (I - b k k^T) Diag(a): scale the rows of S and T by a and
+       * those of That by a / m, then X <- X - b k (k^T X) for all three;
+       * then S += b k v^T */
+      const double m = max_gate(at, dk);
+      for (int i = 0; i < dk; ++i) {
+        for (int j = 0; j < dv; ++j) S[i * dv + j] *= at[i];
+        for (int j = 0; j < dk; ++j) {
+          T[i * dk + j] *= at[i];
+          Th[i * dk + j] *= at[i] / m;
+        }
+      }
+      double *X[3] = {S, T, Th};
+      const int W[3] = {dv, dk, dk};
+      for (int x = 0; x < 3; ++x) {
+        for (int j = 0; j < W[x]; ++j) {
+          double s = 0.0;
+          for (int i = 0; i < dk; ++i) s += kt[i] * X[x][i * W[x] + j];
+          kS[j] = s;
+        }
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < W[x]; ++j) X[x][i * W[x] + j] -= bt * kt[i] * kS[j];
+      }
+      for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[i * dv + j] += bt * kt[i] * vt[j];
     } else {
       /* T_t = a (I - b k k^T):  X <- a (X - b k (k^T X)) for X = S, T;
        * That <- That - b k (k^T That);  then S += b k v^T */
@@ -304,7 +352,7 @@ static void build_unit(void *vctx, int64_t item) {
 int oracle_build(int form, int literal, int B, int H, int dk, int dv, int64_t N, const double *k,
                  const double *v, const double *alpha, const double *beta, const int64_t *offsets,
                  int n_seg, double *lam, double *That, double *T, double *S, int n_threads) {
-  if (form < 0 || form > 2 || B < 0 || H < 0 || dk <= 0 || dv <= 0 || n_seg < 0) return -1;
+  if (form < 0 || form > 3 || B < 0 || H < 0 || dk <= 0 || dv <= 0 || n_seg < 0) return -1;
   if (offsets[0] != 0 || offsets[n_seg] != N) return -1;
   for (int i = 0; i < n_seg; ++i)
     if (offsets[i + 1] < offsets[i]) return -1;
@@ -351,7 +399,7 @@ static void recurrence_unit(void *vctx, int64_t item) {
 int oracle_recurrence(int form, int B, int H, int dk, int dv, int64_t N, const double *k,
                       const double *v, const double *alpha, const double *beta,
                       const double *S_in, double *S_out, int n_threads) {
-  if (form < 0 || form > 2 || dk <= 0 || dv <= 0) return -1;
+  if (form < 0 || form > 3 || dk <= 0 || dv <= 0) return -1;
   rec_ctx r;
   memset(&r, 0, sizeof(r));
   r.bc.form = form;
@@ -418,7 +466,7 @@ static void compose_unit(void *vctx, int64_t item) {
     for (int i = 0; i < dk; ++i) {
       for (int j = 0; j < dk; ++j) {
         double eye = (i == j) ? 1.0 : 0.0;
-        double th = (form == ORACLE_DENSE) ? c->That[unit * dk * dk + i * dk + j] : eye;
+        double th = (form == ORACLE_DENSE || form == ORACLE_KDA) ? c->That[unit * dk * dk + i * dk + j] : eye;
         double scale = exp(lp[form == ORACLE_DIAG ? i : 0]);
         T[i * dk + j] = scale * th;
       }
@@ -428,7 +476,7 @@ static void compose_unit(void *vctx, int64_t item) {
     for (int i = 0; i < dk * dv; ++i) S[i] = tmp[i] + Sp[i];
     /* the chain's own pair: lambda sums, That multiplies on the left */
     for (int i = 0; i < nlam; ++i) lacc[i] += lp[i];
-    if (form == ORACLE_DENSE) {
+    if (form == ORACLE_DENSE || form == ORACLE_KDA) {
       matmul(dk, dk, dk, c->That + unit * dk * dk, Tacc, Ttmp);
       memcpy(Tacc, Ttmp, sizeof(double) * dk * dk);
     }
@@ -458,8 +506,8 @@ int oracle_compose(int form, int B, int H, int dk, int dv, int64_t P, const doub
                    const double *That, const double *S, int n_req, const int64_t *chain_off,
                    const int32_t *chain_idx, const double *S_in, double *S_out, double *lam_out,
                    double *That_out, int n_threads) {
-  if (form < 0 || form > 2 || check_chains(P, n_req, chain_off, chain_idx)) return -1;
-  if (form == ORACLE_DENSE && That == NULL) return -1;
+  if (form < 0 || form > 3 || check_chains(P, n_req, chain_off, chain_idx)) return -1;
+  if ((form == ORACLE_DENSE || form == ORACLE_KDA) && That == NULL) return -1;
   comp_ctx c = {form, B,         H,       dk,   dv,    0,       lam,    That,
                 S,    chain_off, chain_idx, S_in, S_out, lam_out, That_out};
   run_items(compose_unit, &c, (int64_t)n_req * B * H, n_threads);

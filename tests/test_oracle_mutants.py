@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_kda_pins as kda_pins
 from tests import test_oracle_seam_pins as seam_pins
 
 _SEAM_OUT = """  /* o_t = S_t^T q_t */
@@ -98,6 +99,18 @@ MUTANTS = [
     ("seam: diagonal gate of channel 0 for every row",
      "const double ai = (form == ORACLE_DIAG) ? at[i] : at[0];",
      "const double ai = at[0];"),
+    ("KDA: gates applied after the erase (rows instead of columns)",
+     "        t = e * at[j];",
+     "        t = e * at[i];"),
+    ("KDA: log scale of channel 0 instead of the largest gate",
+     "      lam[0] += log(max_gate(at, dk));",
+     "      lam[0] += log(at[0]);"),
+    ("KDA specialised: ungated factor keeps the gate scale",
+     "          Th[i * dk + j] *= at[i] / m;",
+     "          Th[i * dk + j] *= at[i];"),
+    ("KDA: smallest gate taken as the scale",
+     "    if (at[i] > m) m = at[i];",
+     "    if (at[i] < m) m = at[i];"),
     ("seam: pair gate scale dropped",
      "Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;",
      "Tp[i * dk + j] = ungated;"),
@@ -132,6 +145,13 @@ def _pin_calls():
             lambda f=form: seam_pins.test_seam_queries_only_reach_outputs(f),
         ]
     calls.append(seam_pins.test_seam_delta_rule_retrieval)
+    calls += [kda_pins.test_kda_literal_equals_specialised,
+              lambda: kda_pins.test_kda_with_shared_gates_is_dense_gdn(False),
+              lambda: kda_pins.test_kda_with_shared_gates_is_dense_gdn(True),
+              kda_pins.test_kda_without_erase_is_diagonal,
+              lambda: kda_pins.test_kda_exact_rational(0),
+              lambda: kda_pins.test_kda_split_compose_equals_unsplit([0, 9, 10, 31]),
+              kda_pins.test_kda_That_is_bounded]
     return calls
 
 
