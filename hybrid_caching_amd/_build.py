@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libpic.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_ws.hip", "k_build_dense_h16.hip",
-           "k_build_scalar_diag.hip", "k_build_sd_pipe.hip", "k_compose_seam.hip"]
+           "k_build_scalar_diag.hip", "k_build_sd_pipe.hip", "k_compose_seam.hip",
+           "k_build_kda.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",

@@ -15,7 +15,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpic.so")
 
-FORM_SCALAR, FORM_DIAG, FORM_DENSE = 0, 1, 2
+FORM_SCALAR, FORM_DIAG, FORM_DENSE, FORM_KDA = 0, 1, 2, 3
+_HAS_T_HAT = (FORM_DENSE, FORM_KDA)
 DT_F32, DT_BF16 = 0, 1
 PREC_FP32, PREC_FP16 = 0, 1
 
@@ -128,10 +129,11 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
     """Cached pairs of every (segment, layer, head).
 
     k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
-    [B, N, H] (diag: [B, N, H, dk]), beta: fp32 [B, N, H] or None (= 1; dense
-    only), seg_offsets: host ints [n_seg+1].  precision: PREC_FP32 or
-    PREC_FP16 (dense with bf16 k/v only).  Returns dict(log_scale, T_hat
-    (dense only), S0) of fp32 device tensors laid out [n_seg, B, H, ...].
+    [B, N, H] (diag, KDA: [B, N, H, dk]), beta: fp32 [B, N, H] or None (= 1;
+    dense and KDA only), seg_offsets: host ints [n_seg+1].  precision:
+    PREC_FP32 or PREC_FP16 (dense with bf16 k/v only).  Returns
+    dict(log_scale, T_hat (dense and KDA only), S0) of fp32 device tensors
+    laid out [n_seg, B, H, ...].
     """
     lib = load()
     B, N, H, dk = k.shape
@@ -149,7 +151,7 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
         lam_shape = (n_seg, B, H, dk) if form == FORM_DIAG else (n_seg, B, H)
         out = {"log_scale": torch.empty(lam_shape, dtype=torch.float32, device=dev),
                "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
-        if form == FORM_DENSE:
+        if form in _HAS_T_HAT:
             out["T_hat"] = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
     ws_n = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
     ws = _workspace(ws_n, dev)
@@ -166,7 +168,7 @@ def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, c
     """Fold chains of pool pairs into states: S <- e^lam That S + S0 per step.
 
     pool_S0: [P, B, H, dk, dv]; pool_log_scale [P, B, H] (diag [P, B, H, dk]);
-    pool_T_hat [P, B, H, dk, dk] (dense; None otherwise).  Returns S_out
+    pool_T_hat [P, B, H, dk, dk] (dense and KDA; None otherwise).  Returns S_out
     [R, B, H, dk, dv] (``out`` may be S_in for an in-place update).  With
     ``want_pair`` returns (S_out, log_scale_out, T_hat_out): the chain's own
     operator, sum of log scales and (dense) That_pn ... That_p1, else None."""
@@ -185,7 +187,7 @@ def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, c
     if want_pair:
         lam_out = torch.empty((R,) + tuple(pool_log_scale.shape[1:]), dtype=torch.float32,
                               device=dev)
-        if form == FORM_DENSE:
+        if form in _HAS_T_HAT:
             T_out = torch.empty((R, B, H, dk, dk), dtype=torch.float32, device=dev)
     ws = _workspace(lib.pic_compose_workspace(R, int(off[-1])), dev)
     rc = lib.pic_compose(form, B, H, dk, dv, P, _ptr(pool_log_scale), _ptr(pool_T_hat),
@@ -263,7 +265,7 @@ def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):
     if form == FORM_DIAG:
         dk = log_scale.shape[-1]
         lead = log_scale.shape[:-1]
-    elif form == FORM_DENSE:
+    elif form in _HAS_T_HAT:
         dk = T_hat.shape[-1]
         lead = log_scale.shape
     else:

@@ -285,7 +285,7 @@ __global__ void materialize_kernel(int form, int64_t n_units, int dk, const floa
     const int64_t u = e / (int64_t(dk) * dk);
     const int i = int((e / dk) % dk), j = int(e % dk);
     float v;
-    if (form == kDense) {
+    if (form == kDense || form == kKda) {
       v = expf(log_scale[u]) * T_hat[e];
     } else if (form == kScalar) {
       v = (i == j) ? expf(log_scale[u]) : 0.f;

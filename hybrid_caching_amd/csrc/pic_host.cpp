@@ -37,6 +37,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
+// forms whose pair carries an operator That (a per-head lambda and a dk x dk matrix)
+bool has_T_hat(int form) { return form == PIC_FORM_DENSE || form == PIC_FORM_KDA; }
+
 // ---------------------------------------------------------------- staging
 // The small per-call tables (segment offsets and order, chain tables) reach
 // the device through pinned host slots: the caller's arrays are copied into
@@ -288,7 +291,7 @@ int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int he
                        const float* S0, const void* workspace, size_t workspace_bytes) {
   (void)q;  // never read: the pair does not depend on queries
   (void)beta;
-  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
     return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
@@ -299,7 +302,7 @@ int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int he
   if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
   if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
   if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
-  const int64_t per_gate = (form == PIC_FORM_DIAG) ? dk : 1;
+  const int64_t per_gate = (form == PIC_FORM_DIAG || form == PIC_FORM_KDA) ? dk : 1;
   if (mul_sizes({batch, n_tokens, heads, std::max(dk, dv)}) < 0 ||
       mul_sizes({n_seg, batch, heads, dk, std::max(dk, dv)}) < 0 ||
       mul_sizes({batch, n_tokens, heads, per_gate}) < 0)
@@ -308,9 +311,9 @@ int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int he
   if (n_tokens > 0 && (!k || !v || !alpha))
     return fail(PIC_ERR_NULL, "k, v and alpha are required");
   if (!log_scale || !S0) return fail(PIC_ERR_NULL, "log_scale and S0 outputs are required");
-  if (form == PIC_FORM_DENSE && !T_hat)
-    return fail(PIC_ERR_NULL, "T_hat output is required for the dense form");
-  if (form != PIC_FORM_DENSE && T_hat)
+  if (has_T_hat(form) && !T_hat)
+    return fail(PIC_ERR_NULL, "T_hat output is required for the dense and KDA forms");
+  if (!has_T_hat(form) && T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
   if (int rc = check_seg_offsets(seg_offsets, n_seg, n_tokens)) return rc;
   if (int rc = check_align({k, v, alpha, beta, log_scale, T_hat, S0, workspace})) return rc;
@@ -353,6 +356,8 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
   if (form == PIC_FORM_DENSE)
     e = (precision == PIC_PREC_FP16) ? pic::launch_build_dense_h16(a, s)
                                      : pic::launch_build_dense(a, s);
+  else if (form == PIC_FORM_KDA)
+    e = pic::launch_build_kda(a, s);
   else
     e = pic::launch_build_scalar_diag(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the build kernel");
@@ -372,7 +377,7 @@ int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t
                          const float* log_scale_out, const float* T_hat_out,
                          const void* workspace, size_t workspace_bytes) {
   (void)S_in;
-  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
   if (mul_sizes({pool_size, batch, heads, dk, std::max(dk, dv)}) < 0 ||
@@ -383,13 +388,13 @@ int pic_validate_compose(int form, int batch, int heads, int dk, int dv, int64_t
   if (n_req > 0 && !S_out) return fail(PIC_ERR_NULL, "S_out is required");
   if (total > 0 && (!pool_S0 || !pool_log_scale))
     return fail(PIC_ERR_NULL, "pool_S0 and pool_log_scale are required");
-  if (total > 0 && form == PIC_FORM_DENSE && !pool_T_hat)
-    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense form");
-  if (form != PIC_FORM_DENSE && pool_T_hat)
+  if (total > 0 && has_T_hat(form) && !pool_T_hat)
+    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense and KDA forms");
+  if (!has_T_hat(form) && pool_T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "pool_T_hat must be NULL for scalar and diagonal forms");
-  if (form != PIC_FORM_DENSE && T_hat_out)
+  if (!has_T_hat(form) && T_hat_out)
     return fail(PIC_ERR_UNSUPPORTED, "T_hat_out must be NULL for scalar and diagonal forms");
-  if (form == PIC_FORM_DENSE && (!log_scale_out) != (!T_hat_out))
+  if (has_T_hat(form) && (!log_scale_out) != (!T_hat_out))
     return fail(PIC_ERR_NULL, "the chain pair needs both log_scale_out and T_hat_out");
   if (mul_sizes({n_req, batch, heads, dk, dk}) < 0)
     return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
@@ -462,7 +467,7 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
                      pool_log_scale, pool_T_hat, pool_S0, n_req, nullptr, nullptr,
                      chain_offsets[n_req], S_in, S_out, log_scale_out, T_hat_out, false, {}, {}};
   if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, a)) return rc;
-  hipError_t e = (form == PIC_FORM_DENSE) ? pic::launch_compose_dense(a, s)
+  hipError_t e = has_T_hat(form) ? pic::launch_compose_dense(a, s)
                                           : pic::launch_compose_elementwise(a, false, s);
   if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
   if (log_scale_out) {
@@ -511,6 +516,8 @@ int pic_validate_compose_seams(int form, int qkv_dtype, int batch, int heads, in
                                const float* O_out, const void* workspace,
                                size_t workspace_bytes) {
   (void)S_in;
+  if (form == PIC_FORM_KDA)
+    return fail(PIC_ERR_UNSUPPORTED, "seam windows are not supported for the KDA form");
   if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
@@ -612,15 +619,15 @@ int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int
 
 int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
                       const float* T_hat, float* T_out, void* stream) {
-  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (!dim_ok(dk)) return fail(PIC_ERR_DIMS, "dk (%d) must be a multiple of 16 in [16, 128]", dk);
   if (n_units < 0 || mul_sizes({n_units, dk, dk}) < 0)
     return fail(PIC_ERR_DIMS, "bad n_units");
   if (n_units == 0) return ok();
   if (!log_scale || !T_out) return fail(PIC_ERR_NULL, "log_scale and T_out are required");
-  if (form == PIC_FORM_DENSE && !T_hat) return fail(PIC_ERR_NULL, "T_hat is required");
-  if (form != PIC_FORM_DENSE && T_hat)
+  if (has_T_hat(form) && !T_hat) return fail(PIC_ERR_NULL, "T_hat is required");
+  if (!has_T_hat(form) && T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
   if (int rc = check_align({log_scale, T_hat, T_out})) return rc;
   hipError_t e = pic::launch_materialize_T(form, n_units, dk, log_scale, T_hat, T_out,

@@ -8,7 +8,7 @@
 
 namespace pic {
 
-enum Form : int { kScalar = 0, kDiag = 1, kDense = 2 };
+enum Form : int { kScalar = 0, kDiag = 1, kDense = 2, kKda = 3 };
 
 // Small plans travel inside the kernel arguments, so a call needs no
 // host-to-device copy before its kernel: up to kInlineSeg segments for a
@@ -130,6 +130,8 @@ hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_ws(const BuildArgs& a, hipStream_t s);
 // fp16 operand precision (bf16 inputs, any dk, dv <= 128)
 hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s);
+// KDA form: token by token in fp32 on the vector units
+hipError_t launch_build_kda(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
 hipError_t launch_compose_seams(const SeamArgs& a, hipStream_t s);

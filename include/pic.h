@@ -26,12 +26,23 @@
  *     PIC_FORM_SCALAR  T_t = alpha_t I                     beta = 1
  *     PIC_FORM_DIAG    T_t = Diag(alpha_t), alpha_t in (0,1]^dk, beta = 1
  *     PIC_FORM_DENSE   T_t = alpha_t (I - beta_t k_t k_t^T)   (GDN form)
+ *     PIC_FORM_KDA     T_t = (I - beta_t k_t k_t^T) Diag(alpha_t),
+ *                      alpha_t in (0,1]^dk            (KDA form: per-channel
+ *                      gates inside the delta rule)
+ * For every form S_t = T_t S_{t-1} + beta_t k_t v_t^T (beta = 1 where the
+ * table above fixes it).
  *
  * Split operator.  At realistic gates T_C underflows fp32 within a few
  * thousand tokens, so the operator is returned as
  *     T_C = e^{lambda_C} * That_C,   lambda_C = sum_t ln(alpha_t)
  * with lambda per head (scalar, dense) or per key channel (diagonal), and
  * That_C = prod_t (I - beta_t k_t k_t^T) (dense only; I for the others).
+ * KDA: the gates do not factor out of the product, so each token gives up
+ * its largest gate m_t = max_i alpha_t,i:
+ *     lambda_C = sum_t ln(m_t),  That_C = prod_t (I - beta_t k_t k_t^T) Diag(alpha_t / m_t)
+ * (the dense split when all channels share one gate; ||That_C||_2 <= 1 for
+ * beta |k|^2 <= 2).  Everywhere below "dense" pairs (a per-head lambda and a
+ * That) include the KDA form's: compose and materialize treat the two alike.
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major (last index fastest).  Device pointers
@@ -39,7 +50,7 @@
  *     of the current HIP device.  Host arrays (offsets, chains) are read during the call only.
  *   - Layout of per-token inputs:  k, q [batch][n_tokens][heads][dk],
  *     v [batch][n_tokens][heads][dv], alpha [batch][n_tokens][heads]
- *     (diag: [batch][n_tokens][heads][dk]), beta [batch][n_tokens][heads].
+ *     (diag, KDA: [batch][n_tokens][heads][dk]), beta [batch][n_tokens][heads].
  *     "batch" indexes independent layers (or layer-sized groups); segments
  *     are token ranges shared by all of them.
  *   - Layout of pairs (a "pool" of cached segments, and the build output):
@@ -82,9 +93,9 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 4
+#define PIC_ABI_VERSION 5
 
-enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2 };
+enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
 
 /* Arithmetic of the build's matrix-core products (the state and every
@@ -130,18 +141,20 @@ const char* pic_last_error(void);
  * form        PIC_FORM_*
  * qkv_dtype   storage type of q, k, v: PIC_DT_BF16 or PIC_DT_F32
  * precision   PIC_PREC_FP32, or PIC_PREC_FP16 (dense form with bf16 k/v only;
- *             any other combination returns PIC_ERR_UNSUPPORTED)
+ *             any other combination returns PIC_ERR_UNSUPPORTED).  The KDA
+ *             build runs token by token in fp32 on the vector units.
  * batch, heads, dk, dv, n_tokens   sizes (see layouts above)
  * q           may be NULL; never read: the pair does not depend on queries
  * k, v        device, qkv_dtype
  * alpha       device fp32 gates in (0, 1]
- * beta        device fp32 [batch][n_tokens][heads]; dense only (ignored for
- *             scalar/diag); NULL means beta = 1
+ * beta        device fp32 [batch][n_tokens][heads]; dense and KDA only
+ *             (ignored for scalar/diag); NULL means beta = 1
  * seg_offsets HOST int64[n_seg+1]: segment s = tokens [off[s], off[s+1]);
  *             off[0] = 0, non-decreasing, off[n_seg] = n_tokens
  * log_scale   device fp32 out, lambda_C, [n_seg][batch][heads] (diag: [..][dk])
  * T_hat       device fp32 out, That_C [n_seg][batch][heads][dk][dk]; required
- *             for PIC_FORM_DENSE, must be NULL otherwise (That = I)
+ *             for PIC_FORM_DENSE and PIC_FORM_KDA, must be NULL otherwise
+ *             (That = I)
  * S0          device fp32 out, S(C|0) [n_seg][batch][heads][dk][dv]
  * workspace   device scratch of at least pic_segment_build_workspace() bytes
  * stream      hipStream_t (NULL = null stream)
@@ -258,6 +271,7 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
  * alpha         device fp32 gates [batch][n_seam][heads] (diag: [..][dk])
  * beta          device fp32 [batch][n_seam][heads], dense only, NULL = 1
  * O_out         device fp32 out [batch][n_seam][heads][dv]
+ * form          scalar, diagonal or dense (PIC_FORM_KDA: PIC_ERR_UNSUPPORTED)
  * q, k, v, alpha and O_out may be NULL only when n_seam = 0.  The chain's own
  * pair is not produced.  The state and all updates are fp32 (seam tokens on
  * the vector units; the pairs as in pic_compose).

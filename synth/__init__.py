@@ -27,8 +27,9 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-SCALAR, DIAG, DENSE = 0, 1, 2
-FORM_NAMES = {SCALAR: "scalar", DIAG: "diag", DENSE: "dense"}
+SCALAR, DIAG, DENSE, KDA = 0, 1, 2, 3
+FORM_NAMES = {SCALAR: "scalar", DIAG: "diag", DENSE: "dense", KDA: "kda"}
+PER_CHANNEL_GATES = (DIAG, KDA)  # forms with one gate per key channel
 
 # --------------------------------------------------------------------------
 # storage rounding
@@ -101,6 +102,12 @@ WORKLOADS = {
     "dense_30L_32x4096": Workload("dense_30L_32x4096", DENSE, 30, 32, 128, 128, (4096,) * 32,
                                   104, True, "l2", 1.0, ("uniform", 0.9, 1.0),
                                   ("uniform", 0.0, 1.0)),
+    # delta rule with per-channel gates (KDA form), the same model shape and
+    # prompt as the dense workload: per-channel gates as in the diagonal
+    # workload, erase strengths as in the dense one
+    "kda_30L_32x4096": Workload("kda_30L_32x4096", KDA, 30, 32, 128, 128, (4096,) * 32, 106,
+                                True, "l2", 1.0, ("sigmoid_normal", 3.0, 1.0),
+                                ("uniform", 0.0, 1.0)),
 }
 
 # Variants with slow gates, so that the T(C2) S(C1) term is a sizeable part of
@@ -114,6 +121,10 @@ WORKLOADS["dense_30L_32x4096_slow"] = replace(WORKLOADS["dense_30L_32x4096"],
                                               name="dense_30L_32x4096_slow",
                                               alpha=("uniform", 0.9995, 1.0),
                                               beta=("uniform", 0.0, 0.02))
+WORKLOADS["kda_30L_32x4096_slow"] = replace(WORKLOADS["kda_30L_32x4096"],
+                                            name="kda_30L_32x4096_slow",
+                                            alpha=("sigmoid_normal", 9.0, 1.0),
+                                            beta=("uniform", 0.0, 0.02))
 
 
 def reuse_pool_lengths(seed: int = 105, pool_size: int = 256, lo: int = 512,
@@ -173,7 +184,8 @@ def torch_seam_inputs(w: Workload, n_seam: int, device, seed_offset: int = 0):
     out = {"q": torch.empty((B, n_seam, H, dk), dtype=sdt, device=device),
            "k": torch.empty((B, n_seam, H, dk), dtype=sdt, device=device),
            "v": torch.empty((B, n_seam, H, dv), dtype=sdt, device=device),
-           "alpha": torch.empty((B, n_seam, H, dk) if w.form == DIAG else (B, n_seam, H),
+           "alpha": torch.empty((B, n_seam, H, dk) if w.form in PER_CHANNEL_GATES
+                                else (B, n_seam, H),
                                 dtype=torch.float32, device=device),
            "beta": torch.empty((B, n_seam, H), dtype=torch.float32, device=device)}
     seam_w = replace(w, seg_lens=(int(n_seam),))
@@ -236,7 +248,7 @@ def _store(w: Workload, x: np.ndarray) -> np.ndarray:
 
 def segment_inputs(w: Workload, layer: int, seg_id: int, L: int, want_q: bool = False):
     """Inputs of one segment of one layer, all heads: k [L,H,dk], v [L,H,dv],
-    alpha [L,H] (diag: [L,H,dk]), beta [L,H] (None when beta = 1), q (opt).
+    alpha [L,H] (diag, KDA: [L,H,dk]), beta [L,H] (None when beta = 1), q (opt).
     k, v, q are fp32 arrays holding the stored (bf16 or fp32) values."""
     H, dk, dv = w.heads, w.dk, w.dv
     x = _rng(w, layer, seg_id, STREAM_K).standard_normal((L, H, dk), dtype=np.float32)
@@ -249,7 +261,7 @@ def segment_inputs(w: Workload, layer: int, seg_id: int, L: int, want_q: bool = 
     v = _store(w, _rng(w, layer, seg_id, STREAM_V).standard_normal((L, H, dv), dtype=np.float32)
                * np.float32(w.v_scale))
     ra = _rng(w, layer, seg_id, STREAM_ALPHA)
-    ashape = (L, H, dk) if w.form == DIAG else (L, H)
+    ashape = (L, H, dk) if w.form in PER_CHANNEL_GATES else (L, H)
     if w.alpha[0] == "uniform":
         alpha = ra.uniform(w.alpha[1], w.alpha[2], size=ashape).astype(np.float32)
     else:
@@ -319,7 +331,7 @@ def torch_layer_inputs(w: Workload, layer: int, device, seed_offset: int = 0):
     del x
     v = (torch.randn((N, H, dv), generator=g, device=device, dtype=torch.float32)
          * float(w.v_scale)).to(sdt)
-    ashape = (N, H, dk) if w.form == DIAG else (N, H)
+    ashape = (N, H, dk) if w.form in PER_CHANNEL_GATES else (N, H)
     if w.alpha[0] == "uniform":
         alpha = torch.rand(ashape, generator=g, device=device, dtype=torch.float32)
         alpha = alpha * (w.alpha[2] - w.alpha[1]) + w.alpha[1]

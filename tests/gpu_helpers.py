@@ -85,7 +85,7 @@ def assert_pair_close(gpu, ref, form, tol):
     e_l = lam_err(gpu["log_scale"], ref["lam"])
     msg = f"S0 err {e_s:.3e}, lambda err {e_l:.3e}"
     e_t = 0.0
-    if form == oracle.DENSE:
+    if form in (oracle.DENSE, oracle.KDA):
         e_t = max_rel_units(gpu["T_hat"], ref["That"])
         msg += f", That err {e_t:.3e}"
     report(msg)

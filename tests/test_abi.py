@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pic.h")
 
 OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
-SCALAR, DIAG, DENSE = 0, 1, 2
+SCALAR, DIAG, DENSE, KDA = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 4
+    assert lib.pic_abi_version() == 5
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -86,13 +86,16 @@ def test_validate_build_accepts_good_arguments(lib):
     assert vbuild(lib, offs=(0, 0, 100, 100)) == OK  # empty segments are allowed
     assert vbuild(lib, prec=1) == OK  # fp16 operands: dense with bf16 k/v
     assert vbuild(lib, prec=1, dk=16, dv=48) == OK
+    assert vbuild(lib, form=KDA) == OK  # per-channel gates, That required
+    assert vbuild(lib, form=KDA, dt=F32, dk=32, dv=96) == OK
     assert lib.pic_last_error().decode() == ""
 
 
 @pytest.mark.parametrize("kw,code", [
     ({"form": 7}, EUNSUP), ({"dt": 5}, EUNSUP), ({"prec": 2}, EUNSUP), ({"prec": -1}, EUNSUP),
     ({"prec": 1, "dt": F32}, EUNSUP), ({"prec": 1, "form": SCALAR, "That": False}, EUNSUP),
-    ({"prec": 1, "form": DIAG, "That": False}, EUNSUP),
+    ({"prec": 1, "form": DIAG, "That": False}, EUNSUP), ({"prec": 1, "form": KDA}, EUNSUP),
+    ({"form": KDA, "That": False}, ENULL), ({"form": 4}, EUNSUP),
     ({"dk": 8}, EDIMS), ({"dv": 144}, EDIMS), ({"dk": 24}, EDIMS), ({"B": 0}, EDIMS),
     ({"H": 0}, EDIMS),
     ({"offs": (1, 40, 100)}, EOFF), ({"offs": (0, 50, 40, 100)}, EOFF),
@@ -143,6 +146,9 @@ def test_validate_compose(lib):
     assert vcompose(lib, off=(0, 3, 2, 5)) == ECHAIN
     assert vcompose(lib, That=False) == ENULL
     assert vcompose(lib, form=DIAG, That=True) == EUNSUP
+    assert vcompose(lib, form=KDA) == OK  # KDA pairs compose like dense ones
+    assert vcompose(lib, form=KDA, That=False) == ENULL
+    assert vcompose(lib, form=4) == EUNSUP
     assert vcompose(lib, ws_bytes=1) == EWS
     assert vcompose(lib, dk=130) == EDIMS
     assert vcompose(lib, S_in=ctypes.c_void_p(A + 2)) == EALIGN
@@ -156,6 +162,8 @@ def test_validate_compose_chain_pair(lib):
     assert vcompose(lib, T_out=P(7)) == ENULL
     assert vcompose(lib, form=SCALAR, That=False, lam_out=P(6)) == OK
     assert vcompose(lib, form=DIAG, That=False, lam_out=P(6)) == OK
+    assert vcompose(lib, form=KDA, lam_out=P(6), T_out=P(7)) == OK
+    assert vcompose(lib, form=KDA, lam_out=P(6)) == ENULL
     assert vcompose(lib, form=SCALAR, That=False, lam_out=P(6), T_out=P(7)) == EUNSUP
     assert vcompose(lib, lam_out=P(6), T_out=ctypes.c_void_p(A + 6 * 4096 + 4)) == EALIGN
 
@@ -278,7 +286,7 @@ def test_validate_compose_seams(lib):
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"form": 3}, EUNSUP), ({"dt": 2}, EUNSUP), ({"dk": 8}, EDIMS),
+    ({"form": KDA}, EUNSUP), ({"form": 4}, EUNSUP), ({"dt": 2}, EUNSUP), ({"dk": 8}, EDIMS),
     ({"seam": (1, 1, 8, 16, 16, 20)}, EOFF), ({"seam": (0, 8, 4, 16, 16, 20)}, EOFF),
     ({"seam": (0, 0, 8, 16, 16, 20), "n_seam": 21}, EOFF),
     ({"seam": (0, 65, 65, 65, 65, 65)}, EDIMS), ({"n_seam": -1}, EDIMS),

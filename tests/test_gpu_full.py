@@ -6,7 +6,8 @@ per chain batch).
 * diagonal gates, 32 heads x d=128, 16 x 4096 tokens: every unit;
 * dense GDN, 30 layers x 32 heads x d=128, 32 x 4096 tokens (128K prompt):
   sampled units (the oracle rebuilds them one by one from the same inputs)
-  and sampled composed chains;
+  and sampled composed chains; the same for the delta rule with per-channel
+  gates (KDA form) at that shape;
 * the slow-gate variants, where the carried term T(C2) S(C1) is a sizeable
   part of the state, so composition really exercises T;
 * composition-heavy reuse, 30 layers x 32 heads x d=128: a pool of 256
@@ -83,7 +84,8 @@ def _dense_full(name, layers, samples, chains, precision=0):
     dev = torch.device("cuda:0")
     k = torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=dev)
     v = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=dev)
-    alpha = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    ashape = (B, N, H, dk) if w.form in synth.PER_CHANNEL_GATES else (B, N, H)
+    alpha = torch.empty(ashape, dtype=torch.float32, device=dev)
     beta = torch.empty((B, N, H), dtype=torch.float32, device=dev)
     for layer in range(B):
         x = synth.torch_layer_inputs(w, layer, dev)
@@ -158,6 +160,32 @@ def test_dense_slow_gates_full_length_sampled(precision):
         return [(0, 0)]
 
     _dense_full("dense_30L_32x4096_slow", 2, samples, chains, precision)
+
+
+def test_kda_full_workload_sampled():
+    """Delta rule with per-channel gates at the dense workload's shape (30
+    layers x 32 heads x d=128, 32 x 4096 tokens) in one build call: sampled
+    units and one composed 32-segment chain against the oracle."""
+    def samples(rng, B, H, n_seg):
+        fixed = [(0, 0, 0), (B - 1, H - 1, n_seg - 1)]
+        return fixed + [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_seg)))]
+
+    def chains(rng, B, H):
+        return [(B // 2, 11)]
+
+    _dense_full("kda_30L_32x4096", None, samples, chains)
+
+
+def test_kda_slow_gates_full_length_sampled():
+    """Slow per-channel gates at the full prompt length (2 layers): the
+    composed chain carries a sizeable T(C2) S(C1) term."""
+    def samples(rng, B, H, n_seg):
+        return [(1, 9, 30)]
+
+    def chains(rng, B, H):
+        return [(0, 2)]
+
+    _dense_full("kda_30L_32x4096_slow", 2, samples, chains)
 
 
 @pytest.mark.timeout(400)
