@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "build_diag_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "build_kda_kernel": ["k_build_kda.hip", "pic_internal.hpp"],
 }
 PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
 
@@ -134,6 +135,13 @@ def dense_build_flops_per_token_head(d: int, c: int = CHUNK) -> float:
     plus the chain update 8*d^2 (U That, K^T N, U S, K^T M, each 2*d^2 per
     token)."""
     return 6.0 * c * d + 8.0 * d * d
+
+
+def kda_build_flops_per_token_head(dk: int, dv: int) -> float:
+    """Algorithmic flops of the token-by-token KDA build per token and head:
+    for each element of S (dk x dv) and That (dk x dk), the gate's multiply
+    (1), the column sum X^T k (2) and the rank-one update (2)."""
+    return 5.0 * dk * (dk + dv)
 
 
 def build_bytes(n_tok, layers, heads, dk, dv, n_seg, qkv_bytes=2):
@@ -288,6 +296,109 @@ def bench_scalar_diag(w, args):
                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs(nb, ms[2]) / PEAK_HBM_GBS},
            "hbm_reference": hbm_copy_reference(torch, dev)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_kda(w, args):
+    """Delta rule with per-channel gates (KDA form): build every pair in one
+    call, compose the segments in prompt order, naive add; one JSON line with
+    the build's fp32 vector-ALU roofline."""
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pic.load()
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    offsets = w.offsets()
+    qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    k = torch.empty((B, N, H, dk), dtype=qdt, device=dev)
+    v = torch.empty((B, N, H, dv), dtype=qdt, device=dev)
+    alpha = torch.empty((B, N, H, dk), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    for layer in range(B):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        k[layer].copy_(x["k"])
+        v[layer].copy_(x["v"])
+        alpha[layer].copy_(x["alpha"])
+        beta[layer].copy_(x["beta"])
+        del x
+    pairs = {"log_scale": torch.empty((n_seg, B, H), dtype=torch.float32, device=dev),
+             "T_hat": torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev),
+             "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
+    S_out = torch.empty((1, B, H, dk, dv), dtype=torch.float32, device=dev)
+    S_naive = torch.empty_like(S_out)
+    chain_off, chain_idx = [0, n_seg], list(range(n_seg))
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record=None):
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs)
+        e[1].record(stream)
+        pic.pic_compose(w.form, pairs["log_scale"], pairs["T_hat"], pairs["S0"], chain_off,
+                        chain_idx, None, out=S_out)
+        e[2].record(stream)
+        pic.pic_naive_add(pairs["S0"], chain_off, chain_idx, None, out=S_naive)
+        e[3].record(stream)
+        if record is not None:
+            record.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    t_build, t_comp, t_naive = [float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs])) / 1e3
+                                for i in range(3)]
+    flops = kda_build_flops_per_token_head(dk, dv) * N * B * H
+    achieved_tf = flops / t_build / 1e12
+    qb = 2 if w.qkv_bf16 else 4
+    bb = N * B * H * ((dk + dv) * qb + 4 * dk + 4) + n_seg * B * H * (dk * dk + dk * dv + 1) * 4
+    cb = compose_bytes(n_seg, B, H, dk, dv)
+    nb = naive_bytes(n_seg, B, H, dk, dv)
+    out = {
+        "metric": "KDA segment build tokens/s + state composes/s (H=32, d=128); "
+                  "% fp32 VALU roofline",
+        "value": N / t_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 state and arithmetic, bf16 k/v",
+        "data": "synthetic",
+        "config": {"workload": w.name, "form": "kda", "layers": B, "heads": H, "dk": dk,
+                   "dv": dv, "segments": n_seg, "segment_tokens": int(w.seg_lens[0]),
+                   "prompt_tokens": N},
+        "build_tokens_per_s": N / t_build,
+        "composes_per_s": n_seg * B / t_comp,
+        "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3},
+        "roofline": {"kernel": "build_kda_kernel", "bound": "alu", "achieved": achieved_tf,
+                     "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tf / PEAK_FP32_VALU_TFLOPS,
+                     "traffic": measured_traffic("build_kda_kernel", w.name),
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
+                     "algorithmic_flops": flops},
+        "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
+                             "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS,
+                             "algorithmic_bytes": cb},
+        "roofline_naive_add": {"bound": "hbm", "achieved": nb / t_naive / 1e9,
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -482,6 +593,8 @@ def main(argv=None):
     w = synth.WORKLOADS[args.workload]
     if args.layers:
         w = synth.scaled(w, layers=args.layers, name=w.name)
+    if w.form == synth.KDA:
+        return bench_kda(w, args)
     if w.form != synth.DENSE:
         return bench_scalar_diag(w, args)
     if w.extra.get("pool_size"):
