@@ -21,6 +21,12 @@ module only marshals numpy arrays into it.  What each call computes:
   tokens of every inner segment are left out of the cache and recomputed on
   reuse; linear layers advance the running state through them and pass each
   token's output up]
+* ``rope_matrix`` / ``rerotate`` -- moving a cached pair to another position
+  under rotary position embeddings on the keys: with R_p the rotation of
+  offset p, S' = R_p S and That' = R_p That R_p^T (lambda unchanged), written
+  as explicit fp64 matrices and matrix products (numpy).  [xix.ai, paragraph
+  on linear layers: variants with rotary embeddings need the cached state
+  re-rotated]
 * ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
   its definition: segments as token ranges cut into 64-token chunks, visited
   longest first; chains applied entry by entry.
@@ -279,3 +285,55 @@ def plan_compose(chain_offsets, chain_idx):
     idx = [int(x) for x in chain_idx]
     rows = [(r, c - off[r], idx[c]) for r in range(len(off) - 1) for c in range(off[r], off[r + 1])]
     return np.array(rows, dtype=np.int64).reshape(len(rows), 3)
+
+
+# --------------------------------------------------------------------------
+# re-rotation of cached pairs (rotary position embeddings on the keys)
+# --------------------------------------------------------------------------
+
+ROPE_INTERLEAVED, ROPE_HALF = 0, 1
+
+
+def rope_matrix(dk, shift, rot_dim, base, pairing=ROPE_INTERLEAVED):
+    """The dk x dk rotation R_shift of rotary position embeddings, fp64.
+
+    Channel pair i (i < rot_dim / 2) is (2i, 2i+1) (interleaved) or
+    (i, i + rot_dim/2) (half); it turns by the angle shift * base^(-2i/rot_dim):
+    (x_a, x_b) -> (cos x_a - sin x_b, sin x_a + cos x_b).  Channels at and past
+    rot_dim are left alone.  Keys at position t are R_t k; R_p R_t = R_(p+t)."""
+    R = np.eye(dk)
+    h = rot_dim // 2
+    for i in range(h):
+        a, b = (2 * i, 2 * i + 1) if pairing == ROPE_INTERLEAVED else (i, i + h)
+        phi = float(shift) * float(base) ** (-2.0 * i / rot_dim)
+        c, s = np.cos(phi), np.sin(phi)
+        R[a, a], R[a, b], R[b, a], R[b, b] = c, -s, s, c
+    return R
+
+
+def rerotate(form, lam, That, S, idx, shift, rot_dim, base, pairing=ROPE_INTERLEAVED):
+    """Pool entries idx[j] moved by shift[j] positions: a segment whose keys
+    were rotated at positions t is given keys rotated at positions t + shift.
+
+    Reading: every key gains the factor R_shift, an orthogonal matrix, so each
+    token transition becomes R T_t R^T (exactly for the scalar and dense
+    forms; for the diagonal and KDA forms only when the gates of the two
+    channels of every rotated pair are equal) and by induction
+    S(C|0) -> R S(C|0), T_C -> R T_C R^T; lambda is unchanged.
+    Returns (lam_out [n, ...], That_out [n, B, H, dk, dk] or None,
+    S_out [n, B, H, dk, dv])."""
+    lam, S = _f64(lam), _f64(S)
+    That = _f64(That) if That is not None else None
+    idx = [int(i) for i in idx]
+    shift = [int(p) for p in shift]
+    dk = S.shape[-2]
+    lam_out = np.stack([lam[i] for i in idx]) if idx else np.zeros((0,) + lam.shape[1:])
+    S_out = np.zeros((len(idx),) + S.shape[1:])
+    T_out = np.zeros((len(idx),) + That.shape[1:]) if That is not None else None
+    for j, (i, p) in enumerate(zip(idx, shift)):
+        R = rope_matrix(dk, p, rot_dim, base, pairing)
+        S_out[j] = np.matmul(R, S[i])
+        if That is not None:
+            T_out[j] = np.matmul(np.matmul(R, That[i]), R.T)
+    return lam_out, T_out, S_out
+
