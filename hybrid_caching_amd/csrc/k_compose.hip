@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   const int n = wave * 32 + cl;  // state column of this lane
   const bool ncol = FULL || n < dv;
   const int64_t sdd = int64_t(dk) * dv;
-  const int per_thr = (F4 + nthr - 1) / nthr;  // <= 16 (DKP = 128, 256 threads)
+  const int per_thr = (F4 + nthr - 1) / nthr;  // <= 16: the launcher gives >= F4 / 16 threads
 
   f32x16 S[NT];
 #pragma unroll
@@ -337,10 +337,13 @@ hipError_t launch_dense_chain(const ComposeArgs& a, hipStream_t s) {
   const int64_t units = int64_t(a.n_req) * a.batch * a.heads;
   if (units <= 0) return hipSuccess;
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int waves = (a.dv + 31) / 32;
+  const int dkp = (a.dk + 31) / 32 * 32;
+  // one wave per 32 state columns, and enough threads to stage a whole
+  // operator at 16 float4 items per thread (waves past dv hold zero columns)
+  const int op_waves = (dkp * dkp / 4 + 16 * 64 - 1) / (16 * 64);
+  const int waves = std::max((a.dv + 31) / 32, op_waves);
   const dim3 grid{unsigned(units), 1, 1};
   const dim3 block{unsigned(64 * waves), 1, 1};
-  const int dkp = (a.dk + 31) / 32 * 32;
   switch (dkp) {
     case 32: launch_dense_t<32, PROD>(a, grid, block, s); break;
     case 64: launch_dense_t<64, PROD>(a, grid, block, s); break;

@@ -20,6 +20,8 @@ def rel_fro(x, ref):
     ref = np.asarray(ref, dtype=np.float64)
     num = np.linalg.norm((x - ref).ravel())
     den = np.linalg.norm(ref.ravel())
+    if np.isnan(num) or np.isnan(den):
+        return np.inf
     if den == 0.0:
         return 0.0 if num == 0.0 else np.inf
     return num / den
@@ -35,7 +37,9 @@ def rel_fro_units(x, ref, unit_ndim=2):
     rs = ref.reshape((-1,) + ref.shape[ref.ndim - unit_ndim:])
     worst = 0.0
     for a, b in zip(xs, rs):
-        worst = max(worst, rel_fro(a, b))
+        e = rel_fro(a, b)
+        if not e <= worst:  # NaN counts as the worst error
+            worst = e if not np.isnan(e) else np.inf
     return worst
 
 

@@ -45,7 +45,9 @@ def max_rel_units(got, ref, unit_ndim=2):
     r = ref.reshape((-1,) + ref.shape[ref.ndim - unit_ndim:])
     worst = 0.0
     for a, b in zip(g, r):
-        worst = max(worst, rel_fro(a, b))
+        e = rel_fro(a, b)
+        if not e <= worst:  # NaN counts as the worst error
+            worst = e if not np.isnan(e) else np.inf
     return worst
 
 

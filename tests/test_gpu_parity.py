@@ -435,3 +435,30 @@ def test_chain_tables_in_arguments_and_in_workspace(form, n_req, steps):
     assert max_rel_units(out.cpu().numpy(), ref) <= TOL_F32
     nv = pic.pic_naive_add(to_dev(S), off, idx, None)
     assert max_rel_units(nv.cpu().numpy(), oracle.naive_add(S, off, idx, None)) <= 1e-6
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (128, 32), (128, 96), (96, 32), (64, 16)])
+def test_dense_compose_with_narrower_state(dk, dv):
+    """dv < dk: the block has fewer state columns than operator rows, and the
+    whole operator must still be staged (regression: half of a 128 x 128
+    operator was left unstaged with a 64-column state)."""
+    import hybrid_caching_amd as pic
+    import torch
+    rng = np.random.default_rng(dk * 7 + dv)
+    P, B, H = 5, 2, 2
+    lam = rng.uniform(-0.5, 0.0, size=(P, B, H)).astype(np.float32)
+    T = (rng.standard_normal((P, B, H, dk, dk)) / np.sqrt(dk)).astype(np.float32)
+    S = rng.standard_normal((P, B, H, dk, dv)).astype(np.float32)
+    chain_off, chain_idx = [0, 3, 3, 8], [4, 0, 2, 1, 1, 3, 0, 2]
+    S_in = rng.standard_normal((3, B, H, dk, dv)).astype(np.float32)
+    for sin in (None, S_in):
+        out, lam_c, T_c = pic.pic_compose(DENSE, to_dev(lam), to_dev(T), to_dev(S), chain_off,
+                                          chain_idx, to_dev(sin), want_pair=True)
+        torch.cuda.synchronize()
+        want, want_l, want_T = oracle.compose(DENSE, lam, T, S, chain_off, chain_idx, sin,
+                                              want_pair=True)
+        e = max_rel_units(out.cpu().numpy(), want)
+        e_t = max_rel_units(T_c.cpu().numpy(), want_T)
+        report(f"dk {dk} dv {dv}: compose err {e:.3e}, chain That err {e_t:.3e}")
+        assert e <= TOL_F32 and e_t <= TOL_F32
+        assert lam_err(lam_c.cpu().numpy(), want_l) <= 1e-6
