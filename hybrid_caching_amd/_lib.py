@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpic.so")
 
 FORM_SCALAR, FORM_DIAG, FORM_DENSE, FORM_KDA = 0, 1, 2, 3
+ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 _HAS_T_HAT = (FORM_DENSE, FORM_KDA)
 DT_F32, DT_BF16 = 0, 1
 PREC_FP32, PREC_FP16 = 0, 1
@@ -49,6 +50,11 @@ SIGNATURES = {
     "pic_compose_seams": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _i64,
                                _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "pic_materialize_T": (_i, [_i, _i64, _i, _p, _p, _p, _p]),
+    "pic_rerotate_workspace": (_sz, [_i32]),
+    "pic_validate_rerotate": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _i,
+                                   ctypes.c_double, _i, _p, _p, _p, _p, _sz]),
+    "pic_rerotate": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _i, ctypes.c_double,
+                          _i, _p, _p, _p, _p, _sz, _p]),
     "pic_plan_dump": (_i, [_i, _i32, _p, _p, _i64, _p, _i64]),
 }
 
@@ -257,6 +263,39 @@ def pic_compose_seams(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offs
                                _ptr(out), _ptr(out_O), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "pic_compose_seams")
     return out, out_O
+
+
+def pic_rerotate(form: int, pool_log_scale, pool_T_hat, pool_S0, idx, shift, rot_dim: int,
+                 base: float = 10000.0, pairing: int = 0, *, out=None):
+    """Pool entries idx[j] moved by shift[j] positions under rotary embeddings
+    on the keys: S0' = R S0, That' = R That R^T, lambda unchanged (R turns
+    channel pair i by shift * base^(-2i/rot_dim); pairing ROPE_INTERLEAVED
+    (2i, 2i+1) or ROPE_HALF (i, i + rot_dim/2)).  Returns dict(log_scale,
+    T_hat (dense and KDA), S0) with n = len(idx) entries."""
+    lib = load()
+    P, B, H, dk, dv = pool_S0.shape
+    for t, n in ((pool_log_scale, "pool_log_scale"), (pool_T_hat, "pool_T_hat"),
+                 (pool_S0, "pool_S0")):
+        _need(t, n, torch.float32)
+    n_out = len(idx)
+    if len(shift) != n_out:
+        raise ValueError("idx and shift must have the same length")
+    ix, ix_p = _host_i32(idx)
+    sh, sh_p = _host_i64(shift)
+    dev = pool_S0.device
+    if out is None:
+        out = {"log_scale": torch.empty((n_out,) + tuple(pool_log_scale.shape[1:]),
+                                        dtype=torch.float32, device=dev),
+               "S0": torch.empty((n_out, B, H, dk, dv), dtype=torch.float32, device=dev)}
+        if form in _HAS_T_HAT:
+            out["T_hat"] = torch.empty((n_out, B, H, dk, dk), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.pic_rerotate_workspace(n_out), dev)
+    rc = lib.pic_rerotate(form, B, H, dk, dv, P, _ptr(pool_log_scale), _ptr(pool_T_hat),
+                          _ptr(pool_S0), n_out, ix_p, sh_p, int(rot_dim), float(base),
+                          int(pairing), _ptr(out["log_scale"]), _ptr(out.get("T_hat")),
+                          _ptr(out["S0"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "pic_rerotate")
+    return out
 
 
 def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):

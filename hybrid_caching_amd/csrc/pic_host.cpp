@@ -5,6 +5,7 @@
 #include "pic.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -612,6 +613,107 @@ int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int
   }
   const hipError_t e = pic::launch_compose_seams(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the seam compose kernel");
+  return ok();
+}
+
+/* ------------------------------------------------------------ re-rotation */
+
+static size_t rerotate_ws_bytes(int32_t n) {
+  if (n < 0) return 0;
+  const size_t m = size_t(std::max<int32_t>(n, 1));
+  return align_up(sizeof(int32_t) * m) + align_up(sizeof(int64_t) * m);
+}
+
+size_t pic_rerotate_workspace(int32_t n) { return rerotate_ws_bytes(n); }
+
+static bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uintptr_t(b_bytes) && y < x + uintptr_t(a_bytes);
+}
+
+int pic_validate_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                          const float* pool_log_scale, const float* pool_T_hat,
+                          const float* pool_S0, int32_t n, const int32_t* idx,
+                          const int64_t* shift, int rot_dim, double rope_base, int pairing,
+                          const float* log_scale_out, const float* T_hat_out,
+                          const float* S0_out, const void* workspace, size_t workspace_bytes) {
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
+  if (pairing != PIC_ROPE_INTERLEAVED && pairing != PIC_ROPE_HALF)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown pairing %d", pairing);
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+    return fail(PIC_ERR_UNSUPPORTED, "rope_base must be positive and finite");
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (rot_dim < 8 || rot_dim > dk || rot_dim % 8 != 0)
+    return fail(PIC_ERR_DIMS, "rot_dim (%d) must be a multiple of 8 in [8, dk = %d]", rot_dim, dk);
+  if (n < 0) return fail(PIC_ERR_DIMS, "n (%d) must be >= 0", n);
+  if (pool_size < 0) return fail(PIC_ERR_DIMS, "pool_size must be >= 0");
+  const int64_t per = (form == PIC_FORM_DIAG) ? dk : 1;
+  if (mul_sizes({pool_size, batch, heads, dk, std::max(dk, dv)}) < 0 ||
+      mul_sizes({n, batch, heads, dk, std::max(dk, dv)}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (n == 0) return ok();
+  if (!idx || !shift) return fail(PIC_ERR_NULL, "idx and shift are required");
+  for (int32_t j = 0; j < n; ++j)
+    if (idx[j] < 0 || int64_t(idx[j]) >= pool_size)
+      return fail(PIC_ERR_CHAIN, "idx[%d] = %d outside [0, %lld)", j, idx[j], (long long)pool_size);
+  if (!pool_log_scale || !pool_S0 || !log_scale_out || !S0_out)
+    return fail(PIC_ERR_NULL, "pool_log_scale, pool_S0, log_scale_out and S0_out are required");
+  if (has_T_hat(form) && (!pool_T_hat || !T_hat_out))
+    return fail(PIC_ERR_NULL, "pool_T_hat and T_hat_out are required for the dense and KDA forms");
+  if (!has_T_hat(form) && (pool_T_hat || T_hat_out))
+    return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
+  if (int rc = check_align({pool_log_scale, pool_T_hat, pool_S0, log_scale_out, T_hat_out, S0_out,
+                            workspace}))
+    return rc;
+  const int64_t units_in = pool_size * batch * heads, units_out = int64_t(n) * batch * heads;
+  const int64_t lam_in = units_in * per * 4, lam_out = units_out * per * 4;
+  const int64_t t_in = units_in * dk * dk * 4, t_out = units_out * dk * dk * 4;
+  const int64_t s_in = units_in * dk * dv * 4, s_out = units_out * dk * dv * 4;
+  const void* ins[3] = {pool_log_scale, pool_T_hat, pool_S0};
+  const int64_t in_b[3] = {lam_in, t_in, s_in};
+  const void* outs[3] = {log_scale_out, T_hat_out, S0_out};
+  const int64_t out_b[3] = {lam_out, t_out, s_out};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (overlap(outs[o], out_b[o], ins[i], in_b[i]))
+        return fail(PIC_ERR_UNSUPPORTED, "output %d overlaps the pool", o);
+    for (int p = o + 1; p < 3; ++p)
+      if (overlap(outs[o], out_b[o], outs[p], out_b[p]))
+        return fail(PIC_ERR_UNSUPPORTED, "outputs %d and %d overlap", o, p);
+  }
+  const size_t need = rerotate_ws_bytes(n);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                 const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
+                 int32_t n, const int32_t* idx, const int64_t* shift, int rot_dim,
+                 double rope_base, int pairing, float* log_scale_out, float* T_hat_out,
+                 float* S0_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_rerotate(form, batch, heads, dk, dv, pool_size, pool_log_scale,
+                                     pool_T_hat, pool_S0, n, idx, shift, rot_dim, rope_base,
+                                     pairing, log_scale_out, T_hat_out, S0_out, workspace,
+                                     workspace_bytes))
+    return rc;
+  if (n == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* d_idx = reinterpret_cast<int32_t*>(ws);
+  int64_t* d_shift = reinterpret_cast<int64_t*>(ws + align_up(sizeof(int32_t) * size_t(n)));
+  hipError_t e = staging().copy({{d_idx, idx, sizeof(int32_t) * size_t(n)},
+                                 {d_shift, shift, sizeof(int64_t) * size_t(n)}},
+                                s);
+  if (e != hipSuccess) return hip_fail(e, "copying the re-rotation tables");
+  pic::RotateArgs a{form,    batch,   heads,   dk,      dv,        pool_log_scale,
+                    pool_T_hat, pool_S0, n,    d_idx,   d_shift,   rot_dim,
+                    rope_base, pairing == PIC_ROPE_HALF, log_scale_out, T_hat_out, S0_out};
+  e = pic::launch_rerotate(a, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the re-rotation kernel");
   return ok();
 }
 

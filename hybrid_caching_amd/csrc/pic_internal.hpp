@@ -124,6 +124,26 @@ __device__ __forceinline__ int64_t seam_offset_t(const SeamArgs& a, int64_t c) {
   else return table_at(a.d_seam_off, c);
 }
 
+// Re-rotation of cached pairs (rotary embeddings on the keys): entry j of the
+// output is pool entry d_idx[j] moved by d_shift[j] positions.
+struct RotateArgs {
+  int form;
+  int batch, heads, dk, dv;
+  const float* pool_log_scale;
+  const float* pool_T_hat;  // null for the scalar and diagonal forms
+  const float* pool_S0;
+  int32_t n;
+  const int32_t* d_idx;     // device [n]
+  const int64_t* d_shift;   // device [n]
+  int rot_dim;              // rotated channels, a multiple of 8 in [8, dk]
+  double base;              // angle of pair i: shift * base^(-2i/rot_dim)
+  bool half;                // pairs (i, i + rot/2); else (2i, 2i+1)
+  float* log_scale_out;
+  float* T_hat_out;
+  float* S0_out;
+};
+
+hipError_t launch_rerotate(const RotateArgs& a, hipStream_t s);
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);

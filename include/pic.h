@@ -93,7 +93,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 5
+#define PIC_ABI_VERSION 6
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -307,6 +307,53 @@ int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int
  * -------------------------------------------------------------------- */
 int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,
                       const float* T_hat, float* T_out, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Re-rotation: move cached pairs to another position under rotary position
+ * embeddings (RoPE) on the keys.
+ *   [xix.ai HYPIC article, paragraph on linear layers: variants with rotary
+ *    embeddings need the cached state re-rotated.]
+ *
+ * A segment built with its keys rotated at positions t = 0, 1, ... and
+ * placed `shift` positions later has every key rotated by R_shift on top, so
+ *     S0' = R S0,   That' = R That R^T,   lambda' = lambda
+ * where R turns channel pair i (i < rot_dim / 2) by the angle
+ * shift * base^(-2i/rot_dim): (x_a, x_b) -> (cos x_a - sin x_b, sin x_a + cos x_b),
+ * with the pair (2i, 2i+1) for PIC_ROPE_INTERLEAVED and (i, i + rot_dim/2) for
+ * PIC_ROPE_HALF; channels from rot_dim on are unchanged.  Exact for the scalar,
+ * dense and KDA forms' transitions when R commutes with the gates: always for
+ * scalar and dense, and for the diagonal and KDA forms only when the two
+ * channels of every rotated pair share their gate (not checked).  Angles are
+ * formed in fp64, the rotation applied in fp32.
+ *
+ * Output entry j is pool entry idx[j] moved by shift[j] (negative shifts move
+ * back; 0 copies).  Arguments:
+ * pool_*          the pool as in pic_compose (pool_T_hat: dense and KDA only)
+ * n               number of output entries (0: nothing to do)
+ * idx, shift      HOST int32[n] pool indices in [0, pool_size), int64[n] shifts
+ * rot_dim         rotated channels: a multiple of 8 in [8, dk] (PIC_ERR_DIMS)
+ * rope_base       > 0 and finite (PIC_ERR_UNSUPPORTED otherwise), e.g. 10000
+ * pairing         PIC_ROPE_INTERLEAVED or PIC_ROPE_HALF
+ * log_scale_out, T_hat_out, S0_out   device fp32 outputs laid out as the pool
+ *                 with n entries (T_hat_out: dense and KDA only, else NULL);
+ *                 they must not overlap the pool (PIC_ERR_UNSUPPORTED)
+ * -------------------------------------------------------------------- */
+enum pic_rope_pairing { PIC_ROPE_INTERLEAVED = 0, PIC_ROPE_HALF = 1 };
+
+size_t pic_rerotate_workspace(int32_t n);
+
+int pic_validate_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                          const float* pool_log_scale, const float* pool_T_hat,
+                          const float* pool_S0, int32_t n, const int32_t* idx,
+                          const int64_t* shift, int rot_dim, double rope_base, int pairing,
+                          const float* log_scale_out, const float* T_hat_out,
+                          const float* S0_out, const void* workspace, size_t workspace_bytes);
+
+int pic_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                 const float* pool_log_scale, const float* pool_T_hat, const float* pool_S0,
+                 int32_t n, const int32_t* idx, const int64_t* shift, int rot_dim,
+                 double rope_base, int pairing, float* log_scale_out, float* T_hat_out,
+                 float* S0_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Plan dump: the host-side bookkeeping a build or compose call would use,

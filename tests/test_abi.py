@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 5
+    assert lib.pic_abi_version() == 6
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -302,3 +302,46 @@ def test_validate_compose_seams_rejects(lib, kw, code):
 
 def test_compose_seams_workspace_grows_with_the_chain(lib):
     assert lib.pic_compose_seams_workspace(4, 100) >= lib.pic_compose_workspace(4, 100) + 8 * 101
+
+
+def vrot(lib, form=DENSE, B=1, H=2, dk=128, dv=128, pool=5, idx=(4, 0, 0), shift=(7, -3, 0),
+         rot=64, base=10000.0, pairing=0, That=True, ws_bytes=None, S0_out=None, T_out=None):
+    i = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    sh = np.ascontiguousarray(np.asarray(shift, dtype=np.int64))
+    n = len(i)
+    need = lib.pic_rerotate_workspace(n)
+    big = 1 << 32  # output buffers far from the pool's
+    return lib.pic_validate_rerotate(
+        form, B, H, dk, dv, pool, P(0), P(1) if That else None, P(2), n,
+        i.ctypes.data_as(ctypes.c_void_p) if n else None,
+        sh.ctypes.data_as(ctypes.c_void_p) if n else None, rot, base, pairing,
+        ctypes.c_void_p(big), (ctypes.c_void_p(2 * big) if T_out is None else T_out) if That else None,
+        ctypes.c_void_p(3 * big) if S0_out is None else S0_out, P(7),
+        need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_rerotate(lib):
+    assert vrot(lib) == OK
+    assert vrot(lib, form=KDA) == OK
+    assert vrot(lib, form=SCALAR, That=False, rot=8, pairing=1) == OK
+    assert vrot(lib, form=DIAG, That=False, dk=16, dv=48, rot=16) == OK
+    assert vrot(lib, idx=(), shift=()) == OK
+    assert lib.pic_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"form": 4}, EUNSUP), ({"pairing": 2}, EUNSUP), ({"base": 0.0}, EUNSUP),
+    ({"base": float("inf")}, EUNSUP), ({"base": float("nan")}, EUNSUP),
+    ({"rot": 0}, EDIMS), ({"rot": 12}, EDIMS), ({"rot": 136}, EDIMS),
+    ({"dk": 16, "dv": 16, "rot": 24}, EDIMS), ({"dk": 8}, EDIMS),
+    ({"idx": (4, 5, 0)}, ECHAIN), ({"idx": (-1, 0, 0)}, ECHAIN),
+    ({"That": False}, ENULL), ({"form": SCALAR, "That": True}, EUNSUP),
+    ({"ws_bytes": 4}, EWS),
+    ({"S0_out": ctypes.c_void_p(A * 3 + 16)}, EUNSUP),   # inside the pool's S0
+    ({"T_out": ctypes.c_void_p((1 << 32) * 3)}, EUNSUP),  # on top of S0_out
+    ({"S0_out": ctypes.c_void_p((1 << 32) * 3 + 4)}, EALIGN),
+])
+def test_validate_rerotate_rejects(lib, kw, code):
+    assert vrot(lib, **kw) == code
+    assert lib.pic_last_error().decode() != ""
+
