@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_kda_kernel": ["k_build_kda.hip", "pic_internal.hpp"],
+    "rerotate_kernel": ["k_rerotate.hip", "pic_internal.hpp"],
 }
 PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
 
@@ -680,6 +681,26 @@ def main(argv=None):
                  "ms": t_other * 1e3, "build_tokens_per_s": N / t_other,
                  "achieved_tflops": flops / t_other / 1e12,
                  "frac_of_bf16_peak": flops / t_other / 1e12 / PEAK_BF16_TFLOPS}
+    # re-rotation of every built pair to a new offset (rotary embeddings on the
+    # keys, rot_dim = d_k, half pairing), out of place; not part of `value`
+    rr_shift = [int(x) for x in np.cumsum([0] + list(w.seg_lens[:-1]))]
+    moved = {"log_scale": torch.empty_like(pairs["log_scale"]),
+             "T_hat": torch.empty_like(pairs["T_hat"]), "S0": torch.empty_like(pairs["S0"])}
+    rr = lambda: pic.pic_rerotate(w.form, pairs["log_scale"], pairs["T_hat"], pairs["S0"],
+                                  list(range(n_seg)), rr_shift, dk, 10000.0, pic.ROPE_HALF,
+                                  out=moved)
+    rr()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(3):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        rr()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t_rr = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs])) / 1e3
+    rrb = 2 * n_seg * B * H * (dk * dk + dk * dv + 1) * 4
     composes = n_seg * B  # pairs applied to a running state, per layer (all heads)
     build_kernel = "build_dense_h16_kernel" if args.prec else "build_dense_ws_kernel"
     cb = compose_bytes(n_seg, B, H, dk, dv)
@@ -720,6 +741,11 @@ def main(argv=None):
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
         "build_hbm_gbs": build_bytes(N, B, H, dk, dv, n_seg) / t_build / 1e9,
+        "rerotate": {"kernel": "rerotate_kernel", "pairs": n_seg * B * H, "ms": t_rr * 1e3,
+                     "bound": "hbm", "achieved": rrb / t_rr / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": rrb / t_rr / 1e9 / PEAK_HBM_GBS,
+                     "algorithmic_bytes": rrb,
+                     "traffic": measured_traffic("rerotate_kernel", w.name)},
     }
     if other is not None:
         out["build_other_precision"] = other

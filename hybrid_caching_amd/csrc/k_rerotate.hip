@@ -13,12 +13,11 @@
 //
 // One workgroup per (entry, layer, head).  The pair's angles are formed in
 // fp64 (an fp32 product p * theta loses the angle at long offsets) and kept in
-// LDS as fp32 cos / sin.  Each thread step writes one float4 of the output:
-// S0 rows combine the row and its partner; That rows are combined the same
-// way, then columns (the partner column lies in the same float4 for the
-// interleaved pairing and in the float4 rot/8 groups away for the half one).
-// Memory bound: every pool float is read once from HBM (partner reads hit the
-// cache) and every output float written once.
+// LDS as fp32 cos / sin.  A thread item holds everything one rotation step
+// mixes: a rotated row pair (or one unrotated row) of float4 groups, and for
+// That also the partner column group (in the same float4 for the interleaved
+// pairing, rot/8 groups away for the half one).  Memory bound: every pool
+// float is read once and every output float written once.
 #include "pic_internal.hpp"
 
 namespace pic {
@@ -27,11 +26,6 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
-__device__ __forceinline__ float4 comb(float c, float s, float4 m, float4 p) {
-  return make_float4(fmaf(s, p.x, c * m.x), fmaf(s, p.y, c * m.y), fmaf(s, p.z, c * m.z),
-                     fmaf(s, p.w, c * m.w));
-}
 
 __global__ __launch_bounds__(kThreads) void rerotate_kernel(RotateArgs a) {
   __shared__ float cs_c[64], cs_s[64];
@@ -53,82 +47,115 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(RotateArgs a) {
     a.log_scale_out[dst * per + t] = a.pool_log_scale[src * per + t];
   __syncthreads();
 
-  // row x of R M = c M[x] + s M[px]  (s carries the sign of x's place in its pair)
-  auto rowrot = [&](int x, float& c, float& s, int& px) {
-    if (x >= rot) {
+  // Work items pair what the rotation mixes, so each thread reads every value
+  // it combines and no value is read twice: a row unit is a rotated row pair
+  // (a, b) (u < rot/2) or one unrotated row; for That a column unit is the
+  // float4 group pair (g, g + rot/8) (half pairing, g < rot/8) or one group
+  // (interleaved pairs sit inside a float4; groups past rot/4 are unrotated).
+  const int n_ru = h2 + (dk - rot);
+  auto row_unit = [&](int u, int& ra, int& rb, float& c, float& s) {
+    if (u < h2) {
+      ra = half ? u : 2 * u;
+      rb = half ? u + h2 : 2 * u + 1;
+      c = cs_c[u];
+      s = cs_s[u];
+    } else {
+      ra = rb = rot + (u - h2);
       c = 1.f;
       s = 0.f;
-      px = x;
-      return;
     }
-    int i;
-    if (half) {
-      const bool first = x < h2;
-      i = first ? x : x - h2;
-      px = first ? x + h2 : x - h2;
-      s = first ? -cs_s[i] : cs_s[i];
-    } else {
-      i = x >> 1;
-      px = x ^ 1;
-      s = (x & 1) ? cs_s[i] : -cs_s[i];
-    }
-    c = cs_c[i];
+  };
+  // (x_a, x_b) -> (c x_a - s x_b, s x_a + c x_b), per float4 lane
+  auto turn = [](float c, float s, float4& xa, float4& xb) {
+    const float4 a0 = xa, b0 = xb;
+    xa = make_float4(fmaf(-s, b0.x, c * a0.x), fmaf(-s, b0.y, c * a0.y), fmaf(-s, b0.z, c * a0.z),
+                     fmaf(-s, b0.w, c * a0.w));
+    xb = make_float4(fmaf(s, a0.x, c * b0.x), fmaf(s, a0.y, c * b0.y), fmaf(s, a0.z, c * b0.z),
+                     fmaf(s, a0.w, c * b0.w));
   };
 
   {
     const float* M = a.pool_S0 + src * int64_t(dk) * dv;
     float* O = a.S0_out + dst * int64_t(dk) * dv;
     const int g4 = dv / 4;
-    for (int e = threadIdx.x; e < dk * g4; e += kThreads) {
-      const int x = e / g4, g = e % g4;
+    for (int e = threadIdx.x; e < n_ru * g4; e += kThreads) {
+      const int u = e / g4, g = e % g4;
+      int ra, rb;
       float c, s;
-      int px;
-      rowrot(x, c, s, px);
-      const float4 r = comb(c, s, ld4(M + int64_t(x) * dv + 4 * g), ld4(M + int64_t(px) * dv + 4 * g));
-      *reinterpret_cast<float4*>(O + int64_t(x) * dv + 4 * g) = r;
+      row_unit(u, ra, rb, c, s);
+      float4 xa = ld4(M + int64_t(ra) * dv + 4 * g);
+      if (ra == rb) {
+        *reinterpret_cast<float4*>(O + int64_t(ra) * dv + 4 * g) = xa;
+        continue;
+      }
+      float4 xb = ld4(M + int64_t(rb) * dv + 4 * g);
+      turn(c, s, xa, xb);
+      *reinterpret_cast<float4*>(O + int64_t(ra) * dv + 4 * g) = xa;
+      *reinterpret_cast<float4*>(O + int64_t(rb) * dv + 4 * g) = xb;
     }
   }
   if (a.pool_T_hat) {
     const float* M = a.pool_T_hat + src * int64_t(dk) * dk;
     float* O = a.T_hat_out + dst * int64_t(dk) * dk;
-    const int g4 = dk / 4;
-    for (int e = threadIdx.x; e < dk * g4; e += kThreads) {
-      const int x = e / g4, g = e % g4;
+    const int r8 = rot / 8, r4 = rot / 4;
+    const int n_cu = half ? r8 + (dk / 4 - r4) : dk / 4;
+    for (int e = threadIdx.x; e < n_ru * n_cu; e += kThreads) {
+      const int u = e / n_cu, v = e % n_cu;
+      int ra, rb;
       float c, s;
-      int px;
-      rowrot(x, c, s, px);
-      const float* mx = M + int64_t(x) * dk;
-      const float* mp = M + int64_t(px) * dk;
-      const float4 own = comb(c, s, ld4(mx + 4 * g), ld4(mp + 4 * g));
-      float4 out = own;
-      if (4 * g < rot) {
-        const float ov[4] = {own.x, own.y, own.z, own.w};
-        float pv[4];
-        if (half) {
-          const int pg = (4 * g < h2) ? g + h2 / 4 : g - h2 / 4;
-          const float4 part = comb(c, s, ld4(mx + 4 * pg), ld4(mp + 4 * pg));
-          pv[0] = part.x; pv[1] = part.y; pv[2] = part.z; pv[3] = part.w;
-        } else {
-          pv[0] = ov[1]; pv[1] = ov[0]; pv[2] = ov[3]; pv[3] = ov[2];
-        }
-        float r[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int y = 4 * g + u;
-          int i;
-          float sc;
-          if (half) {
-            i = y < h2 ? y : y - h2;
-            sc = y < h2 ? -cs_s[i] : cs_s[i];
-          } else {
-            i = y >> 1;
-            sc = (y & 1) ? cs_s[i] : -cs_s[i];
-          }
-          r[u] = fmaf(sc, pv[u], cs_c[i] * ov[u]);
-        }
-        out = make_float4(r[0], r[1], r[2], r[3]);
+      row_unit(u, ra, rb, c, s);
+      const bool rpair = ra != rb;
+      // column groups of this item: ga and (half pairing, rotated) gb
+      int ga, gb;
+      if (half) {
+        ga = v < r8 ? v : r4 + (v - r8);
+        gb = v < r8 ? v + r8 : ga;
+      } else {
+        ga = gb = v;
       }
-      *reinterpret_cast<float4*>(O + int64_t(x) * dk + 4 * g) = out;
+      const bool cpair = ga != gb;
+      float4 aa = ld4(M + int64_t(ra) * dk + 4 * ga), ba = aa, ab = aa, bb = aa;
+      if (rpair) ba = ld4(M + int64_t(rb) * dk + 4 * ga);
+      if (cpair) {
+        ab = ld4(M + int64_t(ra) * dk + 4 * gb);
+        if (rpair) bb = ld4(M + int64_t(rb) * dk + 4 * gb);
+      }
+      // rows
+      if (rpair) {
+        turn(c, s, aa, ba);
+        if (cpair) turn(c, s, ab, bb);
+      }
+      // columns
+      if (cpair) {
+        // column 4 ga + l pairs with 4 gb + l, angle index 4 ga + l
+        const float4 cc = make_float4(cs_c[4 * ga], cs_c[4 * ga + 1], cs_c[4 * ga + 2], cs_c[4 * ga + 3]);
+        const float4 ss = make_float4(cs_s[4 * ga], cs_s[4 * ga + 1], cs_s[4 * ga + 2], cs_s[4 * ga + 3]);
+        auto cturn = [&](float4& xa, float4& xb) {
+          const float4 a0 = xa, b0 = xb;
+          xa = make_float4(fmaf(-ss.x, b0.x, cc.x * a0.x), fmaf(-ss.y, b0.y, cc.y * a0.y),
+                           fmaf(-ss.z, b0.z, cc.z * a0.z), fmaf(-ss.w, b0.w, cc.w * a0.w));
+          xb = make_float4(fmaf(ss.x, a0.x, cc.x * b0.x), fmaf(ss.y, a0.y, cc.y * b0.y),
+                           fmaf(ss.z, a0.z, cc.z * b0.z), fmaf(ss.w, a0.w, cc.w * b0.w));
+        };
+        cturn(aa, ab);
+        if (rpair) cturn(ba, bb);
+      } else if (!half && 4 * ga < rot) {
+        // interleaved: columns (4ga, 4ga+1) and (4ga+2, 4ga+3), angles 2ga, 2ga+1
+        const float c0 = cs_c[2 * ga], s0 = cs_s[2 * ga], c1 = cs_c[2 * ga + 1], s1 = cs_s[2 * ga + 1];
+        auto iturn = [&](float4& x) {
+          const float4 y = x;
+          x = make_float4(fmaf(-s0, y.y, c0 * y.x), fmaf(s0, y.x, c0 * y.y),
+                          fmaf(-s1, y.w, c1 * y.z), fmaf(s1, y.z, c1 * y.w));
+        };
+        iturn(aa);
+        if (rpair) iturn(ba);
+      }
+      *reinterpret_cast<float4*>(O + int64_t(ra) * dk + 4 * ga) = aa;
+      if (rpair) *reinterpret_cast<float4*>(O + int64_t(rb) * dk + 4 * ga) = ba;
+      if (cpair) {
+        *reinterpret_cast<float4*>(O + int64_t(ra) * dk + 4 * gb) = ab;
+        if (rpair) *reinterpret_cast<float4*>(O + int64_t(rb) * dk + 4 * gb) = bb;
+      }
     }
   }
 }
