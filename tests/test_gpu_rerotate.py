@@ -77,11 +77,12 @@ def test_rerotate_nothing_to_do():
     assert out["S0"].shape[0] == 0
 
 
-@pytest.mark.parametrize("form", [DENSE, SCALAR])
+@pytest.mark.parametrize("form", [DENSE, SCALAR, KDA])
 def test_moved_segments_compose_into_the_prompt(form):
     """Segments built on the GPU with keys rotated at positions relative to
     each segment, moved to their offsets, composed: the oracle's recurrence
-    over the same keys rotated at absolute positions."""
+    over the same keys rotated at absolute positions.  KDA gates are shared
+    within each rotated channel pair (the condition of the reading)."""
     import hybrid_caching_amd as pic
     import torch
     B, H, dk, dv = 2, 2, 128, 64
@@ -91,9 +92,13 @@ def test_moved_segments_compose_into_the_prompt(form):
     k = rng.standard_normal((B, N, H, dk))
     k /= np.linalg.norm(k, axis=-1, keepdims=True)
     v = rng.standard_normal((B, N, H, dv)).astype(np.float32)
-    a = rng.uniform(0.995, 1.0, size=(B, N, H)).astype(np.float32)
-    b = rng.uniform(0.0, 0.05, size=(B, N, H)).astype(np.float32) if form == DENSE else None
     rot, base = 64, 10000.0
+    if form == KDA:
+        a = rng.uniform(0.995, 1.0, size=(B, N, H, dk)).astype(np.float32)
+        a[..., rot // 2:rot] = a[..., :rot // 2]  # half pairing: channel i pairs with i + rot/2
+    else:
+        a = rng.uniform(0.995, 1.0, size=(B, N, H)).astype(np.float32)
+    b = rng.uniform(0.0, 0.05, size=(B, N, H)).astype(np.float32) if form != SCALAR else None
     n = len(cuts) - 1
     rel = np.concatenate([rope_keys(k[:, cuts[s]:cuts[s + 1]], np.arange(cuts[s + 1] - cuts[s]),
                                     rot, base, ROPE_HALF) for s in range(n)], axis=1)
