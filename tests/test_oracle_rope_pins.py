@@ -162,3 +162,41 @@ def test_segments_built_at_zero_moved_and_composed_equal_the_prompt(form):
     absk = rope_keys(k, np.arange(N), rot, base, ROPE_HALF)
     want = oracle.recurrence(form, absk, v, a, b)
     assert rel_fro(got[0], want) <= 1e-11
+
+
+def _mutant_rope(kind):
+    """rope_matrix with one planted mistake."""
+    def R(dk, shift, rot_dim, base, pairing=ROPE_INTERLEAVED):
+        M = np.eye(dk)
+        h = rot_dim // 2
+        for i in range(h):
+            a, b = (2 * i, 2 * i + 1) if pairing == ROPE_INTERLEAVED else (i, i + h)
+            if kind == "pairing swapped":
+                a, b = (i, i + h) if pairing == ROPE_INTERLEAVED else (2 * i, 2 * i + 1)
+            expo = -1.0 * i / rot_dim if kind == "exponent -i/d" else -2.0 * i / rot_dim
+            phi = float(shift) * float(base) ** expo
+            c, s = np.cos(phi), np.sin(phi)
+            if kind == "transposed":
+                s = -s
+            M[a, a], M[a, b], M[b, a], M[b, b] = c, -s, s, c
+            if kind == "last pair skipped" and i == h - 1:
+                M[a, a], M[a, b], M[b, a], M[b, b] = 1.0, 0.0, 0.0, 1.0
+        return M
+    return R
+
+
+@pytest.mark.parametrize("kind", ["pairing swapped", "exponent -i/d", "transposed",
+                                  "last pair skipped"])
+def test_pins_catch_planted_mistakes(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "rope_matrix", _mutant_rope(kind))
+    checks = [lambda: test_rerotated_pair_is_the_pair_at_the_new_position(DENSE, ROPE_HALF, 8),
+              lambda: test_rerotated_pair_is_the_pair_at_the_new_position(DENSE,
+                                                                          ROPE_INTERLEAVED, 8),
+              test_rope_matrix_hand_values]
+    caught = 0
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, kind
