@@ -27,6 +27,11 @@ module only marshals numpy arrays into it.  What each call computes:
   as explicit fp64 matrices and matrix products (numpy).  [xix.ai, paragraph
   on linear layers: variants with rotary embeddings need the cached state
   re-rotated]
+* ``conv_warmup`` -- the first tokens of a segment under a short causal
+  depthwise convolution of width W, recomputed with the previous segment's
+  last raw inputs as history: y_t = sum_j w_j x_(t-j), written as plain loops.
+  [xix.ai, paragraph on linear layers: variants with a short convolution need
+  the convolution state warmed up]
 * ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
   its definition: segments as token ranges cut into 64-token chunks, visited
   longest first; chains applied entry by entry.
@@ -336,4 +341,39 @@ def rerotate(form, lam, That, S, idx, shift, rot_dim, base, pairing=ROPE_INTERLE
         if That is not None:
             T_out[j] = np.matmul(np.matmul(R, That[i]), R.T)
     return lam_out, T_out, S_out
+
+
+# --------------------------------------------------------------------------
+# convolution warm-up (short causal depthwise convolution before the layer)
+# --------------------------------------------------------------------------
+
+def conv_warmup(weight, x, hist_end, hist_len, head_start, n_warm):
+    """Conv outputs of the first n_warm tokens of each entry's segment.
+
+    weight [H, dc, W]: y_t = sum_{j < W} weight[..., j] * x_(t-j) per channel
+    (j = 0 the token itself).  x [B, N, H, dc] raw inputs.  Entry e reads its
+    head tokens x[:, head_start[e] + t] and, for t - j < 0, the history token
+    x[:, hist_end[e] + (t - j)] when -(t - j) <= hist_len[e], else 0 (no
+    history: the independent prefill).  Returns y [B, n * n_warm, H, dc],
+    entry e's tokens at rows e * n_warm .. e * n_warm + n_warm - 1."""
+    w = _f64(weight)
+    x = _f64(x)
+    B, N, H, dc = x.shape
+    W = w.shape[-1]
+    n = len(head_start)
+    y = np.zeros((B, n * n_warm, H, dc))
+    for e in range(n):
+        for t in range(n_warm):
+            acc = np.zeros((B, H, dc))
+            for j in range(W):
+                tau = t - j
+                if tau >= 0:
+                    xv = x[:, int(head_start[e]) + tau]
+                elif -tau <= int(hist_len[e]):
+                    xv = x[:, int(hist_end[e]) + tau]
+                else:
+                    continue
+                acc = acc + w[None, :, :, j] * xv
+            y[:, e * n_warm + t] = acc
+    return y
 
