@@ -50,6 +50,11 @@ SIGNATURES = {
     "pic_compose_seams": (_i, [_i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _i64,
                                _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "pic_materialize_T": (_i, [_i, _i64, _i, _p, _p, _p, _p]),
+    "pic_conv_warmup_workspace": (_sz, [_i32]),
+    "pic_validate_conv_warmup": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _i32, _i32, _p, _p, _p, _p,
+                                      _p, _sz]),
+    "pic_conv_warmup": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _i32, _i32, _p, _p, _p, _p, _p, _sz,
+                             _p]),
     "pic_rerotate_workspace": (_sz, [_i32]),
     "pic_validate_rerotate": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _i,
                                    ctypes.c_double, _i, _p, _p, _p, _p, _sz]),
@@ -295,6 +300,36 @@ def pic_rerotate(form: int, pool_log_scale, pool_T_hat, pool_S0, idx, shift, rot
                           int(pairing), _ptr(out["log_scale"]), _ptr(out.get("T_hat")),
                           _ptr(out["S0"]), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "pic_rerotate")
+    return out
+
+
+def pic_conv_warmup(weight, x, head_start, hist_end, hist_len, n_warm: int, *, out=None):
+    """Conv outputs y_t = sum_j weight[..., j] x_(t-j) of the first n_warm tokens
+    of each entry's segment, with the previous segment's raw tail as history.
+
+    weight fp32 [H, dc, W]; x [B, N, H, dc] (bf16 or fp32, raw inputs);
+    head_start, hist_end: host ints [n]; hist_len: host ints [n] in [0, W-1].
+    Returns y [B, n * n_warm, H, dc] in x's dtype (the seam layout)."""
+    lib = load()
+    B, N, H, dc = x.shape
+    W = weight.shape[-1]
+    _need(weight, "weight", torch.float32)
+    _need(x, "x", None)
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bfloat16 or float32")
+    dt = DT_BF16 if x.dtype == torch.bfloat16 else DT_F32
+    n = len(head_start)
+    if len(hist_end) != n or len(hist_len) != n:
+        raise ValueError("head_start, hist_end and hist_len must have the same length")
+    hs, hs_p = _host_i64(head_start)
+    he, he_p = _host_i64(hist_end)
+    hl, hl_p = _host_i32(hist_len)
+    if out is None:
+        out = torch.empty((B, n * n_warm, H, dc), dtype=x.dtype, device=x.device)
+    ws = _workspace(lib.pic_conv_warmup_workspace(n), x.device)
+    rc = lib.pic_conv_warmup(dt, B, H, dc, W, N, _ptr(weight), _ptr(x), n, int(n_warm), hs_p,
+                             he_p, hl_p, _ptr(out), _ptr(ws), ws.numel(), _stream(x.device))
+    _check(rc, "pic_conv_warmup")
     return out
 
 

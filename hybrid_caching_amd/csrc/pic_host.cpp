@@ -717,6 +717,84 @@ int pic_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_si
   return ok();
 }
 
+/* ------------------------------------------------------------ conv warm-up */
+
+static size_t conv_ws_bytes(int32_t n) {
+  if (n < 0) return 0;
+  const size_t m = size_t(std::max<int32_t>(n, 1));
+  return 2 * align_up(sizeof(int64_t) * m) + align_up(sizeof(int32_t) * m);
+}
+
+size_t pic_conv_warmup_workspace(int32_t n) { return conv_ws_bytes(n); }
+
+int pic_validate_conv_warmup(int x_dtype, int batch, int heads, int dc, int width,
+                             int64_t n_tokens, const float* weight, const void* x, int32_t n,
+                             int32_t n_warm, const int64_t* head_start, const int64_t* hist_end,
+                             const int32_t* hist_len, const void* y_out, const void* workspace,
+                             size_t workspace_bytes) {
+  if (x_dtype != PIC_DT_F32 && x_dtype != PIC_DT_BF16)
+    return fail(PIC_ERR_UNSUPPORTED, "unknown dtype %d", x_dtype);
+  if (int rc = check_common_dims(batch, heads, dc, dc)) return rc;
+  if (width < 1 || width > PIC_MAX_CONV)
+    return fail(PIC_ERR_DIMS, "width (%d) must be in [1, %d]", width, PIC_MAX_CONV);
+  if (n < 0 || n_warm < 0 || n_warm > PIC_MAX_SEAM || n_tokens < 0)
+    return fail(PIC_ERR_DIMS, "n, n_tokens >= 0 and n_warm in [0, %d] required", PIC_MAX_SEAM);
+  if (mul_sizes({batch, n_tokens, heads, dc}) < 0 || mul_sizes({batch, n, n_warm, heads, dc}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (n > 0 && (!head_start || !hist_end || !hist_len))
+    return fail(PIC_ERR_NULL, "head_start, hist_end and hist_len are required");
+  for (int32_t e = 0; e < n; ++e) {
+    if (hist_len[e] < 0 || hist_len[e] > width - 1)
+      return fail(PIC_ERR_OFFSETS, "hist_len[%d] = %d outside [0, width - 1]", e, hist_len[e]);
+    if (hist_len[e] > 0 && (hist_end[e] < hist_len[e] || hist_end[e] > n_tokens))
+      return fail(PIC_ERR_OFFSETS, "history of entry %d outside the %lld tokens", e,
+                  (long long)n_tokens);
+    if (n_warm > 0 && (head_start[e] < 0 || head_start[e] > n_tokens - n_warm))
+      return fail(PIC_ERR_OFFSETS, "head of entry %d outside the %lld tokens", e,
+                  (long long)n_tokens);
+  }
+  if (int64_t(n) * n_warm == 0) return ok();
+  if (!weight || !x || !y_out) return fail(PIC_ERR_NULL, "weight, x and y_out are required");
+  if (int rc = check_align({weight, x, y_out, workspace})) return rc;
+  const int64_t es = (x_dtype == PIC_DT_BF16) ? 2 : 4;
+  const int64_t y_b = int64_t(batch) * n * n_warm * heads * dc * es;
+  if (overlap(y_out, y_b, x, int64_t(batch) * n_tokens * heads * dc * es) ||
+      overlap(y_out, y_b, weight, int64_t(heads) * dc * width * 4))
+    return fail(PIC_ERR_UNSUPPORTED, "y_out overlaps x or weight");
+  const size_t need = conv_ws_bytes(n);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_conv_warmup(int x_dtype, int batch, int heads, int dc, int width, int64_t n_tokens,
+                    const float* weight, const void* x, int32_t n, int32_t n_warm,
+                    const int64_t* head_start, const int64_t* hist_end, const int32_t* hist_len,
+                    void* y_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_conv_warmup(x_dtype, batch, heads, dc, width, n_tokens, weight, x, n,
+                                        n_warm, head_start, hist_end, hist_len, y_out, workspace,
+                                        workspace_bytes))
+    return rc;
+  if (int64_t(n) * n_warm == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t b64 = align_up(sizeof(int64_t) * size_t(n));
+  int64_t* d_head = reinterpret_cast<int64_t*>(ws);
+  int64_t* d_hend = reinterpret_cast<int64_t*>(ws + b64);
+  int32_t* d_hlen = reinterpret_cast<int32_t*>(ws + 2 * b64);
+  hipError_t e = staging().copy({{d_head, head_start, sizeof(int64_t) * size_t(n)},
+                                 {d_hend, hist_end, sizeof(int64_t) * size_t(n)},
+                                 {d_hlen, hist_len, sizeof(int32_t) * size_t(n)}},
+                                s);
+  if (e != hipSuccess) return hip_fail(e, "copying the warm-up tables");
+  pic::ConvArgs a{x_dtype == PIC_DT_BF16, batch, heads, dc, width, n_tokens, weight, x, n,
+                  n_warm, d_hend, d_hlen, d_head, y_out};
+  e = pic::launch_conv_warmup(a, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the warm-up kernel");
+  return ok();
+}
+
 /* ------------------------------------------------------------ materialize */
 
 int pic_materialize_T(int form, int64_t n_units, int dk, const float* log_scale,

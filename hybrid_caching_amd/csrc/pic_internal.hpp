@@ -144,6 +144,23 @@ struct RotateArgs {
 };
 
 hipError_t launch_rerotate(const RotateArgs& a, hipStream_t s);
+
+// Convolution warm-up: conv outputs of the first n_warm tokens of each entry's
+// segment, with the previous segment's raw tail as history.
+struct ConvArgs {
+  bool bf16;                   // x and y are bf16 (else fp32)
+  int batch, heads, dc, width;
+  int64_t n_tokens;
+  const float* weight;         // [heads][dc][width]
+  const void* x;               // [batch][n_tokens][heads][dc]
+  int32_t n, n_warm;
+  const int64_t* d_hist_end;   // device [n]
+  const int32_t* d_hist_len;   // device [n]
+  const int64_t* d_head_start; // device [n]
+  void* y;                     // [batch][n * n_warm][heads][dc]
+};
+
+hipError_t launch_conv_warmup(const ConvArgs& a, hipStream_t s);
 hipError_t launch_build_scalar_diag(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_sd_pipe(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);

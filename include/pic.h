@@ -93,7 +93,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 6
+#define PIC_ABI_VERSION 7
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -354,6 +354,52 @@ int pic_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_si
                  int32_t n, const int32_t* idx, const int64_t* shift, int rot_dim,
                  double rope_base, int pairing, float* log_scale_out, float* T_hat_out,
                  float* S0_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Convolution warm-up: for variants with a short causal depthwise
+ * convolution of width W in front of the linear layer,
+ *     y_t = sum_{j < W} weight[h][c][j] * x_(t-j)       (j = 0 the token itself)
+ * a segment's first W-1 outputs read the previous segment's raw inputs, so
+ * they are kept out of its cached pair and recomputed on reuse: this call
+ * writes them in the seam layout, ready for pic_compose_seams (as its q, k or
+ * v, one call per stream), with the pair covering the tokens after them.
+ * Any per-token activation or normalisation the model applies after the
+ * convolution is the caller's, between this call and the seam compose.
+ *   [xix.ai HYPIC article, paragraph on linear layers: variants with a short
+ *    convolution need the convolution state warmed up.]
+ *
+ * x_dtype      PIC_DT_BF16 or PIC_DT_F32: the type of x and y_out
+ * dc           channels per head (dk for q / k, dv for v): as dk in the sizes rule
+ * width        W in [1, PIC_MAX_CONV]
+ * weight       device fp32 [heads][dc][width]
+ * x            device [batch][n_tokens][heads][dc], raw inputs (the caller's
+ *              store of the cached segments' inputs)
+ * n, n_warm    entries and output tokens per entry (0 <= n_warm <= PIC_MAX_SEAM;
+ *              usually W - 1)
+ * head_start   HOST int64[n]: entry e's head tokens are x[:, head_start[e] + t],
+ *              t < n_warm (head_start + n_warm <= n_tokens)
+ * hist_end, hist_len  HOST int64[n], int32[n]: entry e's history is
+ *              x[:, hist_end[e] - hist_len[e] .. hist_end[e] - 1], the raw
+ *              inputs just before its segment (0 <= hist_len <= W - 1; 0 = no
+ *              history, as in an independent prefill; absent taps read 0)
+ * y_out        device [batch][n * n_warm][heads][dc] (x_dtype), entry e at rows
+ *              e * n_warm ..; must not overlap x or weight
+ * Accumulation in fp32; bf16 outputs are rounded to nearest even.
+ * -------------------------------------------------------------------- */
+#define PIC_MAX_CONV 16
+
+size_t pic_conv_warmup_workspace(int32_t n);
+
+int pic_validate_conv_warmup(int x_dtype, int batch, int heads, int dc, int width,
+                             int64_t n_tokens, const float* weight, const void* x, int32_t n,
+                             int32_t n_warm, const int64_t* head_start, const int64_t* hist_end,
+                             const int32_t* hist_len, const void* y_out, const void* workspace,
+                             size_t workspace_bytes);
+
+int pic_conv_warmup(int x_dtype, int batch, int heads, int dc, int width, int64_t n_tokens,
+                    const float* weight, const void* x, int32_t n, int32_t n_warm,
+                    const int64_t* head_start, const int64_t* hist_end, const int32_t* hist_len,
+                    void* y_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Plan dump: the host-side bookkeeping a build or compose call would use,

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 6
+    assert lib.pic_abi_version() == 7
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -343,5 +343,39 @@ def test_validate_rerotate(lib):
 ])
 def test_validate_rerotate_rejects(lib, kw, code):
     assert vrot(lib, **kw) == code
+    assert lib.pic_last_error().decode() != ""
+
+
+def vconv(lib, dt=BF16, B=2, H=2, dc=64, W=4, N=100, heads=((0, 0, 0), (40, 40, 3)), n_warm=3,
+          ws_bytes=None, y=None, x=None):
+    hs = np.ascontiguousarray(np.asarray([h[0] for h in heads], dtype=np.int64))
+    he = np.ascontiguousarray(np.asarray([h[1] for h in heads], dtype=np.int64))
+    hl = np.ascontiguousarray(np.asarray([h[2] for h in heads], dtype=np.int32))
+    n = len(heads)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p) if n else None
+    need = lib.pic_conv_warmup_workspace(n)
+    return lib.pic_validate_conv_warmup(dt, B, H, dc, W, N, P(0), x or P(1), n, n_warm, p(hs),
+                                        p(he), p(hl), y or ctypes.c_void_p(1 << 32), P(3),
+                                        need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_conv_warmup(lib):
+    assert vconv(lib) == OK
+    assert vconv(lib, dt=F32, W=1, n_warm=0, heads=((5, 0, 0),)) == OK
+    assert vconv(lib, heads=()) == OK
+    assert vconv(lib, heads=((97, 97, 3),)) == OK  # the last head that fits
+    assert lib.pic_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dt": 3}, EUNSUP), ({"W": 0}, EDIMS), ({"W": 17}, EDIMS), ({"dc": 24}, EDIMS),
+    ({"n_warm": 65}, EDIMS), ({"n_warm": -1}, EDIMS),
+    ({"heads": ((0, 0, 4),)}, EOFF), ({"heads": ((0, 2, 3),)}, EOFF),
+    ({"heads": ((0, 101, 1),)}, EOFF), ({"heads": ((98, 98, 3),)}, EOFF),
+    ({"heads": ((-1, 0, 0),)}, EOFF), ({"ws_bytes": 4}, EWS),
+    ({"y": ctypes.c_void_p(A * 2 + 32)}, EUNSUP), ({"y": ctypes.c_void_p((1 << 32) + 2)}, EALIGN),
+])
+def test_validate_conv_warmup_rejects(lib, kw, code):
+    assert vconv(lib, **kw) == code
     assert lib.pic_last_error().decode() != ""
 
