@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_kda_kernel": ["k_build_kda.hip", "pic_internal.hpp"],
     "rerotate_kernel": ["k_rerotate.hip", "pic_internal.hpp"],
+    "conv_warmup_kernel": ["k_conv_warmup.hip", "pic_internal.hpp"],
 }
 PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
 
@@ -528,6 +529,45 @@ def bench_reuse(w, args):
                      "valu_time_at_peak_ms": t_valu * 1e3,
                      "hbm_time_at_peak_ms": cb / (PEAK_HBM_GBS * 1e9) * 1e3,
                      "output_tokens_per_s": n_seam * B / t_comp}
+    conv_info = None
+    if seam_w:
+        # convolution warm-up of width 4 (windows of 3 tokens) for every chain
+        # entry, one call per stream (q, k, v), over the seam inputs as the raw
+        # store; not part of `value`
+        cw = 4
+        n_e = steps_total
+        heads_at = [int(min(seam_off[c], n_seam - (cw - 1))) for c in range(n_e)]
+        hist = [int(min(cw - 1, h)) for h in heads_at]
+        wts = {nm: torch.randn((H, d, cw), generator=torch.Generator(device=dev).manual_seed(5),
+                               device=dev) / cw for nm, d in (("q", dk), ("k", dk), ("v", dv))}
+        ys = {nm: torch.empty((B, n_e * (cw - 1), H, si[nm].shape[-1]), dtype=si[nm].dtype,
+                              device=dev) for nm in ("q", "k", "v")}
+
+        def warm():
+            for nm in ("q", "k", "v"):
+                pic.pic_conv_warmup(wts[nm], si[nm], heads_at, heads_at, hist, cw - 1,
+                                    out=ys[nm])
+
+        warm()
+        torch.cuda.synchronize()
+        cr = []
+        for _ in range(3):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            warm()
+            e1.record(stream)
+            cr.append((e0, e1))
+        torch.cuda.synchronize()
+        t_cw = float(np.mean([a.elapsed_time(b) for a, b in cr])) / 1e3 / 3  # per launch
+        # per launch (one stream; q, k, v have d = 128 here), bf16: each output
+        # token written once, each entry's head and history tokens read once
+        cwb = 3 * B * H * dk * n_e * (cw - 1) * 2
+        conv_info = {"kernel": "conv_warmup_kernel", "width": cw, "entries": n_e,
+                     "tokens": n_e * (cw - 1), "ms_per_launch": t_cw * 1e3,
+                     "launches": "3 (q, k, v)", "bound": "hbm",
+                     "achieved": cwb / t_cw / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": cwb / t_cw / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": cwb,
+                     "traffic": measured_traffic("conv_warmup_kernel", w.name)}
     gbs = cb / t_comp / 1e9
     out = {"metric": "state composes/s (dense delta, H=32, d=128), composition-heavy reuse"
                      + (" with seam windows" if seam_w else "") + "; % HBM roofline",
@@ -546,6 +586,7 @@ def bench_reuse(w, args):
            "fresh_build": {"tokens_per_s": fresh_tokens / (fresh_ms / 1e3), "ms": fresh_ms,
                            "segments": n_fresh, "layers": B},
            "seam": seam_info,
+           "conv_warmup": conv_info,
            "pool_and_input_preparation_s": prep_s,
            "hbm_reference": hbm_copy_reference(torch, dev)}
     print(json.dumps(out), flush=True)

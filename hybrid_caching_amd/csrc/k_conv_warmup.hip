@@ -10,15 +10,17 @@
 // segment's raw tail, into the seam layout [B][n * n_warm][H][dc] that the
 // seam compose takes; the cached pair covers the tokens after them.
 //
-// One thread per four output channels; the taps are gathered from the head or
-// the history (absent history reads as zero) and accumulated in fp32; the
-// result is stored in the input's type (bf16 rounded to nearest even).
-#include <algorithm>
-
+// A thread owns four channels of one head, keeps their taps in registers and
+// walks 32 output tokens (weights are read once per 32 tokens, not per
+// token); the taps are gathered from the head or the history (absent history
+// reads as zero) and accumulated in fp32; the result is stored in the input's
+// type (bf16 rounded to nearest even).
 #include "pic_internal.hpp"
 
 namespace pic {
 namespace {
+
+constexpr int kMaxConv = 16;  // widest convolution (the header's limit)
 
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* x, int64_t off) {
@@ -36,39 +38,47 @@ __device__ __forceinline__ unsigned bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // nearest even (finite inputs)
 }
 
+constexpr int kRows = 32;  // output tokens per block
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void conv_warmup_kernel(ConvArgs a) {
-  const int g4 = a.dc / 4;
-  const int64_t total = int64_t(a.batch) * a.n * a.n_warm * a.heads * g4;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const int c = 4 * int(i % g4);
-    int64_t r = i / g4;
-    const int h = int(r % a.heads);
-    r /= a.heads;
-    const int64_t row = r % (int64_t(a.n) * a.n_warm);  // entry * n_warm + t
-    const int b = int(r / (int64_t(a.n) * a.n_warm));
-    const int e = int(row / a.n_warm), t = int(row % a.n_warm);
+__global__ __launch_bounds__(256) void conv_warmup_kernel(ConvArgs a, int item_blocks) {
+  // a thread owns four channels of one head and its taps (in registers) and
+  // walks kRows output tokens (layer, entry, t)
+  const int g4 = a.dc / 4, items = a.heads * g4;
+  const int it = (blockIdx.x % item_blocks) * 256 + threadIdx.x;
+  if (it >= items) return;
+  const int h = it / g4, c = 4 * (it - h * g4);
+  float w[kMaxConv][4];
+#pragma unroll
+  for (int j = 0; j < kMaxConv; ++j)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[j][u] = (j < a.width) ? a.weight[(int64_t(h) * a.dc + c + u) * a.width + j] : 0.f;
+  const int64_t per_b = int64_t(a.n) * a.n_warm, rows = int64_t(a.batch) * per_b;
+  const int64_t r0 = int64_t(blockIdx.x / item_blocks) * kRows;
+  const int64_t r1 = r0 + kRows < rows ? r0 + kRows : rows;
+  for (int64_t rr = r0; rr < r1; ++rr) {
+    const int b = int(rr / per_b);
+    const int64_t row = rr - int64_t(b) * per_b;  // entry * n_warm + t
+    const int e = int(row / a.n_warm), t = int(row - int64_t(e) * a.n_warm);
     const int64_t head = table_at(a.d_head_start, e), hend = table_at(a.d_hist_end, e);
     const int hlen = table_at(a.d_hist_len, e);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* w = a.weight + (int64_t(h) * a.dc + c) * a.width;
-    for (int j = 0; j < a.width; ++j) {
+#pragma unroll
+    for (int j = 0; j < kMaxConv; ++j) {
       const int tau = t - j;
-      int64_t src;
-      if (tau >= 0)
-        src = head + tau;
-      else if (-tau <= hlen)
-        src = hend + tau;
-      else
-        continue;
-      const float4 xv = load4<BF16>(a.x, ((int64_t(b) * a.n_tokens + src) * a.heads + h) * a.dc + c);
-      acc[0] = fmaf(w[j], xv.x, acc[0]);
-      acc[1] = fmaf(w[a.width + j], xv.y, acc[1]);
-      acc[2] = fmaf(w[2 * a.width + j], xv.z, acc[2]);
-      acc[3] = fmaf(w[3 * a.width + j], xv.w, acc[3]);
+      // taps past the width, and history taps past the history, read nothing
+      if (j < a.width && (tau >= 0 || -tau <= hlen)) {
+        const int64_t src = (tau >= 0) ? head + tau : hend + tau;
+        const float4 xv =
+            load4<BF16>(a.x, ((int64_t(b) * a.n_tokens + src) * a.heads + h) * a.dc + c);
+        acc[0] = fmaf(w[j][0], xv.x, acc[0]);
+        acc[1] = fmaf(w[j][1], xv.y, acc[1]);
+        acc[2] = fmaf(w[j][2], xv.z, acc[2]);
+        acc[3] = fmaf(w[j][3], xv.w, acc[3]);
+      }
     }
-    const int64_t o = ((int64_t(b) * a.n * a.n_warm + row) * a.heads + h) * a.dc + c;
+    const int64_t o = (rr * a.heads + h) * a.dc + c;
     if constexpr (BF16) {
       const uint2 u = make_uint2(bf16_bits(acc[0]) | (bf16_bits(acc[1]) << 16),
                                  bf16_bits(acc[2]) | (bf16_bits(acc[3]) << 16));
@@ -83,14 +93,15 @@ __global__ __launch_bounds__(256) void conv_warmup_kernel(ConvArgs a) {
 }  // namespace
 
 hipError_t launch_conv_warmup(const ConvArgs& a, hipStream_t s) {
-  const int64_t total = int64_t(a.batch) * a.n * a.n_warm * a.heads * (a.dc / 4);
-  if (total <= 0) return hipSuccess;
-  if (a.dc % 4) return hipErrorInvalidConfiguration;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  const int64_t rows = int64_t(a.batch) * a.n * a.n_warm;  // output tokens
+  if (rows <= 0 || a.heads <= 0 || a.dc <= 0) return hipSuccess;
+  const int item_blocks = (a.heads * (a.dc / 4) + 255) / 256;
+  const int64_t blocks = (rows + kRows - 1) / kRows * item_blocks;
+  if (a.dc % 4 || a.width > kMaxConv || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.bf16)
-    hipLaunchKernelGGL(conv_warmup_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(conv_warmup_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a, item_blocks);
   else
-    hipLaunchKernelGGL(conv_warmup_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(conv_warmup_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a, item_blocks);
   return hipGetLastError();
 }
 
