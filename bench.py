@@ -206,6 +206,7 @@ def bench_scalar_diag(w, args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()
+    pic.pic_staging_reserve()  # asynchronous copies of large plan tables
     B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
     offsets = w.offsets()
     qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
@@ -312,6 +313,7 @@ def bench_kda(w, args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()
+    pic.pic_staging_reserve()  # asynchronous copies of large plan tables
     B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
     offsets = w.offsets()
     qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
@@ -430,6 +432,7 @@ def bench_reuse(w, args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()
+    pic.pic_staging_reserve()  # asynchronous copies of large plan tables
     fw = synth.reuse_fresh_workload(w)
     off, idx = synth.reuse_chains(w)
     B, H, dk, dv = w.layers, w.heads, w.dk, w.dv
@@ -644,6 +647,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()
+    pic.pic_staging_reserve()  # asynchronous copies of large plan tables
     B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
     offsets = w.offsets()
 

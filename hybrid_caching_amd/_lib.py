@@ -61,6 +61,9 @@ SIGNATURES = {
     "pic_rerotate": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _i, ctypes.c_double,
                           _i, _p, _p, _p, _p, _sz, _p]),
     "pic_plan_dump": (_i, [_i, _i32, _p, _p, _i64, _p, _i64]),
+    "pic_staging_reserve": (_i, []),
+    "pic_staging_release": (_i, []),
+    "pic_staging_bytes": (_sz, []),
 }
 
 PLAN_BUILD, PLAN_COMPOSE = 0, 1
@@ -324,13 +327,35 @@ def pic_conv_warmup(weight, x, head_start, hist_end, hist_len, n_warm: int, *, o
     hs, hs_p = _host_i64(head_start)
     he, he_p = _host_i64(hist_end)
     hl, hl_p = _host_i32(hist_len)
+    shape = (B, n * int(n_warm), H, dc)
     if out is None:
-        out = torch.empty((B, n * n_warm, H, dc), dtype=x.dtype, device=x.device)
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    else:
+        _need(out, "out", x.dtype)
+        if tuple(out.shape) != shape or out.device != x.device:
+            raise ValueError(f"out must be {shape} on {x.device}, got {tuple(out.shape)} on "
+                             f"{out.device}")
     ws = _workspace(lib.pic_conv_warmup_workspace(n), x.device)
     rc = lib.pic_conv_warmup(dt, B, H, dc, W, N, _ptr(weight), _ptr(x), n, int(n_warm), hs_p,
                              he_p, hl_p, _ptr(out), _ptr(ws), ws.numel(), _stream(x.device))
     _check(rc, "pic_conv_warmup")
     return out
+
+
+def pic_staging_reserve():
+    """Opt into the pinned host pool (current device) for large plan tables,
+    so that calls with such tables do not wait for their stream."""
+    _check(load().pic_staging_reserve(), "pic_staging_reserve")
+
+
+def pic_staging_release():
+    """Free every pinned staging pool (after their pending copies)."""
+    _check(load().pic_staging_release(), "pic_staging_release")
+
+
+def pic_staging_bytes() -> int:
+    """Pinned host bytes the library holds now (0 unless reserved)."""
+    return int(load().pic_staging_bytes())
 
 
 def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):

@@ -42,18 +42,18 @@ bool dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 bool has_T_hat(int form) { return form == PIC_FORM_DENSE || form == PIC_FORM_KDA; }
 
 // ---------------------------------------------------------------- staging
-// The small per-call tables (segment offsets and order, chain tables) reach
-// the device through pinned host slots: the caller's arrays are copied into
-// a slot and the slot is copied to the workspace with hipMemcpyAsync, which
-// is then asynchronous, so back-to-back calls queue on the stream without
-// waiting for the device.  A slot is reused after the copy that last read it
-// has completed (one event per slot; with 64 slots that wait is normally
-// already over).  Tables larger than a slot (or when pinned memory cannot be
-// had) are copied from the caller's memory and the call waits for the
-// stream, so the source may be released on return.  Slots
-// are per device and shared by all threads (a mutex guards the choice of
-// slot).  Not usable under stream capture: a captured copy would read a slot
-// that later calls overwrite.
+// Tables too large for the kernel arguments (segment offsets and order,
+// chain tables, ...) reach the caller's workspace by hipMemcpyAsync.  By
+// default they are copied straight from host memory that is gone (or may be
+// reused) once the call returns, so the call then waits for its stream; the
+// library holds no memory between calls.  pic_staging_reserve() opts into a
+// pool of pinned host slots on the current device: the tables are first
+// copied into a slot, and the slot's copy to the device is asynchronous, so
+// back-to-back calls queue on the stream without waiting for the device.  A
+// slot is reused after the copy that last read it has completed (one event
+// per slot; with 64 slots that wait is normally already over).  The pool is
+// held until pic_staging_release().  A mutex guards the pools.  Neither way
+// is usable under stream capture.
 struct Piece {
   void* dst;
   const void* src;
@@ -64,6 +64,7 @@ class Staging {
  public:
   static constexpr int kSlots = 64;
   static constexpr size_t kSlotBytes = 64 * 1024;
+  static constexpr int kMaxDevices = 64;
 
   hipError_t copy(std::initializer_list<Piece> pieces, hipStream_t s) {
     size_t total = 0;
@@ -72,27 +73,16 @@ class Staging {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (total > kSlotBytes || dev < 0 || dev >= kMaxDevices) return copy_pageable(pieces, s);
     std::lock_guard<std::mutex> lock(mu_);
+    if (total > kSlotBytes || dev < 0 || dev >= kMaxDevices || !pools_[dev].host)
+      return copy_pageable(pieces, s);
     Pool& pool = pools_[dev];
-    if (!pool.host) {
-      e = hipHostMalloc(reinterpret_cast<void**>(&pool.host), kSlots * kSlotBytes,
-                        hipHostMallocDefault);
-      if (e != hipSuccess) {
-        pool.host = nullptr;
-        return copy_pageable(pieces, s);
-      }
-      for (int i = 0; i < kSlots; ++i) {
-        e = hipEventCreateWithFlags(&pool.ev[i], hipEventDisableTiming);
-        if (e != hipSuccess) return e;
-        pool.pending[i] = false;
-      }
-    }
     const int i = pool.next;
     pool.next = (pool.next + 1) % kSlots;
     if (pool.pending[i]) {
       e = hipEventSynchronize(pool.ev[i]);
       if (e != hipSuccess) return e;
+      pool.pending[i] = false;
     }
     // The pieces go to ascending places of one workspace: lay them out in
     // the slot as they lie there and move the whole span with one copy.
@@ -129,8 +119,67 @@ class Staging {
     return e;
   }
 
+  // pinned pool of the current device (no-op if it exists)
+  hipError_t reserve() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu_);
+    Pool& pool = pools_[dev];
+    if (pool.host) return hipSuccess;
+    e = hipHostMalloc(reinterpret_cast<void**>(&pool.host), kSlots * kSlotBytes,
+                      hipHostMallocDefault);
+    if (e != hipSuccess) {
+      pool.host = nullptr;
+      return e;
+    }
+    for (int i = 0; i < kSlots; ++i) {
+      e = hipEventCreateWithFlags(&pool.ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(pool.ev[j]);
+        (void)hipHostFree(pool.host);
+        pool.host = nullptr;
+        return e;
+      }
+      pool.pending[i] = false;
+    }
+    pool.next = 0;
+    held_ += kSlots * kSlotBytes;
+    return hipSuccess;
+  }
+
+  // every pool: wait for the copies that read it, then free it
+  hipError_t release() {
+    std::lock_guard<std::mutex> lock(mu_);
+    hipError_t first = hipSuccess;
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (int dev = 0; dev < kMaxDevices; ++dev) {
+      Pool& pool = pools_[dev];
+      if (!pool.host) continue;
+      (void)hipSetDevice(dev);
+      for (int i = 0; i < kSlots; ++i) {
+        hipError_t e = pool.pending[i] ? hipEventSynchronize(pool.ev[i]) : hipSuccess;
+        if (e == hipSuccess) e = hipEventDestroy(pool.ev[i]);
+        if (e != hipSuccess && first == hipSuccess) first = e;
+        pool.pending[i] = false;
+      }
+      const hipError_t e = hipHostFree(pool.host);
+      if (e != hipSuccess && first == hipSuccess) first = e;
+      pool.host = nullptr;
+      held_ -= kSlots * kSlotBytes;
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    return first;
+  }
+
+  size_t held() {
+    std::lock_guard<std::mutex> lock(mu_);
+    return held_;
+  }
+
  private:
-  static constexpr int kMaxDevices = 64;
   static constexpr size_t kSlack = 256;  // alignment gaps between the pieces
   struct Pool {
     char* host = nullptr;
@@ -148,10 +197,13 @@ class Staging {
   }
   std::mutex mu_;
   Pool pools_[kMaxDevices];
+  size_t held_ = 0;
 };
 
 Staging& staging() {
-  static Staging* st = new Staging();  // never destroyed: pinned memory lives until exit
+  // the object itself is never destroyed (calls may come from other static
+  // destructors); the pinned memory it holds is freed by pic_staging_release
+  static Staging* st = new Staging();
   return *st;
 }
 
@@ -276,6 +328,20 @@ const char* pic_status_string(int status) {
 }
 
 const char* pic_last_error(void) { return g_last_error; }
+
+int pic_staging_reserve(void) {
+  const hipError_t e = staging().reserve();
+  if (e != hipSuccess) return hip_fail(e, "allocating the pinned staging pool");
+  return ok();
+}
+
+int pic_staging_release(void) {
+  const hipError_t e = staging().release();
+  if (e != hipSuccess) return hip_fail(e, "releasing the pinned staging pools");
+  return ok();
+}
+
+size_t pic_staging_bytes(void) { return staging().held(); }
 
 /* ------------------------------------------------------------------ build */
 

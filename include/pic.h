@@ -64,10 +64,11 @@
  *     *_workspace query).  Small tables (builds of up to 32 segments,
  *     composes of up to 16 requests and 64 chain entries) travel in the
  *     kernel arguments instead and leave the workspace untouched.  Larger
- *     ones are copied through a pool of pinned host buffers that the library
- *     allocates on first use (per device, 4 MiB, kept until the process
- *     ends), so that the copy does not wait for the stream.  Calls are not
- *     safe under stream capture.
+ *     ones are copied from host memory, and the call then waits for its stream
+ *     (the source is gone once the call returns); the library holds no
+ *     memory between calls.  A caller that wants those copies asynchronous
+ *     opts into a pinned host pool with pic_staging_reserve() and frees it
+ *     with pic_staging_release().  Calls are not safe under stream capture.
  *   - Asynchrony: a return of PIC_OK means the work is validated and
  *     enqueued on `stream` (a hipStream_t; NULL = the null stream).  Results
  *     are ready once the stream is synchronised.  Host arrays may be reused
@@ -93,7 +94,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 7
+#define PIC_ABI_VERSION 8
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -132,6 +133,25 @@ const char* pic_status_string(int status);
 
 /* Message of the calling thread's last failing call ("" if none). */
 const char* pic_last_error(void);
+
+/* ----------------------------------------------------------------------
+ * Pinned staging pool (opt-in).  Plan tables too large for the kernel
+ * arguments are copied into the caller's workspace.  Without a pool the copy
+ * reads the host arrays directly and the call waits for its stream before it
+ * returns.  pic_staging_reserve() allocates, for the current HIP device, a
+ * pool of 64 pinned host slots of 64 KiB (4 MiB); from then on tables that
+ * fit a slot are staged there and copied asynchronously (a slot is reused
+ * once its copy has completed), so back-to-back calls do not wait for the
+ * device.  A second reserve on the same device does nothing.
+ * pic_staging_release() waits for the pending copies of every pool, frees
+ * all of them and returns the library to holding no memory; it must not
+ * run concurrently with calls that stage tables.  pic_staging_bytes()
+ * gives the pinned bytes held now.  Errors: PIC_ERR_HIP (detail in
+ * pic_last_error()).
+ * ---------------------------------------------------------------------- */
+int pic_staging_reserve(void);
+int pic_staging_release(void);
+size_t pic_staging_bytes(void);
 
 /* ----------------------------------------------------------------------
  * Segment build: the cached pair of every (segment, layer, head).

@@ -33,8 +33,10 @@ module only marshals numpy arrays into it.  What each call computes:
   [xix.ai, paragraph on linear layers: variants with a short convolution need
   the convolution state warmed up]
 * ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
-  its definition: segments as token ranges cut into 64-token chunks, visited
-  longest first; chains applied entry by entry.
+  its definition: segments as token ranges cut into 64-token chunks (in
+  segment order; the order a launch visits them in is the library's
+  schedule); chains applied entry by entry.  Pinned against hand-written
+  tables.
 
 Forms: 0 = scalar decay, 1 = diagonal gate, 2 = dense gated delta (GDN form),
 3 = dense delta with per-channel gates (KDA form, T_t = (I - b k k^T) Diag(a)).
@@ -266,26 +268,30 @@ CHUNK = 64
 
 
 def plan_build(seg_offsets):
-    """One row per segment, in visiting order (longest first, ties by lower
-    index): (segment, start, length, n_chunks, tail), where n_chunks =
-    ceil(length / 64) and tail = tokens in the last chunk (0 if empty).
-    [segments are token ranges cut at their boundaries; xix.ai HYPIC article,
-    paragraph on linear layers]"""
+    """One row per segment, in segment order: (segment, start, length,
+    n_chunks, tail).  Segment s covers tokens [off[s], off[s+1]); it is cut
+    into n_chunks = ceil(length / 64) chunks of 64 tokens, the last holding
+    tail = length - 64 (n_chunks - 1) tokens (1..64), or none when the segment
+    is empty (n_chunks = tail = 0).  The order in which a launch visits the
+    segments is the library's schedule, not part of this definition.
+    [each segment is a token range found from its boundaries and gets its own
+    pair; xix.ai HYPIC article, paragraph on linear layers]"""
     off = [int(x) for x in seg_offsets]
-    n = len(off) - 1
-    lengths = [off[s + 1] - off[s] for s in range(n)]
-    order = sorted(range(n), key=lambda s: (-lengths[s], s))
     rows = []
-    for s in order:
-        length = lengths[s]
+    for s in range(len(off) - 1):
+        length = off[s + 1] - off[s]
         n_chunks = (length + CHUNK - 1) // CHUNK
         tail = length - CHUNK * (n_chunks - 1) if n_chunks else 0
         rows.append((s, off[s], length, n_chunks, tail))
-    return np.array(rows, dtype=np.int64).reshape(n, 5)
+    return np.array(rows, dtype=np.int64).reshape(len(rows), 5)
 
 
 def plan_compose(chain_offsets, chain_idx):
-    """One row per chain entry, in application order: (request, step, pool index)."""
+    """One row per chain entry, in application order: (request, step, pool
+    index), where request r owns entries [off[r], off[r+1]) and step counts
+    from the request's own first entry.  [the cached pairs of a request are
+    applied to its running state one after another, in prompt order; xix.ai
+    HYPIC article, paragraph on linear layers]"""
     off = [int(x) for x in chain_offsets]
     idx = [int(x) for x in chain_idx]
     rows = [(r, c - off[r], idx[c]) for r in range(len(off) - 1) for c in range(off[r], off[r + 1])]

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 7
+    assert lib.pic_abi_version() == 8
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -183,12 +183,19 @@ def _plan_cases():
 
 
 def test_build_plan_matches_oracle_plan():
+    """The library's rows are the oracle's rows (per segment), in the
+    library's visiting order: longest segment first, ties by lower index (a
+    schedule, checked here as a property of the library, not of the method)."""
     import oracle
     from hybrid_caching_amd import _lib
     for off in _plan_cases():
         got = _lib.pic_plan_dump(_lib.PLAN_BUILD, off, limit=off[-1])
         ref = oracle.plan_build(off)
-        assert got.dtype == np.int64 and np.array_equal(got, ref), off
+        assert got.dtype == np.int64 and got.shape == ref.shape, off
+        assert np.array_equal(got[np.argsort(got[:, 0], kind="stable")], ref), off
+        assert sorted(got[:, 0].tolist()) == list(range(len(off) - 1)), off
+        key = [(-int(r[2]), int(r[0])) for r in got]
+        assert key == sorted(key), off
 
 
 def test_compose_plan_matches_oracle_plan():
@@ -219,6 +226,11 @@ def test_plan_dump_errors(lib):
     i = np.array([0, 3], dtype=np.int32)
     c, c_p = offsets((0, 2))
     assert lib.pic_plan_dump(1, 1, c_p, i.ctypes.data_as(ctypes.c_void_p), 3, t_p, 4) == ECHAIN
+
+
+def test_no_memory_is_held_by_default(lib):
+    """The library holds no pinned memory unless the caller reserves it."""
+    assert lib.pic_staging_bytes() == 0
 
 
 def test_validate_naive_add(lib):

@@ -50,6 +50,33 @@ def test_conv_warmup_matches_oracle(bf16, W, dc):
     assert e <= (4e-3 if bf16 else TOL_F32)
 
 
+@pytest.mark.parametrize("W,n_warm", [(4, 3), (4, 7), (9, 8), (16, 15), (5, 12)])
+def test_conv_warmup_many_blocks(W, n_warm):
+    """A launch of several channel-item blocks (32 heads x 128 channels = 4
+    blocks of 256 items) and many 32-row blocks (2 layers x 20 entries x
+    n_warm rows), widths up to the header's limit of 16 and windows longer
+    than W - 1, with full, partial and absent history."""
+    import hybrid_caching_amd as pic
+    import torch
+    rng = np.random.default_rng(1000 + 31 * W + n_warm)
+    B, H, dc, N, n = 2, 32, 128, 700, 20
+    x = synth.bf16_round(rng.standard_normal((B, N, H, dc)).astype(np.float32))
+    w = (rng.standard_normal((H, dc, W)) / W).astype(np.float32)
+    starts = sorted(rng.choice(np.arange(0, N - n_warm), size=n, replace=False).tolist())
+    hist_end = [int(s) for s in starts]
+    hist_len = [min(W - 1, int(s), int(rng.integers(0, W))) for s in starts]
+    hist_len[0] = min(W - 1, starts[0])
+    y = pic.pic_conv_warmup(to_dev(w), to_dev(x, torch.bfloat16), starts, hist_end, hist_len,
+                            n_warm)
+    torch.cuda.synchronize()
+    assert y.shape == (B, n * n_warm, H, dc)
+    assert B * n * n_warm > 32 and H * dc // 4 > 256
+    want = oracle.conv_warmup(w, x, hist_end, hist_len, starts, n_warm)
+    e = max_rel_units(y.float().cpu().numpy(), want)
+    report(f"many blocks W {W} n_warm {n_warm}: err {e:.3e}")
+    assert e <= 4e-3
+
+
 def test_conv_warmup_through_seams_equals_the_prompt():
     """The whole method on the GPU, fp32: pairs of each segment's tokens
     after its window (conv on the segment alone), the windows recomputed by

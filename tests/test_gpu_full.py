@@ -189,10 +189,15 @@ def test_kda_slow_gates_full_length_sampled():
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name,layers", [("reuse_256x30", None), ("reuse_256x30_slow", 2)])
-def test_reuse_workload_sampled(name, layers):
+@pytest.mark.parametrize("name,layers,precision",
+                         [("reuse_256x30", None, 0), ("reuse_256x30", None, 1),
+                          ("reuse_256x30_slow", 2, 0), ("reuse_256x30_slow", 2, 1)])
+def test_reuse_workload_sampled(name, layers, precision):
     """At the base gates the carried term underflows (composition gives the
-    last segment's S0 exactly); the slow-gate variant makes it sizeable."""
+    last segment's S0 exactly); the slow-gate variant makes it sizeable.
+    Precision 1 (fp16 operands) is the build the benchmark times: 768
+    variable-length segments of 512..8192 tokens per layer through the
+    workspace plan."""
     import hybrid_caching_amd as pic
     import torch
     from oracle import DENSE
@@ -229,10 +234,10 @@ def test_reuse_workload_sampled(name, layers):
     for layer in range(w.layers):
         x = synth.torch_layer_inputs(w, layer, dev)
         pic.pic_segment_build(DENSE, x["k"][None], x["v"][None], x["alpha"][None],
-                              x["beta"][None], p_off, out=pool_out)
+                              x["beta"][None], p_off, out=pool_out, precision=precision)
         y = synth.torch_layer_inputs(fw, layer, dev)
         pic.pic_segment_build(DENSE, y["k"][None], y["v"][None], y["alpha"][None],
-                              y["beta"][None], f_off, out=fresh_out)
+                              y["beta"][None], f_off, out=fresh_out, precision=precision)
         want = layer in sampled_layers
         res = pic.pic_compose(DENSE, buf["log_scale"], buf["T_hat"], buf["S0"], off, idx,
                               want_pair=want)
@@ -246,13 +251,14 @@ def test_reuse_workload_sampled(name, layers):
         for s in smp["pool"]:
             ref = oracle.build(DENSE, *unit(x, p_off, s, h), [0, int(lens[s])])
             gpu = {key: t[s, 0, h].cpu().numpy()[None, None, None] for key, t in buf.items()}
-            report(f"{name} layer {layer}: pool unit {s} ({int(lens[s])} tokens), head {h}")
+            report(f"{name} precision {precision} layer {layer}: pool unit {s} "
+                   f"({int(lens[s])} tokens), head {h}")
             assert_pair_close(gpu, ref, DENSE, TOL_BF16)
         for s in smp["fresh"]:
             ref = oracle.build(DENSE, *unit(y, f_off, s, h), [0, fw.seg_lens[s]])
             gpu = {key: t[n_pool + s, 0, h].cpu().numpy()[None, None, None]
                    for key, t in buf.items()}
-            report(f"{name} layer {layer}: fresh unit {s}, head {h}")
+            report(f"{name} precision {precision} layer {layer}: fresh unit {s}, head {h}")
             assert_pair_close(gpu, ref, DENSE, TOL_BF16)
         for r, hh in zip(smp["reqs"], smp["heads"][1:]):
             ids = idx[off[r]:off[r + 1]]
@@ -276,8 +282,10 @@ def test_reuse_workload_sampled(name, layers):
 
 
 @pytest.mark.timeout(400)
-@pytest.mark.parametrize("name,layers", [("reuse_seam_256x30", 3), ("reuse_seam_256x30_slow", 2)])
-def test_reuse_seam_workload_sampled(name, layers):
+@pytest.mark.parametrize("name,layers,precision",
+                         [("reuse_seam_256x30", 3, 0), ("reuse_seam_256x30", 3, 1),
+                          ("reuse_seam_256x30_slow", 2, 0)])
+def test_reuse_seam_workload_sampled(name, layers, precision):
     """Reuse with 8-token seam windows on every inner chain entry, at the
     benchmark's per-layer launch size (768 pool and fresh segments, 64 requests
     x 56-entry chains, 32 heads, d = 128), layer by layer; sampled chains
@@ -304,10 +312,10 @@ def test_reuse_seam_workload_sampled(name, layers):
     for layer in range(w.layers):
         x = synth.torch_layer_inputs(w, layer, dev)
         pic.pic_segment_build(DENSE, x["k"][None], x["v"][None], x["alpha"][None],
-                              x["beta"][None], w.offsets(), out=pool_out)
+                              x["beta"][None], w.offsets(), out=pool_out, precision=precision)
         y = synth.torch_layer_inputs(fw, layer, dev)
         pic.pic_segment_build(DENSE, y["k"][None], y["v"][None], y["alpha"][None],
-                              y["beta"][None], fw.offsets(), out=fresh_out)
+                              y["beta"][None], fw.offsets(), out=fresh_out, precision=precision)
         del x, y
         si = synth.torch_seam_inputs(one, NS, dev, seed_offset=1000 * layer)
         S_out, O = pic.pic_compose_seams(DENSE, buf["log_scale"], buf["T_hat"], buf["S0"], off,

@@ -150,6 +150,43 @@ def test_one_hot_dense_build_is_bitwise():
         assert lam_err(gpu["log_scale"][s, 0], lam) <= 1e-6
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_one_hot_dense_build_is_bitwise_fp16(d):
+    """The fp16-operand build (PIC_PREC_FP16, the kernel the dense benchmark
+    times) on the exact one-hot case, bit for bit: k_t one-hot, beta = 1,
+    integer v in [-8, 8), alpha = 1/2 on every 257th token (else 1).
+
+    fp16 keeps 11 significant bits.  Every intermediate of the chunked
+    algorithm is then a small integer times a power of two: the UT inverse
+    has entries in {0, +-1}, the in-chunk gate ratios and chunk decays are
+    powers of two, That's entries are 0 or 1 (its power-of-two column scale
+    is exact), and a state row mixes values whose exponents differ by at most
+    the halvings of one segment (at most 4 here), so 4 + 4 + 1 bits suffice.
+    Cuts give tails of 63, 64, 65 and 1 tokens, an empty segment and a long
+    one of 1024 tokens."""
+    from tests.test_oracle_pins import one_hot_expected
+    dk = dv = d
+    H = 2
+    cuts = [0, 63, 127, 127, 192, 193, 193 + 1024]
+    N = cuts[-1]
+    rng = np.random.default_rng(82 + d)
+    j = rng.integers(0, dk, size=(N, H))
+    k = np.zeros((1, N, H, dk), dtype=np.float32)
+    k[0, np.arange(N)[:, None], np.arange(H)[None, :], j] = 1.0
+    v = rng.integers(-8, 8, size=(1, N, H, dv)).astype(np.float32)
+    t = np.arange(N)
+    alpha = np.broadcast_to(np.where(t % 257 == 100, 0.5, 1.0)[None, :, None],
+                            (1, N, H)).astype(np.float32)
+    beta = np.ones((1, N, H), dtype=np.float32)
+    gpu, _ = build_both(DENSE, k, v, alpha, beta, cuts, True, precision=1)
+    for s in range(len(cuts) - 1):
+        S, That, lam = one_hot_expected(k.astype(np.float64), v.astype(np.float64),
+                                        alpha.astype(np.float64), j, cuts[s], cuts[s + 1])
+        assert np.array_equal(gpu["S0"][s, 0], S.astype(np.float32)), f"segment {s}"
+        assert np.array_equal(gpu["T_hat"][s, 0], That.astype(np.float32)), f"segment {s}"
+        assert lam_err(gpu["log_scale"][s, 0], lam) <= 1e-6
+
+
 def test_query_is_not_read():
     k, v, a, b = rand_case(DENSE, 1, 2, 64, 64, [0, 70], seed=9)
     q1 = np.zeros_like(k)
