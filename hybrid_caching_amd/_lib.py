@@ -61,6 +61,8 @@ SIGNATURES = {
     "pic_rerotate": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _i, ctypes.c_double,
                           _i, _p, _p, _p, _p, _sz, _p]),
     "pic_plan_dump": (_i, [_i, _i32, _p, _p, _i64, _p, _i64]),
+    "pic_compose_noalloc": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
+                                 _p, _p]),
     "pic_staging_reserve": (_i, []),
     "pic_staging_release": (_i, []),
     "pic_staging_bytes": (_sz, []),
@@ -208,6 +210,37 @@ def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, c
                          _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in), _ptr(out), _ptr(lam_out),
                          _ptr(T_out), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "pic_compose")
+    if want_pair:
+        return out, lam_out, T_out
+    return out
+
+
+def pic_compose_noalloc(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets,
+                        chain_idx, S_in=None, *, out=None, want_pair: bool = False):
+    """``pic_compose`` through the library's static scratch: no workspace and
+    no allocation inside the call (the outputs are allocated here unless
+    given).  Calls that overlap on one device race on the scratch."""
+    lib = load()
+    P, B, H, dk, dv = pool_S0.shape
+    for t, n in ((pool_log_scale, "pool_log_scale"), (pool_T_hat, "pool_T_hat"),
+                 (pool_S0, "pool_S0"), (S_in, "S_in"), (out, "out")):
+        _need(t, n, torch.float32)
+    off, off_p = _host_i64(chain_offsets)
+    idx, idx_p = _host_i32(chain_idx)
+    R = len(off) - 1
+    dev = pool_S0.device
+    if out is None:
+        out = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=dev)
+    lam_out = T_out = None
+    if want_pair:
+        lam_out = torch.empty((R,) + tuple(pool_log_scale.shape[1:]), dtype=torch.float32,
+                              device=dev)
+        if form in _HAS_T_HAT:
+            T_out = torch.empty((R, B, H, dk, dk), dtype=torch.float32, device=dev)
+    rc = lib.pic_compose_noalloc(form, B, H, dk, dv, P, _ptr(pool_log_scale), _ptr(pool_T_hat),
+                                 _ptr(pool_S0), R, off_p, idx_p, _ptr(S_in), _ptr(out),
+                                 _ptr(lam_out), _ptr(T_out), _stream(dev))
+    _check(rc, "pic_compose_noalloc")
     if want_pair:
         return out, lam_out, T_out
     return out

@@ -306,6 +306,35 @@ int check_seg_offsets(const int64_t* seg_offsets, int32_t n_seg, int64_t n_token
   return PIC_OK;
 }
 
+// ------------------------------------------------------- static scratch
+// Device memory for pic_compose_noalloc: its chain tables live in this
+// file-scope array (one copy per device, held until the process ends), so
+// that entry point needs neither a workspace nor an allocation.  In host code
+// the array's name is only a stand-in: the device address of each device's
+// copy is looked up once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = PIC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[Staging::kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= Staging::kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -498,9 +527,9 @@ int pic_validate_naive_add(int batch, int heads, int dk, int dv, int64_t pool_si
 
 // chain tables into the arguments (small) or the workspace (copied)
 static int enqueue_chains(int32_t n_req, const int64_t* off, const int32_t* idx, void* workspace,
-                          hipStream_t s, pic::ComposeArgs& a) {
+                          hipStream_t s, pic::ComposeArgs& a, bool force_table = false) {
   const int64_t total = off[n_req];
-  a.inl = n_req <= pic::kInlineReq && total <= pic::kInlineIdx;
+  a.inl = !force_table && n_req <= pic::kInlineReq && total <= pic::kInlineIdx;
   if (a.inl) {
     std::copy(off, off + n_req + 1, a.inl_off);
     if (total > 0) std::copy(idx, idx + total, a.inl_idx);
@@ -536,6 +565,52 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
   if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, workspace, s, a)) return rc;
   hipError_t e = has_T_hat(form) ? pic::launch_compose_dense(a, s)
                                           : pic::launch_compose_elementwise(a, false, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
+  if (log_scale_out) {
+    e = pic::launch_chain_log_scale(a, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the chain log-scale kernel");
+  }
+  if (T_hat_out) {
+    e = pic::launch_chain_T_hat(a, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the chain operator kernel");
+  }
+  return ok();
+}
+
+int pic_compose_noalloc(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                        const float* pool_log_scale, const float* pool_T_hat,
+                        const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                        const int32_t* chain_idx, const float* S_in, float* S_out,
+                        float* log_scale_out, float* T_hat_out, void* stream) {
+  // validation as for pic_compose, with the static scratch as the workspace
+  // (a stand-in address: validation never dereferences it)
+  if (n_req >= 0 && chain_offsets && chain_offsets[0] == 0) {
+    bool mono = true;
+    for (int32_t r = 0; r < n_req && mono; ++r) mono = chain_offsets[r + 1] >= chain_offsets[r];
+    if (mono) {
+      const size_t need = compose_ws_bytes(n_req, chain_offsets[n_req]);
+      if (need > kScratchBytes)
+        return fail(PIC_ERR_WORKSPACE,
+                    "chain tables of %zu bytes exceed the static scratch of %zu bytes", need,
+                    kScratchBytes);
+    }
+  }
+  if (int rc = pic_validate_compose(form, batch, heads, dk, dv, pool_size, pool_log_scale,
+                                    pool_T_hat, pool_S0, n_req, chain_offsets, chain_idx, S_in,
+                                    S_out, log_scale_out, T_hat_out,
+                                    reinterpret_cast<void*>(uintptr_t(kAlign)), kScratchBytes))
+    return rc;
+  if (n_req == 0) return ok();
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "looking up the static scratch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pic::ComposeArgs a{form,    batch,    heads,    dk,     dv,       pool_size,
+                     pool_log_scale, pool_T_hat, pool_S0, n_req, nullptr, nullptr,
+                     chain_offsets[n_req], S_in, S_out, log_scale_out, T_hat_out, false, {}, {}};
+  // the tables always go through the scratch (never the kernel arguments)
+  if (int rc = enqueue_chains(n_req, chain_offsets, chain_idx, ws, s, a, true)) return rc;
+  e = has_T_hat(form) ? pic::launch_compose_dense(a, s) : pic::launch_compose_elementwise(a, false, s);
   if (e != hipSuccess) return hip_fail(e, "launching the compose kernel");
   if (log_scale_out) {
     e = pic::launch_chain_log_scale(a, s);

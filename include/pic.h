@@ -246,6 +246,31 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
+ * Compose that allocates nothing: for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as pic_compose, without the workspace.
+ * The chain tables go into a static device array of
+ * PIC_NOALLOC_SCRATCH_BYTES (1 MiB) that the library image holds on every
+ * device it runs on until the process ends; a call whose tables need more
+ * (pic_compose_workspace(n_req, chain_offsets[n_req]) bytes) returns
+ * PIC_ERR_WORKSPACE before doing anything.  The call makes no hipMalloc,
+ * hipFree or other allocation.  The tables are copied from the host arrays
+ * and the call waits for its stream (or, with a staging pool reserved,
+ * copies asynchronously through it).  Every call on one device shares that
+ * device's array, which keeps the last call's tables: calls that overlap on
+ * one device (other streams or threads) race and are not allowed.
+ * -------------------------------------------------------------------- */
+#define PIC_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+int pic_compose_noalloc(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
+                        const float* pool_log_scale, const float* pool_T_hat,
+                        const float* pool_S0, int32_t n_req, const int64_t* chain_offsets,
+                        const int32_t* chain_idx, const float* S_in, float* S_out,
+                        float* log_scale_out, float* T_hat_out, void* stream);
+
+/* ----------------------------------------------------------------------
  * Naive add (the ablation): S_out[r] = S_in[r] + sum over the chain of S0_p.
  *   [xix.ai HYPIC article, paragraph on linear layers: adding zero-start
  *    final states is exact only for plain linear attention; it leaves out
