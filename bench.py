@@ -596,6 +596,75 @@ def bench_reuse(w, args):
     return 0
 
 
+def phase_timing(w, args) -> int:
+    """Per-role clocks of the dense fp16 build (diagnostic): runs one build of
+    `w` (by default 2 of its layers) through ``libpic_timing.so``, whose dense
+    fp16 kernel records, per wave, each pipeline phase's length and the wait at
+    its closing barrier, and prints per role the mean clocks per 64-token cycle:
+    phase A / phase B length, busy time (length - wait) and the cycle total."""
+    import ctypes
+    import torch
+    import synth
+    from hybrid_caching_amd import _build, _lib
+    if not os.path.exists(_build.TIMING_LIB_PATH):
+        raise SystemExit(f"{_build.TIMING_LIB_PATH} is missing: run the build first")
+    lib = _lib.load(_build.TIMING_LIB_PATH)
+    lib.pic_phase_timing_set.restype = ctypes.c_int
+    lib.pic_phase_timing_set.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = args.layers or 2
+    w = synth.scaled(w, layers=layers, name=w.name)
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    k = torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=dev)
+    alpha = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    for layer in range(B):
+        x = synth.torch_layer_inputs(w, layer, dev)
+        k[layer].copy_(x["k"])
+        v[layer].copy_(x["v"])
+        alpha[layer].copy_(x["alpha"])
+        beta[layer].copy_(x["beta"])
+        del x
+    lam = torch.empty((n_seg, B, H), dtype=torch.float32, device=dev)
+    T = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
+    S = torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)
+    blocks = n_seg * B * H
+    out = torch.zeros((blocks, 8, 8), dtype=torch.int64, device=dev)
+    off = np.ascontiguousarray(np.asarray(w.offsets(), dtype=np.int64))
+    ws = torch.empty(max(int(lib.pic_segment_build_workspace(2, B, H, dk, dv, N, n_seg)), 256),
+                     dtype=torch.uint8, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if lib.pic_phase_timing_set(P(out), blocks) != 0:
+        raise SystemExit("pic_phase_timing_set failed")
+    for _ in range(2):  # the second run is the one read
+        rc = lib.pic_segment_build(2, 1, 1, B, H, dk, dv, N, None, P(k), P(v), P(alpha), P(beta),
+                                   off.ctypes.data_as(ctypes.c_void_p), n_seg, P(lam), P(T), P(S),
+                                   P(ws), ws.numel(), stream)
+        if rc != 0:
+            raise SystemExit(f"build failed: {lib.pic_last_error().decode()}")
+        torch.cuda.synchronize()
+    r = out.cpu().numpy().astype(np.float64)  # [block][wave][field]
+    cyc = np.maximum(r[:, :, 5], 1)
+    roles = {"consumer": [0, 1, 2, 3], "solver": [4], "K staging": [5, 6], "V staging": [7]}
+    rows = {}
+    for name, waves in roles.items():
+        x = r[:, waves]
+        c = cyc[:, waves]
+        lenA, waitA = (x[..., 0] / c).mean(), (x[..., 1] / c).mean()
+        lenB, waitB = (x[..., 2] / c).mean(), (x[..., 3] / c).mean()
+        rows[name] = {"phase_A": round(lenA), "busy_A": round(lenA - waitA),
+                      "phase_B": round(lenB), "busy_B": round(lenB - waitB),
+                      "cycle": round((x[..., 4] / c).mean())}
+    print(json.dumps({"phase_timing": "build_dense_h16_kernel", "workload": w.name,
+                      "layers": layers, "clocks_per_64_token_cycle": rows}))
+    for name, row in rows.items():
+        print(f"{name:10s} " + "  ".join(f"{k} {v:6d}" for k, v in row.items()), file=sys.stderr)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -617,6 +686,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES (read BYTES, write BYTES) before "
                          "timing, as a reference for hardware byte counters")
+    ap.add_argument("--phase-timing", action="store_true",
+                    help="diagnostic: per-role clocks per pipeline cycle of the dense fp16 build "
+                         "(loads libpic_timing.so; 2 layers unless --layers)")
     ap.add_argument("--source-digest", action="store_true",
                     help="print the source digest of each timed kernel and exit")
     args = ap.parse_args(argv)
@@ -636,6 +708,8 @@ def main(argv=None):
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.phase_timing:
+        return phase_timing(w, args)
     if args.layers:
         w = synth.scaled(w, layers=args.layers, name=w.name)
     if w.form == synth.KDA:

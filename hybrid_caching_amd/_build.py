@@ -15,6 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpic.so")
+# diagnostic twin of the library: the dense fp16 build with per-wave barrier
+# timers (-DPIC_PHASE_TIMING), every other object shared
+TIMING_LIB_PATH = os.path.join(HERE, "libpic_timing.so")
+TIMED_SOURCES = ["k_build_dense_h16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_ws.hip", "k_build_dense_h16.hip",
@@ -27,8 +31,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-ta
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), suffix: str = "") -> str:
+    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + suffix + ".o")
     lang = ["-x", "hip"]  # host-only sources also go through the HIP driver
     cmd = [HIPCC, *COMMON, *lang, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,16 +47,22 @@ def _compile(src: str, extra=()) -> str:
 
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print("built", LIB_PATH)
+    jobs = [(s, tuple(extra), "") for s in SOURCES]
+    jobs += [(s, tuple(extra) + ("-DPIC_PHASE_TIMING",), "_timing") for s in TIMED_SOURCES]
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    plain = objs[:len(SOURCES)]
+    timed = dict(zip(TIMED_SOURCES, objs[len(SOURCES):]))
+    timing_objs = [timed.get(s, o) for s, o in zip(SOURCES, plain)]
+    for path, objects in ((LIB_PATH, plain), (TIMING_LIB_PATH, timing_objs)):
+        tmp = path + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objects]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+        os.replace(tmp, path)
+        if verbose:
+            print("built", path)
     return LIB_PATH
 
 

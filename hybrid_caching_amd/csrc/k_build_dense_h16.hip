@@ -17,9 +17,12 @@
 // norm is ~1e-4 after 4096 tokens at the usual gates), far below fp16's
 // normal range, so each consumer wave keeps its columns of That scaled by a
 // power of two (a column scaling commutes with left multiplication, and a
-// power of two is exact) and re-normalises them every other chunk; the
-// exponent is applied when That is written.  S, U, W and the keys stay within fp16's
-// range for unit-norm keys and values of moderate size.
+// power of two is exact) and re-normalises them every fourth chunk; the
+// exponent is applied when That is written.  S is decayed lazily: the
+// consumers keep S / G with G >= 2^-5 the product of the chunk decays since
+// the last eager multiply, so most sub-chunks need no pass over S (the 1/G
+// of the W seed is folded into beta * r by the gate wave).  S / G, U, W and
+// the keys stay within fp16's range for unit-norm keys and |S| below ~2e3.
 //
 // One workgroup per (segment, layer, head): four consumer waves, each holding
 // columns [32c, 32c+32) of both That and S in MFMA accumulators for the whole
@@ -48,7 +51,8 @@
 //                      ci-1 -> -U fragments
 //            V wave:   V rows of chunk ci-1
 //            solver:   diagonal blocks of chunk ci; U^T tiles 6, 7 of ci-1
-//   phase B: consumers: W seeds of chunk ci-1, chain sub-chunk 0 of ci-1
+//   phase B: consumers: W seed and chain of sub-chunk 0 of chunk ci-1, then
+//                       the W seed of its sub-chunk 1 (kept for phase A)
 //            K waves:  G of chunk ci+1 (wave s: sub-chunk s)
 //            V wave:   the gates of chunk ci+1
 //            solver:   off-diagonal blocks of chunk ci -> A, A'
@@ -72,6 +76,70 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// Optional phase timing (built only with -DPIC_PHASE_TIMING, into a separate
+// diagnostic library): every wave adds up, per phase of the pipeline cycle,
+// the clocks from the barrier that opens the phase to the one that closes it
+// (the phase's length, the same for every wave) and the clocks it waits at
+// the closing barrier; its busy time in the phase is the difference.  Clocks
+// are the shader-clock counter read by s_memtime.
+#ifdef PIC_PHASE_TIMING
+}  // namespace
+__device__ unsigned long long* pic_phase_out;  // [block][wave][8], blocks < pic_phase_blocks
+__device__ int pic_phase_blocks;
+namespace {
+struct PhaseClock {
+  unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  // barrier i-1: arrival a1, release b1, phase it opened ph1; barrier i-2:
+  // release b2, phase ph2.  A timestamp is used only after the next
+  // barrier's fence (which waits for it anyway), so reading the clock adds
+  // no wait of its own.
+  unsigned long long a1 = 0, b1 = 0, b2 = 0;
+  int ph1 = -1, ph2 = -1;
+  unsigned long long wait_end[2] = {0, 0}, len[2] = {0, 0};
+  unsigned cycles = 0;
+};
+#define PIC_PHASE_DECL PhaseClock pic_pc_
+// barrier that opens phase `ph` (and closes the other one)
+#define PIC_BAR(ph)                                                  \
+  do {                                                               \
+    const unsigned long long pic_a_ = __builtin_amdgcn_s_memtime(); \
+    __syncthreads();                                                 \
+    __builtin_amdgcn_sched_barrier(0);                               \
+    if (pic_pc_.ph2 >= 0) {                                          \
+      pic_pc_.len[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.b2;           \
+      pic_pc_.wait_end[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.a1;      \
+    }                                                                \
+    pic_pc_.b2 = pic_pc_.b1;                                         \
+    pic_pc_.ph2 = pic_pc_.ph1;                                       \
+    pic_pc_.a1 = pic_a_;                                             \
+    pic_pc_.ph1 = (ph);                                              \
+    pic_pc_.b1 = __builtin_amdgcn_s_memtime();                       \
+    pic_pc_.cycles += (ph);                                          \
+    __builtin_amdgcn_sched_barrier(0);                               \
+  } while (0)
+#define PIC_PHASE_SAVE                                                                   \
+  do {                                                                                   \
+    if (pic_pc_.ph2 >= 0) {                                                              \
+      pic_pc_.len[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.b2;                               \
+      pic_pc_.wait_end[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.a1;                          \
+    }                                                                                    \
+    if (int(blockIdx.x) < pic_phase_blocks && (threadIdx.x & 63) == 0) {                \
+      unsigned long long* o =                                                            \
+          pic_phase_out + (blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * 8;        \
+      o[0] = pic_pc_.len[0];                                                             \
+      o[1] = pic_pc_.wait_end[0];                                                        \
+      o[2] = pic_pc_.len[1];                                                             \
+      o[3] = pic_pc_.wait_end[1];                                                        \
+      o[4] = __builtin_amdgcn_s_memtime() - pic_pc_.t0;                                 \
+      o[5] = pic_pc_.cycles;                                                             \
+    }                                                                                    \
+  } while (0)
+#else
+#define PIC_PHASE_DECL
+#define PIC_BAR(ph) __syncthreads()
+#define PIC_PHASE_SAVE
+#endif
+
 constexpr int DP = 128;        // padded head size
 constexpr int C = 64;          // tokens staged per chunk
 constexpr int NT = DP / 32;    // consumer waves = 32-row tiles
@@ -80,6 +148,7 @@ constexpr int THREADS = (NT + 1 + NHW) * 64;
 constexpr int NKB = 4;         // K buffers (chunks alive at once)
 
 constexpr int RLD = DP + 16;   // row stride (halves) of K and V
+constexpr float kLazyLog2 = -5.f;  // lazy decay of S: G >= 2^-5
 constexpr int A_LD = 40;       // A, A' rows (fp16, 32 tokens + pad)
 
 constexpr int ROWS_BYTES = C * RLD * 2;
@@ -93,8 +162,8 @@ constexpr int L_UF = L_AB + 2 * AB_HALFS * 2;
 constexpr int UF_BYTES = 2 * NT * 2 * 64 * 16;  // [s][t][h][lane] x 16 B
 constexpr int L_GB = L_UF + 2 * UF_BYTES;       // beta (masked), two chunks
 constexpr int L_GBR = L_GB + 2 * C * 4;         // beta * r, two chunks
-constexpr int L_GG = L_GBR + 2 * C * 4;         // gamma ring [4][2]
-constexpr int LDS_TOTAL = L_GG + 8 * 4;
+constexpr int L_GG = L_GBR + 2 * C * 4;         // eager multiplier ring [4][2], final log2 scale
+constexpr int LDS_TOTAL = L_GG + 12 * 4;
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of a CU");
 static_assert(L_V % 16 == 0 && L_NM % 16 == 0 && L_AB % 16 == 0 && L_UF % 16 == 0 &&
               L_GB % 16 == 0 && L_GBR % 16 == 0 && (RLD * 2) % 16 == 0, "alignment");
@@ -424,8 +493,9 @@ __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
 // ===========================================================================
 __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
+  PIC_PHASE_DECL;
   const int c = wid;
-  f32x16 XT[NT], XS[NT], PM[2];
+  f32x16 XT[NT], XS[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     XS[t] = zero16();
@@ -435,61 +505,83 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
       XT[t][q] = (row == col && row < dk) ? 1.f : 0.f;
     }
   }
-  PM[0] = PM[1] = zero16();
   int E = 0;
 
-  // sub-chunk s of chunk j: S *= gamma; N = -U That, M = W - U S;
-  // That += K^T N, S += K^T M
-  auto chain_sub = [&](int s, int j) {
+  // Lazy decay of S.  XS holds S / G, where G is the product of the
+  // sub-chunk decays gamma since the last eager step, so that a lazy step
+  // needs no pass over the state: S' = gamma S + K^T (W - U gamma S) becomes
+  // XS' = XS + K^T (W / G' - U XS) with G' = G gamma, and the 1/G' of the W
+  // seed is already folded into beta * r by the gate wave.  When G gamma would
+  // drop below 2^kLazyLog2 the step is eager instead: XS *= G gamma, G = 1.
+  // So |XS| <= 2^-kLazyLog2 |S| (the fp16 operand range bounds |S|).
+
+  // sub-chunk s of chunk j, seed P = W / G' (this wave's columns):
+  // [eager: S *= em]; N = -U That, M = W - U S; That += K^T N, S += K^T M
+  auto chain_sub = [&](int s, int j, f32x16 P) {
     const char* uf = Uf0 + (j & 1) * UF_BYTES;
     const _Float16* kb = Kb0 + (j % NKB) * (C * RLD);
-    const float gam = gg[(j & 3) * 2 + s];
+    // every -U fragment of the sub-chunk, read before anything waits
+    f16x8 uu[2 * NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) XS[t] *= gam;
-    f32x16 PN = zero16(), P = PM[s];
+    for (int ks = 0; ks < 2 * NT; ++ks)
+      uu[ks] = *reinterpret_cast<const f16x8*>(uf + uf_off(s, ks >> 1, ks & 1, lane));
+    const int emi = rfl(__float_as_int(gg[(j & 3) * 2 + s]));
+    if (emi >= 0) {  // eager step (uniform)
+      const float em = __int_as_float(emi);
 #pragma unroll
-    for (int ks = 0; ks < 2 * NT; ++ks) {
-      const int t = ks >> 1, hh = ks & 1;
-      const f16x8 tb = acc_h8(XT[t], hh), sb = acc_h8(XS[t], hh);
-      const f16x8 u = *reinterpret_cast<const f16x8*>(uf + uf_off(s, t, hh, lane));
-      PN = mfma16(u, tb, PN);
-      P = mfma16(u, sb, P);
+      for (int t = 0; t < NT; ++t) XS[t] *= em;
     }
     // K^T fragment of K-step hh, tile t: lane (g, m) needs K[token][32t + m]
     // for tokens kperm(hh, g, 0..7) = 16 hh + 4 g + {0..3, 8..11} of the
     // sub-chunk -- the row order of the N / M accumulator halves
     const _Float16* kbase = kb + (32 * s + 4 * g + tr_row) * RLD + tr_col;
+    f16x8 kf[2][NT];
+    f32x16 PN = zero16();
+    // k-steps in source order (a scheduling barrier after each), so that the
+    // -U fragments die one by one and the K^T reads of the second stage are
+    // issued while the first stage still has matrix work queued
+#pragma unroll
+    for (int ks = 0; ks < 2 * NT; ++ks) {
+      const int t = ks >> 1, hh = ks & 1;
+      const f16x8 tb = acc_h8(XT[t], hh), sb = acc_h8(XS[t], hh);
+      PN = mfma16(uu[ks], tb, PN);
+      P = mfma16(uu[ks], sb, P);
+      if (ks == 3 || ks == 5) {
+        const int kh = ks == 3 ? 0 : 1;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const _Float16* p0 = kbase + 16 * kh * RLD + 32 * tt;
+          kf[kh][tt] = tr_h8(p0, p0 + 8 * RLD);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const f16x8 nb = acc_h8(PN, hh), mb = acc_h8(P, hh);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const _Float16* p0 = kbase + 16 * hh * RLD + 32 * t;
-        const f16x8 kf = tr_h8(p0, p0 + 8 * RLD);
-        XT[t] = mfma16(kf, nb, XT[t]);
-        XS[t] = mfma16(kf, mb, XS[t]);
+        XT[t] = mfma16(kf[hh][t], nb, XT[t]);
+        XS[t] = mfma16(kf[hh][t], mb, XS[t]);
       }
     }
   };
 
-  // W seeds of both sub-chunks of chunk j: M_s = A'_s V_s (this wave's
-  // columns)
-  auto seeds = [&](int j) {
+  // W seed of sub-chunk s of chunk j: M_s = A'_s V_s (this wave's columns;
+  // A' carries the lazy 1/G')
+  auto seed = [&](int j, int s) {
     const _Float16* Ap = AB0 + (j & 1) * AB_HALFS + 64 * A_LD;
     // V^T fragment: lane (g, n) needs V[token 16 kk + 8 g + 0..7][32 c + n]
     const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 32 * c + tr_col;
+    f32x16 acc = zero16();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const f16x8 ph = lds_h8(Ap + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
-        const _Float16* p0 = vbase + (32 * s + 16 * kk) * RLD;
-        const f16x8 vf = tr_h8(p0, p0 + 4 * RLD);
-        acc = mfma16(ph, vf, acc);
-      }
-      PM[s] = acc;
+    for (int kk = 0; kk < 2; ++kk) {
+      const f16x8 ph = lds_h8(Ap + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
+      const _Float16* p0 = vbase + (32 * s + 16 * kk) * RLD;
+      const f16x8 vf = tr_h8(p0, p0 + 4 * RLD);
+      acc = mfma16(ph, vf, acc);
     }
+    return acc;
   };
   // re-normalise this wave's columns of That by a power of two -- branch-free,
   // so that no copy of the state is made
@@ -511,59 +603,62 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 
   // Cycles -1 .. n+1 of the pipeline, peeled so that the steady-state loop
   // has no branch around the chain (see the schedule at the top).
-  __syncthreads();  // cycle -1, phase A
-  __syncthreads();  //           phase B
-  __syncthreads();  // cycle 0,  phase A
-  __syncthreads();  //           phase B
+  PIC_BAR(0);  // cycle -1, phase A
+  PIC_BAR(1);  //           phase B
+  PIC_BAR(0);  // cycle 0,  phase A
+  PIC_BAR(1);  //           phase B
   if (n >= 1) {
-    __syncthreads();  // cycle 1, phase A
-    __syncthreads();  //          phase B
-    seeds(0);
+    PIC_BAR(0);  // cycle 1, phase A
+    PIC_BAR(1);  //          phase B
     renorm();
-    chain_sub(0, 0);
+    chain_sub(0, 0, seed(0, 0));
+    f32x16 PM1 = seed(0, 1);  // (V of the chunk is replaced in the next phase)
     int ci = 2;
-    // (the re-normalisation every other chunk sits at the end of phase A:
-    // between the same two chain steps as at the start of phase B, but in
-    // the phase where the consumers have the shorter part of the work)
+    // (the re-normalisation of That every fourth chunk sits at the end of
+    // phase A; That's norm shrinks by about 0.87 per chunk at the usual gates,
+    // so four chunks stay far inside fp16's range)
 #pragma unroll 1
     for (; ci + 1 <= n; ci += 2) {
-      __syncthreads();  // phase A
-      chain_sub(1, ci - 2);
-      __syncthreads();  // phase B
-      seeds(ci - 1);
-      chain_sub(0, ci - 1);
-      __syncthreads();  // phase A
-      chain_sub(1, ci - 1);
-      renorm();
-      __syncthreads();  // phase B
-      seeds(ci);
-      chain_sub(0, ci);
+      PIC_BAR(0);  // phase A
+      chain_sub(1, ci - 2, PM1);
+      PIC_BAR(1);  // phase B
+      chain_sub(0, ci - 1, seed(ci - 1, 0));
+      PM1 = seed(ci - 1, 1);
+      PIC_BAR(0);  // phase A
+      chain_sub(1, ci - 1, PM1);
+      if (((ci >> 1) & 1) == 0) renorm();  // every fourth chunk
+      PIC_BAR(1);  // phase B
+      chain_sub(0, ci, seed(ci, 0));
+      PM1 = seed(ci, 1);
     }
     if (ci <= n) {
-      __syncthreads();  // phase A
-      chain_sub(1, ci - 2);
-      __syncthreads();  // phase B
-      seeds(ci - 1);
-      chain_sub(0, ci - 1);
+      PIC_BAR(0);  // phase A
+      chain_sub(1, ci - 2, PM1);
+      PIC_BAR(1);  // phase B
+      chain_sub(0, ci - 1, seed(ci - 1, 0));
+      PM1 = seed(ci - 1, 1);
     }
-    __syncthreads();  // cycle n+1, phase A
-    chain_sub(1, n - 1);
-    __syncthreads();  //            phase B
+    PIC_BAR(0);  // cycle n+1, phase A
+    chain_sub(1, n - 1, PM1);
+    PIC_BAR(1);  //            phase B
   } else {
-    __syncthreads();  // cycle 1, phase A
-    __syncthreads();  //          phase B
+    PIC_BAR(0);  // cycle 1, phase A
+    PIC_BAR(1);  //          phase B
   }
 
-  // write this wave's columns of S(C|0) and That_C
+  PIC_PHASE_SAVE;
+  // write this wave's columns of S(C|0) (= 2^lg XS, lg the final log2 G of
+  // the lazy decay) and That_C
   const int ncol = c * 32 + cl;
   if (ncol < dv) {
     float* out = out_S + unit * int64_t(dk) * dv;
+    const float gs = n >= 1 ? exp2f(gg[8]) : 1.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) gstore(out + int64_t(row) * dv + ncol, float(XS[t][q]));
+        if (row < dk) gstore(out + int64_t(row) * dv + ncol, float(XS[t][q]) * gs);
       }
   }
   if (ncol < dk) {
@@ -594,6 +689,7 @@ constexpr int XS_LD = 48;  // scratch row stride (halves): 96 bytes, so that the
                            // four rows of a transposed read hit distinct banks
 __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
+  PIC_PHASE_DECL;
   const int s = lane >> 5, blk = (lane >> 4) & 1, jr = lane & 15;
   float acc[16], bt[16];
 #pragma unroll 1
@@ -603,7 +699,7 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
     const float* gbp = gb0 + (ci & 1) * C;                 // masked beta
     const float* grp = gbr0 + (ci & 1) * C;                // beta * r
     _Float16* ab = AB0 + (ci & 1) * AB_HALFS;              // scratch, then A / A'
-    __syncthreads();  // phase A
+    PIC_BAR(0);  // phase A
     if (solve) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -626,7 +722,7 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
       ut_tiles<2>(Kb0 + (j % NKB) * (C * RLD), AB0 + (j & 1) * AB_HALFS, Uf0 + (j & 1) * UF_BYTES,
                   6, lane);
     }
-    __syncthreads();  // phase B
+    PIC_BAR(1);  // phase B
     if (solve) {
       // off-diagonal blocks; 16x16x16 layouts: lane l holds A[l%16][4(l/16)+e],
       // B[4(l/16)+e][l%16], D[4(l/16)+e][l%16], e = 0..3
@@ -698,6 +794,7 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
       }
     }
   }
+  PIC_PHASE_SAVE;
 }
 
 // ===========================================================================
@@ -705,6 +802,7 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
 // ===========================================================================
 __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
+  PIC_PHASE_DECL;
   const int pw = wid - NT - 1;  // 0 or 1
   const int HDk = H * dk;       // element stride between tokens
   const int kch = min(8 * (lane & 15), dk - 8);
@@ -718,7 +816,7 @@ __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
   for (int ci = -1; ci <= n + 1; ++ci) {
     // ---------------- phase A: K rows of chunk ci+1, load chunk ci+2's;
     // U^T tiles 3 pw .. 3 pw + 2 of chunk ci-1
-    __syncthreads();
+    PIC_BAR(0);
     if (ci + 1 < n)
       stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, dk, i0, lane);
     if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, lane);
@@ -728,15 +826,17 @@ __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
                   3 * pw, lane);
     }
     // ---------------- phase B: G of sub-chunk pw of chunk ci+1
-    __syncthreads();
+    PIC_BAR(1);
     if (ci + 1 < n)
       gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane, pw);
   }
+  PIC_PHASE_SAVE;
 }
 
 // V rows and gates (the last wave)
 __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   PIC_H16_ROLE_PROLOGUE;
+  PIC_PHASE_DECL;
   const float* bsrc = beta ? beta : alpha;
   const int HDv = H * dv;  // element stride between tokens
   const int vch = min(8 * (lane & 15), dv - 8);
@@ -745,6 +845,7 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   // that no register holding a pending load is copied
   float pa[2] = {1.f, 1.f}, pb[2] = {0.f, 0.f};
   float lam = 0.f;
+  float lg = 0.f;  // log2 G of the lazy decay, uniform
   auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
   auto load_gates = [&](int j, float& ra, float& rb) {
     const int64_t gi = row0(j) + int64_t(min(lane, chunk_len(j) - 1)) * H;
@@ -756,11 +857,11 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   auto cycle = [&](int ci, auto par) {
     constexpr int P = decltype(par)::value;
     // ---------------- phase A: V rows of chunk ci-1, then load chunk ci's
-    __syncthreads();
+    PIC_BAR(0);
     if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, dv, 0, lane);
     if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), 0, lane);
     // ---------------- phase B: gates of chunk ci+1
-    __syncthreads();
+    PIC_BAR(1);
     if (ci + 1 < n) {
       // log2 prefix per sub-chunk (one per half wave)
       const int jn = ci + 1;
@@ -771,11 +872,30 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
       const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 63));
       const float bend = g ? e1 : e0;
       const float bt = lane < len ? (beta ? pb[P] : 1.f) : 0.f;  // masked beta
+      // lazy decay of S (see the consumer): per sub-chunk, either the
+      // consumers keep S / G with G <- G gamma (lazy: the W seed takes 1/G),
+      // or, when G gamma would drop below 2^kLazyLog2, they multiply S by
+      // G gamma and G restarts at 1 (eager: em >= 0)
+      float em[2], sl[2];
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const float e = ss ? e1 : e0;
+        if (lg + e >= kLazyLog2) {
+          lg += e;
+          em[ss] = -1.f;
+          sl[ss] = -lg;
+        } else {
+          em[ss] = exp2f(lg + e);
+          lg = 0.f;
+          sl[ss] = 0.f;
+        }
+      }
       gb0[(jn & 1) * C + lane] = bt;
-      gbr0[(jn & 1) * C + lane] = bt * exp2f(bend - x2);
+      gbr0[(jn & 1) * C + lane] = bt * exp2f(bend - x2 + (g ? sl[1] : sl[0]));
       if (lane == 0) {
-        gg[(jn & 3) * 2] = exp2f(e0);
-        gg[(jn & 3) * 2 + 1] = exp2f(e1);
+        gg[(jn & 3) * 2] = em[0];
+        gg[(jn & 3) * 2 + 1] = em[1];
+        if (jn == n - 1) gg[8] = lg;  // S(C|0) = 2^lg x the consumers' S
       }
       lam += e0 + e1;
       // the slot of chunk jn now takes chunk jn + 2
@@ -792,6 +912,7 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
     if (ci + 1 <= n + 1) cycle(ci + 1, std::integral_constant<int, 1>{});
   }
   if (lane == 0) gstore(out_lam + unit, lam * kLn2);
+  PIC_PHASE_SAVE;
 }
 
 }  // namespace
@@ -804,3 +925,17 @@ hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s) {
 }
 
 }  // namespace pic
+
+#ifdef PIC_PHASE_TIMING
+// Diagnostic library only: where the dense fp16 build writes its per-wave
+// phase clocks ([block][wave][8]: length of phase A, wait at its end, length
+// of phase B, wait at its end, total clocks, cycles, 2 unused) for blocks
+// below `blocks`.
+extern "C" int pic_phase_timing_set(void* dev_buf, int blocks) {
+  if (hipMemcpyToSymbol(HIP_SYMBOL(pic::pic_phase_out), &dev_buf, sizeof(dev_buf)) != hipSuccess)
+    return -7;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(pic::pic_phase_blocks), &blocks, sizeof(blocks)) != hipSuccess)
+    return -7;
+  return 0;
+}
+#endif

@@ -108,8 +108,9 @@ enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
  *                  dense form with bf16 k/v only.  The ungated product That
  *                  is kept at a power-of-two column scale internally, so its
  *                  decay along a segment does not leave fp16's range; keys
- *                  are assumed unit-norm (beta |k|^2 <= 2) and |v|, |S| well
- *                  below 6e4.  Typical relative Frobenius error against fp64
+ *                  are assumed unit-norm (beta |k|^2 <= 2), |v| well below
+ *                  6e4 and |S| below about 2e3 (the state is kept at up to
+ *                  32x its size between decays).  Typical relative Frobenius error against fp64
  *                  at 4096-8192 tokens: ~2e-3 on That, ~3e-4 on S(C|0). */
 enum pic_precision { PIC_PREC_FP32 = 0, PIC_PREC_FP16 = 1 };
 
