@@ -32,6 +32,11 @@ module only marshals numpy arrays into it.  What each call computes:
   last raw inputs as history: y_t = sum_j w_j x_(t-j), written as plain loops.
   [xix.ai, paragraph on linear layers: variants with a short convolution need
   the convolution state warmed up]
+* ``prefill`` -- the independent prefill of every segment with per-token
+  outputs o_t = S_t^T q_t (the state after the token's own update), beside
+  the pair: the build's token loop with a readout after every update.
+  [remio.ai, section on how HYPIC composes linear-attention states: the pair
+  is built at the segment's first prefill]
 * ``plan_build`` / ``plan_compose`` -- the host bookkeeping of a call, from
   its definition: segments as token ranges cut into 64-token chunks (in
   segment order; the order a launch visits them in is the library's
@@ -76,6 +81,11 @@ def _bind(lib):
     lib.oracle_build.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, _dp,
                                  _i64p, ctypes.c_int, _dp, _dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_prefill.restype = ctypes.c_int
+    lib.oracle_prefill.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, _dp,
+                                   _dp, _i64p, ctypes.c_int, _dp, _dp, _dp, _dp, _dp,
+                                   ctypes.c_int]
     lib.oracle_recurrence.restype = ctypes.c_int
     lib.oracle_recurrence.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int64, _dp, _dp, _dp, _dp, _dp, _dp,
@@ -155,6 +165,43 @@ def build(form, k, v, alpha, beta, offsets, *, literal=False, want_T=False, thre
     if rc != 0:
         raise ValueError("oracle_build rejected its arguments")
     out = {"lam": lam, "S": S}
+    if That is not None:
+        out["That"] = That
+    if T is not None:
+        out["T"] = T
+    return out
+
+
+def prefill(form, q, k, v, alpha, beta, offsets, *, literal=False, threads=None, lib=None):
+    """Independent prefill of every segment with per-token outputs.
+
+    Each segment starts from the zero state; after every token's update
+    S_t = T_t S_(t-1) + beta_t k_t v_t^T its output is o_t = S_t^T q_t (the
+    readout of the state that includes the token).  q: [B, N, H, dk]; the
+    rest as for ``build``.  Returns ``build``'s dict plus O [B, N, H, dv].
+    [the pair is cached at a segment's first prefill, alongside the prefill's
+    own outputs; remio.ai HYPIC article (Japanese), section on how HYPIC
+    composes linear-attention states]"""
+    lib = lib or load()
+    q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
+    beta = _f64(beta) if (beta is not None and form in (DENSE, KDA)) else None
+    B, N, H, dk = k.shape
+    dv = v.shape[3]
+    if q.shape != k.shape:
+        raise ValueError("q must have k's shape")
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n_seg = len(offs) - 1
+    lam = np.zeros((n_seg, B, H, dk) if form == DIAG else (n_seg, B, H))
+    That = np.zeros((n_seg, B, H, dk, dk)) if form in (DENSE, KDA) else None
+    T = np.zeros((n_seg, B, H, dk, dk)) if literal else None
+    S = np.zeros((n_seg, B, H, dk, dv))
+    O = np.zeros((B, N, H, dv))
+    rc = lib.oracle_prefill(form, int(bool(literal)), B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(alpha), _ptr(beta), _ptr(offs, _i64p), n_seg, _ptr(lam),
+                            _ptr(That), _ptr(T), _ptr(S), _ptr(O), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    out = {"lam": lam, "S": S, "O": O}
     if That is not None:
         out["That"] = That
     if T is not None:

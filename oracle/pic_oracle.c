@@ -50,6 +50,13 @@
  *    of the rest of the segment is applied (oracle_seam_compose, below).
  *    [xix.ai, paragraph on full-attention layers: seam windows of w tokens.]
  *
+ *  - Prefill with outputs: a segment prefilled on its own (from the zero
+ *    state) also gives every token's output o_t = S_t^T q_t, read from the
+ *    state right after the token's update (oracle_prefill, below): the
+ *    computation in which the pair is built at first prefill.
+ *    [remio.ai (Japanese), same section: the pair is cached at the
+ *     segment's first prefill, a small add-on to it.]
+ *
  *  Because T_C underflows fp32 at realistic gate values, the pair is also
  *  given in split form: lambda_C = sum_t ln(alpha_t) (per head for scalar
  *  and dense, per key channel for diagonal) and, for the dense form,
@@ -201,6 +208,8 @@ typedef struct {
   const int64_t *offsets;
   int n_seg;
   double *lam, *That, *T, *S;
+  const double *q; /* prefill only: queries [B][N][H][dk] */
+  double *O;       /* prefill only: outputs [B][N][H][dv], o_t = S_t^T q_t */
 } build_ctx;
 
 static inline const double *k_at(const build_ctx *c, int b, int64_t t, int h) {
@@ -329,6 +338,17 @@ static void build_unit(void *vctx, int64_t item) {
       for (int i = 0; i < dk; ++i)
         for (int j = 0; j < dk; ++j) Th[i * dk + j] -= bt * kt[i] * kS[j];
     }
+    if (c->O) {
+      /* the token's output reads the state after its own update:
+       * o_t = S_t^T q_t */
+      const double *qt = c->q + (((int64_t)b * c->N + t) * c->H + h) * dk;
+      double *ot = c->O + (((int64_t)b * c->N + t) * c->H + h) * dv;
+      for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];
+        ot[j] = acc;
+      }
+    }
   }
 
   memcpy(c->S + item * dk * dv, S, sizeof(double) * dk * dv);
@@ -357,6 +377,26 @@ int oracle_build(int form, int literal, int B, int H, int dk, int dv, int64_t N,
   for (int i = 0; i < n_seg; ++i)
     if (offsets[i + 1] < offsets[i]) return -1;
   build_ctx c = {form, literal, B, H, dk, dv, N, k, v, alpha, beta, offsets, n_seg, lam, That, T, S};
+  run_items(build_unit, &c, (int64_t)n_seg * B * H, n_threads);
+  return 0;
+}
+
+/* Independent prefill of every segment with outputs: the build above, and
+ * for every token the output of the state right after its own update,
+ * o_t = S_t^T q_t, with the state starting from zero at each segment's first
+ * token (a cached segment is prefilled on its own).  O [B][N][H][dv]. */
+int oracle_prefill(int form, int literal, int B, int H, int dk, int dv, int64_t N,
+                   const double *q, const double *k, const double *v, const double *alpha,
+                   const double *beta, const int64_t *offsets, int n_seg, double *lam,
+                   double *That, double *T, double *S, double *O, int n_threads) {
+  if (form < 0 || form > 3 || B < 0 || H < 0 || dk <= 0 || dv <= 0 || n_seg < 0) return -1;
+  if (!q || !O) return -1;
+  if (offsets[0] != 0 || offsets[n_seg] != N) return -1;
+  for (int i = 0; i < n_seg; ++i)
+    if (offsets[i + 1] < offsets[i]) return -1;
+  build_ctx c = {form, literal, B, H, dk, dv, N, k, v, alpha, beta, offsets, n_seg, lam, That, T, S};
+  c.q = q;
+  c.O = O;
   run_items(build_unit, &c, (int64_t)n_seg * B * H, n_threads);
   return 0;
 }

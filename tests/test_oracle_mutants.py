@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_kda_pins as kda_pins
+from tests import test_oracle_prefill_pins as prefill_pins
 from tests import test_oracle_seam_pins as seam_pins
 
 _SEAM_OUT = """  /* o_t = S_t^T q_t */
@@ -111,6 +112,18 @@ MUTANTS = [
     ("KDA: smallest gate taken as the scale",
      "    if (at[i] > m) m = at[i];",
      "    if (at[i] < m) m = at[i];"),
+    ("prefill: output read before the token's update",
+     ["    if (c->O) {\n", "  for (int64_t t = t0; t < t1; ++t) {\n    const double *kt = k_at(c, b, t, h), *vt = v_at(c, b, t, h), *at = a_at(c, b, t, h);\n"],
+     ["    if (0) {\n", "  for (int64_t t = t0; t < t1; ++t) {\n    if (c->O) {\n      const double *qt = c->q + (((int64_t)b * c->N + t) * c->H + h) * dk;\n      double *ot = c->O + (((int64_t)b * c->N + t) * c->H + h) * dv;\n      for (int j = 0; j < dv; ++j) {\n        double acc = 0.0;\n        for (int i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];\n        ot[j] = acc;\n      }\n    }\n    const double *kt = k_at(c, b, t, h), *vt = v_at(c, b, t, h), *at = a_at(c, b, t, h);\n"]),
+    ("prefill: output transposed",
+     "for (int i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];",
+     "for (int i = 0; i < dk; ++i) acc += qt[i] * S[(j * dk + i) % (dk * dv)];"),
+    ("prefill: queries read with the value stride",
+     "const double *qt = c->q + (((int64_t)b * c->N + t) * c->H + h) * dk;",
+     "const double *qt = c->q + (((int64_t)b * c->N + t) * c->H + h) * dv;"),
+    ("prefill: output written to the previous token's row",
+     "double *ot = c->O + (((int64_t)b * c->N + t) * c->H + h) * dv;",
+     "double *ot = c->O + (((int64_t)b * c->N + (t > 0 ? t - 1 : 0)) * c->H + h) * dv;"),
     ("seam: pair gate scale dropped",
      "Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;",
      "Tp[i * dk + j] = ungated;"),
@@ -152,6 +165,13 @@ def _pin_calls():
               lambda: kda_pins.test_kda_exact_rational(0),
               lambda: kda_pins.test_kda_split_compose_equals_unsplit([0, 9, 10, 31]),
               kda_pins.test_kda_That_is_bounded]
+    calls += [lambda: prefill_pins.test_plain_linear_attention_is_masked_product(False),
+              prefill_pins.test_scalar_decay_closed_form,
+              prefill_pins.test_diagonal_gate_closed_form,
+              lambda: prefill_pins.test_outputs_are_prefix_recurrences_read_out(pins.DENSE),
+              lambda: prefill_pins.test_delta_rule_retrieval(False)]
+    for form in (pins.SCALAR, pins.DIAG, pins.DENSE):
+        calls.append(lambda f=form: prefill_pins.test_exact_rational_brute_force(f, False))
     return calls
 
 
