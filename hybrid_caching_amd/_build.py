@@ -21,7 +21,7 @@ TIMING_LIB_PATH = os.path.join(HERE, "libpic_timing.so")
 TIMED_SOURCES = ["k_build_dense_h16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_ws.hip", "k_build_dense_h16.hip",
+SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_ws.hip", "k_build_dense_h16.hip", "k_dense_fp16.hip",
            "k_build_scalar_diag.hip", "k_build_sd_pipe.hip", "k_compose_seam.hip",
            "k_build_kda.hip", "k_rerotate.hip", "k_conv_warmup.hip"]
 

@@ -37,6 +37,10 @@ SIGNATURES = {
                                 _p, _p, _p, _sz]),
     "pic_segment_build": (_i, [_i, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
                                _p, _p, _p, _sz, _p]),
+    "pic_validate_prefill": (_i, [_i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p,
+                                  _p, _p, _sz]),
+    "pic_segment_prefill": (_i, [_i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p,
+                                 _p, _p, _sz, _p]),
     "pic_compose_workspace": (_sz, [_i32, _i64]),
     "pic_validate_compose": (_i, [_i, _i, _i, _i, _i, _i64, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
                                   _p, _p, _sz]),
@@ -176,6 +180,49 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
                                _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
                                _stream(dev))
     _check(rc, "pic_segment_build")
+    return out
+
+
+def pic_segment_prefill(q, k, v, alpha, beta, seg_offsets, *, track_T: bool = True, out=None):
+    """Independent prefill of every segment with per-token outputs (dense
+    form, bf16 q/k/v, fp16 operand precision): o_t = S_t^T q_t from the zero
+    state at each segment's start, plus the segment's pair.
+
+    q, k: bf16 [B, N, H, dk]; v: bf16 [B, N, H, dv]; alpha, beta: fp32
+    [B, N, H] (beta may be None = 1); seg_offsets: host ints [n_seg+1].
+    Returns dict: log_scale [n_seg, B, H], S0 [n_seg, B, H, dk, dv], O bf16
+    [B, N, H, dv] and, with track_T, T_hat [n_seg, B, H, dk, dk]."""
+    lib = load()
+    B, N, H, dk = k.shape
+    dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16)
+    _need(alpha, "alpha", torch.float32)
+    _need(beta, "beta", torch.float32)
+    if tuple(q.shape) != tuple(k.shape):
+        raise ValueError("q must have k's shape")
+    off, off_p = _host_i64(seg_offsets)
+    n_seg = len(off) - 1
+    dev = k.device
+    if out is None:
+        out = {"log_scale": torch.empty((n_seg, B, H), dtype=torch.float32, device=dev),
+               "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev),
+               "O": torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=dev)}
+        if track_T:
+            out["T_hat"] = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
+    _need(out["log_scale"], "log_scale", torch.float32)
+    _need(out["S0"], "S0", torch.float32)
+    _need(out["O"], "O", torch.bfloat16)
+    if tuple(out["O"].shape) != (B, N, H, dv):
+        raise ValueError(f"O must be {(B, N, H, dv)}")
+    T = out.get("T_hat")
+    _need(T, "T_hat", torch.float32)
+    ws = _workspace(lib.pic_segment_build_workspace(FORM_DENSE, B, H, dk, dv, N, n_seg), dev)
+    rc = lib.pic_segment_prefill(B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), off_p, n_seg, _ptr(out["log_scale"]), _ptr(T),
+                                 _ptr(out["S0"]), _ptr(out["O"]), _ptr(ws), ws.numel(),
+                                 _stream(dev))
+    _check(rc, "pic_segment_prefill")
     return out
 
 

@@ -266,6 +266,12 @@ int check_chains(int64_t pool_size, int32_t n_req, const int64_t* off, const int
   return PIC_OK;
 }
 
+bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uintptr_t(b_bytes) && y < x + uintptr_t(a_bytes);
+}
+
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // every non-null device pointer must be 16-byte aligned
@@ -374,6 +380,29 @@ size_t pic_staging_bytes(void) { return staging().held(); }
 
 /* ------------------------------------------------------------------ build */
 
+// the segment plan (offsets and longest-first order) into the arguments
+// (small) or the workspace (copied)
+static int enqueue_build_plan(const int64_t* seg_offsets, int32_t n_seg, void* workspace,
+                              hipStream_t s, pic::BuildArgs& a) {
+  const std::vector<int32_t> order = build_order(seg_offsets, n_seg);
+  if (n_seg <= pic::kInlineSeg) {
+    std::copy(seg_offsets, seg_offsets + n_seg + 1, a.inl_off);
+    std::copy(order.begin(), order.end(), a.inl_order);
+    return PIC_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  int64_t* d_off = reinterpret_cast<int64_t*>(ws);
+  int32_t* d_order =
+      reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
+  const hipError_t e = staging().copy({{d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1)},
+                                       {d_order, order.data(), sizeof(int32_t) * size_t(n_seg)}},
+                                      s);
+  if (e != hipSuccess) return hip_fail(e, "copying the segment plan");
+  a.d_offsets = d_off;
+  a.d_order = d_order;
+  return PIC_OK;
+}
+
 size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int dv,
                                    int64_t n_tokens, int32_t n_seg) {
   (void)form; (void)batch; (void)heads; (void)dk; (void)dv; (void)n_tokens;
@@ -430,25 +459,10 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
                                   workspace, workspace_bytes))
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const std::vector<int32_t> order = build_order(seg_offsets, n_seg);
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
                    k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
+  if (int rc = enqueue_build_plan(seg_offsets, n_seg, workspace, s, a)) return rc;
   hipError_t e = hipSuccess;
-  if (n_seg <= pic::kInlineSeg) {
-    std::copy(seg_offsets, seg_offsets + n_seg + 1, a.inl_off);
-    std::copy(order.begin(), order.end(), a.inl_order);
-  } else {
-    char* ws = static_cast<char*>(workspace);
-    int64_t* d_off = reinterpret_cast<int64_t*>(ws);
-    int32_t* d_order =
-        reinterpret_cast<int32_t*>(ws + align_up(sizeof(int64_t) * (size_t(n_seg) + 1)));
-    e = staging().copy({{d_off, seg_offsets, sizeof(int64_t) * (size_t(n_seg) + 1)},
-                        {d_order, order.data(), sizeof(int32_t) * size_t(n_seg)}},
-                       s);
-    if (e != hipSuccess) return hip_fail(e, "copying the segment plan");
-    a.d_offsets = d_off;
-    a.d_order = d_order;
-  }
   if (form == PIC_FORM_DENSE)
     e = (precision == PIC_PREC_FP16) ? pic::launch_build_dense_h16(a, s)
                                      : pic::launch_build_dense(a, s);
@@ -457,6 +471,60 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
   else
     e = pic::launch_build_scalar_diag(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the build kernel");
+  return ok();
+}
+
+/* ---------------------------------------------------------------- prefill */
+
+int pic_validate_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const int64_t* seg_offsets, int32_t n_seg, const float* log_scale,
+                         const float* T_hat, const float* S0, const void* O_out,
+                         const void* workspace, size_t workspace_bytes) {
+  if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
+  if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
+  if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
+  if (mul_sizes({batch, n_tokens, heads, std::max(dk, dv)}) < 0 ||
+      mul_sizes({n_seg, batch, heads, dk, std::max(dk, dv)}) < 0)
+    return fail(PIC_ERR_DIMS, "sizes overflow 64-bit indexing");
+  if (!seg_offsets) return fail(PIC_ERR_NULL, "seg_offsets is NULL");
+  if (n_tokens > 0 && (!q || !k || !v || !alpha))
+    return fail(PIC_ERR_NULL, "q, k, v and alpha are required");
+  if (n_tokens > 0 && !O_out) return fail(PIC_ERR_NULL, "O_out is required");
+  if (!log_scale || !S0) return fail(PIC_ERR_NULL, "log_scale and S0 outputs are required");
+  if (int rc = check_seg_offsets(seg_offsets, n_seg, n_tokens)) return rc;
+  if (int rc = check_align({q, k, v, alpha, beta, log_scale, T_hat, S0, O_out, workspace}))
+    return rc;
+  const int64_t o_b = int64_t(batch) * n_tokens * heads * dv * 2;
+  const int64_t qk_b = int64_t(batch) * n_tokens * heads * dk * 2;
+  const int64_t g_b = int64_t(batch) * n_tokens * heads * 4;
+  if (overlap(O_out, o_b, q, qk_b) || overlap(O_out, o_b, k, qk_b) || overlap(O_out, o_b, v, o_b) ||
+      overlap(O_out, o_b, alpha, g_b) || overlap(O_out, o_b, beta, g_b))
+    return fail(PIC_ERR_UNSUPPORTED, "O_out overlaps an input");
+  const size_t need = build_ws_bytes(n_seg);
+  if (!workspace || workspace_bytes < need)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  return ok();
+}
+
+int pic_segment_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, const void* q,
+                        const void* k, const void* v, const float* alpha, const float* beta,
+                        const int64_t* seg_offsets, int32_t n_seg, float* log_scale,
+                        float* T_hat, float* S0, void* O_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_prefill(batch, heads, dk, dv, n_tokens, q, k, v, alpha, beta,
+                                    seg_offsets, n_seg, log_scale, T_hat, S0, O_out, workspace,
+                                    workspace_bytes))
+    return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pic::BuildArgs a{PIC_FORM_DENSE, true, batch, heads, dk, dv, n_tokens, n_seg,
+                   k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
+  a.q = q;
+  a.O = O_out;
+  if (int rc = enqueue_build_plan(seg_offsets, n_seg, workspace, s, a)) return rc;
+  const hipError_t e = pic::launch_dense_prefill(a, T_hat != nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the prefill kernel");
   return ok();
 }
 
@@ -767,11 +835,6 @@ static size_t rerotate_ws_bytes(int32_t n) {
 
 size_t pic_rerotate_workspace(int32_t n) { return rerotate_ws_bytes(n); }
 
-static bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
-  if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + uintptr_t(b_bytes) && y < x + uintptr_t(a_bytes);
-}
 
 int pic_validate_rerotate(int form, int batch, int heads, int dk, int dv, int64_t pool_size,
                           const float* pool_log_scale, const float* pool_T_hat,

@@ -36,6 +36,8 @@ struct BuildArgs {
   float* S0;
   int64_t inl_off[kInlineSeg + 1];  // the offsets and order when n_seg <= kInlineSeg
   int32_t inl_order[kInlineSeg];
+  const void* q = nullptr;    // prefill with outputs only: queries
+  void* O = nullptr;          // prefill with outputs only: outputs [batch][n_tokens][heads][dv]
 };
 
 // a plan table entry in device memory, read as global memory: a pointer that
@@ -167,6 +169,9 @@ hipError_t launch_build_dense(const BuildArgs& a, hipStream_t s);
 hipError_t launch_build_dense_ws(const BuildArgs& a, hipStream_t s);
 // fp16 operand precision (bf16 inputs, any dk, dv <= 128)
 hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s);
+// prefill with per-token outputs (dense form, bf16 q/k/v, fp16 operands),
+// That tracked when track_T
+hipError_t launch_dense_prefill(const BuildArgs& a, bool track_T, hipStream_t s);
 // KDA form: token by token in fp32 on the vector units
 hipError_t launch_build_kda(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);

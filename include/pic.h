@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 8
+#define PIC_ABI_VERSION 9
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -194,6 +194,49 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
                       const float* alpha, const float* beta, const int64_t* seg_offsets,
                       int32_t n_seg, float* log_scale, float* T_hat, float* S0,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Prefill with outputs: the independent prefill of every segment, in which
+ * the pair is built, with the per-token outputs of the linear layer.
+ *   [remio.ai HYPIC article (Japanese), section on how HYPIC composes
+ *    linear-attention states: the pair is built at a segment's first
+ *    prefill, a small add-on to it; xix.ai HYPIC article, paragraph on linear
+ *    layers.]
+ * Every segment starts from the zero state; after token t's update
+ * S_t = T_t S_(t-1) + beta_t k_t v_t^T its output is o_t = S_t^T q_t (the
+ * readout of the state that includes the token; no scale: a model's 1/sqrt(d)
+ * belongs to q).  Besides O the call writes the segment's pair exactly as
+ * pic_segment_build does: log_scale and S0 always, T_hat when given (That
+ * tracked alongside the prefill; T_hat = NULL leaves it out, which is the
+ * plain prefill).
+ * Provided for the dense form (PIC_FORM_DENSE) with bf16 q, k, v at fp16
+ * operand precision (the arithmetic and preconditions of PIC_PREC_FP16).
+ *
+ * q, k        device bf16 [batch][n_tokens][heads][dk]
+ * v           device bf16 [batch][n_tokens][heads][dv]
+ * alpha       device fp32 [batch][n_tokens][heads] in (0, 1]
+ * beta        device fp32 [batch][n_tokens][heads], or NULL (= 1)
+ * seg_offsets HOST int64[n_seg+1], as for pic_segment_build
+ * log_scale   device fp32 out [n_seg][batch][heads]
+ * T_hat       device fp32 out [n_seg][batch][heads][dk][dk], or NULL
+ * S0          device fp32 out [n_seg][batch][heads][dk][dv]
+ * O_out       device bf16 out [batch][n_tokens][heads][dv] (rounded to
+ *             nearest even from fp32); must not overlap the inputs
+ * workspace   device scratch of at least pic_segment_build_workspace() bytes
+ * Errors as for pic_segment_build; PIC_ERR_NULL when q or O_out is NULL with
+ * tokens present.
+ * -------------------------------------------------------------------- */
+int pic_validate_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         const int64_t* seg_offsets, int32_t n_seg, const float* log_scale,
+                         const float* T_hat, const float* S0, const void* O_out,
+                         const void* workspace, size_t workspace_bytes);
+
+int pic_segment_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, const void* q,
+                        const void* k, const void* v, const float* alpha, const float* beta,
+                        const int64_t* seg_offsets, int32_t n_seg, float* log_scale,
+                        float* T_hat, float* S0, void* O_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Compose: fold chains of cached pairs into running states.

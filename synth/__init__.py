@@ -310,12 +310,15 @@ def layer_inputs(w: Workload, layers=None, seg_ids=None, want_q: bool = False):
 # --------------------------------------------------------------------------
 
 
-def torch_layer_inputs(w: Workload, layer: int, device, seed_offset: int = 0):
+def torch_layer_inputs(w: Workload, layer: int, device, seed_offset: int = 0,
+                       want_q: bool = False):
     """Draw one layer's inputs directly on a device with torch's generator.
 
     Same distributions and layout as ``layer_inputs`` (different random
     stream).  Returns torch tensors k/v (bf16 or fp32), alpha, beta (fp32 or
-    None) for all segments of the layer concatenated along tokens."""
+    None) for all segments of the layer concatenated along tokens, and with
+    ``want_q`` queries q ~ N(0, 1/dk) from a stream of their own (the other
+    draws do not change)."""
     import torch
 
     g = torch.Generator(device=device)
@@ -343,7 +346,13 @@ def torch_layer_inputs(w: Workload, layer: int, device, seed_offset: int = 0):
     if w.beta[0] == "uniform":
         beta = torch.rand((N, H), generator=g, device=device, dtype=torch.float32)
         beta = beta * (w.beta[2] - w.beta[1]) + w.beta[1]
-    return {"k": k, "v": v, "alpha": alpha, "beta": beta}
+    out = {"k": k, "v": v, "alpha": alpha, "beta": beta}
+    if want_q:
+        gq = torch.Generator(device=device)
+        gq.manual_seed(int(w.seed) * 1000003 + int(layer) * 7919 + int(seed_offset) + 104729)
+        out["q"] = (torch.randn((N, H, dk), generator=gq, device=device, dtype=torch.float32)
+                    * (1.0 / np.sqrt(dk))).to(sdt)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 8
+    assert lib.pic_abi_version() == 9
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -120,6 +120,32 @@ def test_validate_build_null_pointers(lib):
         bad[i] = None
         rc = lib.pic_validate_build(*bad)
         assert rc in (ENULL, EWS), (i, rc)
+
+
+def vprefill(lib, B=1, H=2, dk=128, dv=128, N=100, offs=(0, 40, 100), That=True, O=True,
+             ws_bytes=None, q=None, O_ptr=None):
+    off, off_p = offsets(offs)
+    n_seg = len(off) - 1
+    need = lib.pic_segment_build_workspace(DENSE, B, H, dk, dv, N, n_seg)
+    return lib.pic_validate_prefill(B, H, dk, dv, N, q or P(8), P(0), P(1), P(2), P(3), off_p,
+                                    n_seg, P(4), P(5) if That else None, P(6),
+                                    (O_ptr or P(9)) if O else None, P(7),
+                                    need if ws_bytes is None else ws_bytes)
+
+
+def test_validate_prefill(lib):
+    assert vprefill(lib) == OK
+    assert vprefill(lib, That=False) == OK  # That is optional: the plain prefill
+    assert vprefill(lib, dk=16, dv=48, offs=(0, 0, 100)) == OK
+    assert vprefill(lib, O=False) == ENULL
+    assert vprefill(lib, q=None, O=True) == OK
+    assert vprefill(lib, dk=24) == EDIMS
+    assert vprefill(lib, offs=(0, 40, 99)) == EOFF
+    assert vprefill(lib, ws_bytes=8, offs=tuple(range(0, 101, 2))) == EWS
+    assert vprefill(lib, O_ptr=ctypes.c_void_p(A + 9 * 4096 + 2)) == EALIGN
+    # outputs overlapping an input are refused (k lies at A + 4096)
+    assert vprefill(lib, O_ptr=ctypes.c_void_p(A + 4096)) == EUNSUP
+    assert lib.pic_last_error().decode() != ""
 
 
 def vcompose(lib, form=DENSE, B=1, H=2, dk=128, dv=128, pool=5, off=(0, 3, 3, 5),
