@@ -238,7 +238,9 @@ def bench_scalar_diag(w, args):
     # group's first event: the events then see the launches run back to back
     # on the device, and the per-launch time is the group's time / reps.
     reps = args.reps
-    hold = hold_cycles(torch, stream, reps * 150e-6)
+    # long enough for the host to enqueue the whole group (a few hundred
+    # microseconds per call at worst)
+    hold = hold_cycles(torch, stream, reps * 600e-6)
 
     def group(fn, e0, e1):
         if hold:
@@ -266,7 +268,8 @@ def bench_scalar_diag(w, args):
     for _ in range(args.steps):
         step(recs)
     torch.cuda.synchronize()
-    ms = [np.mean([r[2 * i].elapsed_time(r[2 * i + 1]) for r in recs]) / reps for i in range(3)]
+    ms = [float(np.median([r[2 * i].elapsed_time(r[2 * i + 1]) for r in recs])) / reps
+          for i in range(3)]
     kname = "build_diag_pipe_kernel" if w.form == synth.DIAG else "build_scalar_pipe_kernel"
     gate_bytes = 4 * (dk if w.form == synth.DIAG else 1)
     lam_out = 4 * (dk if w.form == synth.DIAG else 1)
@@ -596,6 +599,93 @@ def bench_reuse(w, args):
     return 0
 
 
+def run_leg(name: str, args, keep):
+    """One workload's bench line from a child process (this file, --workload
+    name), reduced to the keys in `keep`; an error entry if it fails."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-cpu-baseline",
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--precision",
+           args.precision]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        return {"error": f"exit {res.returncode}", "stderr": res.stderr[-400:]}
+    line = [x for x in res.stdout.splitlines() if x.startswith("{")][-1]
+    d = json.loads(line)
+    return {key: d[key] for key in keep if d.get(key) is not None}
+
+
+def prefill_flops_per_token_head(dk: int, dv: int, track_T: bool, sub: int = 32) -> float:
+    """Matrix-core work of the prefill with outputs per token and head, at the
+    kernel's sub-chunks of `sub` tokens: K K^T (2 sub dk), Y = K S (2 dk dv),
+    the W seed and A Y (2 sub dv each), S += K^T P (2 dk dv), the outputs Q S
+    (2 dk dv), K Q^T (2 sub dk) and (K Q^T)^T P (2 sub dv); tracking That adds
+    K That, A Y and That += K^T N (2 dk^2 + 2 sub dk + 2 dk^2)."""
+    f = 2.0 * sub * dk + 2 * dk * dv + 4.0 * sub * dv + 2 * dk * dv + 2 * dk * dv \
+        + 2.0 * sub * dk + 2.0 * sub * dv
+    if track_T:
+        f += 4.0 * dk * dk + 2.0 * sub * dk
+    return f
+
+
+def prefill_leg(w, k, v, alpha, beta, pairs, args):
+    """The prefill with per-token outputs over the whole workload (one call for
+    all segments, layers and heads), without and with That: times, rates and
+    the measured overhead of building the pair in the prefill."""
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+    dev = k.device
+    B, N, H = k.shape[0], k.shape[1], k.shape[2]
+    dk, dv = k.shape[3], v.shape[3]
+    q = torch.empty_like(k)
+    for layer in range(B):
+        q[layer].copy_(synth.torch_layer_queries(w, layer, dev))
+    O = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=dev)
+    offsets = w.offsets()
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for track in (False, True):
+        out = {"log_scale": pairs["log_scale"], "S0": pairs["S0"], "O": O}
+        if track:
+            out["T_hat"] = pairs["T_hat"]
+        run = lambda: pic.pic_segment_prefill(q, k, v, alpha, beta, offsets, track_T=track,
+                                              out=out)
+        for _ in range(max(1, args.warmup)):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        res[track] = float(np.mean(ts))
+    del q, O
+    th = N * B * H
+    nbytes = th * ((2 * dk + dv) * 2 + 8 + dv * 2)  # q, k, v, alpha, beta in; O out (bf16)
+    legs = {}
+    for track, name in ((False, "prefill"), (True, "prefill_with_pair")):
+        t = res[track]
+        pb = w.n_seg * B * H * ((dk * dk if track else 0) + dk * dv + 1) * 4
+        fl = prefill_flops_per_token_head(dk, dv, track) * th
+        bb = nbytes + pb
+        t_hbm, t_mfma = bb / (PEAK_HBM_GBS * 1e9), fl / (PEAK_BF16_TFLOPS * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        legs[name] = {"kernel": "dense_fp16_kernel", "ms": t * 1e3, "tokens_per_s": N / t,
+                      "output_token_heads_per_s": th / t,
+                      "roofline": {"bound": bound,
+                                   "achieved": bb / t / 1e9 if bound == "hbm" else fl / t / 1e12,
+                                   "peak": PEAK_HBM_GBS if bound == "hbm" else PEAK_BF16_TFLOPS,
+                                   "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                                   "frac": (t_hbm if bound == "hbm" else t_mfma) / t,
+                                   "algorithmic_bytes": bb, "algorithmic_flops": fl,
+                                   "mfma_frac": t_mfma / t}}
+    legs["pair_overhead_in_prefill"] = res[True] / res[False] - 1.0
+    return legs
+
+
 def phase_timing(w, args) -> int:
     """Per-role clocks of the dense fp16 build (diagnostic): runs one build of
     `w` (by default 2 of its layers) through ``libpic_timing.so``, whose dense
@@ -686,6 +776,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES (read BYTES, write BYTES) before "
                          "timing, as a reference for hardware byte counters")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="default workload: skip the extra legs (prefill with outputs, scalar, "
+                         "diagonal, reuse)")
     ap.add_argument("--phase-timing", action="store_true",
                     help="diagnostic: per-role clocks per pipeline cycle of the dense fp16 build "
                          "(loads libpic_timing.so; 2 layers unless --layers)")
@@ -718,6 +811,14 @@ def main(argv=None):
         return bench_scalar_diag(w, args)
     if w.extra.get("pool_size"):
         return bench_reuse(w, args)
+    child_legs = {}
+    if not args.no_legs and w.name == "dense_30L_32x4096":
+        # the other workloads, each in a process of its own, run before this
+        # process touches the device (their timings then see no other context)
+        keep = ("value", "unit", "ms", "roofline", "roofline_compose", "roofline_naive_add",
+                "fresh_build", "config")
+        for name in ("scalar_8x2048", "diag_16x4096", "reuse_256x30"):
+            child_legs[name] = run_leg(name, args, keep)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pic.load()
@@ -869,6 +970,13 @@ def main(argv=None):
     if other is not None:
         out["build_other_precision"] = other
     out["hbm_reference"] = hbm_copy_reference(torch, dev)
+    if not args.no_legs and w.name == "dense_30L_32x4096":
+        # the other parts of the path, measured in the same run (each with its
+        # own roofline; not part of `value`)
+        legs = prefill_leg(w, k, v, alpha, beta, pairs, args)
+        legs["pair_overhead_vs_separate_build"] = t_build / (legs["prefill"]["ms"] / 1e3)
+        legs.update(child_legs)
+        out["legs"] = legs
     if not args.no_cpu_baseline:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))

@@ -348,11 +348,20 @@ def torch_layer_inputs(w: Workload, layer: int, device, seed_offset: int = 0,
         beta = beta * (w.beta[2] - w.beta[1]) + w.beta[1]
     out = {"k": k, "v": v, "alpha": alpha, "beta": beta}
     if want_q:
-        gq = torch.Generator(device=device)
-        gq.manual_seed(int(w.seed) * 1000003 + int(layer) * 7919 + int(seed_offset) + 104729)
-        out["q"] = (torch.randn((N, H, dk), generator=gq, device=device, dtype=torch.float32)
-                    * (1.0 / np.sqrt(dk))).to(sdt)
+        out["q"] = torch_layer_queries(w, layer, device, seed_offset)
     return out
+
+
+def torch_layer_queries(w: Workload, layer: int, device, seed_offset: int = 0):
+    """The queries of one layer, q ~ N(0, 1/dk) on the device, from a stream of
+    their own (the ``q`` of ``torch_layer_inputs(..., want_q=True)``)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(w.seed) * 1000003 + int(layer) * 7919 + int(seed_offset) + 104729)
+    sdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    return (torch.randn((w.n_tokens, w.heads, w.dk), generator=g, device=device,
+                        dtype=torch.float32) * (1.0 / np.sqrt(w.dk))).to(sdt)
 
 
 # --------------------------------------------------------------------------
