@@ -1,6 +1,8 @@
 // k_compose.hip -- reuse-time kernels of the segment transform:
 //   * dense compose      S <- e^lambda_p * That_p * S + S0_p along a chain,
-//                        one 128x128x128 split-bf16 MFMA product per step;
+//                        one 128x128x128 split-bf16 MFMA product per step
+//                        (two workgroups per compute unit at full size, one's
+//                        products under the other's loads);
 //   * elementwise compose (scalar / diagonal forms)  S <- e^lambda_p (.) S + S0_p;
 //   * naive add          S <- S + S0_p (the ablation);
 //   * materialize        plain fp32 T_C = e^lambda That.
@@ -85,15 +87,13 @@ __global__ __launch_bounds__(kElemThreads) void compose_elem_kernel(ComposeArgs 
 // Then S <- e^lambda * (That S) + S0_p.  The next step's operator is loaded
 // into registers while the current step's MFMAs run, and S0_p is loaded
 // before them.  Sizes not a multiple of 32 are zero-padded, which leaves the
-// result unchanged.
+// result unchanged.  This kernel serves the padded sizes (dk or dv below
+// DKP); dk = dv = DKP runs compose_dense_full_kernel below.
 // PROD = true forms the chain's operator instead: the "state" is dk x dk,
 // starts at I, and each step is X <- That_p X (no scale, no additive term);
 // the launcher passes dv = dk and S_out = the That output.
-// FULL = true when dk = dv = DKP: no padding, so every operator and S0
-// access is an unconditional load at a loop-invariant offset from the step's
-// (uniform) base address.
 // INL: the chain tables travel in the kernel arguments
-template <int DKP, bool PROD, bool FULL, bool INL>
+template <int DKP, bool PROD, bool INL>
 __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   constexpr int NT = DKP / 32;
   // row stride of the staged operator (bf16): 16-byte aligned rows whose
@@ -105,14 +105,13 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, cl = lane & 31;
-  // with FULL the block is 64 * DKP / 32 threads (one wave per 32 columns)
-  const int nthr = FULL ? 64 * NT : int(blockDim.x);
+  const int nthr = int(blockDim.x);
   const int dk = a.dk, dv = a.dv;
   const int64_t BH = int64_t(a.batch) * a.heads;
   const int64_t unit = blockIdx.x;
   const int64_t r = unit / BH, bh = unit % BH;
   const int n = wave * 32 + cl;  // state column of this lane
-  const bool ncol = FULL || n < dv;
+  const bool ncol = n < dv;
   const int64_t sdd = int64_t(dk) * dv;
   const int per_thr = (F4 + nthr - 1) / nthr;  // <= 16: the launcher gives >= F4 / 16 threads
 
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
       if (PROD)
         S[t][q] = (row == n && row < dk) ? 1.f : 0.f;
       else
-        S[t][q] = (a.S_in && ncol && (FULL || row < dk)) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
+        S[t][q] = (a.S_in && ncol && row < dk) ? a.S_in[unit * sdd + int64_t(row) * dv + n] : 0.f;
     }
   }
 
@@ -133,13 +132,6 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
   float4 pre[16];
   auto load_op = [&](int64_t pu) {
     const float* Tp = a.pool_T_hat + pu * int64_t(dk) * dk;
-    if (FULL) {
-      // item e is float4 e of the row-major operator
-#pragma unroll
-      for (int it = 0; it < 16; ++it)
-        if (it < per_thr) pre[it] = reinterpret_cast<const float4*>(Tp)[threadIdx.x + it * nthr];
-      return;
-    }
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int e = threadIdx.x + it * nthr;
@@ -184,7 +176,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int e = threadIdx.x + it * nthr;
-      if (it < per_thr && (FULL || e < F4)) {
+      if (it < per_thr && e < F4) {
         const int row = (e * 4) / DKP, col = (e * 4) % DKP;
         unsigned h0, l0, h1, l1;
         split2(pre[it].x, pre[it].y, h0, l0);
@@ -210,10 +202,7 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = t * 32 + acc_row(q, g);
-          if (FULL)
-            s0[t][q] = S0p[row * DKP + n];
-          else
-            s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
+          s0[t][q] = (ncol && row < dk) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
       scale = expf(lam);
     }
@@ -251,10 +240,161 @@ __global__ __launch_bounds__(256) void compose_dense_kernel(ComposeArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (FULL || row < dk) a.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
+        if (row < dk) a.S_out[unit * sdd + int64_t(row) * dv + n] = S[t][q];
       }
     }
   }
+}
+
+// Full-size dense compose (dk = dv = DKP), laid out so that two workgroups
+// share a compute unit and one's products run under the other's loads.
+// That_p lands in LDS as plain fp32 straight from memory (16-byte
+// global-to-LDS loads, no registers on the way), its float4 columns XOR
+// swizzled by row so the A-fragment reads are bank-conflict free; each wave
+// splits its A fragments into hi/lo bf16 as it reads them.  S0_p is loaded
+// straight into the accumulators, and e^lambda scales S before the product:
+// S <- That_p (e^lambda S) + S0_p.
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16 i (lds is the same for the whole wave)
+__device__ __forceinline__ void load_lds16(const float4* src, float4* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+template <int DKP>
+struct FullTile {
+  static constexpr int NT = DKP / 32;
+  static constexpr int NTHR = 64 * NT;
+  static constexpr int R4 = DKP / 4;                          // float4 per row
+  static constexpr int SWZ = (DKP == 96) ? 7 : (R4 >= 16 ? 15 : R4 - 1);
+  static constexpr int PER = DKP * DKP / 4 / NTHR;            // float4 per thread
+};
+
+template <int DKP, bool PROD, bool INL>
+__global__ __launch_bounds__(64 * (DKP / 32)) __attribute__((amdgpu_waves_per_eu(2)))
+void compose_dense_full_kernel(ComposeArgs a) {
+  using F = FullTile<DKP>;
+  constexpr int NT = F::NT, R4 = F::R4, SWZ = F::SWZ, PER = F::PER;
+  __shared__ __attribute__((aligned(16))) float4 tl[DKP * R4];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, cl = lane & 31;
+  const int64_t BH = int64_t(a.batch) * a.heads;
+  const int64_t unit = blockIdx.x;
+  const int64_t r = unit / BH, bh = unit % BH;
+  const int n = wave * 32 + cl;  // state column of this lane
+  constexpr int64_t sdd = int64_t(DKP) * DKP;
+
+  f32x16 S[NT], acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = t * 32 + acc_row(q, g);
+      if (PROD)
+        S[t][q] = (row == n) ? 1.f : 0.f;
+      else
+        S[t][q] = a.S_in ? a.S_in[unit * sdd + int64_t(row) * DKP + n] : 0.f;
+    }
+  }
+
+  const int64_t c0 = chain_offset_t<INL>(a, r), c1 = chain_offset_t<INL>(a, r + 1);
+  // chain entries and log scales, 64 at a time, one per lane (see above)
+  int64_t cb = c0;
+  int ent_l = 0;
+  float lam_l = 0.f;
+  auto fetch = [&](int64_t base) {
+    cb = base;
+    const int64_t cc = base + lane;
+    int e = 0;
+    float l = 0.f;
+    if (cc < c1) {
+      e = chain_entry_t<INL>(a, cc);
+      if (!PROD) l = table_at(a.pool_log_scale, int64_t(e) * BH + bh);
+    }
+    ent_l = e;
+    lam_l = l;
+  };
+  auto entry_at = [&](int64_t c) { return __builtin_amdgcn_readlane(ent_l, int(c - cb)); };
+  // That_p into LDS: instruction it of wave w fills slots [(it * NT + w) * 64, +64),
+  // slot s holding row s / R4, float4 column (s % R4) ^ (row & SWZ)
+  auto load_op = [&](int64_t pu) {
+    const float4* Tp = reinterpret_cast<const float4*>(a.pool_T_hat + pu * sdd);
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int s0 = (it * NT + wave) * 64;
+      const int s = s0 + lane;
+      const int row = s / R4, c4 = (s % R4) ^ (row & SWZ);
+      load_lds16(Tp + row * R4 + c4, tl + s0);
+    }
+  };
+  // S0_p straight into the accumulators
+  auto load_s0 = [&](int64_t pu) {
+    const float* S0p = a.pool_S0 + pu * sdd;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (PROD)
+          acc[t][q] = 0.f;
+        else
+          acc[t][q] = S0p[(t * 32 + acc_row(q, g)) * DKP + n];
+      }
+  };
+  if (c0 < c1) {
+    fetch(c0);
+    const int64_t pu = int64_t(entry_at(c0)) * BH + bh;
+    load_op(pu);
+    load_s0(pu);
+  }
+  for (int64_t c = c0; c < c1; ++c) {
+    const float lam = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam_l), int(c - cb)));
+    // this wave's global-to-LDS loads have landed; after the barrier, everyone's
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!PROD) {
+      const float scale = expf(lam);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) S[t][q] *= scale;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2 * NT; ++ks) {
+      const int t = ks >> 1, h = ks & 1;
+      bf16x8 bhi, blo;
+      split_acc_half(S[t], h, bhi, blo);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        // K index j of lane group g is column 16 ks + 8 (j >> 2) + 4 g + (j & 3),
+        // the state row that split_acc_half put at the same place
+        const int row = mt * 32 + cl;
+        const float4 x0 = tl[row * R4 + ((4 * ks + g) ^ (row & SWZ))];
+        const float4 x1 = tl[row * R4 + ((4 * ks + 2 + g) ^ (row & SWZ))];
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        bf16x8 ahi, alo;
+        split8(x, ahi, alo);
+        acc[mt] = mfma32(alo, bhi, acc[mt]);
+        acc[mt] = mfma32(ahi, blo, acc[mt]);
+        acc[mt] = mfma32(ahi, bhi, acc[mt]);
+      }
+    }
+    __syncthreads();  // every wave is done reading That_p
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S[t] = acc[t];
+    if (c + 1 < c1) {
+      if (c + 1 - cb >= 64) fetch(c + 1);
+      const int64_t pu = int64_t(entry_at(c + 1)) * BH + bh;
+      load_op(pu);
+      load_s0(pu);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      a.S_out[unit * sdd + int64_t(t * 32 + acc_row(q, g)) * DKP + n] = S[t][q];
 }
 
 // ---------------------------------------------------------------------------
@@ -320,9 +460,10 @@ hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStrea
 template <int DKP, bool PROD, bool INL>
 void launch_dense_i(const ComposeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   if (a.dk == DKP && a.dv == DKP)
-    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, true, INL>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((compose_dense_full_kernel<DKP, PROD, INL>), grid,
+                       dim3(FullTile<DKP>::NTHR), 0, s, a);
   else
-    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, false, INL>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((compose_dense_kernel<DKP, PROD, INL>), grid, block, 0, s, a);
 }
 template <int DKP, bool PROD>
 void launch_dense_t(const ComposeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
