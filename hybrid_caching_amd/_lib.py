@@ -23,7 +23,7 @@ PREC_FP32, PREC_FP16 = 0, 1
 
 STATUS = {0: "PIC_OK", -1: "PIC_ERR_NULL", -2: "PIC_ERR_DIMS", -3: "PIC_ERR_OFFSETS",
           -4: "PIC_ERR_CHAIN", -5: "PIC_ERR_WORKSPACE", -6: "PIC_ERR_UNSUPPORTED",
-          -7: "PIC_ERR_HIP", -8: "PIC_ERR_ALIGN"}
+          -7: "PIC_ERR_HIP", -8: "PIC_ERR_ALIGN", -9: "PIC_ERR_NONFINITE"}
 
 _i, _i32, _i64, _sz, _p = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -70,6 +70,7 @@ SIGNATURES = {
     "pic_staging_reserve": (_i, []),
     "pic_staging_release": (_i, []),
     "pic_staging_bytes": (_sz, []),
+    "pic_nonfinite_check": (_i, [_p]),
 }
 
 PLAN_BUILD, PLAN_COMPOSE = 0, 1
@@ -145,7 +146,7 @@ def _workspace(nbytes: int, device):
 
 
 def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=None,
-                      precision: int = PREC_FP32):
+                      precision: int = PREC_FP32, check_finite: bool = False):
     """Cached pairs of every (segment, layer, head).
 
     k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
@@ -153,7 +154,9 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
     dense and KDA only), seg_offsets: host ints [n_seg+1].  precision:
     PREC_FP32 or PREC_FP16 (dense with bf16 k/v only).  Returns
     dict(log_scale, T_hat (dense and KDA only), S0) of fp32 device tensors
-    laid out [n_seg, B, H, ...].
+    laid out [n_seg, B, H, ...].  check_finite (PREC_FP16): wait for the
+    stream and raise PicError when an fp16 operand overflowed (see
+    pic_nonfinite_check).
     """
     lib = load()
     B, N, H, dk = k.shape
@@ -180,10 +183,13 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
                                _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
                                _stream(dev))
     _check(rc, "pic_segment_build")
+    if check_finite and precision == PREC_FP16:
+        pic_nonfinite_check(dev)
     return out
 
 
-def pic_segment_prefill(q, k, v, alpha, beta, seg_offsets, *, track_T: bool = True, out=None):
+def pic_segment_prefill(q, k, v, alpha, beta, seg_offsets, *, track_T: bool = True, out=None,
+                        check_finite: bool = False):
     """Independent prefill of every segment with per-token outputs (dense
     form, bf16 q/k/v, fp16 operand precision): o_t = S_t^T q_t from the zero
     state at each segment's start, plus the segment's pair.
@@ -191,7 +197,9 @@ def pic_segment_prefill(q, k, v, alpha, beta, seg_offsets, *, track_T: bool = Tr
     q, k: bf16 [B, N, H, dk]; v: bf16 [B, N, H, dv]; alpha, beta: fp32
     [B, N, H] (beta may be None = 1); seg_offsets: host ints [n_seg+1].
     Returns dict: log_scale [n_seg, B, H], S0 [n_seg, B, H, dk, dv], O bf16
-    [B, N, H, dv] and, with track_T, T_hat [n_seg, B, H, dk, dk]."""
+    [B, N, H, dv] and, with track_T, T_hat [n_seg, B, H, dk, dk].
+    check_finite: wait for the stream and raise PicError when an fp16
+    operand overflowed (see pic_nonfinite_check)."""
     lib = load()
     B, N, H, dk = k.shape
     dv = v.shape[-1]
@@ -223,7 +231,17 @@ def pic_segment_prefill(q, k, v, alpha, beta, seg_offsets, *, track_T: bool = Tr
                                  _ptr(out["S0"]), _ptr(out["O"]), _ptr(ws), ws.numel(),
                                  _stream(dev))
     _check(rc, "pic_segment_prefill")
+    if check_finite:
+        pic_nonfinite_check(dev)
     return out
+
+
+def pic_nonfinite_check(device=None):
+    """Wait for the device's current stream, then raise PicError
+    (PIC_ERR_NONFINITE) if an fp16-operand build or prefill since the last
+    check stored a value that is not finite; clears the device's flag."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    _check(load().pic_nonfinite_check(_stream(dev)), "pic_nonfinite_check")
 
 
 def pic_compose(form: int, pool_log_scale, pool_T_hat, pool_S0, chain_offsets, chain_idx,

@@ -417,6 +417,7 @@ struct Core {
   float* log_scale;
   float* T_hat;
   float* S0;
+  unsigned* nonfinite;
 };
 
 // the workgroup's LDS, at file scope so that every role function addresses
@@ -440,7 +441,8 @@ __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
   x.N = a.n_tokens;
   x.n = int((x.t_end - x.t_begin + C - 1) / C);
   x.unit = (int64_t(seg) * a.batch + x.b) * a.heads + x.h;
-  const Core core{a.heads, a.dk, a.dv, a.k, a.v, a.alpha, a.beta, a.log_scale, a.T_hat, a.S0};
+  const Core core{a.heads, a.dk, a.dv,      a.k,    a.v,  a.alpha,
+                  a.beta,  a.log_scale, a.T_hat, a.S0, a.nonfinite};
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (wid < NT)
     consumer_role(core, x);
@@ -650,6 +652,7 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   // write this wave's columns of S(C|0) (= 2^lg XS, lg the final log2 G of
   // the lazy decay) and That_C
   const int ncol = c * 32 + cl;
+  bool bad = false;
   if (ncol < dv) {
     float* out = out_S + unit * int64_t(dk) * dv;
     const float gs = n >= 1 ? exp2f(gg[8]) : 1.f;
@@ -658,7 +661,9 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) gstore(out + int64_t(row) * dv + ncol, float(XS[t][q]) * gs);
+        const float v = float(XS[t][q]) * gs;
+        bad |= not_finite(v);
+        if (row < dk) gstore(out + int64_t(row) * dv + ncol, v);
       }
   }
   if (ncol < dk) {
@@ -668,9 +673,12 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) gstore(out + int64_t(row) * dk + ncol, ldexpf(XT[t][q], E));
+        const float v = ldexpf(XT[t][q], E);
+        bad |= not_finite(v);
+        if (row < dk) gstore(out + int64_t(row) * dk + ncol, v);
       }
   }
+  report_nonfinite(a.nonfinite, bad);
 }
 
 // ===========================================================================

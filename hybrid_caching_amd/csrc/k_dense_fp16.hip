@@ -291,6 +291,7 @@ struct Core {
   float* T_hat;
   float* S0;
   __bf16* O;
+  unsigned* nonfinite;
 };
 
 #define PIC_DFP_PROLOGUE                                                        \
@@ -388,8 +389,9 @@ __global__ __launch_bounds__(THREADS) void dense_fp16_kernel(BuildArgs a) {
   x.N = a.n_tokens;
   x.n = int((x.t_end - x.t_begin + C - 1) / C);
   x.unit = (int64_t(seg) * a.batch + x.b) * a.heads + x.h;
-  const Core core{a.heads, a.dk, a.dv, a.q, a.k, a.v, a.alpha, a.beta,
-                  a.log_scale, a.T_hat, a.S0, static_cast<__bf16*>(a.O)};
+  const Core core{a.heads, a.dk,      a.dv,    a.q,  a.k,  a.v,
+                  a.alpha, a.beta,    a.log_scale, a.T_hat, a.S0,
+                  static_cast<__bf16*>(a.O), a.nonfinite};
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (wid < 4)
     consumer_role<TRACK_T, OUTPUT>(core, x);
@@ -447,14 +449,18 @@ __global__ __launch_bounds__(THREADS) void dense_fp16_kernel(BuildArgs a) {
 #define PIC_DFP_THAT_STORE(st, p)                                                    \
   do {                                                                               \
     const int ncol_ = (p) * 32 + cl;                                                 \
+    bool bad_ = false;                                                               \
     if (ncol_ < dk) {                                                                \
       float* out_ = rflp(a.T_hat) + unit * int64_t(dk) * dk;                         \
       _Pragma("unroll") for (int t = 0; t < NT; ++t)                                 \
       _Pragma("unroll") for (int q = 0; q < 16; ++q) {                               \
         const int row_ = t * 32 + acc_row(q, g);                                     \
-        if (row_ < dk) gstore(out_ + int64_t(row_) * dk + ncol_, ldexpf((st).XT[t][q], (st).E)); \
+        const float v_ = ldexpf((st).XT[t][q], (st).E);                              \
+        bad_ |= not_finite(v_);                                                      \
+        if (row_ < dk) gstore(out_ + int64_t(row_) * dk + ncol_, v_);                \
       }                                                                              \
     }                                                                                \
+    report_nonfinite(a.nonfinite, bad_);                                             \
   } while (0)
 
 // ===========================================================================
@@ -464,6 +470,7 @@ template <bool TRACK_T, bool OUTPUT>
 __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   PIC_DFP_PROLOGUE;
   const int c = wid;
+  bool obad = false;  // a stored output or state value is not finite
   f32x16 XS[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) XS[t] = zero16();
@@ -566,8 +573,11 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * i + 4 * g + e;
-          if (r < len && ncol < dv)
-            gstore(ob + int64_t(r) * H * dv, static_cast<__bf16>(O[4 * i + e] * scv[e]));
+          if (r < len && ncol < dv) {
+            const float v = O[4 * i + e] * scv[e];
+            obad |= not_finite(v);
+            gstore(ob + int64_t(r) * H * dv, static_cast<__bf16>(v));
+          }
         }
       }
     }
@@ -594,9 +604,12 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = t * 32 + acc_row(q, g);
-        if (row < dk) gstore(out + int64_t(row) * dv + ncol, float(XS[t][q]) * gs);
+        const float v = float(XS[t][q]) * gs;
+        obad |= not_finite(v);
+        if (row < dk) gstore(out + int64_t(row) * dv + ncol, v);
       }
   }
+  report_nonfinite(a.nonfinite, obad);
 }
 
 // ===========================================================================

@@ -321,24 +321,44 @@ int check_seg_offsets(const int64_t* seg_offsets, int32_t n_seg, int64_t n_token
 constexpr size_t kScratchBytes = PIC_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
-std::mutex g_scratch_mu;
+std::mutex g_symbol_mu;
 void* g_scratch_ptr[Staging::kMaxDevices] = {};
 
-hipError_t scratch_address(void** out) {
+// Device address of a file-scope __device__ variable on the current device,
+// looked up once per device (each device holds its own copy) and kept.
+hipError_t symbol_address(const void* symbol, void** cache, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= Staging::kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
+  std::lock_guard<std::mutex> lock(g_symbol_mu);
+  if (!cache[dev]) {
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, symbol);
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
-    g_scratch_ptr[dev] = p;
+    cache[dev] = p;
   }
-  *out = g_scratch_ptr[dev];
+  *out = cache[dev];
   return hipSuccess;
+}
+
+hipError_t scratch_address(void** out) {
+  return symbol_address(HIP_SYMBOL(scratch), g_scratch_ptr, out);
+}
+
+// ------------------------------------------------------- fp16 overflow flag
+// One word per device, set by the fp16-operand kernels (a vector atomic OR)
+// when a value they store is not finite; read and cleared by
+// pic_nonfinite_check.  Zero-initialised with the code object.
+static __device__ __align__(4) unsigned int nonfinite_flag[1];
+void* g_flag_ptr[Staging::kMaxDevices] = {};
+
+hipError_t flag_address(unsigned** out) {
+  void* p = nullptr;
+  const hipError_t e = symbol_address(HIP_SYMBOL(nonfinite_flag), g_flag_ptr, &p);
+  *out = static_cast<unsigned*>(p);
+  return e;
 }
 
 }  // namespace
@@ -358,6 +378,7 @@ const char* pic_status_string(int status) {
     case PIC_ERR_UNSUPPORTED: return "unsupported form, dtype or argument combination";
     case PIC_ERR_HIP: return "HIP runtime error";
     case PIC_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case PIC_ERR_NONFINITE: return "an fp16-operand call stored a value that is not finite";
     default: return "unknown status";
   }
 }
@@ -461,6 +482,10 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
   hipStream_t s = static_cast<hipStream_t>(stream);
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
                    k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
+  if (precision == PIC_PREC_FP16) {
+    const hipError_t fe = flag_address(&a.nonfinite);
+    if (fe != hipSuccess) return hip_fail(fe, "looking up the overflow flag");
+  }
   if (int rc = enqueue_build_plan(seg_offsets, n_seg, workspace, s, a)) return rc;
   hipError_t e = hipSuccess;
   if (form == PIC_FORM_DENSE)
@@ -522,10 +547,31 @@ int pic_segment_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, 
                    k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
   a.q = q;
   a.O = O_out;
+  const hipError_t fe = flag_address(&a.nonfinite);
+  if (fe != hipSuccess) return hip_fail(fe, "looking up the overflow flag");
   if (int rc = enqueue_build_plan(seg_offsets, n_seg, workspace, s, a)) return rc;
   const hipError_t e = pic::launch_dense_prefill(a, T_hat != nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "launching the prefill kernel");
   return ok();
+}
+
+int pic_nonfinite_check(void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned* flag = nullptr;
+  hipError_t e = flag_address(&flag);
+  if (e != hipSuccess) return hip_fail(e, "looking up the overflow flag");
+  unsigned h = 0;
+  e = hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the overflow flag");
+  if (h == 0) return ok();
+  const unsigned zero = 0;
+  e = hipMemcpyAsync(flag, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "clearing the overflow flag");
+  return fail(PIC_ERR_NONFINITE,
+              "an fp16-operand build or prefill stored a value that is not finite (an fp16 "
+              "operand overflowed: inputs outside the PIC_PREC_FP16 preconditions)");
 }
 
 /* ---------------------------------------------------------------- compose */

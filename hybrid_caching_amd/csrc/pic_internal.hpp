@@ -38,7 +38,16 @@ struct BuildArgs {
   int32_t inl_order[kInlineSeg];
   const void* q = nullptr;    // prefill with outputs only: queries
   void* O = nullptr;          // prefill with outputs only: outputs [batch][n_tokens][heads][dv]
+  unsigned* nonfinite = nullptr;  // fp16 kernels: set to 1 when an output is not finite
 };
+
+// The fp16-operand kernels' overflow report: a lane that stored a value that
+// is not finite (an fp16 operand overflowed somewhere upstream: inf or NaN
+// propagate to the outputs) sets the flag word with a vector atomic.
+__device__ __forceinline__ bool not_finite(float x) { return !__builtin_isfinite(x); }
+__device__ __forceinline__ void report_nonfinite(unsigned* flag, bool bad) {
+  if (bad && flag) atomicOr(flag, 1u);
+}
 
 // a plan table entry in device memory, read as global memory: a pointer that
 // may point either into the kernel arguments or into device memory would be

@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 9
+#define PIC_ABI_VERSION 10
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -111,7 +111,10 @@ enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
  *                  are assumed unit-norm (beta |k|^2 <= 2), |v| well below
  *                  6e4 and |S| below about 2e3 (the state is kept at up to
  *                  32x its size between decays).  Typical relative Frobenius error against fp64
- *                  at 4096-8192 tokens: ~2e-3 on That, ~3e-4 on S(C|0). */
+ *                  at 4096-8192 tokens: ~2e-3 on That, ~3e-4 on S(C|0).
+ *                  Inputs outside these bounds can overflow an fp16 operand;
+ *                  the kernels then flag it on the device (the stored values
+ *                  are inf or NaN) and pic_nonfinite_check reports it. */
 enum pic_precision { PIC_PREC_FP32 = 0, PIC_PREC_FP16 = 1 };
 
 enum pic_status {
@@ -123,7 +126,9 @@ enum pic_status {
   PIC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the query result   */
   PIC_ERR_UNSUPPORTED = -6, /* unknown form or dtype                             */
   PIC_ERR_HIP = -7,         /* a HIP call failed after validation                */
-  PIC_ERR_ALIGN = -8        /* a device pointer is not 16-byte aligned           */
+  PIC_ERR_ALIGN = -8,       /* a device pointer is not 16-byte aligned           */
+  PIC_ERR_NONFINITE = -9    /* pic_nonfinite_check: an fp16-operand call stored a
+                               value that is not finite                          */
 };
 
 /* ABI version of the loaded library (PIC_ABI_VERSION at build time). */
@@ -237,6 +242,22 @@ int pic_segment_prefill(int batch, int heads, int dk, int dv, int64_t n_tokens, 
                         const int64_t* seg_offsets, int32_t n_seg, float* log_scale,
                         float* T_hat, float* S0, void* O_out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Overflow report of the fp16-operand calls (pic_segment_build with
+ * PIC_PREC_FP16, pic_segment_prefill).  Those calls are asynchronous and
+ * return PIC_OK once launched; a kernel that stores a value that is not
+ * finite (an fp16 operand overflowed because the inputs are outside the
+ * PIC_PREC_FP16 preconditions) sets a flag word on the device instead.
+ * pic_nonfinite_check waits for `stream` (hipStream_t, NULL = null stream),
+ * reads the current device's flag and clears it: PIC_OK when no such call
+ * since the last check stored a non-finite value, PIC_ERR_NONFINITE when one
+ * did (then the outputs of the calls since the last check are suspect).
+ * The flag is per device and shared by all streams and threads of the
+ * process: check after the work you want covered has been enqueued.
+ * Errors: PIC_ERR_HIP when the copy or the synchronisation fails.
+ * -------------------------------------------------------------------- */
+int pic_nonfinite_check(void* stream);
 
 /* ----------------------------------------------------------------------
  * Compose: fold chains of cached pairs into running states.

@@ -48,8 +48,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 9
-    for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN):
+    assert lib.pic_abi_version() == 10
+    for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN, -9):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.pic_status_string(12345).decode() == "unknown status"

@@ -124,7 +124,11 @@ def test_seam_compose_unequal_dims(dk, dv):
 
 @pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
 def test_seam_windows_empty_equal_compose(form):
-    """With every window empty the call is a plain compose."""
+    """With every window empty the call is a plain compose.  The dense
+    kernels multiply by e^lambda on different sides of the split-bf16 product
+    (each product is exact to about 2^-16 relative), so the dense form agrees
+    to a few 1e-6 rather than to the last bit; each is pinned against the
+    oracle on its own."""
     import hybrid_caching_amd as pic
     import torch
     P, B, H, d = 10, 2, 3, 128
@@ -138,7 +142,7 @@ def test_seam_windows_empty_equal_compose(form):
     want = pic.pic_compose(form, to_dev(lam), to_dev(That), to_dev(S), off, idx, to_dev(S_in))
     torch.cuda.synchronize()
     assert O.shape == (B, 0, H, d)
-    assert max_rel_units(got.cpu().numpy(), want.cpu().numpy()) <= 1e-6
+    assert max_rel_units(got.cpu().numpy(), want.cpu().numpy()) <= (3e-5 if form == DENSE else 1e-6)
 
 
 def test_seam_delta_rule_retrieval():
