@@ -43,11 +43,12 @@ KERNEL_SOURCES = {
     "build_dense_h16_kernel": ["k_build_dense_h16.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_scalar_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_diag_pipe_kernel": ["k_build_sd_pipe.hip", "mfma_util.hpp", "pic_internal.hpp"],
-    "compose_dense_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
+    "compose_dense_full_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_kda_kernel": ["k_build_kda.hip", "pic_internal.hpp"],
     "rerotate_kernel": ["k_rerotate.hip", "pic_internal.hpp"],
     "conv_warmup_kernel": ["k_conv_warmup.hip", "pic_internal.hpp"],
+    "dense_fp16_kernel": ["k_dense_fp16.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
 PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
 
@@ -392,7 +393,7 @@ def bench_kda(w, args):
                      "traffic": measured_traffic("build_kda_kernel", w.name),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
                      "algorithmic_flops": flops},
-        "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
+        "roofline_compose": {"kernel": "compose_dense_full_kernel", "bound": "hbm",
                              "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS,
                              "algorithmic_bytes": cb},
@@ -522,7 +523,7 @@ def bench_reuse(w, args):
     composes = steps_total * B                     # pair applications per layer, all heads
     # every step reads its pair once; the states are written once (no S_in)
     cb = compose_bytes(steps_total, B, H, dk, dv, n_req=0) + R * B * H * dk * dv * 4
-    kname, seam_info = "compose_dense_kernel", None
+    kname, seam_info = "compose_dense_full_kernel", None
     if seam_w:
         # each seam token reads q, k, v (bf16), alpha, beta and writes its output
         # (fp32); its update u = S^T k, S <- a S + k c^T, o = S^T q is 7 dk dv flops
@@ -673,6 +674,9 @@ def prefill_leg(w, k, v, alpha, beta, pairs, args):
         bb = nbytes + pb
         t_hbm, t_mfma = bb / (PEAK_HBM_GBS * 1e9), fl / (PEAK_BF16_TFLOPS * 1e12)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        # the two launches are two instantiations of the kernel; the counter
+        # summary keys them by workload name (with "_pair" for That tracked)
+        traffic = measured_traffic("dense_fp16_kernel", w.name + ("_pair" if track else ""))
         legs[name] = {"kernel": "dense_fp16_kernel", "ms": t * 1e3, "tokens_per_s": N / t,
                       "output_token_heads_per_s": th / t,
                       "roofline": {"bound": bound,
@@ -681,7 +685,8 @@ def prefill_leg(w, k, v, alpha, beta, pairs, args):
                                    "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
                                    "frac": (t_hbm if bound == "hbm" else t_mfma) / t,
                                    "algorithmic_bytes": bb, "algorithmic_flops": fl,
-                                   "mfma_frac": t_mfma / t}}
+                                   "mfma_frac": t_mfma / t, "traffic": traffic,
+                                   "traffic_unit": "HBM bytes per launch"}}
     legs["pair_overhead_in_prefill"] = res[True] / res[False] - 1.0
     return legs
 
@@ -779,6 +784,10 @@ def main(argv=None):
     ap.add_argument("--no-legs", action="store_true",
                     help="default workload: skip the extra legs (prefill with outputs, scalar, "
                          "diagonal, reuse)")
+    ap.add_argument("--no-child-legs", action="store_true",
+                    help="default workload: keep the prefill leg (this process) but skip the "
+                         "scalar, diagonal and reuse legs (child processes), e.g. under a "
+                         "profiler")
     ap.add_argument("--phase-timing", action="store_true",
                     help="diagnostic: per-role clocks per pipeline cycle of the dense fp16 build "
                          "(loads libpic_timing.so; 2 layers unless --layers)")
@@ -812,7 +821,7 @@ def main(argv=None):
     if w.extra.get("pool_size"):
         return bench_reuse(w, args)
     child_legs = {}
-    if not args.no_legs and w.name == "dense_30L_32x4096":
+    if not args.no_legs and not args.no_child_legs and w.name == "dense_30L_32x4096":
         # the other workloads, each in a process of its own, run before this
         # process touches the device (their timings then see no other context)
         keep = ("value", "unit", "ms", "roofline", "roofline_compose", "roofline_naive_add",
@@ -952,10 +961,10 @@ def main(argv=None):
                      "traffic": measured_traffic(build_kernel, w.name),
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes": build_bytes(N, B, H, dk, dv, n_seg)},
-        "roofline_compose": {"kernel": "compose_dense_kernel", "bound": "hbm",
+        "roofline_compose": {"kernel": "compose_dense_full_kernel", "bound": "hbm",
                              "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS,
-                             "traffic": measured_traffic("compose_dense_kernel", w.name),
+                             "traffic": measured_traffic("compose_dense_full_kernel", w.name),
                              "algorithmic_bytes": cb},
         "roofline_naive_add": {"bound": "hbm", "achieved": nb / t_naive / 1e9,
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
