@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "compose_dense_full_kernel": ["k_compose.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "compose_seam_kernel": ["k_compose_seam.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "build_kda_kernel": ["k_build_kda.hip", "pic_internal.hpp"],
+    "build_kda_chunk_kernel": ["k_build_kda_chunk.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "rerotate_kernel": ["k_rerotate.hip", "pic_internal.hpp"],
     "conv_warmup_kernel": ["k_conv_warmup.hip", "pic_internal.hpp"],
     "dense_fp16_kernel": ["k_dense_fp16.hip", "mfma_util.hpp", "pic_internal.hpp"],
@@ -309,8 +310,11 @@ def bench_scalar_diag(w, args):
 
 def bench_kda(w, args):
     """Delta rule with per-channel gates (KDA form): build every pair in one
-    call, compose the segments in prompt order, naive add; one JSON line with
-    the build's fp32 vector-ALU roofline."""
+    call, compose the segments in prompt order, naive add; one JSON line.
+    At fp16 operand precision the build runs in chunks of 32 tokens on the
+    matrix cores (roofline against the fp16 MFMA peak); at fp32 token by token
+    on the vector units (fp32 VALU roofline).  The build at the other
+    precision is timed as a secondary figure, outside `value`."""
     import torch
     import hybrid_caching_amd as pic
     import synth
@@ -321,6 +325,7 @@ def bench_kda(w, args):
     B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
     offsets = w.offsets()
     qdt = torch.bfloat16 if w.qkv_bf16 else torch.float32
+    prec = args.prec if (w.qkv_bf16 and dk == 128 and dv == 128) else 0
     k = torch.empty((B, N, H, dk), dtype=qdt, device=dev)
     v = torch.empty((B, N, H, dv), dtype=qdt, device=dev)
     alpha = torch.empty((B, N, H, dk), dtype=torch.float32, device=dev)
@@ -347,7 +352,7 @@ def bench_kda(w, args):
     def step(record=None):
         e = [ev() for _ in range(4)]
         e[0].record(stream)
-        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs)
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs, precision=prec)
         e[1].record(stream)
         pic.pic_compose(w.form, pairs["log_scale"], pairs["T_hat"], pairs["S0"], chain_off,
                         chain_idx, None, out=S_out)
@@ -368,31 +373,47 @@ def bench_kda(w, args):
     t_step = (time.perf_counter() - t0) / args.steps
     t_build, t_comp, t_naive = [float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs])) / 1e3
                                 for i in range(3)]
-    flops = kda_build_flops_per_token_head(dk, dv) * N * B * H
-    achieved_tf = flops / t_build / 1e12
+    if prec:
+        pic.pic_nonfinite_check(dev)  # the timed builds stayed inside fp16's range
     qb = 2 if w.qkv_bf16 else 4
     bb = N * B * H * ((dk + dv) * qb + 4 * dk + 4) + n_seg * B * H * (dk * dk + dk * dv + 1) * 4
     cb = compose_bytes(n_seg, B, H, dk, dv)
     nb = naive_bytes(n_seg, B, H, dk, dv)
+
+    def build_roofline(p, t):
+        if p:
+            flops = dense_build_flops_per_token_head(dk) * N * B * H
+            tf = flops / t / 1e12
+            return {"kernel": "build_kda_chunk_kernel", "bound": "mfma", "achieved": tf,
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                    "traffic": measured_traffic("build_kda_chunk_kernel", w.name),
+                    "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
+                    "algorithmic_flops": flops}
+        flops = kda_build_flops_per_token_head(dk, dv) * N * B * H
+        tf = flops / t / 1e12
+        return {"kernel": "build_kda_kernel", "bound": "alu", "achieved": tf,
+                "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / PEAK_FP32_VALU_TFLOPS,
+                "traffic": measured_traffic("build_kda_kernel", w.name),
+                "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
+                "algorithmic_flops": flops}
+
     out = {
         "metric": "KDA segment build tokens/s + state composes/s (H=32, d=128); "
-                  "% fp32 VALU roofline",
+                  "% of the build's roofline",
         "value": N / t_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32 state and arithmetic, bf16 k/v",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("f16 matrix-core operands, f32 accumulation and state, bf16 k/v" if prec else
+                  "f32 state and arithmetic, bf16 k/v" if w.qkv_bf16 else "f32"),
         "data": "synthetic",
         "config": {"workload": w.name, "form": "kda", "layers": B, "heads": H, "dk": dk,
                    "dv": dv, "segments": n_seg, "segment_tokens": int(w.seg_lens[0]),
-                   "prompt_tokens": N},
+                   "prompt_tokens": N, "build_precision": "fp16" if prec else "fp32"},
         "build_tokens_per_s": N / t_build,
         "composes_per_s": n_seg * B / t_comp,
         "ms": {"build": t_build * 1e3, "compose": t_comp * 1e3, "naive_add": t_naive * 1e3},
-        "roofline": {"kernel": "build_kda_kernel", "bound": "alu", "achieved": achieved_tf,
-                     "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tf / PEAK_FP32_VALU_TFLOPS,
-                     "traffic": measured_traffic("build_kda_kernel", w.name),
-                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": bb,
-                     "algorithmic_flops": flops},
+        "roofline": build_roofline(prec, t_build),
         "roofline_compose": {"kernel": "compose_dense_full_kernel", "bound": "hbm",
                              "achieved": cb / t_comp / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": cb / t_comp / 1e9 / PEAK_HBM_GBS,
@@ -401,6 +422,22 @@ def bench_kda(w, args):
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": nb / t_naive / 1e9 / PEAK_HBM_GBS},
     }
+    if prec and not args.no_fp32_build:
+        # the token-by-token fp32 build of the same inputs, for reference
+        pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs, precision=0)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(2):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, out=pairs, precision=0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        t32 = float(np.mean(ts))
+        out["build_other_precision"] = {"precision": "fp32 (token by token)", "ms": t32 * 1e3,
+                                        "tokens_per_s": N / t32,
+                                        "roofline": build_roofline(0, t32)}
     if not args.no_cpu_baseline:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))
@@ -825,8 +862,8 @@ def main(argv=None):
         # the other workloads, each in a process of its own, run before this
         # process touches the device (their timings then see no other context)
         keep = ("value", "unit", "ms", "roofline", "roofline_compose", "roofline_naive_add",
-                "fresh_build", "config")
-        for name in ("scalar_8x2048", "diag_16x4096", "reuse_256x30"):
+                "fresh_build", "build_other_precision", "config")
+        for name in ("scalar_8x2048", "diag_16x4096", "reuse_256x30", "kda_30L_32x4096"):
             child_legs[name] = run_leg(name, args, keep)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pic_host.cpp", "k_compose.hip", "k_build_dense.hip", "k_build_dense_ws.hip", "k_build_dense_h16.hip", "k_dense_fp16.hip",
            "k_build_scalar_diag.hip", "k_build_sd_pipe.hip", "k_compose_seam.hip",
-           "k_build_kda.hip", "k_rerotate.hip", "k_conv_warmup.hip"]
+           "k_build_kda.hip", "k_build_kda_chunk.hip", "k_rerotate.hip", "k_conv_warmup.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",

@@ -152,7 +152,8 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
     k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
     [B, N, H] (diag, KDA: [B, N, H, dk]), beta: fp32 [B, N, H] or None (= 1;
     dense and KDA only), seg_offsets: host ints [n_seg+1].  precision:
-    PREC_FP32 or PREC_FP16 (dense with bf16 k/v only).  Returns
+    PREC_FP32 or PREC_FP16 (dense with bf16 k/v; KDA with bf16 k/v and
+    dk = dv = 128).  Returns
     dict(log_scale, T_hat (dense and KDA only), S0) of fp32 device tensors
     laid out [n_seg, B, H, ...].  check_finite (PREC_FP16): wait for the
     stream and raise PicError when an fp16 operand overflowed (see

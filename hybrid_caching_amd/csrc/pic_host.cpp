@@ -443,8 +443,12 @@ int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int he
     return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
   if (precision != PIC_PREC_FP32 && precision != PIC_PREC_FP16)
     return fail(PIC_ERR_UNSUPPORTED, "unknown precision %d", precision);
-  if (precision == PIC_PREC_FP16 && (form != PIC_FORM_DENSE || qkv_dtype != PIC_DT_BF16))
-    return fail(PIC_ERR_UNSUPPORTED, "PIC_PREC_FP16 needs the dense form with bf16 k/v");
+  if (precision == PIC_PREC_FP16 &&
+      ((form != PIC_FORM_DENSE && form != PIC_FORM_KDA) || qkv_dtype != PIC_DT_BF16))
+    return fail(PIC_ERR_UNSUPPORTED, "PIC_PREC_FP16 needs the dense or KDA form with bf16 k/v");
+  if (precision == PIC_PREC_FP16 && form == PIC_FORM_KDA && (dk != 128 || dv != 128))
+    return fail(PIC_ERR_UNSUPPORTED, "the KDA form at PIC_PREC_FP16 needs dk = dv = 128 (%d, %d)",
+                dk, dv);
   if (int rc = check_common_dims(batch, heads, dk, dv)) return rc;
   if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
   if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
@@ -492,7 +496,8 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
     e = (precision == PIC_PREC_FP16) ? pic::launch_build_dense_h16(a, s)
                                      : pic::launch_build_dense(a, s);
   else if (form == PIC_FORM_KDA)
-    e = pic::launch_build_kda(a, s);
+    e = (precision == PIC_PREC_FP16) ? pic::launch_build_kda_chunk(a, s)
+                                     : pic::launch_build_kda(a, s);
   else
     e = pic::launch_build_scalar_diag(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the build kernel");

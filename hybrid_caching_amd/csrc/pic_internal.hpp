@@ -183,6 +183,9 @@ hipError_t launch_build_dense_h16(const BuildArgs& a, hipStream_t s);
 hipError_t launch_dense_prefill(const BuildArgs& a, bool track_T, hipStream_t s);
 // KDA form: token by token in fp32 on the vector units
 hipError_t launch_build_kda(const BuildArgs& a, hipStream_t s);
+// KDA form in chunks of 32 tokens on the matrix cores (bf16 k/v, fp16
+// operands, dk = dv = 128)
+hipError_t launch_build_kda_chunk(const BuildArgs& a, hipStream_t s);
 hipError_t launch_compose_dense(const ComposeArgs& a, hipStream_t s);
 hipError_t launch_compose_elementwise(const ComposeArgs& a, bool naive, hipStream_t s);
 hipError_t launch_compose_seams(const SeamArgs& a, hipStream_t s);

@@ -105,7 +105,9 @@ enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
  *                  terms and a product takes up to three bf16 products
  *                  (~2^-16 relative per product); all forms and dtypes.
  *   PIC_PREC_FP16  one fp16 product per operand pair (11 significant bits);
- *                  dense form with bf16 k/v only.  The ungated product That
+ *                  dense form with bf16 k/v, and KDA form with bf16 k/v and
+ *                  dk = dv = 128 (gate range: see pic_segment_build).  The
+ *                  ungated product That
  *                  is kept at a power-of-two column scale internally, so its
  *                  decay along a segment does not leave fp16's range; keys
  *                  are assumed unit-norm (beta |k|^2 <= 2), |v| well below
@@ -166,9 +168,16 @@ size_t pic_staging_bytes(void);
  *
  * form        PIC_FORM_*
  * qkv_dtype   storage type of q, k, v: PIC_DT_BF16 or PIC_DT_F32
- * precision   PIC_PREC_FP32, or PIC_PREC_FP16 (dense form with bf16 k/v only;
- *             any other combination returns PIC_ERR_UNSUPPORTED).  The KDA
- *             build runs token by token in fp32 on the vector units.
+ * precision   PIC_PREC_FP32, or PIC_PREC_FP16 (dense form with bf16 k/v, or
+ *             KDA form with bf16 k/v and dk = dv = 128; any other combination
+ *             returns PIC_ERR_UNSUPPORTED).  The KDA build at PIC_PREC_FP32
+ *             runs token by token in fp32 on the vector units; at
+ *             PIC_PREC_FP16 in chunks of 32 tokens on the matrix cores, whose
+ *             operands hold products of up to 16 consecutive gates of a
+ *             channel, or their inverses, times k: gates whose 16-token
+ *             products in some channel fall below about 2^-16 overflow those
+ *             operands, and the stored pair is then not finite and reported
+ *             by pic_nonfinite_check.
  * batch, heads, dk, dv, n_tokens   sizes (see layouts above)
  * q           may be NULL; never read: the pair does not depend on queries
  * k, v        device, qkv_dtype

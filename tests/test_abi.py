@@ -88,13 +88,16 @@ def test_validate_build_accepts_good_arguments(lib):
     assert vbuild(lib, prec=1, dk=16, dv=48) == OK
     assert vbuild(lib, form=KDA) == OK  # per-channel gates, That required
     assert vbuild(lib, form=KDA, dt=F32, dk=32, dv=96) == OK
+    assert vbuild(lib, form=KDA, prec=1) == OK  # chunked: bf16 k/v, dk = dv = 128
     assert lib.pic_last_error().decode() == ""
 
 
 @pytest.mark.parametrize("kw,code", [
     ({"form": 7}, EUNSUP), ({"dt": 5}, EUNSUP), ({"prec": 2}, EUNSUP), ({"prec": -1}, EUNSUP),
     ({"prec": 1, "dt": F32}, EUNSUP), ({"prec": 1, "form": SCALAR, "That": False}, EUNSUP),
-    ({"prec": 1, "form": DIAG, "That": False}, EUNSUP), ({"prec": 1, "form": KDA}, EUNSUP),
+    ({"prec": 1, "form": DIAG, "That": False}, EUNSUP),
+    ({"prec": 1, "form": KDA, "dk": 64, "dv": 64}, EUNSUP),
+    ({"prec": 1, "form": KDA, "dv": 64}, EUNSUP), ({"prec": 1, "form": KDA, "dt": F32}, EUNSUP),
     ({"form": KDA, "That": False}, ENULL), ({"form": 4}, EUNSUP),
     ({"dk": 8}, EDIMS), ({"dv": 144}, EDIMS), ({"dk": 24}, EDIMS), ({"B": 0}, EDIMS),
     ({"H": 0}, EDIMS),

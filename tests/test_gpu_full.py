@@ -162,10 +162,12 @@ def test_dense_slow_gates_full_length_sampled(precision):
     _dense_full("dense_30L_32x4096_slow", 2, samples, chains, precision)
 
 
-def test_kda_full_workload_sampled():
+@pytest.mark.parametrize("precision", [0, 1])
+def test_kda_full_workload_sampled(precision):
     """Delta rule with per-channel gates at the dense workload's shape (30
-    layers x 32 heads x d=128, 32 x 4096 tokens) in one build call: sampled
-    units and one composed 32-segment chain against the oracle."""
+    layers x 32 heads x d=128, 32 x 4096 tokens) in one build call, token by
+    token in fp32 and in chunks with fp16 operands: sampled units and one
+    composed 32-segment chain against the oracle."""
     def samples(rng, B, H, n_seg):
         fixed = [(0, 0, 0), (B - 1, H - 1, n_seg - 1)]
         return fixed + [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_seg)))]
@@ -173,10 +175,11 @@ def test_kda_full_workload_sampled():
     def chains(rng, B, H):
         return [(B // 2, 11)]
 
-    _dense_full("kda_30L_32x4096", None, samples, chains)
+    _dense_full("kda_30L_32x4096", None, samples, chains, precision)
 
 
-def test_kda_slow_gates_full_length_sampled():
+@pytest.mark.parametrize("precision", [0, 1])
+def test_kda_slow_gates_full_length_sampled(precision):
     """Slow per-channel gates at the full prompt length (2 layers): the
     composed chain carries a sizeable T(C2) S(C1) term."""
     def samples(rng, B, H, n_seg):
@@ -185,7 +188,7 @@ def test_kda_slow_gates_full_length_sampled():
     def chains(rng, B, H):
         return [(0, 2)]
 
-    _dense_full("kda_30L_32x4096_slow", 2, samples, chains)
+    _dense_full("kda_30L_32x4096_slow", 2, samples, chains, precision)
 
 
 @pytest.mark.timeout(400)

@@ -4,9 +4,15 @@ through the C ABI: the build of every (segment, layer, head) pair, compose of
 KDA pairs (against the oracle's compose and the unsplit recurrence), the
 chain's own pair, the plain operator, and the argument checks.
 
-The KDA build computes in fp32 on the vector units from the stored inputs, so
-bf16 inputs are held to the fp32 tolerance as well (both sides read the same
-bf16-exact values).
+The token-by-token KDA build (PIC_PREC_FP32) computes in fp32 on the vector
+units from the stored inputs, so bf16 inputs are held to the fp32 tolerance
+as well (both sides read the same bf16-exact values).  The chunked build
+(PIC_PREC_FP16: bf16 k/v, dk = dv = 128, fp16 matrix-core operands with fp32
+accumulation and state) is held to the bf16-input contract bound, 2e-2
+relative Frobenius error per unit: ragged chunk tails and empty segments,
+long and many segments, slow gates, beta = NULL, shared gates against the
+dense oracle, repeated calls, the overflow report outside its gate range and
+the rejected shapes.
 """
 import numpy as np
 import pytest
@@ -14,8 +20,8 @@ import pytest
 import oracle
 import synth
 from oracle import DENSE, KDA
-from tests.gpu_helpers import (TOL_F32, assert_pair_close, build_both, lam_err, max_rel_units,
-                               report, to_dev)
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, assert_pair_close, build_both, lam_err,
+                               max_rel_units, report, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,6 +137,127 @@ def test_kda_all_segments_empty():
     assert torch.count_nonzero(out["S0"]).item() == 0
     eye = torch.eye(32, device=dev).expand(2, 1, 2, 32, 32)
     assert torch.equal(out["T_hat"], eye)
+
+
+# --------------------------------------------------------------------------
+# chunked build on the matrix cores (PIC_PREC_FP16)
+# --------------------------------------------------------------------------
+
+FP16 = 1
+NONFINITE, UNSUPPORTED = -9, -6
+# lengths 31, 1, 0, 65, 63, 1: a partial chunk, single tokens, an empty
+# segment, two whole chunks and a 1-token tail, a whole chunk and a 31-token tail
+RAGGED32 = [0, 31, 32, 32, 97, 160, 161]
+
+
+def test_kda_fp16_ragged_segments():
+    k, v, a, b = kda_case(2, 3, 128, 128, RAGGED32, seed=1100)
+    gpu, ref = build_both(KDA, k, v, a, b, RAGGED32, True, precision=FP16)
+    assert_pair_close(gpu, ref, KDA, TOL_BF16)
+    # the empty segment: zero state, identity That, lambda 0
+    assert not gpu["S0"][2].any() and not gpu["log_scale"][2].any()
+    assert np.array_equal(gpu["T_hat"][2], np.broadcast_to(np.eye(128, dtype=np.float32),
+                                                           gpu["T_hat"][2].shape))
+
+
+@pytest.mark.parametrize("n", [1024, 4096])
+def test_kda_fp16_long_segments(n):
+    """Whole segments of the workload's length: That decays far below fp16's
+    range and is carried at a power-of-two scale."""
+    offs = [0, n]
+    k, v, a, b = kda_case(1, 2, 128, 128, offs, seed=1200 + n)
+    gpu, ref = build_both(KDA, k, v, a, b, offs, True, precision=FP16)
+    assert_pair_close(gpu, ref, KDA, TOL_BF16)
+
+
+def test_kda_fp16_slow_gates():
+    offs = [0, 1000, 2048]
+    k, v, a, b = kda_case(1, 2, 128, 128, offs, seed=1300, gate=(9.0, 1.0), beta=(0.0, 0.02))
+    gpu, ref = build_both(KDA, k, v, a, b, offs, True, precision=FP16)
+    assert_pair_close(gpu, ref, KDA, TOL_BF16)
+
+
+def test_kda_fp16_beta_null_means_one():
+    offs = [0, 70, 130]
+    k, v, a, _ = kda_case(1, 2, 128, 128, offs, seed=1400, beta=None)
+    ones = np.ones(a.shape[:3], dtype=np.float32)
+    gpu, _ = build_both(KDA, k, v, a, None, offs, True, precision=FP16)
+    ref1 = oracle.build(KDA, k, v, a, ones, offs)
+    assert_pair_close(gpu, ref1, KDA, TOL_BF16)
+
+
+def test_kda_fp16_shared_gates_match_the_dense_oracle():
+    offs = [0, 77, 200]
+    k, v, a, b = kda_case(1, 2, 128, 128, offs, seed=1500)
+    a1 = a[..., 0]
+    a_all = np.ascontiguousarray(np.repeat(a1[..., None], 128, axis=-1))
+    gpu, _ = build_both(KDA, k, v, a_all, b, offs, True, precision=FP16)
+    ref = oracle.build(DENSE, k, v, a1, b, offs)
+    assert_pair_close(gpu, ref, DENSE, TOL_BF16)
+
+
+def test_kda_fp16_many_segments_use_the_workspace_plan():
+    lens = np.random.default_rng(1600).integers(0, 80, size=40)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    k, v, a, b = kda_case(1, 2, 128, 128, offs, seed=1601)
+    gpu, ref = build_both(KDA, k, v, a, b, offs, True, precision=FP16)
+    assert_pair_close(gpu, ref, KDA, TOL_BF16)
+
+
+def test_kda_fp16_repeated_calls_are_bit_identical_and_flag_clear():
+    import hybrid_caching_amd as pic
+    import torch
+    offs = [0, 50, 129]
+    k, v, a, b = kda_case(1, 2, 128, 128, offs, seed=1700)
+    dt = torch.bfloat16
+    args = (to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(b), offs)
+    try:
+        pic.pic_nonfinite_check()
+    except pic.PicError:
+        pass
+    x = pic.pic_segment_build(KDA, *args, precision=FP16, check_finite=True)
+    y = pic.pic_segment_build(KDA, *args, precision=FP16, check_finite=True)
+    torch.cuda.synchronize()
+    for key in x:
+        assert torch.equal(x[key], y[key]), key
+
+
+def test_kda_fp16_fast_gates_leave_the_range_and_are_reported():
+    """Gates near 0.1 in every channel: a 16-token gate product is about
+    1e-16, far outside fp16's range, so the chunked build overflows and its
+    report says so; the fp32 build of the same inputs matches the oracle."""
+    import hybrid_caching_amd as pic
+    import torch
+    offs = [0, 64]
+    rng = np.random.default_rng(1800)
+    k, v, _, b = kda_case(1, 1, 128, 128, offs, seed=1801)
+    a = rng.uniform(0.05, 0.2, size=k.shape).astype(np.float32)
+    try:
+        pic.pic_nonfinite_check()
+    except pic.PicError:
+        pass
+    dt = torch.bfloat16
+    with pytest.raises(pic.PicError) as err:
+        pic.pic_segment_build(KDA, to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(b), offs,
+                              precision=FP16, check_finite=True)
+    assert err.value.code == NONFINITE
+    pic.pic_nonfinite_check()  # cleared by the report
+    gpu, ref = build_both(KDA, k, v, a, b, offs, True)
+    assert_pair_close(gpu, ref, KDA, TOL_F32)
+
+
+@pytest.mark.parametrize("dk,dv,bf16", [(64, 64, True), (128, 64, True), (128, 128, False)])
+def test_kda_fp16_rejects_other_shapes(dk, dv, bf16):
+    import hybrid_caching_amd as pic
+    import torch
+    dt = torch.bfloat16 if bf16 else torch.float32
+    dev = torch.device("cuda:0")
+    k = torch.zeros((1, 8, 1, dk), dtype=dt, device=dev)
+    v = torch.zeros((1, 8, 1, dv), dtype=dt, device=dev)
+    a = torch.ones((1, 8, 1, dk), dtype=torch.float32, device=dev)
+    with pytest.raises(pic.PicError) as err:
+        pic.pic_segment_build(KDA, k, v, a, None, [0, 8], precision=FP16)
+    assert err.value.code == UNSUPPORTED
 
 
 # --------------------------------------------------------------------------
