@@ -382,7 +382,8 @@ def bench_kda(w, args):
 
     def build_roofline(p, t):
         if p:
-            flops = dense_build_flops_per_token_head(dk) * N * B * H
+            # the chunked KDA build works in chunks of 32 tokens
+            flops = dense_build_flops_per_token_head(dk, 32) * N * B * H
             tf = flops / t / 1e12
             return {"kernel": "build_kda_chunk_kernel", "bound": "mfma", "achieved": tf,
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
