@@ -449,6 +449,84 @@ def bench_kda(w, args):
     return 0
 
 
+def bench_split(w, args):
+    """Few-unit launch (one long segment per layer): the build whole and cut
+    into pieces that are built and merged (pic_segment_build split=n with
+    n = suggest_split); one JSON line with both times, the split build's
+    roofline and the two results' relative difference."""
+    import torch
+    import hybrid_caching_amd as pic
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pic.load()
+    pic.pic_staging_reserve()
+    B, H, dk, dv, N, n_seg = w.layers, w.heads, w.dk, w.dv, w.n_tokens, w.n_seg
+    offsets = w.offsets()
+    dense = w.form == synth.DENSE
+    prec = args.prec if dense else 0
+    x = synth.torch_layer_inputs(w, 0, dev)
+    k, v, alpha = x["k"][None].contiguous(), x["v"][None].contiguous(), x["alpha"][None].contiguous()
+    beta = x["beta"][None].contiguous() if x.get("beta") is not None else None
+    n_split = pic.suggest_split(B, H, offsets)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    outs = {}
+
+    def timed(split):
+        out = None
+        for _ in range(args.warmup + 1):
+            out = pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, precision=prec,
+                                        split=split, out=out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            pic.pic_segment_build(w.form, k, v, alpha, beta, offsets, precision=prec,
+                                  split=split, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        outs[split] = out
+        return float(np.median(ts))
+
+    t_whole = timed(1)
+    t_split = timed(n_split)
+    rel = float(torch.linalg.norm(outs[n_split]["S0"] - outs[1]["S0"]) /
+                torch.linalg.norm(outs[1]["S0"]))
+    if dense:
+        flops = dense_build_flops_per_token_head(dk) * N * B * H
+        roof = {"kernel": "build_dense_h16_kernel" if prec else "build_dense_ws_kernel",
+                "bound": "mfma", "achieved": flops / t_split / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": flops / t_split / 1e12 / PEAK_BF16_TFLOPS,
+                "algorithmic_flops": flops}
+    else:
+        nb = build_bytes(N, B, H, dk, dv, n_seg) - n_seg * B * H * dk * dk * 4
+        roof = {"kernel": "build_scalar_pipe_kernel", "bound": "hbm",
+                "achieved": nb / t_split / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": nb / t_split / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": nb}
+    out = {
+        "metric": "segment build tokens/s, few-unit launch: whole vs split into pieces and "
+                  "merged by composition",
+        "value": N / t_split, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_split * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("f32 state, bf16 k/v, fp16 MFMA operands" if prec else
+                  "f32 state, bf16 k/v, split-bf16 MFMA"),
+        "data": "synthetic",
+        "config": {"workload": w.name, "form": synth.FORM_NAMES[w.form], "layers": B,
+                   "heads": H, "dk": dk, "dv": dv, "segments": n_seg, "prompt_tokens": N,
+                   "units": n_seg * B * H, "pieces_per_segment": n_split},
+        "ms": {"whole": t_whole * 1e3, "split": t_split * 1e3},
+        "speedup": t_whole / t_split,
+        "split_vs_whole_rel_diff_S0": rel,
+        "roofline": roof,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def _group_segments(lens, max_tokens):
     """Consecutive runs of segments holding at most max_tokens tokens each."""
     groups, cur, tot = [], [], 0
@@ -852,6 +930,8 @@ def main(argv=None):
         return phase_timing(w, args)
     if args.layers:
         w = synth.scaled(w, layers=args.layers, name=w.name)
+    if w.extra.get("split_demo"):
+        return bench_split(w, args)
     if w.form == synth.KDA:
         return bench_kda(w, args)
     if w.form != synth.DENSE:
@@ -863,8 +943,9 @@ def main(argv=None):
         # the other workloads, each in a process of its own, run before this
         # process touches the device (their timings then see no other context)
         keep = ("value", "unit", "ms", "roofline", "roofline_compose", "roofline_naive_add",
-                "fresh_build", "build_other_precision", "config")
-        for name in ("scalar_8x2048", "diag_16x4096", "reuse_256x30", "kda_30L_32x4096"):
+                "fresh_build", "build_other_precision", "speedup", "config")
+        for name in ("scalar_8x2048", "diag_16x4096", "reuse_256x30", "kda_30L_32x4096",
+                     "few_dense_1x65536"):
             child_legs[name] = run_leg(name, args, keep)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -37,6 +37,10 @@ SIGNATURES = {
                                 _p, _p, _p, _sz]),
     "pic_segment_build": (_i, [_i, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p,
                                _p, _p, _p, _sz, _p]),
+    "pic_segment_build_split_workspace": (_sz, [_i, _i, _i, _i, _i, _i64, _i32, _i32]),
+    "pic_split_plan": (_i, [_i32, _p, _i64, _i32, _p, _i64, _p, _p]),
+    "pic_segment_build_split": (_i, [_i, _i, _i, _i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p,
+                                     _i32, _i32, _p, _p, _p, _p, _sz, _p]),
     "pic_validate_prefill": (_i, [_i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p,
                                   _p, _p, _sz]),
     "pic_segment_prefill": (_i, [_i, _i, _i, _i, _i64, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p,
@@ -145,8 +149,23 @@ def _workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def suggest_split(batch: int, heads: int, seg_offsets, units_wanted: int = 512,
+                  min_piece_tokens: int = 1024) -> int:
+    """Pieces per segment for pic_segment_build(split=...): 1 when the launch
+    already has units_wanted (segment, layer, head) units, else enough pieces
+    to reach it, none shorter than min_piece_tokens (of the longest segment)."""
+    off = [int(x) for x in seg_offsets]
+    n_seg = len(off) - 1
+    units = n_seg * batch * heads
+    if units >= units_wanted or n_seg == 0:
+        return 1
+    longest = max(off[i + 1] - off[i] for i in range(n_seg))
+    want = -(-units_wanted // units)
+    return max(1, min(want, longest // min_piece_tokens))
+
+
 def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=None,
-                      precision: int = PREC_FP32, check_finite: bool = False):
+                      precision: int = PREC_FP32, check_finite: bool = False, split: int = 1):
     """Cached pairs of every (segment, layer, head).
 
     k: [B, N, H, dk], v: [B, N, H, dv] (both bf16 or both fp32), alpha: fp32
@@ -157,7 +176,9 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
     dict(log_scale, T_hat (dense and KDA only), S0) of fp32 device tensors
     laid out [n_seg, B, H, ...].  check_finite (PREC_FP16): wait for the
     stream and raise PicError when an fp16 operand overflowed (see
-    pic_nonfinite_check).
+    pic_nonfinite_check).  split > 1: every segment is cut into up to `split`
+    pieces of whole 64-token chunks whose pairs are built and merged in order
+    (pic_segment_build_split; see suggest_split).
     """
     lib = load()
     B, N, H, dk = k.shape
@@ -177,13 +198,22 @@ def pic_segment_build(form: int, k, v, alpha, beta, seg_offsets, q=None, *, out=
                "S0": torch.empty((n_seg, B, H, dk, dv), dtype=torch.float32, device=dev)}
         if form in _HAS_T_HAT:
             out["T_hat"] = torch.empty((n_seg, B, H, dk, dk), dtype=torch.float32, device=dev)
-    ws_n = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
-    ws = _workspace(ws_n, dev)
-    rc = lib.pic_segment_build(form, dt, precision, B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                               _ptr(beta), offs_p, n_seg, _ptr(out["log_scale"]),
-                               _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
-                               _stream(dev))
-    _check(rc, "pic_segment_build")
+    if split > 1:
+        ws_n = lib.pic_segment_build_split_workspace(form, B, H, dk, dv, N, n_seg, int(split))
+        ws = _workspace(ws_n, dev)
+        rc = lib.pic_segment_build_split(form, dt, precision, B, H, dk, dv, N, _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(alpha), _ptr(beta), offs_p, n_seg,
+                                         int(split), _ptr(out["log_scale"]), _ptr(out.get("T_hat")),
+                                         _ptr(out["S0"]), _ptr(ws), ws.numel(), _stream(dev))
+        _check(rc, "pic_segment_build_split")
+    else:
+        ws_n = lib.pic_segment_build_workspace(form, B, H, dk, dv, N, n_seg)
+        ws = _workspace(ws_n, dev)
+        rc = lib.pic_segment_build(form, dt, precision, B, H, dk, dv, N, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(alpha), _ptr(beta), offs_p, n_seg, _ptr(out["log_scale"]),
+                                   _ptr(out.get("T_hat")), _ptr(out["S0"]), _ptr(ws), ws.numel(),
+                                   _stream(dev))
+        _check(rc, "pic_segment_build")
     if check_finite and precision == PREC_FP16:
         pic_nonfinite_check(dev)
     return out
@@ -480,6 +510,23 @@ def pic_materialize_T(form: int, log_scale, T_hat=None, dk: int | None = None):
                                _stream(log_scale.device))
     _check(rc, "pic_materialize_T")
     return out
+
+
+def pic_split_plan(seg_offsets, n_split: int):
+    """The pieces of the split build (pure host code): (piece_offsets [P+1],
+    seg_pieces [n_seg+1]) as int64 numpy arrays."""
+    lib = load()
+    off, off_p = _host_i64(seg_offsets)
+    n_seg = len(off) - 1
+    n_p = ctypes.c_int64(0)
+    seg_p = np.zeros(n_seg + 1, dtype=np.int64)
+    cap = n_seg * max(int(n_split), 1) + 1
+    pieces = np.zeros(cap, dtype=np.int64)
+    rc = lib.pic_split_plan(n_seg, off_p, int(off[-1]) if n_seg >= 0 else 0, int(n_split),
+                            pieces.ctypes.data_as(ctypes.c_void_p), cap,
+                            seg_p.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_p))
+    _check(rc, "pic_split_plan")
+    return pieces[:n_p.value + 1], seg_p
 
 
 def pic_plan_dump(kind: int, offsets, chain_idx=None, limit: int = 0):

@@ -430,11 +430,16 @@ size_t pic_segment_build_workspace(int form, int batch, int heads, int dk, int d
   return build_ws_bytes(n_seg);
 }
 
-int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
-                       int64_t n_tokens, const void* q, const void* k, const void* v,
-                       const float* alpha, const float* beta, const int64_t* seg_offsets,
-                       int32_t n_seg, const float* log_scale, const float* T_hat,
-                       const float* S0, const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+// checks of a build's arguments; the workspace must hold `need` bytes
+// (need = SIZE_MAX: not checked here)
+static int validate_build_args(int form, int qkv_dtype, int precision, int batch, int heads,
+                               int dk, int dv, int64_t n_tokens, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta,
+                               const int64_t* seg_offsets, int32_t n_seg, const float* log_scale,
+                               const float* T_hat, const float* S0, const void* workspace,
+                               size_t workspace_bytes, size_t need) {
   (void)q;  // never read: the pair does not depend on queries
   (void)beta;
   if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
@@ -467,23 +472,20 @@ int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int he
     return fail(PIC_ERR_UNSUPPORTED, "T_hat must be NULL for scalar and diagonal forms");
   if (int rc = check_seg_offsets(seg_offsets, n_seg, n_tokens)) return rc;
   if (int rc = check_align({k, v, alpha, beta, log_scale, T_hat, S0, workspace})) return rc;
-  const size_t need = build_ws_bytes(n_seg);
+  if (need == SIZE_MAX) return ok();
   if (!workspace || workspace_bytes < need)
     return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : size_t(0));
   return ok();
 }
 
-int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
-                      int64_t n_tokens, const void* q, const void* k, const void* v,
-                      const float* alpha, const float* beta, const int64_t* seg_offsets,
-                      int32_t n_seg, float* log_scale, float* T_hat, float* S0,
-                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = pic_validate_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q, k, v,
-                                  alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0,
-                                  workspace, workspace_bytes))
-    return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// the build of validated arguments: plan, then the kernel of the form and
+// precision
+static int enqueue_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk,
+                         int dv, int64_t n_tokens, const void* k, const void* v,
+                         const float* alpha, const float* beta, const int64_t* seg_offsets,
+                         int32_t n_seg, float* log_scale, float* T_hat, float* S0,
+                         void* workspace, hipStream_t s) {
   pic::BuildArgs a{form, qkv_dtype == PIC_DT_BF16, batch, heads, dk, dv, n_tokens, n_seg,
                    k, v, alpha, beta, nullptr, nullptr, log_scale, T_hat, S0, {}, {}};
   if (precision == PIC_PREC_FP16) {
@@ -501,6 +503,81 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
   else
     e = pic::launch_build_scalar_diag(a, s);
   if (e != hipSuccess) return hip_fail(e, "launching the build kernel");
+  return PIC_OK;
+}
+
+// pieces of every segment for the split build: whole 64-token chunks, as
+// equal as they allow; chain_off[s] .. chain_off[s+1] are segment s's pieces
+static std::vector<int64_t> split_pieces(const int64_t* off, int32_t n_seg, int32_t n_split,
+                                         std::vector<int64_t>& chain_off) {
+  constexpr int64_t kChunk = 64;
+  std::vector<int64_t> sub(1, 0);
+  chain_off.assign(1, 0);
+  for (int32_t i = 0; i < n_seg; ++i) {
+    const int64_t len = off[i + 1] - off[i];
+    const int64_t chunks = (len + kChunk - 1) / kChunk;
+    const int64_t p = std::min<int64_t>(n_split, std::max<int64_t>(chunks, 1));
+    const int64_t q = chunks / p, r = chunks % p;
+    int64_t at = off[i];
+    for (int64_t j = 0; j < p; ++j) {
+      at = (j == p - 1) ? off[i + 1] : at + (q + (j < r ? 1 : 0)) * kChunk;
+      sub.push_back(at);
+    }
+    chain_off.push_back(chain_off.back() + p);
+  }
+  return sub;
+}
+
+// workspace of the split build for P pieces: their pairs, then the build plan,
+// then the merge's chain tables
+struct SplitLayout {
+  size_t lam = 0, T = 0, S = 0, plan = 0, chains = 0, total = 0;
+};
+static SplitLayout split_layout(int form, int batch, int heads, int dk, int dv, int64_t P,
+                                int32_t n_seg) {
+  SplitLayout L;
+  const size_t units = size_t(P) * size_t(batch) * size_t(heads);
+  const size_t per_lam = (form == PIC_FORM_DIAG) ? size_t(dk) : 1;
+  size_t at = 0;
+  L.lam = at;
+  at += align_up(units * per_lam * sizeof(float));
+  L.T = at;
+  if (has_T_hat(form)) at += align_up(units * size_t(dk) * size_t(dk) * sizeof(float));
+  L.S = at;
+  at += align_up(units * size_t(dk) * size_t(dv) * sizeof(float));
+  L.plan = at;
+  at += build_ws_bytes(int32_t(P));
+  L.chains = at;
+  at += compose_ws_bytes(n_seg, P);
+  L.total = at;
+  return L;
+}
+
+extern "C" {
+
+int pic_validate_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
+                       int64_t n_tokens, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, const int64_t* seg_offsets,
+                       int32_t n_seg, const float* log_scale, const float* T_hat,
+                       const float* S0, const void* workspace, size_t workspace_bytes) {
+  return validate_build_args(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q, k, v,
+                             alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0, workspace,
+                             workspace_bytes, n_seg >= 0 ? build_ws_bytes(n_seg) : SIZE_MAX);
+}
+
+int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int heads, int dk, int dv,
+                      int64_t n_tokens, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const int64_t* seg_offsets,
+                      int32_t n_seg, float* log_scale, float* T_hat, float* S0,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = pic_validate_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q, k, v,
+                                  alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0,
+                                  workspace, workspace_bytes))
+    return rc;
+  if (int rc = enqueue_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, k, v,
+                             alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0, workspace,
+                             static_cast<hipStream_t>(stream)))
+    return rc;
   return ok();
 }
 
@@ -692,6 +769,89 @@ int pic_compose(int form, int batch, int heads, int dk, int dv, int64_t pool_siz
   if (T_hat_out) {
     e = pic::launch_chain_T_hat(a, s);
     if (e != hipSuccess) return hip_fail(e, "launching the chain operator kernel");
+  }
+  return ok();
+}
+
+/* ------------------------------------------------------ split build */
+
+int pic_split_plan(int32_t n_seg, const int64_t* seg_offsets, int64_t n_tokens, int32_t n_split,
+                   int64_t* piece_offsets, int64_t piece_capacity, int64_t* seg_pieces,
+                   int64_t* n_pieces) {
+  if (n_seg < 1) return fail(PIC_ERR_DIMS, "n_seg (%d) must be >= 1", n_seg);
+  if (n_split < 1) return fail(PIC_ERR_DIMS, "n_split (%d) must be >= 1", n_split);
+  if (n_tokens < 0) return fail(PIC_ERR_DIMS, "n_tokens must be >= 0");
+  if (!n_pieces || !seg_pieces) return fail(PIC_ERR_NULL, "n_pieces and seg_pieces are required");
+  if (int rc = check_seg_offsets(seg_offsets, n_seg, n_tokens)) return rc;
+  std::vector<int64_t> chain_off;
+  const std::vector<int64_t> sub = split_pieces(seg_offsets, n_seg, n_split, chain_off);
+  *n_pieces = int64_t(sub.size()) - 1;
+  if (piece_capacity < int64_t(sub.size()))
+    return fail(PIC_ERR_WORKSPACE, "%lld piece offsets needed, room for %lld",
+                (long long)sub.size(), (long long)piece_capacity);
+  if (!piece_offsets) return fail(PIC_ERR_NULL, "piece_offsets is NULL");
+  std::copy(sub.begin(), sub.end(), piece_offsets);
+  std::copy(chain_off.begin(), chain_off.end(), seg_pieces);
+  return ok();
+}
+
+size_t pic_segment_build_split_workspace(int form, int batch, int heads, int dk, int dv,
+                                         int64_t n_tokens, int32_t n_seg, int32_t n_split) {
+  if (n_seg < 0 || n_split < 1 || n_tokens < 0 || batch < 1 || heads < 1 || dk < 1 || dv < 1)
+    return 0;
+  // a segment of c chunks gives at most min(n_split, max(c, 1)) pieces, and
+  // sum over segments of max(c, 1) <= n_tokens / 64 + 2 n_seg
+  const int64_t P = std::min<int64_t>(int64_t(n_seg) * n_split, n_tokens / 64 + 2 * int64_t(n_seg));
+  return std::max(split_layout(form, batch, heads, dk, dv, P, n_seg).total,
+                  build_ws_bytes(n_seg));
+}
+
+int pic_segment_build_split(int form, int qkv_dtype, int precision, int batch, int heads, int dk,
+                            int dv, int64_t n_tokens, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const int64_t* seg_offsets,
+                            int32_t n_seg, int32_t n_split, float* log_scale, float* T_hat,
+                            float* S0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_split < 1) return fail(PIC_ERR_DIMS, "n_split (%d) must be >= 1", n_split);
+  if (n_split == 1)
+    return pic_segment_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q, k, v,
+                             alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0, workspace,
+                             workspace_bytes, stream);
+  if (int rc = validate_build_args(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, q,
+                                   k, v, alpha, beta, seg_offsets, n_seg, log_scale, T_hat, S0,
+                                   workspace, workspace_bytes, SIZE_MAX))
+    return rc;
+  std::vector<int64_t> chain_off;
+  const std::vector<int64_t> sub = split_pieces(seg_offsets, n_seg, n_split, chain_off);
+  const int64_t P = int64_t(sub.size()) - 1;
+  if (P > 0x7fffffffLL || mul_sizes({P, batch, heads, dk, std::max(dk, dv)}) < 0)
+    return fail(PIC_ERR_DIMS, "the pieces' sizes overflow 64-bit indexing");
+  const SplitLayout L = split_layout(form, batch, heads, dk, dv, P, n_seg);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(PIC_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : size_t(0));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* p_lam = reinterpret_cast<float*>(ws + L.lam);
+  float* p_T = has_T_hat(form) ? reinterpret_cast<float*>(ws + L.T) : nullptr;
+  float* p_S = reinterpret_cast<float*>(ws + L.S);
+  if (int rc = enqueue_build(form, qkv_dtype, precision, batch, heads, dk, dv, n_tokens, k, v,
+                             alpha, beta, sub.data(), int32_t(P), p_lam, p_T, p_S, ws + L.plan, s))
+    return rc;
+  // merge: segment i's pair is the chain pair of pieces chain_off[i] .. in order
+  std::vector<int32_t> idx(static_cast<size_t>(P));
+  for (int64_t j = 0; j < P; ++j) idx[size_t(j)] = int32_t(j);
+  pic::ComposeArgs a{form,  batch,    heads,   dk,      dv,     P,      p_lam,     p_T,
+                     p_S,   n_seg,    nullptr, nullptr, P,      nullptr, S0,       log_scale,
+                     T_hat, false,    {},      {}};
+  if (int rc = enqueue_chains(n_seg, chain_off.data(), idx.data(), ws + L.chains, s, a)) return rc;
+  hipError_t e = has_T_hat(form) ? pic::launch_compose_dense(a, s)
+                                 : pic::launch_compose_elementwise(a, false, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the merge of the pieces");
+  e = pic::launch_chain_log_scale(a, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the merge of the pieces' log-scales");
+  if (T_hat) {
+    e = pic::launch_chain_T_hat(a, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the merge of the pieces' operators");
   }
   return ok();
 }

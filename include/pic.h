@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define PIC_ABI_VERSION 10
+#define PIC_ABI_VERSION 11
 
 enum pic_form { PIC_FORM_SCALAR = 0, PIC_FORM_DIAG = 1, PIC_FORM_DENSE = 2, PIC_FORM_KDA = 3 };
 enum pic_dtype { PIC_DT_F32 = 0, PIC_DT_BF16 = 1 };
@@ -208,6 +208,50 @@ int pic_segment_build(int form, int qkv_dtype, int precision, int batch, int hea
                       const float* alpha, const float* beta, const int64_t* seg_offsets,
                       int32_t n_seg, float* log_scale, float* T_hat, float* S0,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------
+ * Split build for launches with few (segment, layer, head) units: every
+ * segment is cut into up to n_split pieces of whole 64-token chunks (a
+ * segment of c chunks gives min(n_split, max(c, 1)) pieces as equal as whole
+ * chunks allow), the pieces' pairs are built into the workspace as by
+ * pic_segment_build, and each segment's pair is the chain pair of its pieces
+ * in token order, merged by the compose of pic_compose:
+ *   lambda = sum of the pieces' lambda, That = That_p ... That_1,
+ *   S = the composed state of the pieces from zero.
+ *   [xix.ai HYPIC article, paragraph on linear layers: the pair of C1.C2 is
+ *    S(C1.C2) = T(C2) S(C1) + S(C2), T(C1.C2) = T(C2) T(C1); a segment's pair
+ *    is the composition of its parts' pairs.]
+ * Equal to pic_segment_build's result up to rounding (the merge is exact in
+ * exact arithmetic).  Worth it when n_seg * batch * heads is well below the
+ * number of compute units and the segments are long: the pieces fill the
+ * GPU, and the merge reads and writes each piece's pair once more.
+ *
+ * Arguments as pic_segment_build, plus
+ * n_split     pieces per segment, >= 1 (1: the plain build)
+ * workspace   device scratch of at least pic_segment_build_split_workspace()
+ *             bytes: the pieces' pairs, their plan and the merge's tables
+ * Errors as pic_segment_build; PIC_ERR_DIMS when n_split < 1 or the pieces'
+ * sizes overflow 64-bit indexing.
+ * -------------------------------------------------------------------- */
+size_t pic_segment_build_split_workspace(int form, int batch, int heads, int dk, int dv,
+                                         int64_t n_tokens, int32_t n_seg, int32_t n_split);
+
+/* The pieces pic_segment_build_split cuts (pure host code, no HIP call):
+ * writes *n_pieces = P, piece_offsets[0..P] (the pieces' token offsets, in
+ * segment order) and seg_pieces[0..n_seg] (segment s's pieces are
+ * seg_pieces[s] .. seg_pieces[s+1] - 1).  seg_offsets is checked as in
+ * pic_validate_build against n_tokens; piece_capacity is the number of
+ * entries piece_offsets holds (PIC_ERR_WORKSPACE, with *n_pieces set, when
+ * fewer than P + 1). */
+int pic_split_plan(int32_t n_seg, const int64_t* seg_offsets, int64_t n_tokens, int32_t n_split,
+                   int64_t* piece_offsets, int64_t piece_capacity, int64_t* seg_pieces,
+                   int64_t* n_pieces);
+
+int pic_segment_build_split(int form, int qkv_dtype, int precision, int batch, int heads, int dk,
+                            int dv, int64_t n_tokens, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const int64_t* seg_offsets,
+                            int32_t n_seg, int32_t n_split, float* log_scale, float* T_hat,
+                            float* S0, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------
  * Prefill with outputs: the independent prefill of every segment, in which

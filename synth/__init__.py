@@ -110,6 +110,16 @@ WORKLOADS = {
                                 ("uniform", 0.0, 1.0)),
 }
 
+# Few-unit launches: one long segment of one layer, 32 heads (32 units on a
+# 256-CU part), the case the split build is for
+WORKLOADS["few_dense_1x65536"] = Workload("few_dense_1x65536", DENSE, 1, 32, 128, 128, (65536,),
+                                          107, True, "l2", 1.0, ("uniform", 0.9, 1.0),
+                                          ("uniform", 0.0, 1.0), extra={"split_demo": True})
+WORKLOADS["few_scalar_1x65536"] = Workload("few_scalar_1x65536", SCALAR, 1, 32, 128, 128,
+                                           (65536,), 108, True, "scaled", 1.0 / np.sqrt(128.0),
+                                           ("uniform", 0.95, 1.0), ("one",),
+                                           extra={"split_demo": True})
+
 # Variants with slow gates, so that the T(C2) S(C1) term is a sizeable part of
 # the composed state and composition checks really exercise T (at the base
 # gate values the incoming state decays below fp32 range across a segment).

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pic_abi_version() == 10
+    assert lib.pic_abi_version() == 11
     for code in (OK, ENULL, EDIMS, EOFF, ECHAIN, EWS, EUNSUP, EHIP, EALIGN, -9):
         s = lib.pic_status_string(code).decode()
         assert s and s != "unknown status"
@@ -420,3 +420,75 @@ def test_validate_conv_warmup_rejects(lib, kw, code):
     assert vconv(lib, **kw) == code
     assert lib.pic_last_error().decode() != ""
 
+
+
+# --------------------------------------------------------------------------
+# split build: the pieces, the workspace, the argument checks (host only)
+# --------------------------------------------------------------------------
+
+def test_split_plan_hand_table(lib):
+    """Segments of 0, 1, 64, 65, 200 and 1000 tokens cut into up to 4 pieces
+    of whole 64-token chunks (expected offsets worked out by hand)."""
+    import hybrid_caching_amd as pic
+    offs = [0, 0, 1, 65, 130, 330, 1330]
+    pieces, seg_pieces = pic.pic_split_plan(offs, 4)
+    assert pieces.tolist() == [0,
+                               0,                     # empty segment: one empty piece
+                               1,                     # 1 token: one piece
+                               65,                    # 64 tokens: one piece
+                               129, 130,              # 65 tokens = 2 chunks: 64 + 1
+                               194, 258, 322, 330,    # 200 tokens = 4 chunks: one each
+                               586, 842, 1098, 1330]  # 1000 tokens = 16 chunks: 4 each
+    assert seg_pieces.tolist() == [0, 1, 2, 3, 5, 9, 13]
+
+
+def test_split_plan_one_piece_is_the_segments(lib):
+    import hybrid_caching_amd as pic
+    offs = [0, 5, 300, 300, 4096]
+    pieces, seg_pieces = pic.pic_split_plan(offs, 1)
+    assert pieces.tolist() == offs
+    assert seg_pieces.tolist() == [0, 1, 2, 3, 4]
+
+
+def test_split_plan_errors(lib):
+    n_p = ctypes.c_int64(0)
+    off, off_p = offsets([0, 200, 400])
+    seg = np.zeros(3, dtype=np.int64)
+    pieces = np.zeros(2, dtype=np.int64)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pic_split_plan(2, off_p, 400, 0, P(pieces), 2, P(seg), ctypes.byref(n_p)) == EDIMS
+    assert lib.pic_split_plan(2, off_p, 401, 2, P(pieces), 2, P(seg), ctypes.byref(n_p)) == EOFF
+    assert lib.pic_split_plan(2, off_p, 400, 2, P(pieces), 2, P(seg), ctypes.byref(n_p)) == EWS
+    assert n_p.value == 4  # 200 tokens = 4 chunks: 2 pieces per segment
+
+
+def test_split_workspace_covers_every_plan(lib):
+    """The workspace query bounds the pieces of any segmentation of n_tokens."""
+    import hybrid_caching_amd as pic
+    rng = np.random.default_rng(9)
+    for _ in range(50):
+        n_seg = int(rng.integers(1, 12))
+        lens = rng.integers(0, 700, size=n_seg)
+        offs = np.concatenate([[0], np.cumsum(lens)])
+        n_split = int(rng.integers(2, 9))
+        pieces, _ = pic.pic_split_plan(offs, n_split)
+        P = len(pieces) - 1
+        for form, t_hat in ((DENSE, True), (SCALAR, False), (DIAG, False)):
+            need_lo = P * 1 * 2 * (128 * 128 * (2 if t_hat else 1) + (128 if form == DIAG else 1)) * 4
+            ws = lib.pic_segment_build_split_workspace(form, 1, 2, 128, 128, int(offs[-1]), n_seg,
+                                                       n_split)
+            assert ws >= need_lo
+    assert lib.pic_segment_build_split_workspace(DENSE, 1, 2, 128, 128, 100, 1, 0) == 0
+
+
+def test_split_build_rejects_before_any_device_call(lib):
+    off, off_p = offsets([0, 300, 700])
+    args = lambda n_split, ws_bytes: (DENSE, BF16, 0, 1, 2, 128, 128, 700, None, P(0), P(1), P(2),
+                                      P(3), off_p, 2, n_split, P(4), P(5), P(6), P(7), ws_bytes,
+                                      None)
+    assert lib.pic_segment_build_split(*args(0, 1 << 30)) == EDIMS
+    assert lib.pic_segment_build_split(*args(4, 64)) == EWS
+    bad_off, bad_p = offsets([0, 300, 699])
+    a = list(args(4, 1 << 30))
+    a[13] = bad_p
+    assert lib.pic_segment_build_split(*a) == EOFF
