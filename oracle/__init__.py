@@ -284,16 +284,16 @@ def seam_compose(form, lam, That, S, chain_offsets, chain_idx, seam_offsets, q, 
 
     Pool as in ``compose``.  Chain entry c (over all requests, in order) has
     the seam tokens [seam_offsets[c], seam_offsets[c+1]) of q, k: [B, NS, H, dk],
-    v: [B, NS, H, dv], alpha: [B, NS, H] (diag: [B, NS, H, dk]), beta: [B, NS, H]
-    or None.  Each entry advances the state through its seam tokens (emitting
+    v: [B, NS, H, dv], alpha: [B, NS, H] (diag, KDA: [B, NS, H, dk]), beta:
+    [B, NS, H] or None (dense, KDA).  Each entry advances the state through its seam tokens (emitting
     o_t = S_t^T q_t) and then applies its pair.  Returns (S_out [R, B, H, dk, dv],
     O [B, NS, H, dv]).
     """
     lib = lib or load()
     lam, S = _f64(lam), _f64(S)
-    That = _f64(That) if form == DENSE else None
+    That = _f64(That) if form in (DENSE, KDA) else None
     q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
-    beta = _f64(beta) if (beta is not None and form == DENSE) else None
+    beta = _f64(beta) if (beta is not None and form in (DENSE, KDA)) else None
     P, B, H, dk, dv = S.shape
     NS = k.shape[1]
     off, idx = _chains(chain_offsets, chain_idx)

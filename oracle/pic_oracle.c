@@ -606,6 +606,18 @@ static void seam_token(const seam_ctx *sc, int b, int h, int64_t t, double *S, d
     matmul(dk, dk, dv, Tt, S, tmp);
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) S[i * dv + j] = tmp[i * dv + j] + bt * kt[i] * vt[j];
+  } else if (form == ORACLE_KDA) {
+    /* S <- (I - b k k^T) Diag(a) S + b k v^T: the rows scaled by their gates,
+       then the erase along k and the write */
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[i * dv + j] *= at[i];
+    for (int j = 0; j < dv; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < dk; ++i) s += kt[i] * S[i * dv + j];
+      tmp[j] = s;
+    }
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[i * dv + j] += bt * kt[i] * (vt[j] - tmp[j]);
   } else if (form == ORACLE_DENSE) {
     /* S <- a (S - b k (k^T S)) + b k v^T */
     for (int j = 0; j < dv; ++j) {
@@ -658,8 +670,9 @@ static void seam_unit(void *vctx, int64_t item) {
     const double *lp = c->lam + unit * nlam;
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dk; ++j) {
-        const double ungated = (form == ORACLE_DENSE) ? c->That[unit * dk * dk + i * dk + j]
-                                                      : (double)(i == j);
+        const double ungated = (form == ORACLE_DENSE || form == ORACLE_KDA)
+                                   ? c->That[unit * dk * dk + i * dk + j]
+                                   : (double)(i == j);
         Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;
       }
     matmul(dk, dk, dv, Tp, S, tmp);
@@ -677,9 +690,9 @@ int oracle_seam_compose(int form, int literal, int B, int H, int dk, int dv, int
                         const int64_t *seam_off, int64_t NS, const double *q, const double *k,
                         const double *v, const double *alpha, const double *beta,
                         const double *S_in, double *S_out, double *O, int n_threads) {
-  if (form < 0 || form > 2 || dk <= 0 || dv <= 0 || check_chains(P, n_req, chain_off, chain_idx))
+  if (form < 0 || form > 3 || dk <= 0 || dv <= 0 || check_chains(P, n_req, chain_off, chain_idx))
     return -1;
-  if (form == ORACLE_DENSE && That == NULL) return -1;
+  if ((form == ORACLE_DENSE || form == ORACLE_KDA) && That == NULL) return -1;
   const int64_t total = chain_off[n_req];
   if (seam_off[0] != 0 || seam_off[total] != NS) return -1;
   for (int64_t e = 0; e < total; ++e)

@@ -30,6 +30,18 @@ _SEAM_LOOP = """    for (int64_t t = sc->seam_off[e]; t < sc->seam_off[e + 1]; +
 """
 _SEAM_PAIR_END = "    for (int i = 0; i < dk * dv; ++i) S[i] = tmp[i] + Sp[i];\n  }\n  free(Tt);"
 
+_KDA_SEAM_GATE = """    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[i * dv + j] *= at[i];
+"""
+_KDA_SEAM_READ = """    for (int j = 0; j < dv; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < dk; ++i) s += kt[i] * S[i * dv + j];
+      tmp[j] = s;
+    }
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) S[i * dv + j] += bt * kt[i] * (vt[j] - tmp[j]);
+"""
+
 MUTANTS = [
     ("dense: gate dropped from the state update",
      "S[i * dv + j] = a * (S[i * dv + j] - bt * kt[i] * kS[j]) + bt * kt[i] * vt[j];",
@@ -124,6 +136,14 @@ MUTANTS = [
     ("prefill: output written to the previous token's row",
      "double *ot = c->O + (((int64_t)b * c->N + t) * c->H + h) * dv;",
      "double *ot = c->O + (((int64_t)b * c->N + (t > 0 ? t - 1 : 0)) * c->H + h) * dv;"),
+    ("seam: KDA gates applied to the erase's key instead of the rows",
+     "      for (int j = 0; j < dv; ++j) S[i * dv + j] *= at[i];\n    for (int j = 0; j < dv; ++j) {",
+     "      for (int j = 0; j < dv; ++j) S[i * dv + j] *= 1.0;\n    for (int j = 0; j < dv; ++j) {"),
+    ("seam: KDA erase read from the state before the gates",
+     _KDA_SEAM_GATE + _KDA_SEAM_READ, _KDA_SEAM_READ + _KDA_SEAM_GATE),
+    ("seam: KDA pair applied without its ungated operator",
+     "        const double ungated = (form == ORACLE_DENSE || form == ORACLE_KDA)",
+     "        const double ungated = (form == ORACLE_DENSE)"),
     ("seam: pair gate scale dropped",
      "Tp[i * dk + j] = exp(lp[nlam == 1 ? 0 : i]) * ungated;",
      "Tp[i * dk + j] = ungated;"),
@@ -157,6 +177,10 @@ def _pin_calls():
             lambda f=form: seam_pins.test_seam_empty_windows_equal_compose(f),
             lambda f=form: seam_pins.test_seam_queries_only_reach_outputs(f),
         ]
+    calls += [lambda: seam_pins.test_seam_split_equals_unsplit(oracle.KDA, False, [7, 9, 5],
+                                                               [0, 3, 3]),
+              lambda: seam_pins.test_seam_exact_rational(oracle.KDA, 0),
+              seam_pins.test_seam_kda_with_shared_gates_is_the_dense_seam]
     calls.append(seam_pins.test_seam_delta_rule_retrieval)
     calls += [kda_pins.test_kda_literal_equals_specialised,
               lambda: kda_pins.test_kda_with_shared_gates_is_dense_gdn(False),

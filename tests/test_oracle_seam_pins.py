@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import DENSE, DIAG, SCALAR
+from oracle import DENSE, DIAG, KDA, SCALAR
 from tests.conftest import rel_fro
 
 
@@ -31,8 +31,8 @@ def _inputs(form, B, H, dk, dv, N, seed, alpha_range=(0.6, 1.0)):
     k /= np.linalg.norm(k, axis=-1, keepdims=True)
     q = rng.standard_normal((B, N, H, dk))
     v = rng.standard_normal((B, N, H, dv))
-    alpha = rng.uniform(*alpha_range, size=(B, N, H, dk) if form == DIAG else (B, N, H))
-    beta = rng.uniform(0.0, 1.0, size=(B, N, H)) if form == DENSE else None
+    alpha = rng.uniform(*alpha_range, size=(B, N, H, dk) if form in (DIAG, KDA) else (B, N, H))
+    beta = rng.uniform(0.0, 1.0, size=(B, N, H)) if form in (DENSE, KDA) else None
     return q, k, v, alpha, beta
 
 
@@ -76,7 +76,7 @@ def run_split(form, seg_lens, seam_lens, B=2, H=2, dk=6, dv=5, seed=0, literal=F
                 seam_pos=seam_pos, N=N)
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 @pytest.mark.parametrize("literal", [False, True])
 @pytest.mark.parametrize("seg_lens,seam_lens", [
     ([7, 9, 5], [0, 3, 3]),
@@ -120,6 +120,9 @@ def test_seam_delta_rule_retrieval():
 
 def _frac_T(form, k, a, b):
     d = len(k)
+    if form == KDA:  # (I - b k k^T) Diag(a): column j carries gate a_j
+        return [[(Fraction(int(i == j)) - b * k[i] * k[j]) * a[j] for j in range(d)]
+                for i in range(d)]
     return [[(a[0] if form != DIAG else a[i]) * (Fraction(int(i == j))
              - (b * k[i] * k[j] if form == DENSE else 0)) for j in range(d)] for i in range(d)]
 
@@ -129,7 +132,7 @@ def _fmat(A, B):
             for i in range(len(A))]
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_seam_exact_rational(form, seed):
     """Exact rationals over explicit matrices: per seam token S <- T_t S + b k v^T
@@ -139,14 +142,14 @@ def test_seam_exact_rational(form, seed):
     dk, dv, NS, P = 3, 2, 5, 3
     dy = lambda shape: rng.integers(-8, 9, size=shape) / 8.0
     q, k, v = dy((NS, dk)), dy((NS, dk)), dy((NS, dv))
-    alpha = rng.integers(1, 9, size=(NS, dk if form == DIAG else 1)) / 8.0
+    alpha = rng.integers(1, 9, size=(NS, dk if form in (DIAG, KDA) else 1)) / 8.0
     beta = rng.integers(0, 9, size=NS) / 8.0
     That = dy((P, dk, dk))
     Sp = dy((P, dk, dv))
     S_in = dy((dk, dv))
     chain = [2, 0, 1]
     seam_off = [0, 2, 2, 5]  # entry 1 has no seam window
-    if form != DENSE:  # scalar / diagonal pairs carry That = I
+    if form not in (DENSE, KDA):  # scalar / diagonal pairs carry That = I
         That = np.broadcast_to(np.eye(dk), (P, dk, dk))
     F = lambda a: [[Fraction(x) for x in r] for r in np.atleast_2d(a)]
     S = F(S_in)
@@ -154,7 +157,7 @@ def test_seam_exact_rational(form, seed):
     for e, p in enumerate(chain):
         for t in range(seam_off[e], seam_off[e + 1]):
             kt, vt, qt = F(k[t])[0], F(v[t])[0], F(q[t])[0]
-            bt = Fraction(beta[t]) if form == DENSE else Fraction(1)
+            bt = Fraction(beta[t]) if form in (DENSE, KDA) else Fraction(1)
             TS = _fmat(_frac_T(form, kt, F(alpha[t])[0], bt), S)
             S = [[TS[i][j] + bt * kt[i] * vt[j] for j in range(dv)] for i in range(dk)]
             O.append([sum(qt[i] * S[i][j] for i in range(dk)) for j in range(dv)])
@@ -163,8 +166,8 @@ def test_seam_exact_rational(form, seed):
         S = [[TS[i][j] + Spp[i][j] for j in range(dv)] for i in range(dk)]
     exact_S = np.array([[float(x) for x in r] for r in S])
     exact_O = np.array([[float(x) for x in r] for r in O])
-    a_in = alpha[None, :, None, :] if form == DIAG else alpha[None, :, None, 0]
-    That_in = That[:, None, None] if form == DENSE else None
+    a_in = alpha[None, :, None, :] if form in (DIAG, KDA) else alpha[None, :, None, 0]
+    That_in = That[:, None, None] if form in (DENSE, KDA) else None
     for literal in (False, True):
         S_out, O_got = oracle.seam_compose(
             form, np.zeros((P, 1, 1, dk) if form == DIAG else (P, 1, 1)), That_in,
@@ -175,18 +178,18 @@ def test_seam_exact_rational(form, seed):
         assert np.abs(O_got[0, :, 0] - exact_O).max() <= 1e-13 * max(1.0, np.abs(exact_O).max())
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 def test_seam_empty_windows_equal_compose(form):
     """With every window empty, reuse with seams is plain composition."""
     B, H, dk, dv, P = 2, 2, 5, 4, 4
     rng = np.random.default_rng(11)
     lam = rng.uniform(-2, 0, size=(P, B, H, dk) if form == DIAG else (P, B, H))
-    That = rng.standard_normal((P, B, H, dk, dk)) * 0.3 if form == DENSE else None
+    That = rng.standard_normal((P, B, H, dk, dk)) * 0.3 if form in (DENSE, KDA) else None
     S = rng.standard_normal((P, B, H, dk, dv))
     S_in = rng.standard_normal((2, B, H, dk, dv))
     off, idx = [0, 3, 5], [1, 3, 0, 2, 2]
     z = np.zeros((B, 0, H, dk))
-    a0 = np.zeros((B, 0, H, dk) if form == DIAG else (B, 0, H))
+    a0 = np.zeros((B, 0, H, dk) if form in (DIAG, KDA) else (B, 0, H))
     got, O = oracle.seam_compose(form, lam, That, S, off, idx, [0] * 6, z, z,
                                  np.zeros((B, 0, H, dv)), a0, None, S_in)
     want = oracle.compose(form, lam, That, S, off, idx, S_in)
@@ -194,7 +197,7 @@ def test_seam_empty_windows_equal_compose(form):
     assert O.shape == (B, 0, H, dv)
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 def test_seam_queries_only_reach_outputs(form):
     """q never changes the state, and the outputs are linear in q."""
     r1 = run_split(form, [6, 7, 5], [0, 3, 2], seed=5)
@@ -226,3 +229,27 @@ def test_seam_oracle_rejects_bad_seam_offsets():
         with pytest.raises(ValueError):
             oracle.seam_compose(SCALAR, lam, None, S, [0, 2], [0, 1], bad, x, x,
                                 np.zeros((B, 3, H, dv)), a, None)
+
+
+def test_seam_kda_with_shared_gates_is_the_dense_seam():
+    """Every channel of a token sharing one gate: the KDA seam step is the
+    dense one ((I - b k k^T) a = a (I - b k k^T)), so state and outputs agree."""
+    seg_lens, seam_lens = [7, 9, 5], [0, 3, 3]
+    B, H, dk, dv = 2, 2, 6, 5
+    N = sum(seg_lens)
+    q, k, v, a1, beta = _inputs(DENSE, B, H, dk, dv, N, seed=21)
+    a_all = np.repeat(a1[..., None], dk, axis=-1)
+    seam_pos, rem_off, seam_off, rem_pos = split_prompt(seg_lens, seam_lens)
+    pool_d = oracle.build(DENSE, _take(k, rem_pos), _take(v, rem_pos), _take(a1, rem_pos),
+                          _take(beta, rem_pos), rem_off)
+    pool_k = oracle.build(KDA, _take(k, rem_pos), _take(v, rem_pos), _take(a_all, rem_pos),
+                          _take(beta, rem_pos), rem_off)
+    S_in = np.random.default_rng(22).standard_normal((1, B, H, dk, dv))
+    args = lambda a: (seam_off, _take(q, seam_pos), _take(k, seam_pos), _take(v, seam_pos),
+                      _take(a, seam_pos), _take(beta, seam_pos), S_in)
+    Sd, Od = oracle.seam_compose(DENSE, pool_d["lam"], pool_d["That"], pool_d["S"], [0, 3],
+                                 [0, 1, 2], *args(a1))
+    Sk, Ok = oracle.seam_compose(KDA, pool_k["lam"], pool_k["That"], pool_k["S"], [0, 3],
+                                 [0, 1, 2], *args(a_all))
+    assert rel_fro(Sk, Sd) <= 1e-12
+    assert rel_fro(Ok, Od) <= 1e-12
