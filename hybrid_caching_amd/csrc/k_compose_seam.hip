@@ -1,9 +1,9 @@
 // k_compose_seam.hip -- reuse with seam windows.  Along a chain of cached
 // pairs, each entry first advances the running state through its seam tokens
 // one token at a time, writing o_t = S_t^T q_t after each, and then applies the
-// entry's pair:  S <- e^lambda That S + S0  (dense: split-bf16 matrix-core
-// products, as in the dense compose; scalar / diagonal: one scale per head or
-// per key row).
+// entry's pair:  S <- e^lambda That S + S0  (dense and KDA: split-bf16
+// matrix-core products, as in the dense compose; scalar / diagonal: one scale
+// per head or per key row).
 // [xix.ai HYPIC article (French), paragraph on full-attention layers: the
 //  first w tokens (8 by default) of every inner segment are kept out of the
 //  cache and recomputed on reuse under the full prefix; the linear layers run
@@ -16,6 +16,7 @@
 // column 32w + c, rows 32t + 8i + 4g + {0..3} of tile t.  A seam token is a
 // rank-one update in fp32 on the vector units:
 //   dense     u = S^T k,  S <- a S + k (b (v - a u))^T
+//   KDA       u = S^T (a (.) k),  S <- Diag(a) S + k (b (v - u))^T
 //   scalar    S <- a S + k v^T
 //   diagonal  S <- Diag(a) S + k v^T
 // Dense and scalar forms with bf16 inputs take a window of up to eight tokens
@@ -30,8 +31,8 @@
 // q are exact in bf16) gives every column sum, one product on wave 0 gives the
 // 8x8 products k_s . k_t and k_s . q_t, each lane runs the short recurrence for
 // its column in fp32, and S <- g S0 + K^T C~ is one more product per tile.
-// The diagonal form and fp32 inputs update token by token on the vector
-// units: a lane holds half of each of its column's rows, so the column sums
+// The diagonal and KDA forms and fp32 inputs update token by token on the
+// vector units: a lane holds half of each of its column's rows, so the column sums
 // S^T k and S^T q take a partial sum over its 64 rows and one exchange with
 // lane l ^ 32.  Seam tokens are staged in LDS eight at a time, zero padded to
 // 128 channels.  The
@@ -57,10 +58,13 @@ constexpr int SLDR = SP + 8;   // row stride of the staged operator (bf16)
 // INL: the chain and seam tables travel in the kernel arguments
 template <int FORM, bool BF16, bool FULL, bool INL>
 __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
-  __shared__ __attribute__((aligned(16))) __bf16 th_hi[FORM == kDense ? SP * SLDR : 8];
-  __shared__ __attribute__((aligned(16))) __bf16 th_lo[FORM == kDense ? SP * SLDR : 8];
+  constexpr bool TH = FORM == kDense || FORM == kKda;   // pairs carry That
+  constexpr bool PCG = FORM == kDiag || FORM == kKda;   // a gate per key channel
+  constexpr bool ERASE = FORM == kDense || FORM == kKda;  // beta and the erase
+  __shared__ __attribute__((aligned(16))) __bf16 th_hi[TH ? SP * SLDR : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 th_lo[TH ? SP * SLDR : 8];
   // window path: dense / scalar forms with bf16 inputs
-  constexpr bool WIN = BF16 && FORM != kDiag;
+  constexpr bool WIN = BF16 && (FORM == kDense || FORM == kScalar);
   __shared__ __attribute__((aligned(16))) float sk[WIN ? 1 : STW][SP];
   __shared__ __attribute__((aligned(16))) float sq[WIN ? 1 : STW][SP];
   __shared__ __attribute__((aligned(16))) __bf16 skb[WIN ? STW : 1][SP];   // k rows
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   __shared__ __attribute__((aligned(16))) __bf16 skT[WIN ? SP : 1][STW];   // k columns
   __shared__ __attribute__((aligned(16))) float skk[WIN ? 2 * STW : 1][STW];  // k.k, q.k
   __shared__ __attribute__((aligned(16))) float sv[STW][SP];
-  __shared__ __attribute__((aligned(16))) float sg[STW][FORM == kDiag ? SP : 4];  // gates
+  __shared__ __attribute__((aligned(16))) float sg[STW][PCG ? SP : 4];  // gates
   __shared__ float sb[STW];                                                       // beta
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -129,12 +133,12 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     pk = piece(sa.k, tok * dk + ck);
     pq = piece(sa.q, tok * dk + ck);
     pv = piece(sa.v, tok * dv + cv);
-    if (FORM == kDiag) pa = *reinterpret_cast<const float4*>(sa.alpha + tok * dk + ck);
+    if (PCG) pa = *reinterpret_cast<const float4*>(sa.alpha + tok * dk + ck);
     if (FORM != kDiag) {
       const int64_t ts = t0 + (threadIdx.x & (STW - 1)) < NS ? t0 + (threadIdx.x & (STW - 1)) : NS - 1;
       const int64_t tk = (int64_t(b) * NS + ts) * H + h;
-      pa1 = sa.alpha[tk];
-      if (FORM == kDense && sa.beta) pb1 = sa.beta[tk];
+      if (!PCG) pa1 = sa.alpha[tk];
+      if (ERASE && sa.beta) pb1 = sa.beta[tk];
     }
   };
   auto as4 = [&](const Piece& x) -> float4 {
@@ -159,16 +163,48 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       *reinterpret_cast<float4*>(&sq[rt][rc]) = rc < dk ? as4(pq) : z;
     }
     *reinterpret_cast<float4*>(&sv[rt][rc]) = rc < dv ? as4(pv) : z;
-    if (FORM == kDiag)
+    if (PCG)
       *reinterpret_cast<float4*>(&sg[rt][rc]) = rc < dk ? pa : make_float4(1.f, 1.f, 1.f, 1.f);
     if (FORM != kDiag && threadIdx.x < STW) {
-      sg[threadIdx.x][0] = pa1;
+      if (!PCG) sg[threadIdx.x][0] = pa1;
       sb[threadIdx.x] = pb1;
     }
   };
 
   // one seam token (staged slot tt, seam token index t): update, then readout
   auto token = [&](int tt, int64_t t) {
+    if constexpr (FORM == kKda) {
+      // the rows decay by their own gates before the erase reads them; the
+      // key is read from LDS on both passes (no register copy of it)
+      const float vn = sv[tt][n];
+      float up[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t4 = 0; t4 < SNT; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&sk[tt][32 * t4 + 8 * i + 4 * g]);
+          const float4 a4 = *reinterpret_cast<const float4*>(&sg[tt][32 * t4 + 8 * i + 4 * g]);
+          const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S[t4][4 * i + e] *= av[e];
+            up[e] = fmaf(kv[e], S[t4][4 * i + e], up[e]);
+          }
+        }
+      float u = (up[0] + up[1]) + (up[2] + up[3]);
+      u += __shfl_xor(u, 32);
+      const float cc = sb[tt] * (vn - u);
+#pragma unroll
+      for (int t4 = 0; t4 < SNT; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&sk[tt][32 * t4 + 8 * i + 4 * g]);
+          S[t4][4 * i + 0] = fmaf(k4.x, cc, S[t4][4 * i + 0]);
+          S[t4][4 * i + 1] = fmaf(k4.y, cc, S[t4][4 * i + 1]);
+          S[t4][4 * i + 2] = fmaf(k4.z, cc, S[t4][4 * i + 2]);
+          S[t4][4 * i + 3] = fmaf(k4.w, cc, S[t4][4 * i + 3]);
+        }
+    } else {
     float kr[SNT][16];
 #pragma unroll
     for (int t4 = 0; t4 < SNT; ++t4)
@@ -209,6 +245,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
           for (int e = 0; e < 4; ++e)
             S[t4][4 * i + e] = fmaf(kr[t4][4 * i + e], vn, gv[e] * S[t4][4 * i + e]);
         }
+    }
     }
     float op[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -376,7 +413,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   const bool seams = NS > 0;
   if (c0 < c1) {
     fetch(c0);
-    if (FORM == kDense) load_op(int64_t(entry_at(c0)) * BH + bh);
+    if (TH) load_op(int64_t(entry_at(c0)) * BH + bh);
     if (seams) load_round(rl64(so0_l, c0));
   }
   // One chain step: after a barrier the entry's operator (dense) and the first
@@ -392,7 +429,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     if (c + 1 < c1 && c + 1 - cb >= 64) fetch(c + 1);  // entries c+1 .. c+64
     const bool win = t_hi > t_lo, one_round = t_hi - t_lo <= STW;
     __syncthreads();  // the previous step's operator and tokens are no longer read
-    if (FORM == kDense) {
+    if (TH) {
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int e = threadIdx.x + it * 256;
@@ -415,6 +452,9 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       const int m0 = int(one_round ? t_hi - t_lo : STW);
       if constexpr (WIN) {
         window(m0, t_lo);
+      } else if constexpr (FORM == kKda) {
+#pragma unroll 1
+        for (int tt = 0; tt < m0; ++tt) token(tt, t_lo + tt);
       } else {
 #pragma unroll
         for (int tt = 0; tt < STW; ++tt)  // unrolled, so that reads run ahead
@@ -435,7 +475,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     }
     // then the entry's pair (its operator is in LDS)
     const float* S0p = sa.c.pool_S0 + pu * sdd;
-    if (FORM == kDense) {
+    if (TH) {
       f32x16 s0[SNT];
 #pragma unroll
       for (int t = 0; t < SNT; ++t)
@@ -527,6 +567,7 @@ hipError_t launch_compose_seams(const SeamArgs& a, hipStream_t s) {
     case kScalar: launch_seam_t<kScalar>(a, grid, s); break;
     case kDiag: launch_seam_t<kDiag>(a, grid, s); break;
     case kDense: launch_seam_t<kDense>(a, grid, s); break;
+    case kKda: launch_seam_t<kKda>(a, grid, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -937,9 +937,7 @@ int pic_validate_compose_seams(int form, int qkv_dtype, int batch, int heads, in
                                const float* O_out, const void* workspace,
                                size_t workspace_bytes) {
   (void)S_in;
-  if (form == PIC_FORM_KDA)
-    return fail(PIC_ERR_UNSUPPORTED, "seam windows are not supported for the KDA form");
-  if (form < PIC_FORM_SCALAR || form > PIC_FORM_DENSE)
+  if (form < PIC_FORM_SCALAR || form > PIC_FORM_KDA)
     return fail(PIC_ERR_UNSUPPORTED, "unknown form %d", form);
   if (qkv_dtype != PIC_DT_F32 && qkv_dtype != PIC_DT_BF16)
     return fail(PIC_ERR_UNSUPPORTED, "unknown qkv dtype %d", qkv_dtype);
@@ -967,9 +965,9 @@ int pic_validate_compose_seams(int form, int qkv_dtype, int batch, int heads, in
   if (n_req > 0 && !S_out) return fail(PIC_ERR_NULL, "S_out is required");
   if (total > 0 && (!pool_S0 || !pool_log_scale))
     return fail(PIC_ERR_NULL, "pool_S0 and pool_log_scale are required");
-  if (total > 0 && form == PIC_FORM_DENSE && !pool_T_hat)
-    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense form");
-  if (form != PIC_FORM_DENSE && pool_T_hat)
+  if (total > 0 && has_T_hat(form) && !pool_T_hat)
+    return fail(PIC_ERR_NULL, "pool_T_hat is required for the dense and KDA forms");
+  if (!has_T_hat(form) && pool_T_hat)
     return fail(PIC_ERR_UNSUPPORTED, "pool_T_hat must be NULL for scalar and diagonal forms");
   if (n_seam > 0 && (!q || !k || !v || !alpha || !O_out))
     return fail(PIC_ERR_NULL, "q, k, v, alpha and O_out are required when there are seam tokens");
@@ -1009,7 +1007,7 @@ int pic_compose_seams(int form, int qkv_dtype, int batch, int heads, int dk, int
   a.k = k;
   a.v = v;
   a.alpha = alpha;
-  a.beta = (form == PIC_FORM_DENSE) ? beta : nullptr;
+  a.beta = has_T_hat(form) ? beta : nullptr;  // dense and KDA erase along k
   a.O = O_out;
   a.c.inl = n_req <= pic::kInlineReq && total <= pic::kInlineIdx;
   if (a.c.inl) {

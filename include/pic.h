@@ -431,10 +431,11 @@ int pic_naive_add(int batch, int heads, int dk, int dv, int64_t pool_size, const
  * n_seam        number of seam tokens of the call (the token axis below)
  * q, k          device [batch][n_seam][heads][dk] (qkv_dtype)
  * v             device [batch][n_seam][heads][dv] (qkv_dtype)
- * alpha         device fp32 gates [batch][n_seam][heads] (diag: [..][dk])
- * beta          device fp32 [batch][n_seam][heads], dense only, NULL = 1
+ * alpha         device fp32 gates [batch][n_seam][heads] (diag, KDA: [..][dk])
+ * beta          device fp32 [batch][n_seam][heads], dense and KDA, NULL = 1
  * O_out         device fp32 out [batch][n_seam][heads][dv]
- * form          scalar, diagonal or dense (PIC_FORM_KDA: PIC_ERR_UNSUPPORTED)
+ * form          any PIC_FORM_*; the KDA token transition is
+ *               (I - beta k k^T) Diag(alpha), its pairs applied as dense ones
  * q, k, v, alpha and O_out may be NULL only when n_seam = 0.  The chain's own
  * pair is not produced.  The state and all updates are fp32 (seam tokens on
  * the vector units; the pairs as in pic_compose).

@@ -323,11 +323,13 @@ def test_validate_compose_seams(lib):
     assert vseams(lib, seam=(0, 0, 0, 0, 0, 0), q=ctypes.c_void_p(0), O=ctypes.c_void_p(0)) == OK
     assert vseams(lib, off=(0,), idx=(), seam=(0,)) == OK
     assert vseams(lib, seam=(0, 64, 64, 64, 64, 64)) == OK  # the largest window
+    assert vseams(lib, form=KDA) == OK  # KDA seams: per-channel gates, That required
     assert lib.pic_last_error().decode() == ""
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"form": KDA}, EUNSUP), ({"form": 4}, EUNSUP), ({"dt": 2}, EUNSUP), ({"dk": 8}, EDIMS),
+    ({"form": KDA, "That": False}, ENULL), ({"form": 4}, EUNSUP), ({"dt": 2}, EUNSUP),
+    ({"dk": 8}, EDIMS),
     ({"seam": (1, 1, 8, 16, 16, 20)}, EOFF), ({"seam": (0, 8, 4, 16, 16, 20)}, EOFF),
     ({"seam": (0, 0, 8, 16, 16, 20), "n_seam": 21}, EOFF),
     ({"seam": (0, 65, 65, 65, 65, 65)}, EDIMS), ({"n_seam": -1}, EDIMS),

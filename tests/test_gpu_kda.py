@@ -2,7 +2,8 @@
 per-channel gates (KDA form, T_t = (I - beta_t k_t k_t^T) Diag(alpha_t)),
 through the C ABI: the build of every (segment, layer, head) pair, compose of
 KDA pairs (against the oracle's compose and the unsplit recurrence), the
-chain's own pair, the plain operator, and the argument checks.
+chain's own pair, the plain operator, and the argument checks (KDA seam
+windows are covered with the other forms in test_gpu_seams.py).
 
 The token-by-token KDA build (PIC_PREC_FP32) computes in fp32 on the vector
 units from the stored inputs, so bf16 inputs are held to the fp32 tolerance
@@ -326,9 +327,9 @@ def test_kda_materialize_T():
     assert max_rel_units(T.cpu().numpy(), ref_T) <= TOL_F32
 
 
-def test_kda_rejections_leave_outputs_untouched():
-    """Seam windows do not take the KDA form; a KDA build needs That; both
-    fail on the host before anything is enqueued."""
+def test_kda_build_without_T_hat_is_rejected_before_any_work():
+    """A KDA build needs That; the call fails on the host before anything is
+    enqueued and leaves the outputs untouched."""
     import hybrid_caching_amd as pic
     import torch
     dev = torch.device("cuda:0")
@@ -340,9 +341,3 @@ def test_kda_rejections_leave_outputs_untouched():
         pic.pic_segment_build(KDA, k, k, a, None, [0, 8], out=out)
     torch.cuda.synchronize()
     assert bool((out["S0"] == 7.0).all()) and bool((out["log_scale"] == 7.0).all())
-    pool_l = torch.zeros((1, 1, 1), device=dev)
-    pool_T = torch.zeros((1, 1, 1, 16, 16), device=dev)
-    pool_S = torch.zeros((1, 1, 1, 16, 16), device=dev)
-    with pytest.raises(pic.PicError):
-        pic.pic_compose_seams(KDA, pool_l, pool_T, pool_S, [0, 1], [0], [0, 0],
-                              k[:, :0], k[:, :0], k[:, :0], a[:, :0])

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from oracle import DENSE, DIAG, SCALAR
+from oracle import DENSE, DIAG, KDA, SCALAR
 from tests.gpu_helpers import TOL_BF16, TOL_F32, max_rel_units, report, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +34,7 @@ def random_pool(form, P, B, H, dk, dv, seed, lam_range=(-1.0, 0.0)):
     rng = np.random.default_rng(seed)
     lam = rng.uniform(*lam_range, size=(P, B, H, dk) if form == DIAG else (P, B, H)).astype(np.float32)
     That = None
-    if form == DENSE:
+    if form in (DENSE, KDA):
         That = np.empty((P, B, H, dk, dk), dtype=np.float32)
         for idx in np.ndindex(P, B, H):
             M = np.eye(dk)
@@ -52,7 +52,7 @@ def seam_inputs(form, B, NS, H, dk, dv, seed, bf16, alpha=(0.9, 1.0), unit_keys=
     storage type: keys L2-normalised (dense) or 1/sqrt(dk)-scaled."""
     rng = np.random.default_rng(seed)
     k = rng.standard_normal((B, NS, H, dk)).astype(np.float32)
-    if form == DENSE and unit_keys:
+    if form in (DENSE, KDA) and unit_keys:
         k /= np.linalg.norm(k, axis=-1, keepdims=True)
     else:
         k *= np.float32(1 / np.sqrt(dk))
@@ -60,11 +60,11 @@ def seam_inputs(form, B, NS, H, dk, dv, seed, bf16, alpha=(0.9, 1.0), unit_keys=
     v = rng.standard_normal((B, NS, H, dv)).astype(np.float32)
     if bf16:
         q, k, v = synth.bf16_round(q), synth.bf16_round(k), synth.bf16_round(v)
-    if form == DIAG:
+    if form in (DIAG, KDA):
         a = (1 / (1 + np.exp(-rng.normal(3.0, 1.0, size=(B, NS, H, dk))))).astype(np.float32)
     else:
         a = rng.uniform(*alpha, size=(B, NS, H)).astype(np.float32)
-    b = rng.uniform(0.0, 1.0, size=(B, NS, H)).astype(np.float32) if form == DENSE else None
+    b = rng.uniform(0.0, 1.0, size=(B, NS, H)).astype(np.float32) if form in (DENSE, KDA) else None
     return q, k, v, a, b
 
 
@@ -89,7 +89,7 @@ CHAINS = ([0, 5, 5, 12, 13], [3, 0, 7, 7, 1, 2, 3, 4, 5, 6, 8, 9, 0])
 WINDOWS = [0, 8, 3, 8, 0, 1, 8, 8, 5, 16, 64, 8, 2]  # per chain entry
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_seam_compose_matches_oracle(form, d, bf16):
@@ -122,7 +122,7 @@ def test_seam_compose_unequal_dims(dk, dv):
     assert out_err(got_O, ref_O) <= TOL_F32
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 def test_seam_windows_empty_equal_compose(form):
     """With every window empty the call is a plain compose.  The dense
     kernels multiply by e^lambda on different sides of the split-bf16 product
@@ -136,13 +136,15 @@ def test_seam_windows_empty_equal_compose(form):
     off, idx = CHAINS
     S_in = synth.random_state((len(off) - 1, B, H, d, d), seed=6)
     z = torch.zeros((B, 0, H, d), dtype=torch.float32, device="cuda")
-    za = torch.zeros((B, 0, H, d) if form == DIAG else (B, 0, H), dtype=torch.float32, device="cuda")
+    za = torch.zeros((B, 0, H, d) if form in (DIAG, KDA) else (B, 0, H), dtype=torch.float32,
+                     device="cuda")
     got, O = pic.pic_compose_seams(form, to_dev(lam), to_dev(That), to_dev(S), off, idx,
                                    [0] * (len(idx) + 1), z, z, z, za, None, to_dev(S_in))
     want = pic.pic_compose(form, to_dev(lam), to_dev(That), to_dev(S), off, idx, to_dev(S_in))
     torch.cuda.synchronize()
     assert O.shape == (B, 0, H, d)
-    assert max_rel_units(got.cpu().numpy(), want.cpu().numpy()) <= (3e-5 if form == DENSE else 1e-6)
+    assert max_rel_units(got.cpu().numpy(), want.cpu().numpy()) <= (3e-5 if form in (DENSE, KDA)
+                                                                    else 1e-6)
 
 
 def test_seam_delta_rule_retrieval():
@@ -165,7 +167,7 @@ def test_seam_delta_rule_retrieval():
     assert np.max(np.abs(ref_O - v)) <= 1e-5
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 @pytest.mark.parametrize("n_req,steps", [(16, 4), (17, 3), (4, 40)])
 def test_seam_tables_in_arguments_and_in_workspace(form, n_req, steps):
     """Chain and seam tables travel in the kernel arguments up to 16 requests
@@ -184,7 +186,7 @@ def test_seam_tables_in_arguments_and_in_workspace(form, n_req, steps):
     assert out_err(got_O, ref_O) <= TOL_F32
 
 
-@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE])
+@pytest.mark.parametrize("form", [SCALAR, DIAG, DENSE, KDA])
 def test_seam_split_equals_unsplit_slow_gates(form):
     """End to end: a prompt of segments whose inner segments start with an
     8-token seam window; the windows' remainders are built on the GPU, then
@@ -198,17 +200,18 @@ def test_seam_split_equals_unsplit_slow_gates(form):
     N = sum(seg_lens)
     rng = np.random.default_rng(900 + form)
     k = rng.standard_normal((B, N, H, d)).astype(np.float32)
-    if form == DENSE:
+    erase = form in (DENSE, KDA)
+    if erase:
         k /= np.linalg.norm(k, axis=-1, keepdims=True)
     else:
         k *= np.float32(1 / np.sqrt(d))
     q = (rng.standard_normal((B, N, H, d)) / np.sqrt(d)).astype(np.float32)
     v = rng.standard_normal((B, N, H, d)).astype(np.float32)
-    if form != DENSE:
+    if not erase:
         v *= np.float32(1 / np.sqrt(d))
     q, k, v = synth.bf16_round(q), synth.bf16_round(k), synth.bf16_round(v)
-    a = rng.uniform(0.999, 1.0, size=(B, N, H, d) if form == DIAG else (B, N, H)).astype(np.float32)
-    b = rng.uniform(0.0, 0.05, size=(B, N, H)).astype(np.float32) if form == DENSE else None
+    a = rng.uniform(0.999, 1.0, size=(B, N, H, d) if form in (DIAG, KDA) else (B, N, H)).astype(np.float32)
+    b = rng.uniform(0.0, 0.05, size=(B, N, H)).astype(np.float32) if erase else None
     seam_pos, rem_pos, seam_off, rem_off, start = [], [], [0], [0], 0
     for i, L in enumerate(seg_lens):
         wi = w if i > 0 else 0
