@@ -115,8 +115,8 @@ __global__ __launch_bounds__(2 * DP * 2) void build_dense_kernel(BuildArgs a) {
   const int g = lane >> 5, cl = lane & 31;
   const int H = a.heads, dk = a.dk, dv = a.dv;
   const int BH = a.batch * H;
-  const int seg = seg_in_order(a, blockIdx.x / BH);
-  const int bh = blockIdx.x % BH, b = bh / H, h = bh % H;
+  const int seg = seg_in_order(a, int(build_unit(a, blockIdx.x) / BH));
+  const int bh = int(build_unit(a, blockIdx.x) % BH), b = bh / H, h = bh % H;
   const int64_t t_begin = seg_offset(a, seg), t_end = seg_offset(a, seg + 1);
   const int64_t N = a.n_tokens;
   const bool s_wave = wave < NT;  // S strip; otherwise That strip

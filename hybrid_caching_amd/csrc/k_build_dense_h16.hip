@@ -431,8 +431,8 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x);
 
 __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
   const int BH = a.batch * a.heads;
-  const int seg = seg_in_order(a, blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  const int seg = seg_in_order(a, int(build_unit(a, blockIdx.x) / BH));
+  const int bh = int(build_unit(a, blockIdx.x) % BH);
   Ctx x;
   x.b = bh / a.heads;
   x.h = bh % a.heads;

@@ -55,8 +55,8 @@ __global__ __launch_bounds__(KTH) void build_kda_kernel(BuildArgs a) {
   const int q = lane & 3, p = lane >> 2;
   const int dk = a.dk, dv = a.dv, H = a.heads;
   const int BH = a.batch * H;
-  const int seg = seg_in_order(a, blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  const int seg = seg_in_order(a, int(build_unit(a, blockIdx.x) / BH));
+  const int bh = int(build_unit(a, blockIdx.x) % BH);
   const int b = bh / H, h = bh % H;
   const int64_t t_begin = seg_offset(a, seg), t_end = seg_offset(a, seg + 1);
   const int64_t N = a.n_tokens;

@@ -216,8 +216,8 @@ __global__ __launch_bounds__(512) void build_kda_chunk_kernel(BuildArgs a) {
   auto kf32 = [&](int buf, int off) { return reinterpret_cast<float*>(sm + buf * T_BUF + off); };
 
   const int H = a.heads, BH = a.batch * H;
-  const int seg = seg_in_order(a, blockIdx.x / BH);
-  const int bh = blockIdx.x % BH, b = bh / H, h = bh % H;
+  const int seg = seg_in_order(a, int(build_unit(a, blockIdx.x) / BH));
+  const int bh = int(build_unit(a, blockIdx.x) % BH), b = bh / H, h = bh % H;
   // segment bounds as wave-uniform values (scalar addressing of the token rows)
   const int64_t t_begin = krfl64(seg_offset(a, seg));
   const int64_t ntok = krfl64(seg_offset(a, seg + 1)) - t_begin;

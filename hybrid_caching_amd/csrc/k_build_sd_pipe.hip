@@ -93,8 +93,8 @@ struct Unit {
 __device__ __forceinline__ Unit unit_of(const BuildArgs& a) {
   Unit u;
   const int H = a.heads, BH = a.batch * H;
-  u.seg = seg_in_order(a, blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  u.seg = seg_in_order(a, int(build_unit(a, blockIdx.x) / BH));
+  const int bh = int(build_unit(a, blockIdx.x) % BH);
   u.b = bh / H;
   u.h = bh % H;
   const int64_t t_begin = seg_offset(a, u.seg);

@@ -68,6 +68,24 @@ __device__ __forceinline__ int seg_in_order(const BuildArgs& a, int i) {
   return table_at(a.d_order, i);
 }
 
+// The build unit a workgroup takes: rank * (batch * heads) + layer * heads +
+// head, with rank the segment's place in the visiting order.  Workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2, and the heads
+// of one (segment, layer) read the same 128-byte lines of the per-head gates
+// and erase strengths; so a group of `heads` units goes to one XCD, one
+// workgroup after another: XCD x's k-th workgroup takes head k % heads of
+// group 8 (k / heads) + x.  Workgroups past the last whole round of 8 groups
+// keep their own index.  A bijection on the units, in about the visiting
+// order.
+__device__ __forceinline__ int64_t build_unit(const BuildArgs& a, int64_t blk) {
+  constexpr int kXcd = 8;
+  const int64_t groups = int64_t(a.n_seg) * a.batch;
+  const int64_t full = (groups / kXcd) * kXcd * a.heads;
+  if (blk >= full) return blk;
+  const int64_t x = blk % kXcd, k = blk / kXcd;
+  return ((k / a.heads) * kXcd + x) * a.heads + k % a.heads;
+}
+
 // One compose / naive-add call, after validation.
 struct ComposeArgs {
   int form;
