@@ -118,18 +118,31 @@ __device__ __forceinline__ ki16x4 ktr4(const _Float16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ki16x4*)(p));
 }
 
-// maximum over the 64 lanes (uniform result)
+// maximum of x over lane pairs (l, l ^ 16) and then (l, l ^ 32), for x >= 0:
+// the 16-lane swap of two copies of x gives the even rows in one result and
+// the odd rows in the other, the 32-lane swap the low and the high halves, so
+// the larger of the two results pairs every lane with its partner.  The
+// comparison is on the bit patterns as signed integers, which orders
+// non-negative floats as their values do (and puts any negative value below
+// them); the compiler folds a float maximum of the two swap results to the
+// first of them.
+__device__ __forceinline__ float kswap_max(float x) {
+  const int a = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  const int m = max(int(r[0]), int(r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return __builtin_bit_cast(float, max(int(q[0]), int(q[1])));
+}
+
+// maximum over the 64 lanes (uniform result): within rows of 16 by DPP,
+// across rows by the 16- and 32-lane swaps
 __device__ __forceinline__ float kwave_max(float x) {
   x = fmaxf(x, dpp_f<0xB1>(x));
   x = fmaxf(x, dpp_f<0x4E>(x));
   x = fmaxf(x, dpp_f<0x141>(x));
   x = fmaxf(x, dpp_f<0x140>(x));
-  const int xi = __builtin_bit_cast(int, x);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  x = kswap_max(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 // maxima over the 64 lanes of four values per lane (one per token): the quad
@@ -145,9 +158,7 @@ __device__ __forceinline__ float ktoken_max4(const float (&v)[4], int lane) {
   k = fmaxf(k, dpp_f<0x4E>(o2 ? a : b));  // lane ^ 2
   k = fmaxf(k, dpp_f<0x124>(k));          // row_ror:4
   k = fmaxf(k, dpp_f<0x128>(k));          // row_ror:8
-  k = fmaxf(k, __shfl_xor(k, 16));
-  k = fmaxf(k, __shfl_xor(k, 32));
-  return k;
+  return kswap_max(k);  // across rows
 }
 
 // One row of X_bb = (I + N_bb)^{-1} for a 16 x 16 diagonal block, from
