@@ -58,8 +58,9 @@
 //            solver:   off-diagonal blocks of chunk ci -> A, A'
 // so a chunk is staged in cycle j-1, solved in cycle j, and chained in cycles
 // j+1 and j+2.  K is kept for four chunks; -U fragments, A/A', G and the
-// masked gates for two; V for one.  Every global load is issued a cycle
-// before its data is staged.  The solver applies beta to the rows of G
+// masked gates for two; V for one.  Every global load (K and V rows, gates)
+// is issued two cycles before its data is staged, into one of two register
+// sets.  The solver applies beta to the rows of G
 // (L = diag(beta) strictly-lower(G)); G = K K^T is symmetric, so each lane
 // writes its accumulator column as a row with four 16-byte stores.
 #include <type_traits>
@@ -76,67 +77,72 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// Barriers.  Nothing is scheduled across a workgroup barrier: register-only
+// work (matrix-core products) is otherwise free to move past it, and products
+// of one phase that slip into the next delay that phase's own work.
+//
 // Optional phase timing (built only with -DPIC_PHASE_TIMING, into a separate
 // diagnostic library): every wave adds up, per phase of the pipeline cycle,
-// the clocks from the barrier that opens the phase to the one that closes it
-// (the phase's length, the same for every wave) and the clocks it waits at
-// the closing barrier; its busy time in the phase is the difference.  Clocks
-// are the shader-clock counter read by s_memtime.
+// its busy clocks (from the barrier that opens the phase to its arrival at the
+// one that closes it) and the phase's length (release to release), in a few
+// words of LDS per wave, so that the timers take no registers from the roles
+// (kept in registers, they spilled to scratch, whose waits distorted the
+// phases).  Clocks are the counter read by s_memtime.
 #ifdef PIC_PHASE_TIMING
 }  // namespace
 __device__ unsigned long long* pic_phase_out;  // [block][wave][8], blocks < pic_phase_blocks
 __device__ int pic_phase_blocks;
 namespace {
-struct PhaseClock {
-  unsigned long long t0 = __builtin_amdgcn_s_memtime();
-  // barrier i-1: arrival a1, release b1, phase it opened ph1; barrier i-2:
-  // release b2, phase ph2.  A timestamp is used only after the next
-  // barrier's fence (which waits for it anyway), so reading the clock adds
-  // no wait of its own.
-  unsigned long long a1 = 0, b1 = 0, b2 = 0;
-  int ph1 = -1, ph2 = -1;
-  unsigned long long wait_end[2] = {0, 0}, len[2] = {0, 0};
-  unsigned cycles = 0;
-};
-#define PIC_PHASE_DECL PhaseClock pic_pc_
+// per wave: busy A, busy B, length A, length B, last release, cycles, start
+__shared__ unsigned h16_tm[8][8];
+#define PIC_PHASE_DECL                                                      \
+  do {                                                                      \
+    if ((threadIdx.x & 63) == 0) {                                          \
+      const unsigned t_ = unsigned(__builtin_amdgcn_s_memtime());          \
+      unsigned* m_ = h16_tm[threadIdx.x >> 6];                              \
+      m_[0] = m_[1] = m_[2] = m_[3] = m_[5] = 0u;                           \
+      m_[4] = m_[6] = t_;                                                   \
+    }                                                                       \
+  } while (0)
 // barrier that opens phase `ph` (and closes the other one)
-#define PIC_BAR(ph)                                                  \
-  do {                                                               \
-    const unsigned long long pic_a_ = __builtin_amdgcn_s_memtime(); \
-    __syncthreads();                                                 \
-    __builtin_amdgcn_sched_barrier(0);                               \
-    if (pic_pc_.ph2 >= 0) {                                          \
-      pic_pc_.len[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.b2;           \
-      pic_pc_.wait_end[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.a1;      \
-    }                                                                \
-    pic_pc_.b2 = pic_pc_.b1;                                         \
-    pic_pc_.ph2 = pic_pc_.ph1;                                       \
-    pic_pc_.a1 = pic_a_;                                             \
-    pic_pc_.ph1 = (ph);                                              \
-    pic_pc_.b1 = __builtin_amdgcn_s_memtime();                       \
-    pic_pc_.cycles += (ph);                                          \
-    __builtin_amdgcn_sched_barrier(0);                               \
+#define PIC_BAR(ph)                                                         \
+  do {                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+    const unsigned a_ = unsigned(__builtin_amdgcn_s_memtime());            \
+    __syncthreads();                                                        \
+    const unsigned r_ = unsigned(__builtin_amdgcn_s_memtime());            \
+    if ((threadIdx.x & 63) == 0) {                                          \
+      unsigned* m_ = h16_tm[threadIdx.x >> 6];                              \
+      const unsigned o_ = m_[4];                                            \
+      m_[1 - (ph)] += a_ - o_;                                              \
+      m_[3 - (ph)] += r_ - o_;                                              \
+      m_[4] = r_;                                                           \
+      m_[5] += (ph);                                                        \
+    }                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                      \
   } while (0)
 #define PIC_PHASE_SAVE                                                                   \
   do {                                                                                   \
-    if (pic_pc_.ph2 >= 0) {                                                              \
-      pic_pc_.len[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.b2;                               \
-      pic_pc_.wait_end[pic_pc_.ph2] += pic_pc_.b1 - pic_pc_.a1;                          \
-    }                                                                                    \
     if (int(blockIdx.x) < pic_phase_blocks && (threadIdx.x & 63) == 0) {                \
+      const unsigned* m_ = h16_tm[threadIdx.x >> 6];                                     \
       unsigned long long* o =                                                            \
           pic_phase_out + (blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * 8;        \
-      o[0] = pic_pc_.len[0];                                                             \
-      o[1] = pic_pc_.wait_end[0];                                                        \
-      o[2] = pic_pc_.len[1];                                                             \
-      o[3] = pic_pc_.wait_end[1];                                                        \
-      o[4] = __builtin_amdgcn_s_memtime() - pic_pc_.t0;                                 \
-      o[5] = pic_pc_.cycles;                                                             \
+      o[0] = m_[2];                                                                      \
+      o[1] = m_[2] - m_[0];                                                              \
+      o[2] = m_[3];                                                                      \
+      o[3] = m_[3] - m_[1];                                                              \
+      o[4] = unsigned(__builtin_amdgcn_s_memtime()) - m_[6];                            \
+      o[5] = m_[5];                                                                      \
     }                                                                                    \
   } while (0)
 #else
 #define PIC_PHASE_DECL
-#define PIC_BAR(ph) __syncthreads()
+#define PIC_BAR(ph)                        \
+  do {                                     \
+    __builtin_amdgcn_sched_barrier(0);     \
+    __syncthreads();                       \
+    __builtin_amdgcn_sched_barrier(0);     \
+  } while (0)
 #define PIC_PHASE_SAVE
 #endif
 
@@ -689,9 +695,8 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
 // with two 16x16x16 matrix-core products (their B operands are read
 // transposed from the scratch tile; the first product's accumulators are
 // already the second one's B operand), then A = X diag(beta) and
-// A' = X diag(beta r) to LDS; then G of the next chunk.  The scratch is the
-// A/A' buffer of the chunk being solved: its previous chunk was last read in
-// the cycle before.  The solver also stages the first half of V.
+// A' = X diag(beta r) to LDS.  The scratch is the A/A' buffer of the chunk
+// being solved: its previous chunk was last read in the cycle before.
 // ===========================================================================
 constexpr int XS_LD = 48;  // scratch row stride (halves): 96 bytes, so that the
                            // four rows of a transposed read hit distinct banks
@@ -815,19 +820,24 @@ __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
   const int HDk = H * dk;       // element stride between tokens
   const int kch = min(8 * (lane & 15), dk - 8);
   // K rows: K wave pw stages rows [32 pw, 32 pw + 32) of each chunk (items
-  // 8 pw .. 8 pw + 7), loaded a cycle ahead
+  // 8 pw .. 8 pw + 7), loaded two cycles ahead
   const int i0 = 8 * pw;
-  uint4 pr[8];
+  uint4 pr0[8], pr1[8];  // two chunks' rows (even and odd chunks)
   auto row0 = [&](int j) { return (int64_t(b) * N + t_begin + int64_t(j) * C) * H + h; };
-  if (n > 0) load_rows(pr, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, lane);
-#pragma unroll 1
-  for (int ci = -1; ci <= n + 1; ++ci) {
-    // ---------------- phase A: K rows of chunk ci+1, load chunk ci+2's;
+  // pr holds the rows of chunk ci+1; once staged, it takes chunk ci+3.  The
+  // chunk index is clamped rather than the load skipped, so that every cycle
+  // issues the same loads and the wait before a staging covers only the set
+  // being staged.
+  auto cycle = [&](int ci, uint4 (&pr)[8]) __attribute__((always_inline)) {
+    // ---------------- phase A: K rows of chunk ci+1, load chunk ci+3's;
     // U^T tiles 3 pw .. 3 pw + 2 of chunk ci-1
     PIC_BAR(0);
     if (ci + 1 < n)
       stage_rows(Kb0 + ((ci + 1) % NKB) * (C * RLD), pr, dk, i0, lane);
-    if (ci + 2 < n) load_rows(pr, kp + row0(ci + 2) * dk + kch, HDk, chunk_len(ci + 2), i0, lane);
+    {
+      const int jl = min(ci + 3, n - 1);
+      load_rows(pr, kp + row0(jl) * dk + kch, HDk, chunk_len(jl), i0, lane);
+    }
     if (ci - 1 >= 0 && ci - 1 < n) {
       const int j = ci - 1;
       ut_tiles<3>(Kb0 + (j % NKB) * (C * RLD), AB0 + (j & 1) * AB_HALFS, Uf0 + (j & 1) * UF_BYTES,
@@ -837,6 +847,23 @@ __device__ __noinline__ void kstage_role(const Core& a, const Ctx& x) {
     PIC_BAR(1);
     if (ci + 1 < n)
       gram(Nm0 + ((ci + 1) & 1) * NM_FLOATS, Kb0 + ((ci + 1) % NKB) * (C * RLD), lane, pw);
+  };
+  if (n > 0) {
+    load_rows(pr0, kp + row0(0) * dk + kch, HDk, chunk_len(0), i0, lane);
+    load_rows(pr1, kp + row0(min(1, n - 1)) * dk + kch, HDk, chunk_len(min(1, n - 1)), i0, lane);
+    int ci = -1;
+#pragma unroll 1
+    for (; ci + 1 <= n + 1; ci += 2) {
+      cycle(ci, pr0);
+      cycle(ci + 1, pr1);
+    }
+    if (ci <= n + 1) cycle(ci, pr0);
+  } else {
+#pragma unroll 1
+    for (int ci = -1; ci <= n + 1; ++ci) {
+      PIC_BAR(0);
+      PIC_BAR(1);
+    }
   }
   PIC_PHASE_SAVE;
 }
@@ -848,7 +875,7 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   const float* bsrc = beta ? beta : alpha;
   const int HDv = H * dv;  // element stride between tokens
   const int vch = min(8 * (lane & 15), dv - 8);
-  uint4 pr[16];  // V rows of a chunk (items 0..15), loaded a cycle ahead
+  uint4 prv[2][16];  // V rows of two chunks (items 0..15), loaded two cycles ahead
   // alpha, beta of lane's token for two chunks, indexed by chunk parity, so
   // that no register holding a pending load is copied
   float pa[2] = {1.f, 1.f}, pb[2] = {0.f, 0.f};
@@ -864,10 +891,14 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
   // one pipeline cycle; P = parity of chunk ci+1 (compile-time register slot)
   auto cycle = [&](int ci, auto par) {
     constexpr int P = decltype(par)::value;
-    // ---------------- phase A: V rows of chunk ci-1, then load chunk ci's
+    // ---------------- phase A: V rows of chunk ci-1, then load chunk ci+1's
+    // into the same set (clamped, as the K rows)
     PIC_BAR(0);
-    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, pr, dv, 0, lane);
-    if (ci >= 0 && ci < n) load_rows(pr, vp + row0(ci) * dv + vch, HDv, chunk_len(ci), 0, lane);
+    if (ci - 1 >= 0 && ci - 1 < n) stage_rows(Vb, prv[P], dv, 0, lane);
+    {
+      const int jl = min(ci + 1, n - 1);
+      load_rows(prv[P], vp + row0(jl) * dv + vch, HDv, chunk_len(jl), 0, lane);
+    }
     // ---------------- phase B: gates of chunk ci+1
     PIC_BAR(1);
     if (ci + 1 < n) {
@@ -906,18 +937,28 @@ __device__ __noinline__ void vstage_role(const Core& a, const Ctx& x) {
         if (jn == n - 1) gg[8] = lg;  // S(C|0) = 2^lg x the consumers' S
       }
       lam += e0 + e1;
-      // the slot of chunk jn now takes chunk jn + 2
-      if (jn + 2 < n) load_gates(jn + 2, pa[P], pb[P]);
     }
+    // the slot of chunk ci+1 now takes chunk ci+3 (clamped)
+    load_gates(min(ci + 3, n - 1), pa[P], pb[P]);
   };
 
-  if (n > 0) load_gates(0, pa[0], pb[0]);
-  if (n > 1) load_gates(1, pa[1], pb[1]);
-  // chunk ci+1 has parity (ci+1) & 1: cycles -1, 1, 3, ... use slot 0
+  if (n > 0) {
+    load_gates(0, pa[0], pb[0]);
+    load_gates(min(1, n - 1), pa[1], pb[1]);
+    // chunk ci+1 has parity (ci+1) & 1: cycles -1, 1, 3, ... use slot 0
+    int ci = -1;
 #pragma unroll 1
-  for (int ci = -1; ci <= n + 1; ci += 2) {
-    cycle(ci, std::integral_constant<int, 0>{});
-    if (ci + 1 <= n + 1) cycle(ci + 1, std::integral_constant<int, 1>{});
+    for (; ci + 1 <= n + 1; ci += 2) {
+      cycle(ci, std::integral_constant<int, 0>{});
+      cycle(ci + 1, std::integral_constant<int, 1>{});
+    }
+    if (ci <= n + 1) cycle(ci, std::integral_constant<int, 0>{});
+  } else {
+#pragma unroll 1
+    for (int ci = -1; ci <= n + 1; ++ci) {
+      PIC_BAR(0);
+      PIC_BAR(1);
+    }
   }
   if (lane == 0) gstore(out_lam + unit, lam * kLn2);
   PIC_PHASE_SAVE;
