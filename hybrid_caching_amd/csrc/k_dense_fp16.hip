@@ -107,7 +107,14 @@ static_assert(L_V % 16 == 0 && L_Q % 16 == 0 && L_G % 16 == 0 && L_NA % 16 == 0 
 
 __shared__ __attribute__((aligned(16))) char dfp_smem[LDS_TOTAL];
 
-#define PIC_BARRIER() __syncthreads()
+// a workgroup barrier that no instruction is scheduled across (register-only
+// matrix-core products would otherwise move into the next phase)
+#define PIC_BARRIER()                    \
+  do {                                   \
+    __builtin_amdgcn_sched_barrier(0);   \
+    __syncthreads();                     \
+    __builtin_amdgcn_sched_barrier(0);   \
+  } while (0)
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c) {
