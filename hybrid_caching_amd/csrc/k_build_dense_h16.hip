@@ -43,7 +43,12 @@
 // 4j + q of the group addresses row r_j, columns c0 + 4q .. c0 + 4q + 3, lane
 // i receives rows r_0..r_3 of column c0 + i: a column of the tile, i.e. a
 // row of its transpose.  The row stride (288 bytes) puts the 16 addresses of
-// a group on distinct banks.
+// a group on distinct banks.  The LDS serves the two groups of a half wave
+// together, and they read the two 16-column halves of one 32-column tile from
+// the same rows: so the columns of a row are stored permuted, the 16-column
+// piece p (columns 16p .. 16p+15) at piece slot (p >> 1) + 4 (p & 1), which
+// puts the two halves of tile t 128 bytes apart (slots t and t + 4) and their
+// banks apart.  G = K K^T sums over all columns and reads them in stored order.
 //
 // Pipeline: cycle ci has two phases separated by workgroup barriers.
 //   phase A: consumers chain sub-chunk 1 of chunk ci-2
@@ -317,10 +322,15 @@ __device__ __forceinline__ void load_rows(uint4 (&pr)[NI], const __bf16* base, i
     for (int i = 0; i < NI; ++i) pr[i] = gload_u4(base + min((lane >> 4) + 4 * (i0 + i), len - 1) * HD);
   }
 }
+// stored position (halves) of columns 8 cg .. 8 cg + 7 of a K or V row (the
+// permutation of 16-column pieces in the header)
+__device__ __forceinline__ int col_slot8(int cg) {
+  return 16 * ((cg >> 2) + 4 * ((cg >> 1) & 1)) + 8 * (cg & 1);
+}
 template <int NI>
 __device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI], int d, int i0, int lane) {
   const int cg = lane & 15;
-  _Float16* row = dst + (lane >> 4) * RLD + 8 * cg;
+  _Float16* row = dst + (lane >> 4) * RLD + col_slot8(cg);
   if (d == DP) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4*>(row + 4 * (i0 + i) * RLD) = bf2h(pr[i]);
@@ -366,7 +376,7 @@ __device__ __forceinline__ void ut_tiles(const _Float16* kb, const _Float16* Ah,
                                          int lane) {
   const int g = lane >> 5, cl = lane & 31;
   const int ti = lane & 15, tg = lane >> 4;
-  const int tr_row = ti >> 2, tr_col = 16 * (tg & 1) + 4 * (ti & 3);
+  const int tr_row = ti >> 2, tr_col = 64 * (tg & 1) + 4 * (ti & 3);  // (stored slots)
   const _Float16* kbase = kb + (8 * g + tr_row) * RLD + tr_col;
   f16x8 kf[NTL][2], ah[NTL][2];
 #pragma unroll
@@ -374,7 +384,7 @@ __device__ __forceinline__ void ut_tiles(const _Float16* kb, const _Float16* Ah,
     const int t = (tile0 + i) % NT, s = (tile0 + i) / NT;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 32 * t;
+      const _Float16* p0 = kbase + (32 * s + 16 * kk) * RLD + 16 * t;
       kf[i][kk] = tr_h8(p0, p0 + 4 * RLD);
       ah[i][kk] = lds_h8(Ah + (32 * s + cl) * A_LD + 16 * kk + 8 * g);
     }
@@ -483,9 +493,10 @@ __global__ __launch_bounds__(THREADS) void build_dense_h16_kernel(BuildArgs a) {
   const int lane = threadIdx.x & 63, g = lane >> 5, cl = lane & 31;             \
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));        \
   /* transposed reads: group lane ti supplies row ti >> 2 of a 4-row block   */ \
-  /* and columns 4 (ti & 3) .. +3 of the group's 16-column half              */ \
+  /* and columns 4 (ti & 3) .. +3 of the group's 16-column half (stored at   */ \
+  /* slot t or t + 4 of tile t: add 16 t)                                     */ \
   const int ti = lane & 15, tg = lane >> 4;                                     \
-  const int tr_row = ti >> 2, tr_col = 16 * (tg & 1) + 4 * (ti & 3);            \
+  const int tr_row = ti >> 2, tr_col = 64 * (tg & 1) + 4 * (ti & 3);            \
   auto chunk_len = [&](int j) {                                                 \
     const int64_t c0 = t_begin + int64_t(j) * C;                                \
     return (t_end - c0 < C) ? int(t_end - c0) : C;                              \
@@ -558,7 +569,7 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
         const int kh = ks == 3 ? 0 : 1;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          const _Float16* p0 = kbase + 16 * kh * RLD + 32 * tt;
+          const _Float16* p0 = kbase + 16 * kh * RLD + 16 * tt;
           kf[kh][tt] = tr_h8(p0, p0 + 8 * RLD);
         }
       }
@@ -580,7 +591,7 @@ __device__ __noinline__ void consumer_role(const Core& a, const Ctx& x) {
   auto seed = [&](int j, int s) {
     const _Float16* Ap = AB0 + (j & 1) * AB_HALFS + 64 * A_LD;
     // V^T fragment: lane (g, n) needs V[token 16 kk + 8 g + 0..7][32 c + n]
-    const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 32 * c + tr_col;
+    const _Float16* vbase = Vb + (8 * g + tr_row) * RLD + 16 * c + tr_col;
     f32x16 acc = zero16();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
