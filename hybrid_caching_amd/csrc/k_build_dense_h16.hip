@@ -257,19 +257,29 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// G's layout.  Row r (32 floats) of sub-chunk s holds its eight 4-float
+// pieces swizzled: piece j at slot j ^ ((r >> 1) & 7) ^ 2s.  The Gram waves
+// write a row per lane, the solver reads 16 rows x one piece per lane (the
+// off-diagonal block) or one row per group of 16 lanes, four groups at once
+// (the diagonal blocks); with the swizzle each of these touches distinct banks.
+__device__ __forceinline__ int g_slot(int r, int j, int s) { return j ^ ((r >> 1) & 7) ^ (2 * s); }
+
 // Back substitution of X_bb (I + L_bb) = I for one row of a 16x16 diagonal
 // block, steps i = 15 .. 1: acc[r] -= X[row][i] L[i][r] for r < i, where
 // L[i][r] = beta_i G[i][r].  Row i of the block of G is a broadcast read
 // (the 16 lanes of a block read the same address), issued PF steps ahead of
-// its use; bt holds beta of the block's 16 tokens.
+// its use; bt holds beta of the block's 16 tokens.  gp[k] points at row 0 of
+// the block, stored slot x ^ k with x = 4 blk ^ 2 s (the block's piece 4 blk
+// + r4 of row i sits at stored slot x ^ (r4 ^ ((i >> 1) & 7))).
 constexpr int PF = 3;
-__device__ __forceinline__ void subst16(float (&acc)[16], const float* grow0, const float (&bt)[16]) {
+__device__ __forceinline__ void subst16(float (&acc)[16], const float* const (&gp)[8],
+                                        const float (&bt)[16]) {
   float4 buf[PF + 1][4];
 #pragma unroll
   for (int p = 0; p < PF; ++p)
 #pragma unroll
     for (int r4 = 0; r4 < (15 - p + 3) / 4; ++r4)
-      buf[p][r4] = *reinterpret_cast<const float4*>(grow0 + (15 - p) * 32 + 4 * r4);
+      buf[p][r4] = *reinterpret_cast<const float4*>(gp[r4 ^ (((15 - p) >> 1) & 7)] + (15 - p) * 32);
 #pragma unroll
   for (int i = 15; i >= 1; --i) {
     const int slot = (15 - i) % (PF + 1);
@@ -278,7 +288,7 @@ __device__ __forceinline__ void subst16(float (&acc)[16], const float* grow0, co
       const int ps = (15 - ip) % (PF + 1);
 #pragma unroll
       for (int r4 = 0; r4 < (ip + 3) / 4; ++r4)
-        buf[ps][r4] = *reinterpret_cast<const float4*>(grow0 + ip * 32 + 4 * r4);
+        buf[ps][r4] = *reinterpret_cast<const float4*>(gp[r4 ^ ((ip >> 1) & 7)] + ip * 32);
     }
     __builtin_amdgcn_sched_barrier(0);
     const float x = acc[i] * bt[i];
@@ -345,7 +355,7 @@ __device__ __forceinline__ void stage_rows(_Float16* dst, const uint4 (&pr)[NI],
 // G_ss = K_s K_s^T of sub-chunk s from the K rows of a chunk (fp32).  G is
 // symmetric: the lane's accumulator column cl is also row cl, with entries
 // 8 k + 4 g + {0..3} in registers 4k .. 4k+3, so each lane writes its row
-// with four 16-byte stores.
+// with four 16-byte stores (pieces 2k + g, swizzled).
 __device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane, int s) {
   const int g = lane >> 5, cl = lane & 31;
   {
@@ -358,10 +368,10 @@ __device__ __forceinline__ void gram(float* gm, const _Float16* kb, int lane, in
       else
         acc0 = mfma16(ak, ak, acc0);
     }
-    float* row = gm + s * 1024 + cl * 32 + 4 * g;
+    float* row = gm + s * 1024 + cl * 32;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
-      *reinterpret_cast<float4*>(row + 8 * k4) =
+      *reinterpret_cast<float4*>(row + 4 * g_slot(cl, 2 * k4 + g, s)) =
           make_float4(acc0[4 * k4] + acc1[4 * k4], acc0[4 * k4 + 1] + acc1[4 * k4 + 1],
                       acc0[4 * k4 + 2] + acc1[4 * k4 + 2], acc0[4 * k4 + 3] + acc1[4 * k4 + 3]);
   }
@@ -732,7 +742,10 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = (r == jr) ? 1.f : 0.f;
-      subst16(acc, gm + s * 1024 + (16 * blk) * 32 + 16 * blk, bt);
+      const float* gp[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) gp[k] = gm + s * 1024 + (16 * blk) * 32 + 4 * ((4 * blk ^ 2 * s) ^ k);
+      subst16(acc, gp, bt);
       // row jr of block blk -> scratch tile (s, blk)
       _Float16* xr = ab + ((2 * s + blk) * 16 + jr) * XS_LD;
       *reinterpret_cast<uint4*>(xr) = make_uint4(pk_h2(acc[0], acc[1]), pk_h2(acc[2], acc[3]),
@@ -754,7 +767,8 @@ __device__ __noinline__ void solver_role(const Core& a, const Ctx& x) {
       f32x4 X10[2];
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
-        const float4 g4 = *reinterpret_cast<const float4*>(gm + ss * 1024 + (16 + m) * 32 + 4 * kq);
+        const float4 g4 =
+            *reinterpret_cast<const float4*>(gm + ss * 1024 + (16 + m) * 32 + 4 * g_slot(16 + m, kq, ss));
         const float bm = gbp[32 * ss + 16 + m];
         const f16x4 l10 = h4(bm * g4.x, bm * g4.y, bm * g4.z, bm * g4.w);
         const _Float16* t00 = ab + (2 * ss) * 16 * XS_LD;
