@@ -510,15 +510,30 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
         for (int q = 0; q < 16; ++q) S[t][q] = fmaf(scale, acc[t][q], s0[t][q]);
     } else {
       const float sc = (FORM == kScalar) ? expf(lam) : 1.f;
-#pragma unroll
-      for (int t = 0; t < SNT; ++t)
+      // S0 one row tile at a time, the next tile's loads issued before this
+      // tile's products (left to itself the compiler waited for each load)
+      auto s0_tile = [&](int t) __attribute__((always_inline)) {
+        f32x16 x;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = t * 32 + acc_row(q, g);
-          const bool in = FULL || (ncol && row < dk);
-          const float rs = (FORM == kDiag) ? (row < dk ? expf(sa.c.pool_log_scale[pu * dk + row]) : 1.f) : sc;
-          S[t][q] = fmaf(rs, S[t][q], in ? S0p[int64_t(row) * dv + n] : 0.f);
+          x[q] = (FULL || (ncol && row < dk)) ? S0p[int64_t(row) * dv + n] : 0.f;
         }
+        return x;
+      };
+      f32x16 nxt = s0_tile(0);
+#pragma unroll
+      for (int t = 0; t < SNT; ++t) {
+        const f32x16 cur = nxt;
+        if (t + 1 < SNT) nxt = s0_tile(t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = t * 32 + acc_row(q, g);
+          const float rs = (FORM == kDiag) ? (row < dk ? expf(sa.c.pool_log_scale[pu * dk + row]) : 1.f) : sc;
+          S[t][q] = fmaf(rs, S[t][q], cur[q]);
+        }
+      }
     }
   }
 
