@@ -56,6 +56,14 @@ constexpr int SLDR = SP + 8;   // row stride of the staged operator (bf16)
 // FULL: dk = dv = 128, so every operator, S0 and state access is an
 // unconditional load at a loop-invariant offset from the step's base address
 // INL: the chain and seam tables travel in the kernel arguments
+// a workgroup barrier that no instruction is scheduled across (the
+// compiler otherwise moves register-only products into the next phase)
+__device__ __forceinline__ void seam_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int FORM, bool BF16, bool FULL, bool INL>
 __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
   constexpr bool TH = FORM == kDense || FORM == kKda;   // pairs carry That
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       bq[e] = g ? xb : racc[4 + e];
       bq[4 + e] = g ? racc[4 + e] : xb;
     }
-    __syncthreads();  // the 8x8 products are in LDS
+    seam_barrier();  // the 8x8 products are in LDS
     float al[STW], cc[STW];
 #pragma unroll
     for (int t = 0; t < STW; ++t) al[t] = sg[t][0];
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     const bool next = seams && c + 1 < c1;
     if (c + 1 < c1 && c + 1 - cb >= 64) fetch(c + 1);  // entries c+1 .. c+64
     const bool win = t_hi > t_lo, one_round = t_hi - t_lo <= STW;
-    __syncthreads();  // the previous step's operator and tokens are no longer read
+    seam_barrier();  // the previous step's operator and tokens are no longer read
     if (TH) {
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
     }
     if (win) store_round();  // the window's first round was loaded ahead
     if (next && (!win || one_round)) load_round(t_hi);
-    __syncthreads();
+    seam_barrier();
     if (win) {
       const int m0 = int(one_round ? t_hi - t_lo : STW);
       if constexpr (WIN) {
@@ -463,9 +471,9 @@ __global__ __launch_bounds__(256) void compose_seam_kernel(SeamArgs sa) {
       for (int64_t t0 = t_lo + STW; t0 < t_hi; t0 += STW) {  // windows longer than a round
         const int m = int(t_hi - t0 < STW ? t_hi - t0 : STW);
         load_round(t0);
-        __syncthreads();
+        seam_barrier();
         store_round();
-        __syncthreads();
+        seam_barrier();
         if constexpr (WIN)
           window(m, t0);
         else
