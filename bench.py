@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "build_kda_chunk_kernel": ["k_build_kda_chunk.hip", "mfma_util.hpp", "pic_internal.hpp"],
     "rerotate_kernel": ["k_rerotate.hip", "pic_internal.hpp"],
     "conv_warmup_kernel": ["k_conv_warmup.hip", "pic_internal.hpp"],
+    "conv_warmup_w4_kernel": ["k_conv_warmup.hip", "pic_internal.hpp"],
     "dense_fp16_kernel": ["k_dense_fp16.hip", "mfma_util.hpp", "pic_internal.hpp"],
 }
 PEAK_FP32_VALU_TFLOPS = 78.6  # MI355X fp32 vector FMA rate without packed instructions
@@ -685,12 +686,15 @@ def bench_reuse(w, args):
         # per launch (one stream; q, k, v have d = 128 here), bf16: each output
         # token written once, each entry's head and history tokens read once
         cwb = 3 * B * H * dk * n_e * (cw - 1) * 2
-        conv_info = {"kernel": "conv_warmup_kernel", "width": cw, "entries": n_e,
+        # (width 4 with up to 13 outputs per entry runs the window-in-registers
+        # kernel, other widths the general one)
+        conv_kernel = "conv_warmup_w4_kernel" if cw == 4 else "conv_warmup_kernel"
+        conv_info = {"kernel": conv_kernel, "width": cw, "entries": n_e,
                      "tokens": n_e * (cw - 1), "ms_per_launch": t_cw * 1e3,
                      "launches": "3 (q, k, v)", "bound": "hbm",
                      "achieved": cwb / t_cw / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": cwb / t_cw / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": cwb,
-                     "traffic": measured_traffic("conv_warmup_kernel", w.name)}
+                     "traffic": measured_traffic(conv_kernel, w.name)}
     gbs = cb / t_comp / 1e9
     out = {"metric": "state composes/s (dense delta, H=32, d=128), composition-heavy reuse"
                      + (" with seam windows" if seam_w else "") + "; % HBM roofline",
