@@ -64,6 +64,14 @@ constexpr int KD = 128;          // head size (dk = dv)
 constexpr int KC = 32;           // tokens per chunk
 constexpr int KNT = KD / 32;     // row tiles of a column strip
 constexpr int KRL = 152;         // row stride (halves) of the token-major fp16 tiles
+// The K- and V tiles, read only transposed (ds_read_b64_tr_b16), have rows of
+// KTL = 144 halves (288 bytes) with their 16-column pieces permuted: piece p
+// (columns 16p .. 16p+15) at slot (p >> 1) + 4 (p & 1).  A transposed read
+// serves two 16-lane groups together, reading the two 16-column halves of one
+// 32-column tile from the same four rows; with the 288-byte stride the four
+// rows of a group fall 8 banks apart and the permutation puts the other
+// group's half 32 banks further, so the two groups never share a bank.
+constexpr int KTL = 144;
 constexpr int KLL = 36;          // row stride (floats) of L
 constexpr int KAL = 40;          // row stride (halves) of A
 constexpr int KXS = 24;          // row stride (halves) of the diagonal blocks' rows
@@ -71,9 +79,10 @@ constexpr int KXS = 24;          // row stride (halves) of the diagonal blocks' 
 constexpr int K_TILE = KC * KRL * 2;
 // one buffer of a chunk's tiles (token-major rows of KRL halves)
 constexpr int T_KH = 0;                 // K^ = k (.) g_t          fp16
-constexpr int T_KB = T_KH + K_TILE;     // K- = k (.) gamma / g_t  fp16
-constexpr int T_VR = T_KB + K_TILE;     // V                        bf16 as loaded
-constexpr int T_KA = T_VR + K_TILE;     // k (.) g_t / g_m          fp16
+constexpr int KT_TILE = KC * KTL * 2;
+constexpr int T_KB = T_KH + K_TILE;     // K- = k (.) gamma / g_t  fp16 (KTL rows)
+constexpr int T_VR = T_KB + KT_TILE;    // V                        bf16 as loaded (KTL rows)
+constexpr int T_KA = T_VR + KT_TILE;    // k (.) g_t / g_m          fp16
 constexpr int T_KC = T_KA + K_TILE;     // k (.) g_m / g_t          fp16
 constexpr int T_DG = T_KC + K_TILE;     // gamma [KD] fp32
 constexpr int T_BT = T_DG + KD * 4;     // beta of the chunk's tokens [C] (0 past the end)
@@ -351,11 +360,13 @@ __global__ __launch_bounds__(512) void build_kda_chunk_kernel(BuildArgs a) {
       const float k0 = kbf_lo(rk[tt]), k1 = kbf_hi(rk[tt]);
       const float kg0 = k0 * g0, kg1 = k1 * g1, kr0 = k0 * r0, kr1 = k1 * r1;
       const int at = (tq + tt) * KRL + 2 * lane;
+      // (K- and V rows: channels 2 lane, 2 lane + 1 at their permuted slot)
+      const int att = (tq + tt) * KTL + 16 * ((lane >> 4) + 4 * ((lane >> 3) & 1)) + 2 * (lane & 7);
       *reinterpret_cast<unsigned*>(kh + at) = kpk(kg0, kg1);
-      *reinterpret_cast<unsigned*>(kbr + at) = kpk(kr0 * tot0, kr1 * tot1);
+      *reinterpret_cast<unsigned*>(kbr + att) = kpk(kr0 * tot0, kr1 * tot1);
       *reinterpret_cast<unsigned*>(ka + at) = kpk(kg0 * im0, kg1 * im1);
       *reinterpret_cast<unsigned*>(kc + at) = kpk(kr0 * mid0, kr1 * mid1);
-      *reinterpret_cast<unsigned*>(vr + at) = rv[tt];
+      *reinterpret_cast<unsigned*>(vr + att) = rv[tt];
     }
   };
 
@@ -537,9 +548,9 @@ __global__ __launch_bounds__(512) void build_kda_chunk_kernel(BuildArgs a) {
       if (!tw) {
         // V at tokens kperm(hh, g, 0..7), column 32 cw + cl (bf16)
         const int r0 = 16 * hh + 4 * g + ((lane & 15) >> 2);
-        const int col = 32 * cw + 16 * (G & 1) + 4 * (lane & 3);
-        const ki16x4 v0 = ktr4(Vr + r0 * KRL + col);
-        const ki16x4 v1 = ktr4(Vr + (r0 + 8) * KRL + col);
+        const int col = 16 * cw + 64 * (G & 1) + 4 * (lane & 3);  // (permuted slots)
+        const ki16x4 v0 = ktr4(Vr + r0 * KTL + col);
+        const ki16x4 v1 = ktr4(Vr + (r0 + 8) * KTL + col);
         auto bf = [](short x) { return __uint_as_float(uint32_t(uint16_t(x)) << 16); };
         ku32x4 w;
         w[0] = kpk(bf(v0[0]) - Y[8 * hh + 0], bf(v0[1]) - Y[8 * hh + 1]);
@@ -558,9 +569,9 @@ __global__ __launch_bounds__(512) void build_kda_chunk_kernel(BuildArgs a) {
 #pragma unroll
       for (int t = 0; t < KNT; ++t) {
         // K-^T rows = channels 32t + cl, tokens kperm(hh, g, 0..7)
-        const int col = 32 * t + 16 * (G & 1) + 4 * (lane & 3);
-        const ki16x4 k0 = ktr4(Kb + r0 * KRL + col);
-        const ki16x4 k1 = ktr4(Kb + (r0 + 8) * KRL + col);
+        const int col = 16 * t + 64 * (G & 1) + 4 * (lane & 3);  // (permuted slots)
+        const ki16x4 k0 = ktr4(Kb + r0 * KTL + col);
+        const ki16x4 k1 = ktr4(Kb + (r0 + 8) * KTL + col);
         const ki16x8 kk = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
         X[t] = kmfma(__builtin_bit_cast(kf16x8, kk), eb, X[t]);
       }
