@@ -50,12 +50,15 @@ def test_conv_warmup_matches_oracle(bf16, W, dc):
     assert e <= (4e-3 if bf16 else TOL_F32)
 
 
-@pytest.mark.parametrize("W,n_warm", [(4, 3), (4, 7), (9, 8), (16, 15), (5, 12)])
+@pytest.mark.parametrize("W,n_warm", [(4, 3), (4, 7), (4, 1), (4, 13), (4, 14), (9, 8), (16, 15),
+                                     (5, 12)])
 def test_conv_warmup_many_blocks(W, n_warm):
     """A launch of several channel-item blocks (32 heads x 128 channels = 4
     blocks of 256 items) and many 32-row blocks (2 layers x 20 entries x
     n_warm rows), widths up to the header's limit of 16 and windows longer
-    than W - 1, with full, partial and absent history."""
+    than W - 1, with full, partial and absent history.  Width 4 runs the
+    window-in-registers kernel up to n_warm = 13 (3 + 13 taps) and the general
+    one beyond."""
     import hybrid_caching_amd as pic
     import torch
     rng = np.random.default_rng(1000 + 31 * W + n_warm)
