@@ -451,14 +451,13 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
     __syncthreads();  // weights of chunks 0 and 1
     stage(I0(), 0, min(2, last));
     __syncthreads();  // chunk 0 staged
+    // The last step stages the chunk past the end (weights of a clamped
+    // chunk, registers of the last one) into the buffer nobody reads any
+    // more: every step runs the same code, so the register sets are never
+    // merged at a join (the copies there would wait for every load in flight).
     auto step = [&](auto D, int cj) __attribute__((always_inline)) {
       using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
-      if (cj + 1 < n) {
-        stage(DN(), cj + 1, min(cj + 3, last));
-      } else {
-        // keep the load sequence of every step the same (see the header)
-        load_all(DN(), last);
-      }
+      stage(DN(), cj + 1, min(cj + 3, last));
       __syncthreads();
     };
     int cj = 0;
@@ -480,14 +479,18 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
 // and RW rows of 8 consecutive tokens (lane = PL * r + p: tokens 8r .. 8r+7
 // of the wave's block, channels 4p .. 4p+3 of its channel part); the waves
 // split the channels into CP parts and the chunk into TG blocks of 8 * RW
-// tokens, so a channel's suffix sums of log2 alpha stay in one wave: serial
-// over a lane's 8 tokens, then over the later rows by ds_bpermute.  A lane's
-// weights are one exp2 of the sum over the later rows times its own later
-// gates.  Kw^T (hi, lo) and V^T go to LDS as channel rows, one 16-byte store
-// (8 tokens) per channel and array; the 16-byte pieces of a row are
-// XOR-swizzled by the row's 8-row group.  Loads: 16 lanes x 8 bytes of k or
-// v or 16 lanes x 16 bytes of gates per token row (whole 128-byte lines);
-// each register set is reloaded as soon as the staging step is done with it.
+// tokens, so a channel's suffix sums of log2 alpha stay in one wave: a lane
+// takes the log2 of the product of its 8 gates, then the sums over the later
+// rows come by ds_bpermute.  A lane's weights are one exp2 of the sum over
+// the later rows times its own later gates.  Kw^T (hi, lo) and V^T go to LDS
+// as channel rows, one 16-byte store (8 tokens) per channel and array; the
+// 16-byte pieces of a row are XOR-swizzled by the row's 8-row group.
+// Loads: 16 lanes x 8 bytes of k or v or 16 lanes x 16 bytes of gates per
+// token row (whole 128-byte lines), nontemporal; a lane's offsets inside a
+// chunk are fixed, so an address costs one add and one clamp.  Each part of
+// a register set (v, gates, k, in the order they are staged) is reloaded as
+// soon as the staging step is done with it.  The producers' step is one
+// code path for every chunk (see stage below), with no branch around loads.
 template <int DP>
 struct DiagShape {
   static constexpr int NC = DP / 32;                    // consumer waves
@@ -511,6 +514,19 @@ struct DiagLds {
   static constexpr int TOTAL = GM + DiagShape<DP>::TG * DP * 4;
 };
 
+
+// Loads with the nontemporal hint: the inputs of a diagonal-gate unit (its
+// own channels of k, v and the gates) are read exactly once.
+typedef float ntf4 __attribute__((ext_vector_type(4)));
+typedef unsigned ntu2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 nt_f4(const char* p) {
+  const ntf4 t = __builtin_nontemporal_load(reinterpret_cast<const ntf4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 nt_u2(const char* p) {
+  const ntu2 t = __builtin_nontemporal_load(reinterpret_cast<const ntu2*>(p));
+  return make_uint2(t.x, t.y);
+}
 struct DiagRegs {
   uint2 k[8], v[8];
   float4 a[8];
@@ -608,48 +624,43 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
   // Tokens past the end of the segment read its last token (a valid
   // address; their weight is 0 and their gate counts as 1); channels past
   // dk / dv read the last channels and only feed rows / columns of S that
-  // are not written.
-  auto tok_ptrs = [&](int ci, int q, const char*& kp, const char*& vp, const char*& ap)
-      __attribute__((always_inline)) {
-    int r, c0, t0;
-    lane_map(r, c0, t0);
-    const int len = chunk_len(u, ci);
-    const unsigned t = unsigned(min(t0 + q, len - 1));
-    const unsigned ck = unsigned(min(c0, dk - 4)), cv = unsigned(min(c0, dv - 4));
-    const int64_t off = int64_t(ci) * C;
-    kp = reinterpret_cast<const char*>(kbase + off * sk) + (t * unsigned(sk) + ck) * 2u;
-    vp = reinterpret_cast<const char*>(vbase + off * sv) + (t * unsigned(sv) + cv) * 2u;
-    ap = reinterpret_cast<const char*>(abase + off * sk) + (t * unsigned(sk) + ck) * 4u;
-  };
+  // are not written.  A lane's byte offsets inside a chunk are fixed: its
+  // first row's offset is computed once, row q adds q rows (a scalar), and
+  // the clamp to the chunk's last token is one unsigned minimum, since the
+  // offsets grow with the token.
+  int lr, lc0, lt0;
+  lane_map(lr, lc0, lt0);
+  (void)lr;
+  const unsigned rk = unsigned(sk) * 2u, rv = unsigned(sv) * 2u, ra = unsigned(sk) * 4u;
+  const unsigned ck2 = unsigned(min(lc0, dk - 4)) * 2u, cv2 = unsigned(min(lc0, dv - 4)) * 2u;
+  const unsigned ok_ = unsigned(lt0) * rk + ck2, ov_ = unsigned(lt0) * rv + cv2,
+                 oa_ = unsigned(lt0) * ra + 2u * ck2;
   auto load_a = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+    const char* ac = reinterpret_cast<const char*>(abase + int64_t(ci) * C * sk);
+    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * ra + 2u * ck2;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const char *kp, *vp, *ap;
-      tok_ptrs(ci, q, kp, vp, ap);
-      st.a[q] = *reinterpret_cast<const float4*>(ap);
-    }
+    for (int q = 0; q < 8; ++q)
+      st.a[q] = nt_f4(ac + min(oa_ + unsigned(q) * ra, lim));
   };
   auto load_k = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+    const char* kc = reinterpret_cast<const char*>(kbase + int64_t(ci) * C * sk);
+    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * rk + ck2;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const char *kp, *vp, *ap;
-      tok_ptrs(ci, q, kp, vp, ap);
-      st.k[q] = *reinterpret_cast<const uint2*>(kp);
-    }
+    for (int q = 0; q < 8; ++q)
+      st.k[q] = nt_u2(kc + min(ok_ + unsigned(q) * rk, lim));
   };
   auto load_v = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+    const char* vc = reinterpret_cast<const char*>(vbase + int64_t(ci) * C * sv);
+    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * rv + cv2;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const char *kp, *vp, *ap;
-      tok_ptrs(ci, q, kp, vp, ap);
-      st.v[q] = *reinterpret_cast<const uint2*>(vp);
-    }
+    for (int q = 0; q < 8; ++q)
+      st.v[q] = nt_u2(vc + min(ov_ + unsigned(q) * rv, lim));
   };
   auto load_all = [&](auto SET, int ci) __attribute__((always_inline)) {
     DiagRegs& st = regs[decltype(SET)::value];
+    load_v(st, ci);
     load_a(st, ci);
     load_k(st, ci);
-    load_v(st, ci);
   };
 
   // stage chunk cs from register set SET into buffer cs & 1, reloading the
@@ -666,34 +677,72 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     lane_map(r, c0, t0);
     const int lane = opaque_i(threadIdx.x) & 63;
     const int len = chunk_len(u, cs);
-    float w[4][8];
-    float gv[4];
+    // channel c0 + j: V of tokens t0 .. t0+7, zero past the end of the
+    // segment (so those tokens add nothing whatever their weights)
+    if (tail) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const unsigned m = t0 + q < len ? 0xffffffffu : 0u;
+        st.v[q].x &= m;
+        st.v[q].y &= m;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float gg[8], l[8];
+      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      unsigned pv[4];
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const unsigned v0 = (j < 2) ? st.v[q].x : st.v[q].y;
+        const unsigned v1 = (j < 2) ? st.v[q + 1].x : st.v[q + 1].y;
+        pv[q / 2] = __builtin_amdgcn_perm(v1, v0, sel);
+      }
+      *reinterpret_cast<uint4*>(Vt + ch_at<KT>(c0 + j, t0)) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
+    }
+    load_v(st, cl);
+    float w[4][8];
+    float gv[4], tot[4], pr[4];
+    // Gates of tokens past the end count as 1 (such a token keeps the state).
+    // A lane's log2 gate sum over its 8 tokens is the log2 of their product,
+    // one logarithm instead of eight, as long as the product is a normal
+    // float (every partial product is then normal too, the gates being at
+    // most 1); otherwise the whole wave takes the gates' logarithms one by one.
+    bool tiny = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const bool ok = !tail || t0 + q < len;
-        const float x = st.a[q][j];
-        gg[q] = ok ? x : 1.f;
-        l[q] = ok ? log2_gate(x) : 0.f;
+        st.a[q][j] = ok ? st.a[q][j] : 1.f;
       }
-      const float tot = ((l[0] + l[1]) + (l[2] + l[3])) + ((l[4] + l[5]) + (l[6] + l[7]));
+      pr[j] = ((st.a[0][j] * st.a[1][j]) * (st.a[2][j] * st.a[3][j])) *
+              ((st.a[4][j] * st.a[5][j]) * (st.a[6][j] * st.a[7][j]));
+      tiny |= __float_as_int(pr[j]) < 0x00800000;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) == 0, 1)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[j] = __builtin_amdgcn_logf(pr[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float l[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l[q] = log2_gate(st.a[q][j]);
+        tot[j] = ((l[0] + l[1]) + (l[2] + l[3])) + ((l[4] + l[5]) + (l[6] + l[7]));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       // sum over the rows r' >= r of the block (same lane position)
-      float incl = tot;
+      float incl = tot[j];
 #pragma unroll
       for (int s2 = 1; s2 < RW; s2 <<= 1) {
         const float o = __shfl(incl, lane + s2 * PL, 64);
         incl += (r + s2 < RW) ? o : 0.f;
       }
-      w[j][7] = exp2_w(incl - tot);  // product of the gates of later rows
+      w[j][7] = exp2_w(incl - tot[j]);  // product of the gates of later rows
 #pragma unroll
-      for (int q = 6; q >= 0; --q) w[j][q] = w[j][q + 1] * gg[q + 1];
-      if (tail) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (t0 + q >= len) w[j][q] = 0.f;
-      }
+      for (int q = 6; q >= 0; --q) w[j][q] = w[j][q + 1] * st.a[q + 1][j];
       lam[j] += incl;  // the block total on rows r == 0, which hold lambda
       gv[j] = exp2_w(incl);
     }
@@ -716,26 +765,13 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
       *reinterpret_cast<uint4*>(Kl + at) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     load_k(st, cl);
-    // channel c0 + j: V of tokens t0 .. t0+7
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      unsigned pv[4];
-#pragma unroll
-      for (int q = 0; q < 8; q += 2) {
-        const unsigned v0 = (j < 2) ? st.v[q].x : st.v[q].y;
-        const unsigned v1 = (j < 2) ? st.v[q + 1].x : st.v[q + 1].y;
-        pv[q / 2] = __builtin_amdgcn_perm(v1, v0, sel);
-      }
-      *reinterpret_cast<uint4*>(Vt + ch_at<KT>(c0 + j, t0)) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
-    }
-    load_v(st, cl);
   };
+  // One path for full and short chunks (and for the chunk past the last, which
+  // the final step stages with every token masked): a branch here makes the
+  // compiler merge the register sets at its join, and the register copies
+  // there wait for every load in flight, including the ones just issued.
   auto stage = [&](auto SET, int cs, int cl) __attribute__((always_inline)) {
-    if (chunk_len(u, cs) == C)
-      stage_t(std::false_type(), SET, cs, cl);
-    else
-      stage_t(std::true_type(), SET, cs, cl);
+    stage_t(std::true_type(), SET, cs, cl);
   };
 
   if (n > 0) {
@@ -744,15 +780,12 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     stage(I0(), 0, min(2, last));
     __syncthreads();  // chunk 0 staged
     // step j: stage chunk j+1 (register set (j+1) & 1, buffer (j+1) & 1),
-    // reloading the set with chunk j+3; one barrier
+    // reloading the set with chunk j+3; one barrier.  The last step stages
+    // the chunk past the end (every token masked: zero weights, no gate) into
+    // the buffer nobody reads any more, so every step runs the same code.
     auto step = [&](auto D, int cj) __attribute__((always_inline)) {
       using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
-      if (cj + 1 < n) {
-        stage(DN(), cj + 1, min(cj + 3, last));
-      } else {
-        // keep the load sequence of every step the same (see the header)
-        load_all(DN(), last);
-      }
+      stage(DN(), cj + 1, min(cj + 3, last));
       __syncthreads();
     };
     int cj = 0;
