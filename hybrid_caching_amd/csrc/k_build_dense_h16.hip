@@ -323,14 +323,17 @@ __device__ __forceinline__ f16x4 h4(float x0, float x1, float x2, float x3) {
 template <int NI>
 __device__ __forceinline__ void load_rows(uint4 (&pr)[NI], const __bf16* base, int HD, int len,
                                           int i0, int lane) {
-  if (len == C) {  // whole chunk: one row address, item offsets are uniform
-    const __bf16* p = base + (lane >> 4) * HD;
+  // One code path for whole and short chunks: row (lane >> 4) + 4 (i0 + i),
+  // clamped to the chunk's last row by an unsigned minimum of byte offsets
+  // (the offsets grow with the row).  With a branch here the compiler tracks
+  // the register sets' loads less precisely across the pipeline loop and
+  // waits for loads of the set issued after the one being staged.
+  const unsigned rb = unsigned(HD) * 2u;
+  const unsigned lim = unsigned(len - 1) * rb;
+  const unsigned o = unsigned((lane >> 4) + 4 * i0) * rb;
+  const char* p = reinterpret_cast<const char*>(base);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) pr[i] = gload_u4(p + 4 * (i0 + i) * HD);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) pr[i] = gload_u4(base + min((lane >> 4) + 4 * (i0 + i), len - 1) * HD);
-  }
+  for (int i = 0; i < NI; ++i) pr[i] = gload_u4(p + min(o + unsigned(4 * i) * rb, lim));
 }
 // stored position (halves) of columns 8 cg .. 8 cg + 7 of a K or V row (the
 // permutation of 16-column pieces in the header)
