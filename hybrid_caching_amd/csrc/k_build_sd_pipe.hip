@@ -635,23 +635,26 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
   const unsigned ck2 = unsigned(min(lc0, dk - 4)) * 2u, cv2 = unsigned(min(lc0, dv - 4)) * 2u;
   const unsigned ok_ = unsigned(lt0) * rk + ck2, ov_ = unsigned(lt0) * rv + cv2,
                  oa_ = unsigned(lt0) * ra + 2u * ck2;
-  auto load_a = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+  auto load_a = [&](DiagRegs& st, int cq) __attribute__((always_inline)) {
+    const int ci = min(cq, last);
     const char* ac = reinterpret_cast<const char*>(abase + int64_t(ci) * C * sk);
-    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * ra + 2u * ck2;
+    const unsigned lim = unsigned(cq > last ? 0 : chunk_len(u, ci) - 1) * ra + 2u * ck2;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       st.a[q] = nt_f4(ac + min(oa_ + unsigned(q) * ra, lim));
   };
-  auto load_k = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+  auto load_k = [&](DiagRegs& st, int cq) __attribute__((always_inline)) {
+    const int ci = min(cq, last);
     const char* kc = reinterpret_cast<const char*>(kbase + int64_t(ci) * C * sk);
-    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * rk + ck2;
+    const unsigned lim = unsigned(cq > last ? 0 : chunk_len(u, ci) - 1) * rk + ck2;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       st.k[q] = nt_u2(kc + min(ok_ + unsigned(q) * rk, lim));
   };
-  auto load_v = [&](DiagRegs& st, int ci) __attribute__((always_inline)) {
+  auto load_v = [&](DiagRegs& st, int cq) __attribute__((always_inline)) {
+    const int ci = min(cq, last);
     const char* vc = reinterpret_cast<const char*>(vbase + int64_t(ci) * C * sv);
-    const unsigned lim = unsigned(chunk_len(u, ci) - 1) * rv + cv2;
+    const unsigned lim = unsigned(cq > last ? 0 : chunk_len(u, ci) - 1) * rv + cv2;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       st.v[q] = nt_u2(vc + min(ov_ + unsigned(q) * rv, lim));
@@ -776,16 +779,18 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
 
   if (n > 0) {
     load_all(I0(), 0);
-    load_all(I1(), min(1, last));
-    stage(I0(), 0, min(2, last));
+    load_all(I1(), 1);
+    stage(I0(), 0, 2);
     __syncthreads();  // chunk 0 staged
     // step j: stage chunk j+1 (register set (j+1) & 1, buffer (j+1) & 1),
     // reloading the set with chunk j+3; one barrier.  The last step stages
     // the chunk past the end (every token masked: zero weights, no gate) into
     // the buffer nobody reads any more, so every step runs the same code.
+    // Reloads for chunks past the last read one row of the last chunk (the
+    // loads must be issued, their data is never used; one row stays cached).
     auto step = [&](auto D, int cj) __attribute__((always_inline)) {
       using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
-      stage(DN(), cj + 1, min(cj + 3, last));
+      stage(DN(), cj + 1, cj + 3);
       __syncthreads();
     };
     int cj = 0;
