@@ -237,6 +237,9 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
     // ---------------- consumers
     const int mt = wave, lane = threadIdx.x & 63;
     const bool scan_wave = wave == 0;
+    // the scan wave (products plus the weights two chunks ahead) is the
+    // busiest of the block: it issues ahead of the producer on its SIMD
+    if (scan_wave) __builtin_amdgcn_s_setprio(1);
     const float* abase = a.alpha + row0(a, u, 1);
     float areg[2] = {1.f, 1.f}, lam = 0.f;
     // gate of token `lane` of chunk ci (clamped inside the segment)
@@ -603,7 +606,9 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     return;
   }
 
-  // ---------------- producers
+  // ---------------- producers (the critical path: they issue ahead of the
+  // consumer wave that shares their SIMD)
+  __builtin_amdgcn_s_setprio(1);
   const int ptid = int(threadIdx.x) - NC * 64;
   const int pw = __builtin_amdgcn_readfirstlane(ptid >> 6);
   const int part = pw % CP, tb = pw / CP;
