@@ -487,12 +487,14 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
 // rows come by ds_bpermute.  A lane's weights are one exp2 of the sum over
 // the later rows times its own later gates.  Kw^T (hi, lo) and V^T go to LDS
 // as channel rows, one 16-byte store (8 tokens) per channel and array; the
-// 16-byte pieces of a row are XOR-swizzled by the row's 8-row group.
-// Loads: 16 lanes x 8 bytes of k or v or 16 lanes x 16 bytes of gates per
-// token row (whole 128-byte lines), nontemporal; a lane's offsets inside a
-// chunk are fixed, so an address costs one add and one clamp.  Each part of
-// a register set (v, gates, k, in the order they are staged) is reloaded as
-// soon as the staging step is done with it.  The producers' step is one
+// 16-byte pieces of a row are XOR-swizzled by the row's 8-row group.  The
+// producers stage the gates and Kw; V is loaded and staged by the consumer
+// wave of the same index with the same lane map (the producers set the pace
+// of a step, the consumers are idle for half of it).  Loads: 16 lanes x 8
+// bytes of k or v or 16 lanes x 16 bytes of gates per token row (whole
+// 128-byte lines), nontemporal; a lane's offsets inside a chunk are fixed,
+// so an address costs one add and one clamp.  Each part of a register set is
+// reloaded as soon as the staging step is done with it.  Every step is one
 // code path for every chunk (see stage below), with no branch around loads.
 template <int DP>
 struct DiagShape {
@@ -531,7 +533,7 @@ __device__ __forceinline__ uint2 nt_u2(const char* p) {
   return make_uint2(t.x, t.y);
 }
 struct DiagRegs {
-  uint2 k[8], v[8];
+  uint2 k[8];
   float4 a[8];
 };
 
@@ -558,10 +560,67 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     f32x16 S[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) S[k] = zero16();
+    // V: consumer wave w loads and stages the rows producer wave w would
+    // (the same lane map), two chunks ahead in two register sets; the
+    // consumers have the time (the producers set the pace of a step), and
+    // their loads add to the bytes in flight.
+    int vr, vc0, vt0;
+    {
+      const int lane = opaque_i(threadIdx.x) & 63;
+      vr = lane / PL;
+      vc0 = 4 * (PL * (wave % CP) + lane % PL);
+      vt0 = BT * (wave / CP) + 8 * vr;
+    }
+    const int sv = H * dv;
+    const __bf16* vbase = static_cast<const __bf16*>(a.v) + row0(a, u, dv);
+    const unsigned rv = unsigned(sv) * 2u, cv2 = unsigned(min(vc0, dv - 4)) * 2u;
+    const unsigned ov_ = unsigned(vt0) * rv + cv2;
+    uint2 vreg[2][8];
+    // chunks past the last read one row of the last chunk (data unused)
+    auto load_v = [&](auto SET, int cq) __attribute__((always_inline)) {
+      const int ci = min(cq, last);
+      const char* vc = reinterpret_cast<const char*>(vbase + int64_t(ci) * C * sv);
+      const unsigned lim = unsigned(cq > last ? 0 : chunk_len(u, ci) - 1) * rv + cv2;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        vreg[decltype(SET)::value][q] = nt_u2(vc + min(ov_ + unsigned(q) * rv, lim));
+    };
+    // V of tokens vt0 .. vt0+7 of chunk cs, channels vc0 .. vc0+3, as channel
+    // rows into buffer cs & 1; zero past the end of the segment (so those
+    // tokens add nothing whatever their weights)
+    auto stage_v = [&](auto SET, int cs) __attribute__((always_inline)) {
+      uint2(&rg)[8] = vreg[decltype(SET)::value];
+      __bf16* Vt = reinterpret_cast<__bf16*>(smem + (cs & 1) * L::TOTAL + L::VT);
+      const int len = chunk_len(u, cs);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const unsigned m = vt0 + q < len ? 0xffffffffu : 0u;
+        rg[q].x &= m;
+        rg[q].y &= m;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        unsigned pv[4];
+#pragma unroll
+        for (int q = 0; q < 8; q += 2) {
+          const unsigned v0 = (j < 2) ? rg[q].x : rg[q].y;
+          const unsigned v1 = (j < 2) ? rg[q + 1].x : rg[q + 1].y;
+          pv[q / 2] = __builtin_amdgcn_perm(v1, v0, sel);
+        }
+        *reinterpret_cast<uint4*>(Vt + ch_at<KT>(vc0 + j, vt0)) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
+      }
+    };
     if (n > 0) {
+      load_v(I0(), 0);
+      load_v(I1(), 1);
+      stage_v(I0(), 0);
+      load_v(I0(), 2);
       __syncthreads();  // chunk 0 staged
-#pragma unroll 1
-      for (int cj = 0; cj < n; ++cj) {
+      // step j: contract chunk j; stage V of chunk j+1 (set (j+1) & 1) and
+      // reload that set with chunk j+3 (one code path for every step)
+      auto cstep = [&](auto D, int cj) __attribute__((always_inline)) {
+        using DN = std::integral_constant<int, (decltype(D)::value + 1) & 1>;
         const char* sb = smem + (cj & 1) * L::TOTAL;
         const __bf16* Kh = reinterpret_cast<const __bf16*>(sb + L::KH);
         const __bf16* Kl = reinterpret_cast<const __bf16*>(sb + L::KL);
@@ -577,6 +636,8 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
 #pragma unroll
           for (int k = 0; k < NC; ++k) vb[k][ks] = lds_load8(Vt + ch_at<KT>(k * 32 + cl, 16 * ks + 8 * g));
         }
+        stage_v(DN(), cj + 1);
+        load_v(DN(), cj + 3);
 #pragma unroll
         for (int bi = 0; bi < TG; ++bi) {
           float f[16];
@@ -598,7 +659,14 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
             }
         }
         __syncthreads();
+      };
+      int cj = 0;
+#pragma unroll 1
+      for (; cj + 2 <= n; cj += 2) {
+        cstep(I0(), cj);
+        cstep(I1(), cj + 1);
       }
+      if (cj < n) cstep(I0(), cj);
     }
     write_tiles<NC>(S, a.S0 + u.unit * int64_t(dk) * dv, mt, 0, dk, dv);
     __syncthreads();  // lambda table
@@ -612,9 +680,8 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
   const int ptid = int(threadIdx.x) - NC * 64;
   const int pw = __builtin_amdgcn_readfirstlane(ptid >> 6);
   const int part = pw % CP, tb = pw / CP;
-  const int sk = H * dk, sv = H * dv;
+  const int sk = H * dk;
   const __bf16* kbase = static_cast<const __bf16*>(a.k) + row0(a, u, dk);
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + row0(a, u, dv);
   const float* abase = a.alpha + row0(a, u, dk);
   float lam[4] = {0.f, 0.f, 0.f, 0.f};
   DiagRegs regs[2];
@@ -636,10 +703,9 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
   int lr, lc0, lt0;
   lane_map(lr, lc0, lt0);
   (void)lr;
-  const unsigned rk = unsigned(sk) * 2u, rv = unsigned(sv) * 2u, ra = unsigned(sk) * 4u;
-  const unsigned ck2 = unsigned(min(lc0, dk - 4)) * 2u, cv2 = unsigned(min(lc0, dv - 4)) * 2u;
-  const unsigned ok_ = unsigned(lt0) * rk + ck2, ov_ = unsigned(lt0) * rv + cv2,
-                 oa_ = unsigned(lt0) * ra + 2u * ck2;
+  const unsigned rk = unsigned(sk) * 2u, ra = unsigned(sk) * 4u;
+  const unsigned ck2 = unsigned(min(lc0, dk - 4)) * 2u;
+  const unsigned ok_ = unsigned(lt0) * rk + ck2, oa_ = unsigned(lt0) * ra + 2u * ck2;
   auto load_a = [&](DiagRegs& st, int cq) __attribute__((always_inline)) {
     const int ci = min(cq, last);
     const char* ac = reinterpret_cast<const char*>(abase + int64_t(ci) * C * sk);
@@ -656,17 +722,8 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     for (int q = 0; q < 8; ++q)
       st.k[q] = nt_u2(kc + min(ok_ + unsigned(q) * rk, lim));
   };
-  auto load_v = [&](DiagRegs& st, int cq) __attribute__((always_inline)) {
-    const int ci = min(cq, last);
-    const char* vc = reinterpret_cast<const char*>(vbase + int64_t(ci) * C * sv);
-    const unsigned lim = unsigned(cq > last ? 0 : chunk_len(u, ci) - 1) * rv + cv2;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      st.v[q] = nt_u2(vc + min(ov_ + unsigned(q) * rv, lim));
-  };
   auto load_all = [&](auto SET, int ci) __attribute__((always_inline)) {
     DiagRegs& st = regs[decltype(SET)::value];
-    load_v(st, ci);
     load_a(st, ci);
     load_k(st, ci);
   };
@@ -685,29 +742,6 @@ __global__ __launch_bounds__(4 * DP) void build_diag_pipe_kernel(BuildArgs a) {
     lane_map(r, c0, t0);
     const int lane = opaque_i(threadIdx.x) & 63;
     const int len = chunk_len(u, cs);
-    // channel c0 + j: V of tokens t0 .. t0+7, zero past the end of the
-    // segment (so those tokens add nothing whatever their weights)
-    if (tail) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const unsigned m = t0 + q < len ? 0xffffffffu : 0u;
-        st.v[q].x &= m;
-        st.v[q].y &= m;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      unsigned pv[4];
-#pragma unroll
-      for (int q = 0; q < 8; q += 2) {
-        const unsigned v0 = (j < 2) ? st.v[q].x : st.v[q].y;
-        const unsigned v1 = (j < 2) ? st.v[q + 1].x : st.v[q + 1].y;
-        pv[q / 2] = __builtin_amdgcn_perm(v1, v0, sel);
-      }
-      *reinterpret_cast<uint4*>(Vt + ch_at<KT>(c0 + j, t0)) = make_uint4(pv[0], pv[1], pv[2], pv[3]);
-    }
-    load_v(st, cl);
     float w[4][8];
     float gv[4], tot[4], pr[4];
     // Gates of tokens past the end count as 1 (such a token keeps the state).
