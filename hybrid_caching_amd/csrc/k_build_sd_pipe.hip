@@ -292,14 +292,15 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
     for (int k = 0; k < NC; ++k) S[k] = zero16();
     float Gs = 0.f;  // S = 2^Gs S' after the chunks contracted so far
     if (n > 0) {
-      if (scan_wave) {
-        load_gate(I0(), 0);
-        load_gate(I1(), min(1, last));
-        weights(I0(), 0, 0);
-        load_gate(I0(), min(2, last));
-        weights(I1(), 1, 1);
-        load_gate(I1(), min(3, last));
-      }
+      // every consumer wave issues the gate loads (a load inside the scan
+      // wave's branch makes the compiler wait for all of them at the join);
+      // only the scan wave uses them
+      load_gate(I0(), 0);
+      load_gate(I1(), min(1, last));
+      if (scan_wave) weights(I0(), 0, 0);
+      load_gate(I0(), min(2, last));
+      if (scan_wave) weights(I1(), 1, 1);
+      load_gate(I1(), min(3, last));
       __syncthreads();  // weights of chunks 0 and 1
       __syncthreads();  // chunk 0 staged
       auto step = [&](auto D, int cj) __attribute__((always_inline)) {
@@ -348,10 +349,8 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
             S[k] = mfma32(al[ks], vb[k][ks], S[k]);
             S[k] = mfma32(ah[ks], vb[k][ks], S[k]);
           }
-        if (scan_wave) {
-          weights(D, cj + 2, (cj + 2) % 3);
-          load_gate(D, min(cj + 4, last));
-        }
+        if (scan_wave) weights(D, cj + 2, (cj + 2) % 3);
+        load_gate(D, min(cj + 4, last));
         __syncthreads();
       };
       int cj = 0;
