@@ -369,7 +369,9 @@ __global__ __launch_bounds__(4 * DP) void build_scalar_pipe_kernel(BuildArgs a) 
     return;
   }
 
-  // ---------------- producers
+  // ---------------- producers (issue ahead of the consumer waves 1..3 that
+  // share their SIMDs, like the scan wave)
+  __builtin_amdgcn_s_setprio(1);
   const int ptid = int(threadIdx.x) - NC * 64;
   const int R = ptid / GPR, i0 = 8 * (ptid % GPR);
   const int sk = H * dk, sv = H * dv;
